@@ -1,0 +1,234 @@
+"""Benchmark of the delta-W4A4 linear layer on one MI355X.
+
+One step = the whole hot path on one batch of synthetic activations already
+resident in HBM: the activation pass (cube cores, deltas, MX codes, X L1)
+followed by the forward GEMMs (core term, delta term, low-rank branch,
+broadcast, token-order fp32 output).  Prints one JSON line.
+
+value  = effective TOPS of the whole step, 2 N Ci Co / t_step (the dense
+         layer's work; the method's own work differs, see 'work' below).
+roofline = the dominant kernel (the forward GEMM over the tokens): its
+         algorithmic flops per launch / its average duration from HIP events
+         on the launch stream, against the MFMA peak of its operand types.
+cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks
+PEAK_FP4 = 10.1e15
+PEAK_FP8 = 5.0e15
+PEAK_BF16 = 2.5e15
+PEAK_HBM = 8.0e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="ffn_up_720p")
+    ap.add_argument("--cube", default=None, help="t,h,w (default: the config's first cube)")
+    ap.add_argument("--x-seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards by whole cubes "
+              "along tokens with no communication, so per-GPU throughput is the one-GPU number.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from w4a4_quantized_linear_cube_amd import dq, synth
+
+    if not os.path.exists(dq.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    dq.load()
+    cfg = synth.CONFIGS[args.config]
+    cube = tuple(int(v) for v in args.cube.split(",")) if args.cube else cfg.cubes[0]
+    xseed = cfg.x_seeds[0] if args.x_seed is None else args.x_seed
+    T, H, W, Ci, Co, r = cfg.T, cfg.H, cfg.W, cfg.Ci, cfg.Co, cfg.rank
+    N = cfg.N
+    dev = torch.device("cuda:0")
+    print(f"[bench] {cfg.name} N={N} Ci={Ci} Co={Co} cube={cube} r={r}: preparing", file=sys.stderr, flush=True)
+
+    wt = synth.config_weight(cfg)
+    weights = dq.dq_prepare_weights(wt, r, seed=cfg.w_seed, device=0)
+    qa = dq.dq_qact_create(weights, (T, H, W) + cube)
+    x = synth.make_activation(T, H, W, Ci, seed=xseed, dtype=cfg.dtype, n_outliers=cfg.n_outliers, device="cuda")
+    y = torch.empty(N, Co, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    # derived sizes of the method's work
+    t_, h_, w_ = cube
+    Tc, Hc, Wc = -(-T // t_), -(-H // h_), -(-W // w_)
+    K = Tc * Hc * Wc
+    S = t_ * h_ * w_
+    dense_flops = 2.0 * N * Ci * Co
+    f_fp4 = 2.0 * N * Ci * Co            # delta term, one row per token
+    f_fp8 = 2.0 * K * Ci * Co            # core term, one row per cube
+    f_bf16 = 2.0 * N * r * (Ci + Co)     # low-rank branch
+    xbytes = 2 if cfg.dtype == "bf16" else 4
+    quant_bytes = N * Ci * xbytes * (2 if S > 64 else 1) + N * Ci * (0.5 + 1 / 32) + K * Ci * (1 + 1 / 32) + 2 * N * r
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        dq.dq_linear(weights, x, qa, y, stream)
+    torch.cuda.synchronize()
+
+    # timed steps; per-phase events on the launch stream
+    t_quant, t_fwd = [], []
+    start = ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    marks = []
+    for _ in range(args.steps):
+        a, b, c = ev(), ev(), ev()
+        a.record(stream)
+        dq.dq_quantize_act(weights, x, qa, stream)
+        b.record(stream)
+        dq.dq_linear_forward(weights, qa, y, stream)
+        c.record(stream)
+        marks.append((a, b, c))
+    end = ev()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    for a, b, c in marks:
+        t_quant.append(a.elapsed_time(b))
+        t_fwd.append(b.elapsed_time(c))
+    ms_step = total_ms / args.steps
+    q_ms = float(np.mean(t_quant))
+    f_ms = float(np.mean(t_fwd))
+
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {nbytes} bytes read, {nbytes} bytes written", file=sys.stderr, flush=True)
+
+    value = dense_flops / (ms_step * 1e-3) / 1e12
+    fwd_flops = f_fp4 + f_fp8 + f_bf16
+    t_min_fwd = f_fp4 / PEAK_FP4 + f_fp8 / PEAK_FP8 + f_bf16 / PEAK_BF16
+    peak_mix = fwd_flops / t_min_fwd
+    achieved = fwd_flops / (f_ms * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, cube, x, weights, dq, args.cpu_tokens)
+
+    out = {
+        "metric": "effective TOPS of fused delta-W4A4 linear + % of MI355X FP4 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (deltas, R) + mxfp8 (cores) + bf16 (low rank), fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: X {N}x{Ci} ({T}x{H}x{W} tokens) {cfg.dtype} -> Y {N}x{Co} fp32, "
+                        f"cube {t_}x{h_}x{w_}, rank {r}",
+            "tokens": N, "Ci": Ci, "Co": Co, "cube": list(cube), "rank": r, "cubes": K,
+        },
+        "pct_fp4_peak_step": round(100 * dense_flops / (ms_step * 1e-3) / PEAK_FP4, 2),
+        "forward": {
+            "ms": round(f_ms, 4),
+            "effective_tops": round(dense_flops / (f_ms * 1e-3) / 1e12, 2),
+            "pct_fp4_peak": round(100 * dense_flops / (f_ms * 1e-3) / PEAK_FP4, 2),
+        },
+        "quantize": {
+            "ms": round(q_ms, 4),
+            "algorithmic_bytes": int(quant_bytes),
+            "GBps": round(quant_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "pct_hbm": round(100 * quant_bytes / (q_ms * 1e-3) / PEAK_HBM, 2),
+        },
+        "roofline": {
+            "kernel": "forward GEMMs (core term + delta term + low-rank branch + store)",
+            "bound": "mfma",
+            "achieved": round(achieved / 1e12, 2),
+            "peak": round(peak_mix / 1e12, 2),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak_mix, 4),
+            "traffic": None,
+            "work": {"fp4_flops": f_fp4, "fp8_flops": f_fp8, "bf16_flops": f_bf16},
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
+    """The oracle, as it stands, on a bounded sample: whole cubes covering
+    about n_tokens tokens, quantized and pushed through the layer on the host
+    (weights prepared beforehand and not timed, as on the GPU)."""
+    import numpy as np
+
+    from oracle import cubes, layer, lowrank
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    e = dq.dq_weights_export(weights)
+    l1, l2 = e["l1"], e["l2"]
+    wf = None
+    g = cubes.Geometry(cfg.T, cfg.H, cfg.W, *cube)
+    rng = np.random.default_rng(0)
+    n_cubes = max(1, n_tokens // g.S)
+    ids = np.sort(rng.choice(g.K, size=min(n_cubes, g.K), replace=False))
+    tbl, _ = cubes.cube_tokens(g, ids)
+    toks = np.sort(tbl[tbl >= 0])
+    if len(toks) > 4 * n_tokens:
+        toks = toks[:n_tokens]
+    # activation rows the sample touches, from the device copy of the input
+    import torch
+    xf = np.zeros((cfg.N, cfg.Ci), dtype=np.float32)
+    need = torch.from_numpy(np.unique(tbl[tbl >= 0])).to(x.device)
+    xf[need.cpu().numpy()] = x.index_select(0, need).float().cpu().numpy()
+    rc, rs = e["rcodes"], e["rscales"]
+    t0 = time.perf_counter()
+    q = layer.quantize_activation(xf, g, l1, cube_ids=ids, tokens=toks)
+    yo = layer.forward(q, g, rc, rs, l2)
+    dt = time.perf_counter() - t0
+    n = len(q["tokens"])
+    return {
+        "value": round(2.0 * n * cfg.Ci * cfg.Co / dt / 1e12, 6),
+        "unit": "TOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(ids)} whole cubes ({n} tokens) of the same layer: activation pass + forward, "
+                  f"{dt:.2f} s wall",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * dq.h -- C ABI of the delta-W4A4 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one of the DeltaQuant notes ("DeltaQuant: 4-bit Video
+ * Diffusion Models with Spatiotemporal Delta Smoothing", papernotes.org,
+ * CVPR 2026), section 方法详解:
+ *
+ *   Y = X L1 L2  +  bcast_k( Q8(core_k) Q4(R) )  +  Q4(delta) Q4(R)
+ *
+ * with X in R^{N x Ci} the flattened (T, H, W) token grid, W = L1 L2 + R an
+ * SVD split of the weight (关键设计 4, the three-term equation), core_k the
+ * mean token of the t x h x w cube k (关键设计 2 and 3, the core/delta
+ * equation), delta = X - core, Q8 = MX-FP8 (E4M3) and Q4 = MX-FP4 (E2M1),
+ * both with one power-of-two E8M0 scale per 32 consecutive channels (关键设计
+ * 4, the quantizer definition, q_max = 6 for FP4 and 448 for FP8).  The core
+ * term is computed once per cube and broadcast to the cube's tokens (the
+ * "dynamic token bias" of 关键设计 4).
+ *
+ * Conventions
+ *  - Pointers named *_host are host memory; *_dev are device memory of the
+ *    handle's device.  Caller-owned buffers are never freed or kept by the
+ *    library beyond the call (device buffers may be read asynchronously by
+ *    work enqueued on the given stream, so keep them alive until it completes).
+ *  - Matrices are dense and row-major.  The weight is given as W^T, i.e. the
+ *    nn.Linear layout [Co][Ci]; token n of X is (t, h, w) with
+ *    n = (t*H + h)*W + w.
+ *  - FP4 codes are packed two per byte, the even channel in the low nibble.
+ *    E8M0 scale codes are e + 127 for a scale of 2^e.
+ *  - Every function validates its arguments first and returns a status; on
+ *    failure nothing has been enqueued and outputs are untouched.  Device
+ *    faults of enqueued work surface at the caller's next synchronisation.
+ *    dq_last_error() gives a message for the last failure on this thread.
+ *  - Streams are hipStream_t values passed as void*; NULL is the null stream.
+ *  - All allocation happens in dq_prepare_weights* and dq_qact_create; the
+ *    hot calls (dq_quantize_act, dq_linear_forward, dq_linear) allocate
+ *    nothing.
+ *  - A dq_weights is read-only after preparation and may be shared by
+ *    streams; a dq_qact must not be used by two streams at once.
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DQ_OK = 0,
+    DQ_ERR_INVALID_ARG = 1,   /* null pointer, unknown dtype, bad rank, ... */
+    DQ_ERR_SHAPE = 2,         /* Ci % 32 != 0, cube larger than the grid, size overflow */
+    DQ_ERR_UNSUPPORTED = 3,   /* device is not gfx950 */
+    DQ_ERR_OUT_OF_MEMORY = 4, /* device or host allocation failed */
+    DQ_ERR_DEVICE = 5         /* a HIP runtime call failed */
+} dq_status;
+
+typedef enum { DQ_F32 = 0, DQ_BF16 = 1 } dq_dtype;
+
+/* Token grid T x H x W and cube t x h x w (1 <= t <= T, 1 <= h <= H,
+ * 1 <= w <= W).  Cubes tile the grid from the origin; cubes at the high end
+ * of an axis that does not divide evenly are clipped, and their core is the
+ * mean of the tokens they hold.  t = T, h = H, w = W is one global cube. */
+typedef struct {
+    int32_t T, H, W;
+    int32_t t, h, w;
+} dq_geom;
+
+typedef struct dq_weights dq_weights;   /* prepared weight: Q4(R), L1, L2 on one device */
+typedef struct dq_qact dq_qact;         /* per-geometry activation workspace on one device */
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* dq_last_error(void);
+const char* dq_status_str(dq_status s);
+
+/* Low-rank factors of W by a truncated SVD on the host (关键设计 4: the split
+ * W = L1 L2 + R borrowed from SVDQuant).  Randomized subspace iteration with
+ * a Gaussian test matrix drawn from `seed`; L1 = U_r sqrt(S_r) and
+ * L2 = sqrt(S_r) V_r^T, each rounded to bf16 (nearest, ties to even).
+ *   w_host   [Co][Ci] W^T, dtype dt
+ *   l1_host  out, [Ci][rank] bf16 bits;  l2_host  out, [rank][Co] bf16 bits
+ * rank 0 is allowed (no low-rank branch; nothing written).  Host only: no
+ * device is touched.  Errors: DQ_ERR_INVALID_ARG for null pointers or
+ * rank > min(Ci, Co); DQ_ERR_SHAPE for Ci or Co < 1. */
+dq_status dq_lowrank_factors(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                             uint64_t seed, uint16_t* l1_host, uint16_t* l2_host);
+
+/* Prepare a weight from given bf16 factors.  On `device` it forms
+ * R^T = fl32(W^T - (L1 L2)^T), the product of every entry summed in fp64 in
+ * rank order, then MX-FP4-encodes each output channel of R along Ci.
+ *   w_host   [Co][Ci] W^T (dtype dt);  l1_host [Ci][rank], l2_host [rank][Co]
+ *            bf16 bits (may be NULL when rank == 0)
+ * Requires Ci % 32 == 0, Ci >= 32, Co >= 1, 0 <= rank <= min(Ci, Co).
+ * The handle owns every device buffer it allocates; free it with
+ * dq_weights_destroy.  Synchronous (returns when the weight is ready). */
+dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                                     const uint16_t* l1_host, const uint16_t* l2_host, int32_t device,
+                                     dq_weights** out);
+
+/* dq_lowrank_factors followed by dq_prepare_weights_lowrank. */
+dq_status dq_prepare_weights(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                             uint64_t seed, int32_t device, dq_weights** out);
+
+void dq_weights_destroy(dq_weights* w);
+
+/* Sizes of a prepared weight (any pointer may be NULL). */
+dq_status dq_weights_info(const dq_weights* w, int64_t* Ci, int64_t* Co, int32_t* rank, int32_t* device);
+
+/* Copy the prepared weight to the host in canonical layout (any pointer may
+ * be NULL): L1 [Ci][rank] and L2 [rank][Co] bf16 bits, R^T [Co][Ci] fp32,
+ * Q4(R) codes [Co][Ci/2] and scale codes [Co][Ci/32].  Synchronous. */
+dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2_host, float* r_host,
+                            uint8_t* rcodes_host, uint8_t* rscales_host);
+
+/* Workspace for activations of one geometry: delta codes and scales, core
+ * codes and scales, U = bf16(bf16(X) L1), and (for cube shapes that need it)
+ * the per-cube core term.  Owns its device buffers (sized from the geometry,
+ * Ci, Co and the rank of `w`); free with dq_qact_destroy.  Errors:
+ * DQ_ERR_SHAPE for an invalid geometry or size overflow. */
+dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out);
+void dq_qact_destroy(dq_qact* q);
+
+/* Sizes of a workspace (any pointer may be NULL): tokens N, cubes K, and the
+ * device bytes it holds. */
+dq_status dq_qact_info(const dq_qact* q, int64_t* N, int64_t* K, int64_t* device_bytes);
+
+/* The activation pass (关键设计 2-4, and the implementation paragraph of
+ * 损失函数/训练策略, which fuses core generation into activation
+ * quantization): for every cube, core = fl32(fp32 sum of its tokens in
+ * lexicographic (dt, dh, dw) order, in blocks of 64, / count); for every
+ * token, delta = fl32(x - core); cores -> MX-FP8, deltas -> MX-FP4 (smallest
+ * power-of-two scale with max|v| <= q_max 2^e, round to nearest even); and
+ * U = bf16(bf16(X) L1) with fp32 accumulation.
+ *   x_dev  [N][Ci] of dtype dt, N = T*H*W of the workspace's geometry.
+ * Asynchronous on `stream`. */
+dq_status dq_quantize_act(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, void* stream);
+
+/* The GEMMs (关键设计 4, the three-term equation): for every token n of cube
+ * k, y[n] = U[n] L2 + Q8(core_k) Q4(R) + Q4(delta_n) Q4(R), fp32 accumulation,
+ * written to y_dev [N][Co] fp32 (every element written).  Uses the state left
+ * in `q` by the last dq_quantize_act.  Asynchronous on `stream`. */
+dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
+
+/* dq_quantize_act followed by dq_linear_forward on the same stream. */
+dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, float* y_dev, void* stream);
+
+/* Copy the state of the last dq_quantize_act to the host in canonical token
+ * order (any pointer may be NULL): delta codes [N][Ci/2], delta scale codes
+ * [N][Ci/32], core codes [K][Ci] (FP8 E4M3), core scale codes [K][Ci/32],
+ * U [N][rank] bf16 bits.  Synchronises `stream` first. */
+dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscales_host, uint8_t* ccodes_host,
+                         uint8_t* cscales_host, uint16_t* u_host, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DQ_H */

@@ -15,11 +15,15 @@ import numpy as np
 from . import cubes, mx
 
 
-def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray, cube_ids=None) -> dict:
+def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray, cube_ids=None, tokens=None) -> dict:
     """What the activation pass produces, for the given cubes (all by default).
 
+    Cores are always formed from every token of a cube; deltas and U are
+    formed for `tokens` (default: all tokens of the given cubes), which must
+    lie in those cubes.
+
     Returns a dict with
-      cube_ids [k]; tokens [n] (the cubes' tokens, ascending);
+      cube_ids [k]; tokens [n] (ascending);
       core [k, Ci] fp32; core_codes [k, Ci] and core_scales [k, Ci/32] (FP8);
       delta [n, Ci] fp32; delta_codes [n, Ci/2] packed and delta_scales
       [n, Ci/32] (FP4); U [n, r] bf16 bits.
@@ -27,8 +31,13 @@ def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray,
     x32 = np.asarray(x32, dtype=np.float32)
     ids = np.arange(g.K, dtype=np.int64) if cube_ids is None else np.asarray(cube_ids, dtype=np.int64)
     core = cubes.cube_core(x32, g, ids)
-    tbl, _ = cubes.cube_tokens(g, ids)
-    tokens = np.sort(tbl[tbl >= 0])
+    if tokens is None:
+        tbl, _ = cubes.cube_tokens(g, ids)
+        tokens = np.sort(tbl[tbl >= 0])
+    else:
+        tokens = np.sort(np.asarray(tokens, dtype=np.int64))
+        if not np.all(np.isin(cubes.cube_of_token(g, tokens), ids)):
+            raise ValueError("tokens outside the given cubes")
     row_of_cube = np.full(g.K, -1, dtype=np.int64)
     row_of_cube[ids] = np.arange(len(ids))
     delta = cubes.cube_delta(x32, core, g, tokens, row_of_cube)

@@ -1,0 +1,451 @@
+// C ABI of the delta-W4A4 layer: argument checks, handle ownership, device
+// buffers, launches.  Every arithmetic step of the layer runs in the HIP
+// kernels of quant.hip and gemm.hip; the host SVD of svd.cpp only produces
+// the low-rank factors.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <memory>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dq.h"
+#include "dq_internal.h"
+
+namespace dq {
+
+void lowrank_svd(const float* wt, int64_t Ci, int64_t Co, int rank, uint64_t seed, uint16_t* l1, uint16_t* l2);
+
+namespace {
+thread_local std::string g_last_error;
+
+dq_status fail(dq_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+// Makes the handle's device current for the scope and restores the caller's.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+dq_status check_device(int device) {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return fail(DQ_ERR_DEVICE, "no HIP device available");
+    if (device < 0 || device >= n) return fail(DQ_ERR_INVALID_ARG, "device index out of range");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return fail(DQ_ERR_DEVICE, "hipGetDeviceProperties failed");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(DQ_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", gfx950 required");
+    return DQ_OK;
+}
+
+dq_status hip_fail(hipError_t e, const char* what) {
+    if (e == hipErrorOutOfMemory) return fail(DQ_ERR_OUT_OF_MEMORY, std::string(what) + ": out of device memory");
+    return fail(DQ_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Zero-filled device allocation.
+template <class T>
+hipError_t dalloc(T** p, size_t count, size_t* total) {
+    *p = nullptr;
+    if (count == 0) return hipSuccess;
+    size_t bytes = count * sizeof(T);
+    hipError_t e = hipMalloc((void**)p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return e;
+    }
+    *total += bytes;
+    return hipMemset(*p, 0, bytes);
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a >= 0 && b >= 0 && (a == 0 || b <= limit / a); }
+
+void free_weights(dq_weights* w) {
+    if (!w) return;
+    DeviceGuard dg(w->device);
+    (void)hipFree(w->rq);
+    (void)hipFree(w->rs);
+    (void)hipFree(w->r);
+    (void)hipFree(w->l1t);
+    (void)hipFree(w->l2t);
+    delete w;
+}
+
+void free_qact(dq_qact* q) {
+    if (!q) return;
+    DeviceGuard dg(q->device);
+    (void)hipFree(q->dq);
+    (void)hipFree(q->ds);
+    (void)hipFree(q->cq);
+    (void)hipFree(q->cs);
+    (void)hipFree(q->u);
+    (void)hipFree(q->bias);
+    (void)hipFree(q->coref);
+    (void)hipFree(q->part);
+    delete q;
+}
+
+long long host_slot_token(const Geom& g, long long slot) {
+    long long k = slot / g.S;
+    int s = (int)(slot - k * g.S);
+    int dw = s % g.w, dh = (s / g.w) % g.h, dt = s / (g.w * g.h);
+    long long kw = k % g.Wc, kh = (k / g.Wc) % g.Hc, kt = k / ((long long)g.Wc * g.Hc);
+    long long ti = kt * g.t + dt, hi = kh * g.h + dh, wi = kw * g.w + dw;
+    if (k >= g.K || ti >= g.T || hi >= g.H || wi >= g.W) return -1;
+    return (ti * g.H + hi) * g.W + wi;
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+}  // namespace dq
+
+using namespace dq;
+
+extern "C" {
+
+const char* dq_last_error(void) { return g_last_error.c_str(); }
+
+const char* dq_status_str(dq_status s) {
+    switch (s) {
+        case DQ_OK: return "ok";
+        case DQ_ERR_INVALID_ARG: return "invalid argument";
+        case DQ_ERR_SHAPE: return "invalid shape";
+        case DQ_ERR_UNSUPPORTED: return "unsupported device";
+        case DQ_ERR_OUT_OF_MEMORY: return "out of memory";
+        case DQ_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+dq_status dq_lowrank_factors(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank, uint64_t seed,
+                             uint16_t* l1_host, uint16_t* l2_host) {
+    g_last_error.clear();
+    if (Ci < 1 || Co < 1) return fail(DQ_ERR_SHAPE, "Ci and Co must be >= 1");
+    if (!mul_ok(Ci, Co, std::numeric_limits<int64_t>::max() / 8)) return fail(DQ_ERR_SHAPE, "Ci * Co overflows");
+    if (!w_host) return fail(DQ_ERR_INVALID_ARG, "w_host is NULL");
+    if (dt != DQ_F32 && dt != DQ_BF16) return fail(DQ_ERR_INVALID_ARG, "unknown dtype");
+    if (rank < 0 || rank > std::min(Ci, Co)) return fail(DQ_ERR_INVALID_ARG, "rank must be in [0, min(Ci, Co)]");
+    if (rank == 0) return DQ_OK;
+    if (!l1_host || !l2_host) return fail(DQ_ERR_INVALID_ARG, "factor output is NULL");
+    std::vector<float> wf;
+    const float* wt = (const float*)w_host;
+    try {
+        if (dt == DQ_BF16) {
+            wf.resize((size_t)(Ci * Co));
+            const uint16_t* b = (const uint16_t*)w_host;
+            for (size_t i = 0; i < wf.size(); ++i) {
+                uint32_t u = (uint32_t)b[i] << 16;
+                std::memcpy(&wf[i], &u, 4);
+            }
+            wt = wf.data();
+        }
+        lowrank_svd(wt, Ci, Co, rank, seed, l1_host, l2_host);
+    } catch (const std::bad_alloc&) {
+        return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    return DQ_OK;
+}
+
+dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                                     const uint16_t* l1_host, const uint16_t* l2_host, int32_t device,
+                                     dq_weights** out) {
+    g_last_error.clear();
+    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w_host) return fail(DQ_ERR_INVALID_ARG, "w_host is NULL");
+    if (dt != DQ_F32 && dt != DQ_BF16) return fail(DQ_ERR_INVALID_ARG, "unknown dtype");
+    if (Ci < 32 || Ci % 32 != 0) return fail(DQ_ERR_SHAPE, "Ci must be a positive multiple of 32");
+    if (Co < 1) return fail(DQ_ERR_SHAPE, "Co must be >= 1");
+    if (Ci > (1 << 24) || Co > (1 << 24)) return fail(DQ_ERR_SHAPE, "Ci and Co must be <= 2^24");
+    if (rank < 0 || rank > std::min(Ci, Co)) return fail(DQ_ERR_INVALID_ARG, "rank must be in [0, min(Ci, Co)]");
+    if (rank > 128) return fail(DQ_ERR_INVALID_ARG, "rank must be <= 128");
+    if (rank > 0 && (!l1_host || !l2_host)) return fail(DQ_ERR_INVALID_ARG, "factors are NULL");
+    dq_status st = check_device(device);
+    if (st != DQ_OK) return st;
+    DeviceGuard dg(device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+
+    auto* w = new (std::nothrow) dq_weights();
+    if (!w) return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    std::unique_ptr<dq_weights, void (*)(dq_weights*)> guard(w, free_weights);
+    w->device = device;
+    w->Ci = Ci;
+    w->Co = Co;
+    w->rank = rank;
+    w->rp = (int)round_up(rank, RPAD);
+    w->Kp = round_up(Ci, KPAD);
+    w->Cop = round_up(Co, NPAD);
+    const size_t esz = dt == DQ_BF16 ? 2 : 4;
+
+    void* wdev = nullptr;
+    uint16_t *l1d = nullptr, *l2d = nullptr;
+    size_t scratch = 0;
+    hipError_t e = hipSuccess;
+    auto cleanup = [&]() {
+        (void)hipFree(wdev);
+        (void)hipFree(l1d);
+        (void)hipFree(l2d);
+    };
+    try {
+        w->l1.assign(l1_host ? l1_host : (const uint16_t*)nullptr, l1_host ? l1_host + Ci * rank : nullptr);
+        w->l2.assign(l2_host ? l2_host : (const uint16_t*)nullptr, l2_host ? l2_host + (int64_t)rank * Co : nullptr);
+    } catch (const std::bad_alloc&) {
+        return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    if ((e = hipMalloc(&wdev, (size_t)(Ci * Co) * esz)) != hipSuccess) { cleanup(); return hip_fail(e, "hipMalloc W"); }
+    if ((e = hipMemcpy(wdev, w_host, (size_t)(Ci * Co) * esz, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(e, "copy W"); }
+    if (rank > 0) {
+        if ((e = dalloc(&l1d, (size_t)(Ci * rank), &scratch)) != hipSuccess ||
+            (e = dalloc(&l2d, (size_t)(rank * Co), &scratch)) != hipSuccess) { cleanup(); return hip_fail(e, "hipMalloc factors"); }
+        if ((e = hipMemcpy(l1d, l1_host, (size_t)(Ci * rank) * 2, hipMemcpyHostToDevice)) != hipSuccess ||
+            (e = hipMemcpy(l2d, l2_host, (size_t)(rank * Co) * 2, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(e, "copy factors"); }
+    }
+    if ((e = dalloc(&w->r, (size_t)(Ci * Co), &w->bytes)) != hipSuccess ||
+        (e = dalloc(&w->rq, (size_t)(w->Cop * w->Kp / 2), &w->bytes)) != hipSuccess ||
+        (e = dalloc(&w->rs, (size_t)(w->Cop * w->Kp / 32), &w->bytes)) != hipSuccess) { cleanup(); return hip_fail(e, "hipMalloc weight"); }
+    if ((e = launch_residual(wdev, dt == DQ_BF16, l1d, l2d, Ci, Co, rank, w->r, nullptr)) != hipSuccess) { cleanup(); return hip_fail(e, "residual kernel"); }
+    if ((e = launch_encode_fp4_rows(w->r, Co, Ci, Ci, w->rq, w->Kp / 2, w->rs, w->Kp / 32, nullptr)) != hipSuccess) { cleanup(); return hip_fail(e, "encode kernel"); }
+    if (w->rp > 0) {
+        std::vector<uint16_t> l1t((size_t)(w->rp * w->Kp), 0), l2t((size_t)(w->Cop * w->rp), 0);
+        for (int64_t c = 0; c < Ci; ++c)
+            for (int q = 0; q < rank; ++q) l1t[(size_t)(q * w->Kp + c)] = l1_host[c * rank + q];
+        for (int q = 0; q < rank; ++q)
+            for (int64_t j = 0; j < Co; ++j) l2t[(size_t)(j * w->rp + q)] = l2_host[(int64_t)q * Co + j];
+        if ((e = dalloc(&w->l1t, l1t.size(), &w->bytes)) != hipSuccess ||
+            (e = dalloc(&w->l2t, l2t.size(), &w->bytes)) != hipSuccess) { cleanup(); return hip_fail(e, "hipMalloc factors"); }
+        if ((e = hipMemcpy(w->l1t, l1t.data(), l1t.size() * 2, hipMemcpyHostToDevice)) != hipSuccess ||
+            (e = hipMemcpy(w->l2t, l2t.data(), l2t.size() * 2, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(e, "copy factors"); }
+    }
+    if ((e = hipDeviceSynchronize()) != hipSuccess) { cleanup(); return hip_fail(e, "weight preparation"); }
+    cleanup();
+    *out = guard.release();
+    return DQ_OK;
+}
+
+dq_status dq_prepare_weights(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank, uint64_t seed,
+                             int32_t device, dq_weights** out) {
+    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (Ci < 1 || Co < 1) return fail(DQ_ERR_SHAPE, "Ci and Co must be >= 1");
+    if (rank < 0 || rank > std::min(Ci, Co)) return fail(DQ_ERR_INVALID_ARG, "rank must be in [0, min(Ci, Co)]");
+    std::vector<uint16_t> l1, l2;
+    try {
+        l1.resize((size_t)(Ci * rank));
+        l2.resize((size_t)(rank * Co));
+    } catch (const std::bad_alloc&) {
+        return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    dq_status st = dq_lowrank_factors(w_host, dt, Ci, Co, rank, seed, l1.data(), l2.data());
+    if (st != DQ_OK) return st;
+    return dq_prepare_weights_lowrank(w_host, dt, Ci, Co, rank, l1.data(), l2.data(), device, out);
+}
+
+void dq_weights_destroy(dq_weights* w) { free_weights(w); }
+
+dq_status dq_weights_info(const dq_weights* w, int64_t* Ci, int64_t* Co, int32_t* rank, int32_t* device) {
+    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    if (Ci) *Ci = w->Ci;
+    if (Co) *Co = w->Co;
+    if (rank) *rank = w->rank;
+    if (device) *device = w->device;
+    return DQ_OK;
+}
+
+dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2_host, float* r_host,
+                            uint8_t* rcodes_host, uint8_t* rscales_host) {
+    g_last_error.clear();
+    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    DeviceGuard dg(w->device);
+    if (l1_host && w->rank) std::memcpy(l1_host, w->l1.data(), w->l1.size() * 2);
+    if (l2_host && w->rank) std::memcpy(l2_host, w->l2.data(), w->l2.size() * 2);
+    hipError_t e;
+    if (r_host && (e = hipMemcpy(r_host, w->r, (size_t)(w->Ci * w->Co) * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_fail(e, "copy R");
+    if (rcodes_host) {
+        e = hipMemcpy2D(rcodes_host, (size_t)(w->Ci / 2), w->rq, (size_t)(w->Kp / 2), (size_t)(w->Ci / 2), (size_t)w->Co,
+                        hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "copy R codes");
+    }
+    if (rscales_host) {
+        e = hipMemcpy2D(rscales_host, (size_t)(w->Ci / 32), w->rs, (size_t)(w->Kp / 32), (size_t)(w->Ci / 32),
+                        (size_t)w->Co, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "copy R scales");
+    }
+    return DQ_OK;
+}
+
+dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
+    g_last_error.clear();
+    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    const dq_geom& G = geom;
+    if (G.T < 1 || G.H < 1 || G.W < 1) return fail(DQ_ERR_SHAPE, "T, H, W must be >= 1");
+    if (G.t < 1 || G.t > G.T || G.h < 1 || G.h > G.H || G.w < 1 || G.w > G.W)
+        return fail(DQ_ERR_SHAPE, "cube extents must satisfy 1 <= t <= T, 1 <= h <= H, 1 <= w <= W");
+    const int64_t lim = int64_t(1) << 40;
+    int64_t N = (int64_t)G.T * G.H * G.W;
+    int Tc = (G.T + G.t - 1) / G.t, Hc = (G.H + G.h - 1) / G.h, Wc = (G.W + G.w - 1) / G.w;
+    int64_t K = (int64_t)Tc * Hc * Wc;
+    int64_t S = (int64_t)G.t * G.h * G.w;
+    if (N > (int64_t(1) << 31) || !mul_ok(K, S, lim)) return fail(DQ_ERR_SHAPE, "token grid too large");
+    int64_t Nslot = K * S;
+    if (Nslot > (int64_t(1) << 31)) return fail(DQ_ERR_SHAPE, "slot count too large");
+    DeviceGuard dg(w->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+
+    auto* q = new (std::nothrow) dq_qact();
+    if (!q) return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    std::unique_ptr<dq_qact, void (*)(dq_qact*)> guard(q, free_qact);
+    q->device = w->device;
+    q->Ci = w->Ci;
+    q->Co = w->Co;
+    q->Kp = w->Kp;
+    q->Cop = w->Cop;
+    q->rp = w->rp;
+    q->rank = w->rank;
+    q->g = Geom{G.T, G.H, G.W, G.t, G.h, G.w, Tc, Hc, Wc, (int)S, (long long)N, (long long)K, (long long)Nslot};
+    q->Nslot_pad = round_up(Nslot, MPAD);
+    q->K_pad = round_up(K, MPAD);
+    q->core_mode = S <= 64 ? 0 : 1;
+    q->nblk = (S + CORE_BLOCK - 1) / CORE_BLOCK;
+    if (!mul_ok(q->Nslot_pad, q->Kp, lim) || !mul_ok(q->K_pad, q->Cop, lim) || !mul_ok(K * q->nblk, q->Kp, lim))
+        return fail(DQ_ERR_SHAPE, "workspace too large");
+    hipError_t e;
+    if ((e = dalloc(&q->dq, (size_t)(q->Nslot_pad * q->Kp / 2), &q->bytes)) != hipSuccess ||
+        (e = dalloc(&q->ds, (size_t)(q->Nslot_pad * q->Kp / 32), &q->bytes)) != hipSuccess ||
+        (e = dalloc(&q->cq, (size_t)(q->K_pad * q->Kp), &q->bytes)) != hipSuccess ||
+        (e = dalloc(&q->cs, (size_t)(q->K_pad * q->Kp / 32), &q->bytes)) != hipSuccess ||
+        (e = dalloc(&q->u, (size_t)(q->Nslot_pad * q->rp), &q->bytes)) != hipSuccess ||
+        (e = dalloc(&q->bias, (size_t)(q->K_pad * q->Cop), &q->bytes)) != hipSuccess)
+        return hip_fail(e, "hipMalloc workspace");
+    if (q->core_mode == 1) {
+        if ((e = dalloc(&q->coref, (size_t)(K * q->Kp), &q->bytes)) != hipSuccess ||
+            (e = dalloc(&q->part, (size_t)(K * q->nblk * q->Kp), &q->bytes)) != hipSuccess)
+            return hip_fail(e, "hipMalloc workspace");
+    }
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "workspace init");
+    *out = guard.release();
+    return DQ_OK;
+}
+
+void dq_qact_destroy(dq_qact* q) { free_qact(q); }
+
+dq_status dq_qact_info(const dq_qact* q, int64_t* N, int64_t* K, int64_t* device_bytes) {
+    if (!q) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    if (N) *N = q->g.N;
+    if (K) *K = q->g.K;
+    if (device_bytes) *device_bytes = (int64_t)q->bytes;
+    return DQ_OK;
+}
+
+static dq_status check_pair(const dq_weights* w, const dq_qact* q) {
+    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    if (!q) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    if (q->Ci != w->Ci || q->Co != w->Co || q->rp != w->rp || q->device != w->device)
+        return fail(DQ_ERR_INVALID_ARG, "workspace was created for a different weight");
+    return DQ_OK;
+}
+
+dq_status dq_quantize_act(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, void* stream) {
+    g_last_error.clear();
+    dq_status st = check_pair(w, q);
+    if (st != DQ_OK) return st;
+    if (!x_dev) return fail(DQ_ERR_INVALID_ARG, "x_dev is NULL");
+    if (((uintptr_t)x_dev) % 16 != 0) return fail(DQ_ERR_INVALID_ARG, "x_dev must be 16-byte aligned");
+    if (dt != DQ_F32 && dt != DQ_BF16) return fail(DQ_ERR_INVALID_ARG, "unknown dtype");
+    DeviceGuard dg(q->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = launch_quantize(w, x_dev, dt == DQ_BF16, q, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "activation pass launch");
+    return DQ_OK;
+}
+
+dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {
+    g_last_error.clear();
+    dq_status st = check_pair(w, q);
+    if (st != DQ_OK) return st;
+    if (!y_dev) return fail(DQ_ERR_INVALID_ARG, "y_dev is NULL");
+    if (((uintptr_t)y_dev) % 4 != 0) return fail(DQ_ERR_INVALID_ARG, "y_dev must be 4-byte aligned");
+    DeviceGuard dg(q->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = launch_forward(w, q, y_dev, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return DQ_OK;
+}
+
+dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, float* y_dev, void* stream) {
+    dq_status st = dq_quantize_act(w, x_dev, dt, q, stream);
+    if (st != DQ_OK) return st;
+    return dq_linear_forward(w, q, y_dev, stream);
+}
+
+dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscales_host, uint8_t* ccodes_host,
+                         uint8_t* cscales_host, uint16_t* u_host, void* stream) {
+    g_last_error.clear();
+    if (!q) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    DeviceGuard dg(q->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    const Geom& g = q->g;
+    const int64_t Ci = q->Ci, Kp = q->Kp;
+    try {
+        auto fetch = [&](const void* src, size_t bytes, std::vector<uint8_t>& dst) -> hipError_t {
+            dst.resize(bytes);
+            return hipMemcpy(dst.data(), src, bytes, hipMemcpyDeviceToHost);
+        };
+        std::vector<uint8_t> buf;
+        if (dcodes_host) {
+            if ((e = fetch(q->dq, (size_t)(g.Nslot * Kp / 2), buf)) != hipSuccess) return hip_fail(e, "copy delta codes");
+            for (long long s = 0; s < g.Nslot; ++s) {
+                long long t = host_slot_token(g, s);
+                if (t >= 0) std::memcpy(dcodes_host + t * (Ci / 2), &buf[(size_t)(s * (Kp / 2))], (size_t)(Ci / 2));
+            }
+        }
+        if (dscales_host) {
+            if ((e = fetch(q->ds, (size_t)(g.Nslot * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy delta scales");
+            for (long long s = 0; s < g.Nslot; ++s) {
+                long long t = host_slot_token(g, s);
+                if (t >= 0) std::memcpy(dscales_host + t * (Ci / 32), &buf[(size_t)(s * (Kp / 32))], (size_t)(Ci / 32));
+            }
+        }
+        if (ccodes_host) {
+            e = hipMemcpy2D(ccodes_host, (size_t)Ci, q->cq, (size_t)Kp, (size_t)Ci, (size_t)g.K, hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "copy core codes");
+        }
+        if (cscales_host) {
+            e = hipMemcpy2D(cscales_host, (size_t)(Ci / 32), q->cs, (size_t)(Kp / 32), (size_t)(Ci / 32), (size_t)g.K,
+                            hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "copy core scales");
+        }
+        if (u_host && q->rank > 0) {
+            if ((e = fetch(q->u, (size_t)(g.Nslot * q->rp * 2), buf)) != hipSuccess) return hip_fail(e, "copy U");
+            const uint16_t* ub = (const uint16_t*)buf.data();
+            for (long long s = 0; s < g.Nslot; ++s) {
+                long long t = host_slot_token(g, s);
+                if (t >= 0) std::memcpy(u_host + t * q->rank, ub + s * q->rp, (size_t)q->rank * 2);
+            }
+        }
+    } catch (const std::bad_alloc&) {
+        return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    return DQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Device helpers shared by the activation pass and the GEMMs (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dq_internal.h"
+
+namespace dq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+// Formats of the scaled MFMA (cbsz / blgp field values).
+constexpr int FMT_FP8 = 0;
+constexpr int FMT_FP4 = 4;
+
+// Scale exponent of an MX group (关键设计 4, quantizer definition, with the
+// scale restricted to a power of two): the smallest e with
+// amax <= q_max * 2^e.  With amax = m 2^E (1 <= m < 2) and
+// q_max = 1.5 * 2^2 (FP4) or 1.75 * 2^8 (FP8), that is E - 2 + [m > 1.5] or
+// E - 8 + [m > 1.75]; zero and subnormal maxima give the floor -127.
+__device__ __forceinline__ int mx_exp_fp4(float amax) {
+    uint32_t b = __float_as_uint(amax);
+    int ef = (int)(b >> 23);
+    int e = ef - 129 + ((b & 0x7fffffu) > 0x400000u ? 1 : 0);
+    return ef == 0 ? -127 : max(e, -127);
+}
+__device__ __forceinline__ int mx_exp_fp8(float amax) {
+    uint32_t b = __float_as_uint(amax);
+    int ef = (int)(b >> 23);
+    int e = ef - 135 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+    return ef == 0 ? -127 : max(e, -127);
+}
+// 2^e as a float operand of the scaled converts (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2f(int e) {
+    return e > -127 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// 32 fp32 values -> 32 FP4 E2M1 codes (16 bytes, element 2i in the low
+// nibble of byte i), each v / 2^e rounded to nearest even by the hardware
+// converter.
+__device__ __forceinline__ uint4 encode_fp4x32(const float* v, float scale) {
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        int w = i >> 2;
+        switch (i & 3) {
+            case 0: d[w] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d[w], v[2 * i], v[2 * i + 1], scale, 0); break;
+            case 1: d[w] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d[w], v[2 * i], v[2 * i + 1], scale, 1); break;
+            case 2: d[w] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d[w], v[2 * i], v[2 * i + 1], scale, 2); break;
+            default: d[w] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d[w], v[2 * i], v[2 * i + 1], scale, 3); break;
+        }
+    }
+    return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// 32 fp32 values -> 32 FP8 E4M3 codes (two 16-byte halves), v / 2^e rounded
+// to nearest even by the hardware converter.
+__device__ __forceinline__ void encode_fp8x32(const float* v, float scale, uint4& lo, uint4& hi) {
+    uint32_t d[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v2s z = {0, 0};
+        v2s a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, v[4 * i], v[4 * i + 1], scale, false);
+        v2s b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, v[4 * i + 2], v[4 * i + 3], scale, true);
+        d[i] = __builtin_bit_cast(uint32_t, b);
+    }
+    lo = make_uint4(d[0], d[1], d[2], d[3]);
+    hi = make_uint4(d[4], d[5], d[6], d[7]);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Slot layout: cube k owns slots [k S, k S + S); slot k S + (dt h + dh) w + dw
+// holds token (kt t + dt, kh h + dh, kw w + dw) if that lies in the grid,
+// else it is a pad slot (-1).  Within a cube the slots run in lexicographic
+// (dt, dh, dw) order.
+__device__ __forceinline__ long long slot_token(const Geom& g, long long slot) {
+    long long k = slot / g.S;
+    int s = (int)(slot - k * g.S);
+    int dw = s % g.w;
+    int dh = (s / g.w) % g.h;
+    int dt = s / (g.w * g.h);
+    long long kw = k % g.Wc;
+    long long kh = (k / g.Wc) % g.Hc;
+    long long kt = k / ((long long)g.Wc * g.Hc);
+    long long ti = kt * g.t + dt, hi = kh * g.h + dh, wi = kw * g.w + dw;
+    if (k >= g.K || ti >= g.T || hi >= g.H || wi >= g.W) return -1;
+    return (ti * g.H + hi) * g.W + wi;
+}
+
+// Token count of cube k (clipped at the high ends of the grid).
+__device__ __forceinline__ int cube_count(const Geom& g, long long k, int* ct, int* ch, int* cw) {
+    long long kw = k % g.Wc;
+    long long kh = (k / g.Wc) % g.Hc;
+    long long kt = k / ((long long)g.Wc * g.Hc);
+    *ct = (int)min((long long)g.t, g.T - kt * g.t);
+    *ch = (int)min((long long)g.h, g.H - kh * g.h);
+    *cw = (int)min((long long)g.w, g.W - kw * g.w);
+    return *ct * *ch * *cw;
+}
+
+// Correctly rounded s / cnt: exact for cnt = 1 and powers of two (a
+// power-of-two scaling), IEEE division otherwise.
+__device__ __forceinline__ float mean_div(float s, int cnt) {
+    if ((cnt & (cnt - 1)) == 0) return s * (1.0f / (float)cnt);
+    return __fdiv_rn(s, (float)cnt);
+}
+
+}  // namespace dq

@@ -1,0 +1,83 @@
+// Internal declarations of the delta-W4A4 library: handle layouts, kernel
+// argument blocks and the host-side launchers implemented in the .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "dq.h"
+
+namespace dq {
+
+// Padding of the internal buffers.  Channel dimensions of code/scale rows are
+// padded to KPAD so the GEMM's 128-wide K steps never leave a row, and row
+// counts to MPAD / NPAD so its 256 x 256 tiles never leave a buffer; padding
+// holds zero codes with zero scale codes, which contribute exactly 0.
+constexpr int KPAD = 128;
+constexpr int MPAD = 256;
+constexpr int NPAD = 256;
+constexpr int RPAD = 32;      // low-rank width padded for 32x32 bf16 MFMA tiles
+constexpr int CORE_BLOCK = 64;  // tokens per fp32 partial sum of a cube's core
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Token grid and cube shape, with derived counts, as kernels see them.
+struct Geom {
+    int T, H, W, t, h, w;
+    int Tc, Hc, Wc, S;
+    long long N, K, Nslot;
+};
+
+}  // namespace dq
+
+struct dq_weights {
+    int device = 0;
+    int64_t Ci = 0, Co = 0, Kp = 0, Cop = 0;
+    int rank = 0, rp = 0;
+    uint8_t* rq = nullptr;     // [Cop][Kp/2]   Q4(R) codes (device)
+    uint8_t* rs = nullptr;     // [Cop][Kp/32]  Q4(R) scale codes (device)
+    float* r = nullptr;        // [Co][Ci]      fp32 residual R^T (device, for export)
+    uint16_t* l1t = nullptr;   // [rp][Kp]      L1^T bf16 (device)
+    uint16_t* l2t = nullptr;   // [Cop][rp]     L2^T bf16 (device)
+    std::vector<uint16_t> l1, l2;   // host copies [Ci][rank], [rank][Co]
+    size_t bytes = 0;
+};
+
+struct dq_qact {
+    int device = 0;
+    int64_t Ci = 0, Co = 0, Kp = 0, Cop = 0;
+    int rp = 0, rank = 0;
+    dq::Geom g{};
+    int64_t Nslot_pad = 0, K_pad = 0;
+    int core_mode = 0;         // 0: cores inside the activation pass (S <= 64); 1: separate passes
+    int64_t nblk = 0;          // 64-token blocks per cube (core_mode 1)
+    uint8_t* dq = nullptr;     // [Nslot_pad][Kp/2]  delta codes, slot order
+    uint8_t* ds = nullptr;     // [Nslot_pad][Kp/32] delta scale codes
+    uint8_t* cq = nullptr;     // [K_pad][Kp]        core FP8 codes
+    uint8_t* cs = nullptr;     // [K_pad][Kp/32]     core scale codes
+    uint16_t* u = nullptr;     // [Nslot_pad][rp]    U = bf16(bf16(X) L1), slot order
+    float* bias = nullptr;     // [K_pad][Cop]       per-cube core term Q8(core) Q4(R)
+    float* coref = nullptr;    // [K][Kp]            fp32 cores (core_mode 1)
+    float* part = nullptr;     // [K*nblk][Kp]       fp32 block partials (core_mode 1)
+    size_t bytes = 0;
+};
+
+namespace dq {
+
+void set_error(const std::string& msg);
+
+// ---- launchers (quant.hip) ----
+hipError_t launch_residual(const void* w_dev, int w_bf16, const uint16_t* l1_dev, const uint16_t* l2_dev,
+                           int64_t Ci, int64_t Co, int rank, float* r_dev, hipStream_t st);
+hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                  uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                                  hipStream_t st);
+hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qact* q, hipStream_t st);
+
+// ---- launchers (gemm.hip) ----
+hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t st);
+
+}  // namespace dq
