@@ -192,6 +192,7 @@ def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
     import numpy as np
 
     from oracle import cubes, layer, lowrank
+    from w4a4_quantized_linear_cube_amd import synth
 
     try:
         from threadpoolctl import threadpool_info
@@ -199,8 +200,9 @@ def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
     except Exception:
         threads = os.cpu_count() or 1
     e = dq.dq_weights_export(weights)
-    l1, l2 = e["l1"], e["l2"]
-    wf = None
+    l1, l2 = e["l1"], e["l2"]          # the host-SVD factors: inputs, like W
+    wf = synth.to_f32_numpy(synth.config_weight(cfg))
+    rc, rs = lowrank.quantize_residual(lowrank.residual(wf, l1, l2))   # weight preparation, not timed
     g = cubes.Geometry(cfg.T, cfg.H, cfg.W, *cube)
     rng = np.random.default_rng(0)
     n_cubes = max(1, n_tokens // g.S)
@@ -214,7 +216,6 @@ def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
     xf = np.zeros((cfg.N, cfg.Ci), dtype=np.float32)
     need = torch.from_numpy(np.unique(tbl[tbl >= 0])).to(x.device)
     xf[need.cpu().numpy()] = x.index_select(0, need).float().cpu().numpy()
-    rc, rs = e["rcodes"], e["rscales"]
     t0 = time.perf_counter()
     q = layer.quantize_activation(xf, g, l1, cube_ids=ids, tokens=toks)
     yo = layer.forward(q, g, rc, rs, l2)

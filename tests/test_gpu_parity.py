@@ -63,29 +63,36 @@ def _check_u(got_bits, want_bits, x_rows, l1_bits):
     assert len(bad) == 0, f"U outside the fp32-accumulation bound at {bad[:5]}"
 
 
+# Per-instruction accuracy of the gfx950 scaled MFMA, measured on random
+# full-lane data against exact sums: FP4 x FP4 returns the exact 64-term sum
+# rounded once (<= 0.5 ulp; two roundings with a nonzero accumulator), while
+# FP8 x FP4 keeps about 13 bits internally (worst 2^-12.6 of sum|products|
+# per instruction on random codes, 2^-10.5 with mostly subnormal FP8).
+MFMA_FP8_REL = 2.0 ** -9
+
+
 def _abs_bound(q, g, rc, rs, l2_bits, x_rows, l1_bits):
-    """Elementwise bound on |y_gpu - y_oracle| from the arithmetic: each of
-    the Ci-term core and delta dot products and the rank-term low-rank dot
-    product is an fp32 accumulation (error <= terms * 2^-23 * sum|products|
-    in any order, allowing truncating MFMA adds), plus the low-rank term's
-    share of the U difference allowed by _check_u, plus the final rounding."""
+    """Elementwise bound on |y_gpu - y_oracle| from the arithmetic: the delta
+    dot product is Ci/64 MFMA blocks of exact sums each rounded (twice) into an
+    fp32 accumulator; the core dot product the same plus MFMA_FP8_REL per
+    block; the low-rank dot product r/16 bf16 blocks; plus the low-rank term's
+    share of the U difference allowed by _check_u.  The final rounding of y is
+    added by the caller."""
     Ci = rc.shape[1] * 2
     r = l2_bits.shape[0]
     rdq = np.abs(mx.mx_dequantize(mx.unpack_fp4(rc), rs, "fp4")).T
     core_abs = np.abs(mx.mx_dequantize(q["core_codes"], q["core_scales"], "fp8"))
     delta_abs = np.abs(mx.mx_dequantize(mx.unpack_fp4(q["delta_codes"]), q["delta_scales"], "fp4"))
     rows = q["row_of_cube"][cubes.cube_of_token(g, q["tokens"])]
-    gamma = (2 * Ci + r + 8) * 2.0 ** -23
-    b = (core_abs @ rdq)[rows] + delta_abs @ rdq
-    extra = 0.0
+    blocks = Ci // 64 + 4
+    bound = (blocks * 2.0 ** -23) * (delta_abs @ rdq) + (MFMA_FP8_REL + blocks * 2.0 ** -23) * (core_abs @ rdq)[rows]
     if r:
         u = np.abs(mx.bf16_bits_to_f64(q["U"]))
         l2a = np.abs(mx.bf16_bits_to_f64(l2_bits))
         xb = np.abs(mx.bf16_bits_to_f64(mx.f32_to_bf16_bits(x_rows)))
         ub = 2 * _ulp_bf16(u) + (Ci - 1) * 2.0 ** -24 * (xb @ np.abs(mx.bf16_bits_to_f64(l1_bits)))
-        b = b + (u + ub) @ l2a
-        extra = ub @ l2a
-    return gamma * b + extra
+        bound = bound + ((r // 16 + 4) * 2.0 ** -23) * ((u + ub) @ l2a) + ub @ l2a
+    return bound
 
 
 def _check_y(y, yo, bound=None):
@@ -98,7 +105,8 @@ def _check_y(y, yo, bound=None):
         diff = np.abs(y.astype(np.float64) - yo.astype(np.float64))
         lim = bound + 2.0 ** -23 * np.abs(yo.astype(np.float64))
         bad = np.argwhere(diff > lim)
-        assert len(bad) == 0, f"{len(bad)} outputs outside the accumulation bound, first {bad[:5]}"
+        worst = float((diff / lim).max())
+        assert len(bad) == 0, f"{len(bad)} outputs outside the accumulation bound (worst {worst:.2f}x), first {bad[:5]}"
     return err, row
 
 

@@ -2,19 +2,34 @@
 //
 // DeltaQuant notes, 关键设计 4 (the three-term equation):
 //   y_n = U_n L2 + Q8(core_k(n)) Q4(R) + Q4(delta_n) Q4(R)
-// The core term is one row per cube ("dynamic token bias", broadcast to the
-// cube's tokens); the delta term is one row per token.  Both are
-// V_MFMA_SCALE_F32_32X32X64_F8F6F4 contractions over Ci with the E8M0 block
-// scales applied inside the instruction (A = FP8 E4M3 for cores, FP4 E2M1 for
-// deltas; B = Q4(R) FP4 E2M1), fp32 accumulation.
+// The core term is one row per cube (the "dynamic token bias", broadcast to
+// the cube's tokens); the delta term is one row per token.  Two launches of
+// one kernel template: the core GEMM (A = FP8 E4M3 cores, one row per cube)
+// writes the per-cube term; the delta GEMM (A = FP4 E2M1 deltas, one row per
+// slot) adds U L2, adds its cube's core term in the epilogue and scatters rows
+// to token order.  Both are V_MFMA_SCALE_F32_32X32X64_F8F6F4 contractions
+// over Ci with the E8M0 block scales applied inside the instruction, fp32
+// accumulation.
 //
-// Tiling: a 256-thread workgroup computes a 256 x 256 output tile; its four
-// waves each own 128 x 128 (4 x 4 MFMA tiles of 32 x 32, 256 accumulator
-// registers).  K advances 128 per step; A/B code tiles and their scale bytes
-// are staged through double-buffered LDS (XOR-swizzled 16-byte chunks) with
-// one barrier per step.  Rows and columns of every operand are padded to the
-// tile size and K to 128, padding holding zero codes and zero scales, so the
-// main loop has no bounds checks.
+// Work decomposition: a 256-thread workgroup computes a 256 x 256 output
+// tile; its four waves each own 128 x 128 (4 x 4 MFMA tiles of 32 x 32,
+// 256 accumulator registers).
+//
+// Data movement: three LDS stages of one K step (128 channels) each.  A
+// codes, B codes and their E8M0 scale bytes go straight from global memory
+// into the stage two steps ahead (global_load_lds, no staging registers)
+// while the MFMAs run on the current stage; before the barrier that ends a
+// step each wave waits only for its copies of the next stage.  LDS rows hold
+// 16-byte chunks XOR-swizzled so every fragment read is free of bank
+// conflicts.  Rows, columns and K of every operand are padded to the tile
+// with zero codes and zero scales, so the main loop has no bounds checks.
+//
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs; tile
+// indices are remapped so the workgroups resident on one XCD at a time cover
+// a compact block of 4 row tiles x 8 column tiles and share their A and B
+// stages in that XCD's L2.
+#include <type_traits>
+
 #include "dq_device.h"
 
 namespace dq {
@@ -28,14 +43,12 @@ struct GemmArgs {
     long long ldb, ldbs;
     int Kp;             // multiple of 128
     int mtiles, ntiles;
-    // plain store epilogue: c[row][col]
-    float* c;
+    float* c;           // plain store epilogue: c[row][col]
     long long ldc;
-    // token epilogue: y[token][col] = acc + U L2 + bias[cube]
-    float* y;
+    float* y;           // token epilogue: y[token][col]
     int Co;
     Geom g;
-    const float* bias;
+    const float* bias;  // per-cube core term [K_pad][ldbias]
     long long ldbias;
     const uint16_t* u;     // [Nslot_pad][rp]
     const uint16_t* l2t;   // [Cop][rp]
@@ -45,69 +58,125 @@ struct GemmArgs {
 constexpr int EPI_STORE = 0;
 constexpr int EPI_TOKENS = 1;
 
+// Direct global -> LDS copies (global_load_lds, saddr form): lane i copies
+// 16 (or 4) bytes from base + voff_i to LDS address m0 + 16 i (or 4 i), with
+// m0 and base uniform over the wave.  Issued as inline assembly: the copies
+// have no destination registers, and keeping them out of the compiler's
+// wait-count bookkeeping is what lets the MFMAs run on one LDS stage while
+// later stages land (the compiler would otherwise wait for every copy in
+// flight before any LDS read).  Completion is awaited explicitly with
+// wait_vm<> and a barrier before any wave reads a stage; the "memory" clobber
+// keeps LDS accesses in program order around the copies.
+// `base` and `lds` are wave-uniform by construction; readfirstlane states it.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    uint64_t v = (uint64_t)(uintptr_t)p;
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff),
+                 "s"(uniform_ptr(base)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff),
+                 "s"(uniform_ptr(base)) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in
+// bits 15:14; expcnt 7 and lgkmcnt 15 mean no wait on those counters)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// XOR swizzles of 16-byte chunks within an LDS row.
+__device__ __forceinline__ int swz64(int row) { return (row >> 1) & 3; }   // 64-byte rows (4 chunks)
+__device__ __forceinline__ int swz128(int row) { return row & 7; }         // 128-byte rows (8 chunks)
+
 template <int AFMT, int OPSEL>
-__device__ __forceinline__ v16f mfma_mx(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+__device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, AFMT, FMT_FP4, OPSEL, sa, OPSEL, sb);
 }
 
+// Tile of workgroup `bid` (see the file comment); returns false for the
+// padding workgroups beyond the tile count.
+__device__ __forceinline__ bool tile_of(int bid, int mt, int nt, int* tm, int* tn) {
+    const int total = mt * nt;
+    const int per = (total + 7) / 8;
+    const int v = (bid & 7) * per + (bid >> 3);
+    if (v >= total) return false;
+    constexpr int GM = 4;
+    const int grp = v / (GM * nt);
+    const int first = grp * GM;
+    const int gm = min(GM, mt - first);
+    const int within = v - grp * GM * nt;
+    *tm = first + within % gm;
+    *tn = within / gm;
+    return true;
+}
+
 template <int AFMT, int EPI>
-__global__ __launch_bounds__(256, 1) void k_mxgemm(GemmArgs p) {
-    constexpr int ABYTES = AFMT == FMT_FP4 ? 64 : 128;   // A bytes per row per 128-wide K step
-    constexpr int ACH = ABYTES / 16;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][256 * ABYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][256 * 64];
-    __shared__ uint32_t lds_as[2][256];
-    __shared__ uint32_t lds_bs[2][256];
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
+    constexpr int AROW = AFMT == FMT_FP4 ? 64 : 128;            // A bytes per row per 128-wide K step
+    constexpr int A_BYTES = 256 * AROW;
+    constexpr int B_BYTES = 256 * 64;
+    constexpr int SA_OFF = A_BYTES + B_BYTES;
+    constexpr int SB_OFF = SA_OFF + 1024;
+    constexpr int STAGE = SB_OFF + 1024;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * STAGE];
     __shared__ long long rtok[EPI == EPI_TOKENS ? 256 : 1];
-    __shared__ long long rcube[EPI == EPI_TOKENS ? 256 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int g = lane >> 5, l32 = lane & 31;
-    const int bid = blockIdx.x;
-    const int tm = bid / p.ntiles, tn = bid - tm * p.ntiles;
+    int tm, tn;
+    if (!tile_of(blockIdx.x, p.mtiles, p.ntiles, &tm, &tn)) return;
     const long long m0 = (long long)tm * 256, n0 = (long long)tn * 256;
 
     if (EPI == EPI_TOKENS) {
         long long slot = m0 + tid;
         rtok[tid] = slot < p.g.Nslot ? slot_token(p.g, slot) : -1;
-        rcube[tid] = slot / p.g.S;
     }
 
-    auto swz_a = [](int row, int ch) { return AFMT == FMT_FP4 ? (ch ^ ((row >> 1) & 3)) : (ch ^ (row & 7)); };
-    auto swz_b = [](int row, int ch) { return ch ^ ((row >> 1) & 3); };
+    // ---- this lane's copy sources: uniform tile bases + per-lane 32-bit offsets.
+    // A: 256 rows x AROW bytes per stage = APC pieces of 1 KB per wave.
+    constexpr int APC = A_BYTES / 1024 / 4;       // pieces per wave (4 or 8)
+    constexpr int ACH = AROW / 16;                // 16-byte chunks per A row
+    constexpr int DMAS = APC + 4 + 2;             // copies per wave per stage
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t aoff[APC], boff[4];
+#pragma unroll
+    for (int j = 0; j < APC; ++j) {
+        int lin = (wv * APC + j) * 64 + lane;     // 16-byte chunk index within the stage
+        int row = lin / ACH, pc = lin % ACH;
+        int ch = AFMT == FMT_FP4 ? (pc ^ swz64(row)) : (pc ^ swz128(row));
+        aoff[j] = (uint32_t)(row * p.lda + ch * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int lin = (wv * 4 + j) * 64 + lane;
+        int row = lin >> 2, pc = lin & 3;
+        boff[j] = (uint32_t)(row * p.ldb + (pc ^ swz64(row)) * 16);
+    }
+    const uint32_t asoff = (uint32_t)((wv * 64 + lane) * p.ldas);
+    const uint32_t bsoff = (uint32_t)((wv * 64 + lane) * p.ldbs);
+    const uint8_t* abase = p.a + m0 * p.lda;
+    const uint8_t* bbase = p.b + n0 * p.ldb;
+    const uint8_t* asbase = p.as + m0 * p.ldas;
+    const uint8_t* bsbase = p.bs + n0 * p.ldbs;
+    const uint32_t lds0 = lds_addr(smem);
 
-    uint4 ra[ACH], rb[4];
-    uint32_t ras, rbs;
-    auto gload = [&](int kt) {
-        const long long ka = (long long)kt * ABYTES, kb = (long long)kt * 64;
+    auto issue = [&](int kt, int buf) {
+        const uint32_t st = lds0 + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            int q = tid + 256 * i, row = q / ACH, ch = q - row * ACH;
-            ra[i] = *(const uint4*)(p.a + (m0 + row) * p.lda + ka + ch * 16);
-        }
+        for (int j = 0; j < APC; ++j) dma16(abase + (long long)kt * AROW, aoff[j], st + (wv * APC + j) * 1024);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int q = tid + 256 * i, row = q >> 2, ch = q & 3;
-            rb[i] = *(const uint4*)(p.b + (n0 + row) * p.ldb + kb + ch * 16);
-        }
-        ras = *(const uint32_t*)(p.as + (m0 + tid) * p.ldas + kt * 4);
-        rbs = *(const uint32_t*)(p.bs + (n0 + tid) * p.ldbs + kt * 4);
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            int q = tid + 256 * i, row = q / ACH, ch = q - row * ACH;
-            *(uint4*)(&lds_a[buf][row * ABYTES + swz_a(row, ch) * 16]) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int q = tid + 256 * i, row = q >> 2, ch = q & 3;
-            *(uint4*)(&lds_b[buf][row * 64 + swz_b(row, ch) * 16]) = rb[i];
-        }
-        lds_as[buf][tid] = ras;
-        lds_bs[buf][tid] = rbs;
+        for (int j = 0; j < 4; ++j) dma16(bbase + kt * 64, boff[j], st + A_BYTES + (wv * 4 + j) * 1024);
+        dma4(asbase + kt * 4, asoff, st + SA_OFF + wv * 256);
+        dma4(bsbase + kt * 4, bsoff, st + SB_OFF + wv * 256);
     };
 
     v16f acc[4][4];
@@ -116,49 +185,103 @@ __global__ __launch_bounds__(256, 1) void k_mxgemm(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
 
-    auto compute_half = [&](int buf, auto KK) {
-        constexpr int kk = decltype(KK)::value;
-        v8i af[4], bfr[4];
-        int sa[4], sb[4];
+    // ---- low-rank branch first (registers are free here): acc = U L2 with
+    // 32x32x16 bf16 MFMAs over the padded rank; the K loop accumulates on top.
+    if (EPI == EPI_TOKENS) {
+        for (int kq = 0; kq < p.rp; kq += 16) {
+            v8bf ua[4], lb[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            int row = wr * 128 + mi * 32 + l32;
-            const uint8_t* base = &lds_a[buf][row * ABYTES];
-            if (AFMT == FMT_FP4) {
-                uint4 v = *(const uint4*)(base + swz_a(row, 2 * kk + g) * 16);
-                af[mi] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            } else {
-                uint4 v0 = *(const uint4*)(base + swz_a(row, 4 * kk + g) * 16);
-                uint4 v1 = *(const uint4*)(base + swz_a(row, 4 * kk + 2 + g) * 16);
-                af[mi] = (v8i){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+            for (int mi = 0; mi < 4; ++mi) {
+                long long row = m0 + wr * 128 + l32 + 32 * mi;
+                ua[mi] = __builtin_bit_cast(v8bf, *(const uint4*)(p.u + row * p.rp + kq + 8 * g));
             }
-            sa[mi] = (int)(lds_as[buf][row] >> (8 * g));
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                long long col = n0 + wc * 128 + l32 + 32 * ni;
+                lb[ni] = __builtin_bit_cast(v8bf, *(const uint4*)(p.l2t + col * p.rp + kq + 8 * g));
+            }
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[mi], lb[ni], acc[mi][ni], 0, 0, 0);
         }
+    }
+    // LDS fragment addresses (bytes within a stage)
+    const int arow0 = wr * 128 + l32;           // + 32 mi
+    const int brow0 = wc * 128 + l32;           // + 32 ni
+    const int sa_sw = AFMT == FMT_FP4 ? swz64(arow0) : swz128(arow0);
+    const int sb_sw = swz64(brow0);
+
+    auto compute = [&](int buf) {
+        const uint8_t* st = smem + buf * STAGE;
+        uint32_t sa_raw[4], sb_raw[4];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            int row = wc * 128 + ni * 32 + l32;
-            uint4 v = *(const uint4*)(&lds_b[buf][row * 64 + swz_b(row, 2 * kk + g) * 16]);
-            bfr[ni] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            sb[ni] = (int)(lds_bs[buf][row] >> (8 * g));
+        for (int mi = 0; mi < 4; ++mi) sa_raw[mi] = *(const uint32_t*)(st + SA_OFF + (arow0 + 32 * mi) * 4) >> (8 * g);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) sb_raw[ni] = *(const uint32_t*)(st + SB_OFF + (brow0 + 32 * ni) * 4) >> (8 * g);
+        // delta term: two 64-wide K halves
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            v8i af[4], bf[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const uint8_t* rowp = st + (arow0 + 32 * mi) * AROW;
+                if (AFMT == FMT_FP4) {
+                    uint4 v = *(const uint4*)(rowp + (((2 * kk + g) ^ sa_sw) << 4));
+                    af[mi] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                } else {
+                    uint4 v0 = *(const uint4*)(rowp + (((4 * kk + g) ^ sa_sw) << 4));
+                    uint4 v1 = *(const uint4*)(rowp + (((4 * kk + 2 + g) ^ sa_sw) << 4));
+                    af[mi] = (v8i){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+                }
+            }
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                uint4 v = *(const uint4*)(st + A_BYTES + (brow0 + 32 * ni) * 64 + (((2 * kk + g) ^ sb_sw) << 4));
+                bf[ni] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    if (kk == 0)
+                        acc[mi][ni] = mfma32<AFMT, 0>(af[mi], bf[ni], acc[mi][ni], (int)sa_raw[mi], (int)sb_raw[ni]);
+                    else
+                        acc[mi][ni] = mfma32<AFMT, 2>(af[mi], bf[ni], acc[mi][ni], (int)sa_raw[mi], (int)sb_raw[ni]);
+                }
         }
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                acc[mi][ni] = mfma_mx<AFMT, 2 * kk>(af[mi], bfr[ni], acc[mi][ni], sa[mi], sb[ni]);
     };
 
+    // ---- K loop over a ring of three stages
     const int nk = p.Kp / 128;
-    gload(0);
-    lstore(0);
+    issue(0, 0);
+    if (nk > 1) {
+        issue(1, 1);
+        wait_vm<DMAS>();            // this wave's copies of stage 0 have landed
+    } else {
+        wait_vm<0>();
+    }
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        compute_half(buf, std::integral_constant<int, 0>{});
-        compute_half(buf, std::integral_constant<int, 1>{});
-        if (kt + 1 < nk) lstore(buf ^ 1);
+    // Steady state without branches, so the MFMAs of a step stay in the loop
+    // block ahead of its wait; then the last two steps, which issue nothing.
+    int buf = 0, kt = 0;
+    for (; kt + 2 < nk; ++kt) {
+        issue(kt + 2, buf == 0 ? 2 : buf - 1);      // stage (kt + 2) % 3
+        compute(buf);
+        // keep this step's MFMAs above the wait: the scheduler would otherwise
+        // sink them below it and stall them on the next stage's copies
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<DMAS>();                            // stage kt + 1 landed; kt + 2 may be in flight
         __syncthreads();
+        buf = buf == 2 ? 0 : buf + 1;
+    }
+    for (; kt < nk; ++kt) {
+        compute(buf);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();
+        __syncthreads();
+        buf = buf == 2 ? 0 : buf + 1;
     }
 
     if (EPI == EPI_STORE) {
@@ -175,82 +298,93 @@ __global__ __launch_bounds__(256, 1) void k_mxgemm(GemmArgs p) {
         return;
     }
 
-    // ---- low-rank branch: acc += U L2 (32x32x16 bf16 MFMA over the padded rank)
-    for (int kq = 0; kq < p.rp; kq += 16) {
-        v8bf ua[4], lb[4];
+    // ---- epilogue: y = acc + bias[cube], rows scattered to token order.
+    // The cube's core-term rows are staged in LDS, 64 slots (one 32-row MFMA
+    // block mi of each wave row) per phase, with the same register-free
+    // direct copies: one 1 KB row per wave instruction.
+    float* bl = (float*)smem;                              // [64 slots][256 columns]
+    const int S = p.g.S;
+    const long long kmax = p.g.K - 1;
+    auto bias_rows = [&](int mi) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            long long row = m0 + wr * 128 + mi * 32 + l32;
-            ua[mi] = __builtin_bit_cast(v8bf, *(const uint4*)(p.u + row * p.rp + kq + 8 * g));
+        for (int j = 0; j < 16; ++j) {
+            const int q = wv * 16 + j;                     // LDS row: wave row q / 32, row q % 32 of block mi
+            const long long slot = m0 + (q >> 5) * 128 + mi * 32 + (q & 31);
+            const long long k = min(slot / S, kmax);       // pad slots: any valid row, never stored
+            dma16(p.bias + k * p.ldbias + n0, (uint32_t)lane * 16, lds0 + q * 1024);
+        }
+    };
+    bias_rows(0);
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        wait_vm<0>();
+        __syncthreads();                                   // phase mi's rows have landed
+        long long yoff[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const long long t = rtok[wr * 128 + mi * 32 + 8 * (i >> 2) + 4 * g + (i & 3)];
+            yoff[i] = t < 0 ? -1 : t * (long long)p.Co + n0;
         }
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-            long long col = n0 + wc * 128 + ni * 32 + l32;
-            lb[ni] = __builtin_bit_cast(v8bf, *(const uint4*)(p.l2t + col * p.rp + kq + 8 * g));
-        }
+            const int col = wc * 128 + ni * 32 + l32;
+            float bv[16];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+            for (int i = 0; i < 16; ++i) bv[i] = bl[(wr * 32 + 8 * (i >> 2) + 4 * g + (i & 3)) * 256 + col];
+            if (n0 + col < p.Co) {
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[mi], lb[ni], acc[mi][ni], 0, 0, 0);
-    }
-
-    // ---- + per-cube core term, scatter rows to token order
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            int r = wr * 128 + mi * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            long long t = rtok[r];
-            if (t < 0) continue;
-            const float* brow = p.bias + rcube[r] * p.ldbias;
-            float* yrow = p.y + t * (long long)p.Co;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                long long col = n0 + wc * 128 + ni * 32 + l32;
-                if (col < p.Co) yrow[col] = acc[mi][ni][i] + brow[col];
+                for (int i = 0; i < 16; ++i)
+                    if (yoff[i] >= 0) p.y[yoff[i] + col] = acc[mi][ni][i] + bv[i];
             }
         }
+        __syncthreads();                                   // every wave is done with phase mi's rows
+        if (mi < 3) bias_rows(mi + 1);
+    }
+}
+
+template <int AFMT, int EPI>
+static hipError_t launch(const GemmArgs& a, hipStream_t st) {
+    int total = a.mtiles * a.ntiles;
+    int grid = (total + 7) / 8 * 8;
+    k_gemm<AFMT, EPI><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t st) {
-    // 1) per-cube core term: bias[k] = Q8(core_k) Q4(R)
-    GemmArgs c{};
-    c.a = q->cq;
-    c.as = q->cs;
-    c.lda = q->Kp;
-    c.ldas = q->Kp / 32;
-    c.b = w->rq;
-    c.bs = w->rs;
-    c.ldb = w->Kp / 2;
-    c.ldbs = w->Kp / 32;
-    c.Kp = (int)w->Kp;
-    c.mtiles = (int)(q->K_pad / 256);
-    c.ntiles = (int)(w->Cop / 256);
-    c.c = q->bias;
-    c.ldc = w->Cop;
-    k_mxgemm<FMT_FP8, EPI_STORE><<<c.mtiles * c.ntiles, 256, 0, st>>>(c);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    // 2) delta term + low-rank branch + broadcast core term -> y (token order)
-    GemmArgs d = c;
+    GemmArgs d{};
+    d.b = w->rq;
+    d.bs = w->rs;
+    d.ldb = w->Kp / 2;
+    d.ldbs = w->Kp / 32;
+    d.Kp = (int)w->Kp;
+    d.ntiles = (int)(w->Cop / 256);
     d.a = q->dq;
     d.as = q->ds;
     d.lda = q->Kp / 2;
     d.ldas = q->Kp / 32;
     d.mtiles = (int)(q->Nslot_pad / 256);
-    d.c = nullptr;
     d.y = y;
     d.Co = (int)w->Co;
     d.g = q->g;
-    d.bias = q->bias;
-    d.ldbias = w->Cop;
     d.u = q->u;
     d.l2t = w->l2t;
     d.rp = w->rp;
-    k_mxgemm<FMT_FP4, EPI_TOKENS><<<d.mtiles * d.ntiles, 256, 0, st>>>(d);
-    return hipGetLastError();
+    // 1) per-cube core term bias[k] = Q8(core_k) Q4(R)
+    GemmArgs c = d;
+    c.a = q->cq;
+    c.as = q->cs;
+    c.lda = q->Kp;
+    c.ldas = q->Kp / 32;
+    c.mtiles = (int)(q->K_pad / 256);
+    c.c = q->bias;
+    c.ldc = w->Cop;
+    hipError_t e = launch<FMT_FP8, EPI_STORE>(c, st);
+    if (e != hipSuccess) return e;
+    // 2) delta term + low-rank branch + the cube's core term -> y (token order)
+    d.bias = q->bias;
+    d.ldbias = w->Cop;
+    return launch<FMT_FP4, EPI_TOKENS>(d, st);
 }
 
 }  // namespace dq
