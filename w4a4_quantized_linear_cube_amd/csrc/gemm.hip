@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     constexpr int SA_OFF = A_BYTES + B_BYTES;
     constexpr int SB_OFF = SA_OFF + 1024;
     constexpr int STAGE = SB_OFF + 1024;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * STAGE];
+    constexpr int NS = AFMT == FMT_FP4 ? 4 : 3;                // LDS stages in the ring
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
     __shared__ long long rtok[EPI == EPI_TOKENS ? 256 : 1];
 
     const int tid = threadIdx.x;
@@ -213,76 +214,155 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     const int sa_sw = AFMT == FMT_FP4 ? swz64(arow0) : swz128(arow0);
     const int sb_sw = swz64(brow0);
 
-    auto compute = [&](int buf) {
+    // Fragments of one K step (both 64-wide halves), read from LDS one step
+    // ahead of their MFMAs into a second register set.
+    struct Frag {
+        uint4 a[2][4], a2[AFMT == FMT_FP4 ? 1 : 2][4], b[2][4];
+        uint32_t sa[4], sb[4];
+    };
+    auto load_frags = [&](int buf, Frag& F) {
         const uint8_t* st = smem + buf * STAGE;
-        uint32_t sa_raw[4], sb_raw[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) sa_raw[mi] = *(const uint32_t*)(st + SA_OFF + (arow0 + 32 * mi) * 4) >> (8 * g);
+        for (int mi = 0; mi < 4; ++mi) F.sa[mi] = *(const uint32_t*)(st + SA_OFF + (arow0 + 32 * mi) * 4) >> (8 * g);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) sb_raw[ni] = *(const uint32_t*)(st + SB_OFF + (brow0 + 32 * ni) * 4) >> (8 * g);
-        // delta term: two 64-wide K halves
+        for (int ni = 0; ni < 4; ++ni) F.sb[ni] = *(const uint32_t*)(st + SB_OFF + (brow0 + 32 * ni) * 4) >> (8 * g);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            v8i af[4], bf[4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 const uint8_t* rowp = st + (arow0 + 32 * mi) * AROW;
-                if (AFMT == FMT_FP4) {
-                    uint4 v = *(const uint4*)(rowp + (((2 * kk + g) ^ sa_sw) << 4));
-                    af[mi] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                if constexpr (AFMT == FMT_FP4) {
+                    F.a[kk][mi] = *(const uint4*)(rowp + (((2 * kk + g) ^ sa_sw) << 4));
                 } else {
+                    F.a[kk][mi] = *(const uint4*)(rowp + (((4 * kk + g) ^ sa_sw) << 4));
+                    F.a2[kk][mi] = *(const uint4*)(rowp + (((4 * kk + 2 + g) ^ sa_sw) << 4));
+                }
+            }
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                F.b[kk][ni] = *(const uint4*)(st + A_BYTES + (brow0 + 32 * ni) * 64 + (((2 * kk + g) ^ sb_sw) << 4));
+        }
+    };
+    auto mfma_step = [&](const Frag& F) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const uint4 v = F.a[kk][mi];
+                v8i af;
+                if constexpr (AFMT == FMT_FP4) {
+                    af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                } else {
+                    const uint4 w = F.a2[kk][mi];
+                    af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, (int)w.x, (int)w.y, (int)w.z, (int)w.w};
+                }
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const uint4 u = F.b[kk][ni];
+                    const v8i bf = (v8i){(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+                    if (kk == 0)
+                        acc[mi][ni] = mfma32<AFMT, 0>(af, bf, acc[mi][ni], (int)F.sa[mi], (int)F.sb[ni]);
+                    else
+                        acc[mi][ni] = mfma32<AFMT, 2>(af, bf, acc[mi][ni], (int)F.sa[mi], (int)F.sb[ni]);
+                }
+            }
+    };
+
+    const int nk = p.Kp / 128;
+    if constexpr (AFMT == FMT_FP4) {
+        // ---- K loop over a ring of NS stages.  Step kt: copies for stage
+        // kt + NS - 1 go out (into the stage whose fragments were read at step
+        // kt - 2, long since consumed); wait for this wave's copies of stage
+        // kt + 1; barrier (now every wave's copies of kt + 1 have landed); read
+        // the fragments of kt + 1; run the MFMAs of kt from the fragments read
+        // one step earlier, so the MFMAs never wait for LDS.
+        for (int st = 0; st < NS - 1; ++st)
+            if (st < nk) issue(st, st);
+        if (nk >= NS - 1) wait_vm<(NS - 2) * DMAS>();   // stage 0 landed
+        else wait_vm<0>();
+        __syncthreads();
+        Frag F0, F1;
+        load_frags(0, F0);
+        auto step = [&](int kt, Frag& cur, Frag& nxt, auto STEADY) {
+            if constexpr (decltype(STEADY)::value) {
+                issue(kt + NS - 1, (kt + NS - 1) % NS);
+                wait_vm<(NS - 2) * DMAS>();              // stage kt + 1 landed; later ones may be in flight
+            } else {
+                if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+                wait_vm<0>();
+            }
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) load_frags((kt + 1) % NS, nxt);
+            mfma_step(cur);
+        };
+        int kt = 0;
+        for (; kt + NS < nk; kt += 2) {                 // steps kt and kt + 1 both issue copies
+            step(kt, F0, F1, std::true_type{});
+            step(kt + 1, F1, F0, std::true_type{});
+        }
+        for (; kt < nk; kt += 2) {                      // kt stays even: F0 always serves even steps
+            step(kt, F0, F1, std::false_type{});
+            if (kt + 1 < nk) step(kt + 1, F1, F0, std::false_type{});
+        }
+    } else {
+        // FP8 fragments are twice as wide, so a second register set does not
+        // fit beside 256 accumulators: read each step's fragments in the step.
+        // Step kt: copies for kt + NS - 1 out, fragments of kt read and MFMAs
+        // run, then wait for stage kt + 1 and barrier.
+        for (int st = 0; st < NS - 1; ++st)
+            if (st < nk) issue(st, st);
+        if (nk >= NS - 1) wait_vm<(NS - 2) * DMAS>();
+        else wait_vm<0>();
+        __syncthreads();
+        // one 64-wide K half at a time keeps only half the fragments live
+        auto compute = [&](int buf) {
+            const uint8_t* st = smem + buf * STAGE;
+            uint32_t sa[4], sb[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) sa[mi] = *(const uint32_t*)(st + SA_OFF + (arow0 + 32 * mi) * 4) >> (8 * g);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) sb[ni] = *(const uint32_t*)(st + SB_OFF + (brow0 + 32 * ni) * 4) >> (8 * g);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                v8i af[4], bf[4];
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const uint8_t* rowp = st + (arow0 + 32 * mi) * AROW;
                     uint4 v0 = *(const uint4*)(rowp + (((4 * kk + g) ^ sa_sw) << 4));
                     uint4 v1 = *(const uint4*)(rowp + (((4 * kk + 2 + g) ^ sa_sw) << 4));
                     af[mi] = (v8i){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
                 }
-            }
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                uint4 v = *(const uint4*)(st + A_BYTES + (brow0 + 32 * ni) * 64 + (((2 * kk + g) ^ sb_sw) << 4));
-                bf[ni] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) {
-                    if (kk == 0)
-                        acc[mi][ni] = mfma32<AFMT, 0>(af[mi], bf[ni], acc[mi][ni], (int)sa_raw[mi], (int)sb_raw[ni]);
-                    else
-                        acc[mi][ni] = mfma32<AFMT, 2>(af[mi], bf[ni], acc[mi][ni], (int)sa_raw[mi], (int)sb_raw[ni]);
+                    uint4 v = *(const uint4*)(st + A_BYTES + (brow0 + 32 * ni) * 64 + (((2 * kk + g) ^ sb_sw) << 4));
+                    bf[ni] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
                 }
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        if (kk == 0) acc[mi][ni] = mfma32<AFMT, 0>(af[mi], bf[ni], acc[mi][ni], (int)sa[mi], (int)sb[ni]);
+                        else acc[mi][ni] = mfma32<AFMT, 2>(af[mi], bf[ni], acc[mi][ni], (int)sa[mi], (int)sb[ni]);
+                    }
+            }
+        };
+        int kt = 0;
+        for (; kt + NS - 1 < nk; ++kt) {
+            issue(kt + NS - 1, (kt + NS - 1) % NS);
+            compute(kt % NS);
+            __builtin_amdgcn_sched_barrier(0);          // keep the MFMAs above the wait
+            wait_vm<(NS - 2) * DMAS>();
+            __syncthreads();
         }
-    };
-
-    // ---- K loop over a ring of three stages
-    const int nk = p.Kp / 128;
-    issue(0, 0);
-    if (nk > 1) {
-        issue(1, 1);
-        wait_vm<DMAS>();            // this wave's copies of stage 0 have landed
-    } else {
-        wait_vm<0>();
+        for (; kt < nk; ++kt) {
+            compute(kt % NS);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm<0>();
+            __syncthreads();
+        }
     }
     __syncthreads();
-    // Steady state without branches, so the MFMAs of a step stay in the loop
-    // block ahead of its wait; then the last two steps, which issue nothing.
-    int buf = 0, kt = 0;
-    for (; kt + 2 < nk; ++kt) {
-        issue(kt + 2, buf == 0 ? 2 : buf - 1);      // stage (kt + 2) % 3
-        compute(buf);
-        // keep this step's MFMAs above the wait: the scheduler would otherwise
-        // sink them below it and stall them on the next stage's copies
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<DMAS>();                            // stage kt + 1 landed; kt + 2 may be in flight
-        __syncthreads();
-        buf = buf == 2 ? 0 : buf + 1;
-    }
-    for (; kt < nk; ++kt) {
-        compute(buf);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<0>();
-        __syncthreads();
-        buf = buf == 2 ? 0 : buf + 1;
-    }
 
     if (EPI == EPI_STORE) {
 #pragma unroll
