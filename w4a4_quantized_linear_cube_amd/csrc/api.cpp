@@ -91,6 +91,7 @@ void free_qact(dq_qact* q) {
     (void)hipFree(q->ds);
     (void)hipFree(q->cq);
     (void)hipFree(q->cs);
+    (void)hipFree(q->stok);
     (void)hipFree(q->u);
     (void)hipFree(q->bias);
     (void)hipFree(q->coref);
@@ -111,6 +112,21 @@ long long host_slot_token(const Geom& g, long long slot) {
 }  // namespace
 
 void set_error(const std::string& msg) { g_last_error = msg; }
+
+// Host copies of the step-major operand layout back to plain rows (exports).
+hipError_t fetch_all(const void* src, size_t bytes, std::vector<uint8_t>& dst) {
+    dst.resize(bytes);
+    return hipMemcpy(dst.data(), src, bytes, hipMemcpyDeviceToHost);
+}
+void unstep_fp4(const std::vector<uint8_t>& buf, long long row, int64_t Ci, int64_t Kp, uint8_t* out) {
+    for (long long G = 0; G < Ci / 32; ++G) std::memcpy(out + 16 * G, &buf[off_fp4(row, G, Kp / 128)], 16);
+}
+void unstep_fp8(const std::vector<uint8_t>& buf, long long row, int64_t Ci, int64_t Kp, uint8_t* out) {
+    for (long long c = 0; c < Ci / 16; ++c) std::memcpy(out + 16 * c, &buf[off_fp8(row, c >> 3, (int)(c & 7), Kp / 128)], 16);
+}
+void unstep_scales(const std::vector<uint8_t>& buf, long long row, int64_t Ci, int64_t Kp, uint8_t* out) {
+    for (long long G = 0; G < Ci / 32; ++G) out[G] = buf[off_scale(row, G, Kp / 128)];
+}
 
 }  // namespace dq
 
@@ -219,7 +235,7 @@ dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci
         (e = dalloc(&w->rq, (size_t)(w->Cop * w->Kp / 2), &w->bytes)) != hipSuccess ||
         (e = dalloc(&w->rs, (size_t)(w->Cop * w->Kp / 32), &w->bytes)) != hipSuccess) { cleanup(); return hip_fail(e, "hipMalloc weight"); }
     if ((e = launch_residual(wdev, dt == DQ_BF16, l1d, l2d, Ci, Co, rank, w->r, nullptr)) != hipSuccess) { cleanup(); return hip_fail(e, "residual kernel"); }
-    if ((e = launch_encode_fp4_rows(w->r, Co, Ci, Ci, w->rq, w->Kp / 2, w->rs, w->Kp / 32, nullptr)) != hipSuccess) { cleanup(); return hip_fail(e, "encode kernel"); }
+    if ((e = launch_encode_fp4_rows(w->r, Co, Ci, Ci, w->Kp, w->rq, w->rs, nullptr)) != hipSuccess) { cleanup(); return hip_fail(e, "encode kernel"); }
     if (w->rp > 0) {
         std::vector<uint16_t> l1t((size_t)(w->rp * w->Kp), 0), l2t((size_t)(w->Cop * w->rp), 0);
         for (int64_t c = 0; c < Ci; ++c)
@@ -276,15 +292,18 @@ dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2
     hipError_t e;
     if (r_host && (e = hipMemcpy(r_host, w->r, (size_t)(w->Ci * w->Co) * 4, hipMemcpyDeviceToHost)) != hipSuccess)
         return hip_fail(e, "copy R");
-    if (rcodes_host) {
-        e = hipMemcpy2D(rcodes_host, (size_t)(w->Ci / 2), w->rq, (size_t)(w->Kp / 2), (size_t)(w->Ci / 2), (size_t)w->Co,
-                        hipMemcpyDeviceToHost);
-        if (e != hipSuccess) return hip_fail(e, "copy R codes");
-    }
-    if (rscales_host) {
-        e = hipMemcpy2D(rscales_host, (size_t)(w->Ci / 32), w->rs, (size_t)(w->Kp / 32), (size_t)(w->Ci / 32),
-                        (size_t)w->Co, hipMemcpyDeviceToHost);
-        if (e != hipSuccess) return hip_fail(e, "copy R scales");
+    try {
+        std::vector<uint8_t> buf;
+        if (rcodes_host) {
+            if ((e = fetch_all(w->rq, (size_t)(w->Cop * w->Kp / 2), buf)) != hipSuccess) return hip_fail(e, "copy R codes");
+            for (int64_t j = 0; j < w->Co; ++j) unstep_fp4(buf, j, w->Ci, w->Kp, rcodes_host + j * (w->Ci / 2));
+        }
+        if (rscales_host) {
+            if ((e = fetch_all(w->rs, (size_t)(w->Cop * w->Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy R scales");
+            for (int64_t j = 0; j < w->Co; ++j) unstep_scales(buf, j, w->Ci, w->Kp, rscales_host + j * (w->Ci / 32));
+        }
+    } catch (const std::bad_alloc&) {
+        return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
     }
     return DQ_OK;
 }
@@ -305,7 +324,7 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
     int64_t S = (int64_t)G.t * G.h * G.w;
     if (N > (int64_t(1) << 31) || !mul_ok(K, S, lim)) return fail(DQ_ERR_SHAPE, "token grid too large");
     int64_t Nslot = K * S;
-    if (Nslot > (int64_t(1) << 31)) return fail(DQ_ERR_SHAPE, "slot count too large");
+    if (Nslot > (int64_t(1) << 31) - MPAD) return fail(DQ_ERR_SHAPE, "slot count too large");
     DeviceGuard dg(w->device);
     if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
 
@@ -332,8 +351,10 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
         (e = dalloc(&q->cq, (size_t)(q->K_pad * q->Kp), &q->bytes)) != hipSuccess ||
         (e = dalloc(&q->cs, (size_t)(q->K_pad * q->Kp / 32), &q->bytes)) != hipSuccess ||
         (e = dalloc(&q->u, (size_t)(q->Nslot_pad * q->rp), &q->bytes)) != hipSuccess ||
-        (e = dalloc(&q->bias, (size_t)(q->K_pad * q->Cop), &q->bytes)) != hipSuccess)
+        (e = dalloc(&q->bias, (size_t)(q->K_pad * q->Cop), &q->bytes)) != hipSuccess ||
+        (e = dalloc(&q->stok, (size_t)q->Nslot_pad, &q->bytes)) != hipSuccess)
         return hip_fail(e, "hipMalloc workspace");
+    if ((e = launch_slot_tokens(q->g, q->stok, q->Nslot_pad, nullptr)) != hipSuccess) return hip_fail(e, "slot table");
     if (q->core_mode == 1) {
         if ((e = dalloc(&q->coref, (size_t)(K * q->Kp), &q->bytes)) != hipSuccess ||
             (e = dalloc(&q->part, (size_t)(K * q->nblk * q->Kp), &q->bytes)) != hipSuccess)
@@ -406,36 +427,31 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
     const Geom& g = q->g;
     const int64_t Ci = q->Ci, Kp = q->Kp;
     try {
-        auto fetch = [&](const void* src, size_t bytes, std::vector<uint8_t>& dst) -> hipError_t {
-            dst.resize(bytes);
-            return hipMemcpy(dst.data(), src, bytes, hipMemcpyDeviceToHost);
-        };
         std::vector<uint8_t> buf;
         if (dcodes_host) {
-            if ((e = fetch(q->dq, (size_t)(g.Nslot * Kp / 2), buf)) != hipSuccess) return hip_fail(e, "copy delta codes");
+            if ((e = fetch_all(q->dq, (size_t)(q->Nslot_pad * Kp / 2), buf)) != hipSuccess) return hip_fail(e, "copy delta codes");
             for (long long s = 0; s < g.Nslot; ++s) {
                 long long t = host_slot_token(g, s);
-                if (t >= 0) std::memcpy(dcodes_host + t * (Ci / 2), &buf[(size_t)(s * (Kp / 2))], (size_t)(Ci / 2));
+                if (t >= 0) unstep_fp4(buf, s, Ci, Kp, dcodes_host + t * (Ci / 2));
             }
         }
         if (dscales_host) {
-            if ((e = fetch(q->ds, (size_t)(g.Nslot * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy delta scales");
+            if ((e = fetch_all(q->ds, (size_t)(q->Nslot_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy delta scales");
             for (long long s = 0; s < g.Nslot; ++s) {
                 long long t = host_slot_token(g, s);
-                if (t >= 0) std::memcpy(dscales_host + t * (Ci / 32), &buf[(size_t)(s * (Kp / 32))], (size_t)(Ci / 32));
+                if (t >= 0) unstep_scales(buf, s, Ci, Kp, dscales_host + t * (Ci / 32));
             }
         }
         if (ccodes_host) {
-            e = hipMemcpy2D(ccodes_host, (size_t)Ci, q->cq, (size_t)Kp, (size_t)Ci, (size_t)g.K, hipMemcpyDeviceToHost);
-            if (e != hipSuccess) return hip_fail(e, "copy core codes");
+            if ((e = fetch_all(q->cq, (size_t)(q->K_pad * Kp), buf)) != hipSuccess) return hip_fail(e, "copy core codes");
+            for (long long k = 0; k < g.K; ++k) unstep_fp8(buf, k, Ci, Kp, ccodes_host + k * Ci);
         }
         if (cscales_host) {
-            e = hipMemcpy2D(cscales_host, (size_t)(Ci / 32), q->cs, (size_t)(Kp / 32), (size_t)(Ci / 32), (size_t)g.K,
-                            hipMemcpyDeviceToHost);
-            if (e != hipSuccess) return hip_fail(e, "copy core scales");
+            if ((e = fetch_all(q->cs, (size_t)(q->K_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy core scales");
+            for (long long k = 0; k < g.K; ++k) unstep_scales(buf, k, Ci, Kp, cscales_host + k * (Ci / 32));
         }
         if (u_host && q->rank > 0) {
-            if ((e = fetch(q->u, (size_t)(g.Nslot * q->rp * 2), buf)) != hipSuccess) return hip_fail(e, "copy U");
+            if ((e = fetch_all(q->u, (size_t)(g.Nslot * q->rp * 2), buf)) != hipSuccess) return hip_fail(e, "copy U");
             const uint16_t* ub = (const uint16_t*)buf.data();
             for (long long s = 0; s < g.Nslot; ++s) {
                 long long t = host_slot_token(g, s);

@@ -24,6 +24,36 @@ constexpr int CORE_BLOCK = 64;  // tokens per fp32 partial sum of a cube's core
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+// Operand layout of the GEMMs.  A code (or scale) matrix of rows x Kp
+// channels, rows a multiple of 256 and Kp of 128, is stored step-major:
+// [row / 256][Kp / 128][row % 256][bytes of one row's 128-channel step], so
+// one GEMM tile's K step (256 rows x 128 channels) is a single contiguous
+// block that the GEMM copies into LDS unchanged.  Inside a row's step the
+// 16-byte chunks are XOR-swizzled by the row, which makes the GEMM's
+// fragment reads from LDS free of bank conflicts:
+//   FP4 codes:  64 bytes per row step, chunk c (channels 32c .. 32c + 31,
+//               element 2i in the low nibble of byte i) at (c ^ swz4(row));
+//   FP8 codes: 128 bytes per row step, chunk c (channels 16c .. 16c + 15)
+//               at (c ^ swz8(row));
+//   E8M0 scale codes: 4 bytes per row step, one per 32-channel group, in
+//               group order (no swizzle).
+__host__ __device__ inline int swz4(int r) { return (r >> 1) & 3; }
+__host__ __device__ inline int swz8(int r) { return r & 7; }
+// byte offset of FP4 group G (32 channels, 16 bytes) of a row
+__host__ __device__ inline size_t off_fp4(long long row, long long G, long long nks) {
+    const int r = (int)(row & 255);
+    return ((size_t)((row >> 8) * nks + (G >> 2)) * 256 + r) * 64 + (size_t)((((int)G & 3) ^ swz4(r)) << 4);
+}
+// byte offset of 16-byte chunk c (channels 16c .. 16c + 15 of the row's step ks) of an FP8 row
+__host__ __device__ inline size_t off_fp8(long long row, long long ks, int c, long long nks) {
+    const int r = (int)(row & 255);
+    return ((size_t)((row >> 8) * nks + ks) * 256 + r) * 128 + (size_t)((c ^ swz8(r)) << 4);
+}
+// byte offset of the scale code of group G of a row
+__host__ __device__ inline size_t off_scale(long long row, long long G, long long nks) {
+    return ((size_t)((row >> 8) * nks + (G >> 2)) * 256 + (size_t)(row & 255)) * 4 + (size_t)(G & 3);
+}
+
 // Token grid and cube shape, with derived counts, as kernels see them.
 struct Geom {
     int T, H, W, t, h, w;
@@ -37,8 +67,8 @@ struct dq_weights {
     int device = 0;
     int64_t Ci = 0, Co = 0, Kp = 0, Cop = 0;
     int rank = 0, rp = 0;
-    uint8_t* rq = nullptr;     // [Cop][Kp/2]   Q4(R) codes (device)
-    uint8_t* rs = nullptr;     // [Cop][Kp/32]  Q4(R) scale codes (device)
+    uint8_t* rq = nullptr;     // Cop x Kp/2    Q4(R) codes, step-major (device)
+    uint8_t* rs = nullptr;     // Cop x Kp/32   Q4(R) scale codes, step-major (device)
     float* r = nullptr;        // [Co][Ci]      fp32 residual R^T (device, for export)
     uint16_t* l1t = nullptr;   // [rp][Kp]      L1^T bf16 (device)
     uint16_t* l2t = nullptr;   // [Cop][rp]     L2^T bf16 (device)
@@ -54,12 +84,13 @@ struct dq_qact {
     int64_t Nslot_pad = 0, K_pad = 0;
     int core_mode = 0;         // 0: cores inside the activation pass (S <= 64); 1: separate passes
     int64_t nblk = 0;          // 64-token blocks per cube (core_mode 1)
-    uint8_t* dq = nullptr;     // [Nslot_pad][Kp/2]  delta codes, slot order
-    uint8_t* ds = nullptr;     // [Nslot_pad][Kp/32] delta scale codes
-    uint8_t* cq = nullptr;     // [K_pad][Kp]        core FP8 codes
-    uint8_t* cs = nullptr;     // [K_pad][Kp/32]     core scale codes
+    uint8_t* dq = nullptr;     // Nslot_pad x Kp/2   delta codes, slot order, step-major
+    uint8_t* ds = nullptr;     // Nslot_pad x Kp/32  delta scale codes, step-major
+    uint8_t* cq = nullptr;     // K_pad x Kp         core FP8 codes, step-major
+    uint8_t* cs = nullptr;     // K_pad x Kp/32      core scale codes, step-major
     uint16_t* u = nullptr;     // [Nslot_pad][rp]    U = bf16(bf16(X) L1), slot order
     float* bias = nullptr;     // [K_pad][Cop]       per-cube core term Q8(core) Q4(R)
+    int* stok = nullptr;       // [Nslot_pad]        token of each slot, -1 for pad slots
     float* coref = nullptr;    // [K][Kp]            fp32 cores (core_mode 1)
     float* part = nullptr;     // [K*nblk][Kp]       fp32 block partials (core_mode 1)
     size_t bytes = 0;
@@ -72,10 +103,10 @@ void set_error(const std::string& msg);
 // ---- launchers (quant.hip) ----
 hipError_t launch_residual(const void* w_dev, int w_bf16, const uint16_t* l1_dev, const uint16_t* l2_dev,
                            int64_t Ci, int64_t Co, int rank, float* r_dev, hipStream_t st);
-hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, int64_t ld_src,
-                                  uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
-                                  hipStream_t st);
+hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, int64_t ld_src, int64_t Kp,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qact* q, hipStream_t st);
+hipError_t launch_slot_tokens(const Geom& g, int* stok, int64_t n, hipStream_t st);
 
 // ---- launchers (gemm.hip) ----
 hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t st);

@@ -4,30 +4,36 @@
 //   y_n = U_n L2 + Q8(core_k(n)) Q4(R) + Q4(delta_n) Q4(R)
 // The core term is one row per cube (the "dynamic token bias", broadcast to
 // the cube's tokens); the delta term is one row per token.  Two launches of
-// one kernel template: the core GEMM (A = FP8 E4M3 cores, one row per cube)
-// writes the per-cube term; the delta GEMM (A = FP4 E2M1 deltas, one row per
+// one kernel template: the core GEMM (FP8 E4M3 cores, one row per cube)
+// writes the per-cube term; the delta GEMM (FP4 E2M1 deltas, one row per
 // slot) adds U L2, adds its cube's core term in the epilogue and scatters rows
 // to token order.  Both are V_MFMA_SCALE_F32_32X32X64_F8F6F4 contractions
 // over Ci with the E8M0 block scales applied inside the instruction, fp32
 // accumulation.
 //
-// Work decomposition: a 256-thread workgroup computes a 256 x 256 output
-// tile; its four waves each own 128 x 128 (4 x 4 MFMA tiles of 32 x 32,
-// 256 accumulator registers).
+// Operand roles: the MFMA's A operand is Q4(R) (its rows are output
+// channels) and its B operand is the activation (rows are slots or cubes), so
+// the accumulator tile is the transposed output: each lane holds, for one
+// token, runs of four consecutive output channels, which the epilogue writes
+// as 16-byte stores straight into the token's output row.
 //
-// Data movement: three LDS stages of one K step (128 channels) each.  A
-// codes, B codes and their E8M0 scale bytes go straight from global memory
-// into the stage two steps ahead (global_load_lds, no staging registers)
-// while the MFMAs run on the current stage; before the barrier that ends a
-// step each wave waits only for its copies of the next stage.  LDS rows hold
-// 16-byte chunks XOR-swizzled so every fragment read is free of bank
-// conflicts.  Rows, columns and K of every operand are padded to the tile
-// with zero codes and zero scales, so the main loop has no bounds checks.
+// Work decomposition: a 256-thread workgroup computes a 256-channel x
+// 256-slot tile; its four waves each own 128 x 128 (4 x 4 MFMA tiles of
+// 32 x 32, 256 accumulator registers).
+//
+// Data movement: all operands are stored step-major (one tile's 256 rows x
+// 128-channel K step is one contiguous block, 16-byte chunks pre-swizzled
+// for conflict-free LDS reads), so a K step lands in LDS by plain 1 KB
+// global_load_lds copies (no staging registers).  A ring of NS stages runs
+// NS - 2 steps ahead of the MFMAs.  Each K step is two 64-channel halves; the
+// fragments of one half are read from LDS while the MFMAs of the other half
+// run, so MFMAs never wait for LDS, and one barrier per step hands a landed
+// stage to all waves and frees the oldest one for the next copy.
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs; tile
 // indices are remapped so the workgroups resident on one XCD at a time cover
-// a compact block of 4 row tiles x 8 column tiles and share their A and B
-// stages in that XCD's L2.
+// a compact block of 4 channel tiles x 8 slot tiles and share their operand
+// steps in that XCD's L2.
 #include <type_traits>
 
 #include "dq_device.h"
@@ -35,19 +41,20 @@
 namespace dq {
 
 struct GemmArgs {
-    const uint8_t* a;   // A codes, rows of lda bytes
-    const uint8_t* as;  // A scale codes, rows of ldas bytes
-    long long lda, ldas;
-    const uint8_t* b;   // B = Q4(R) codes [Cop][Kp/2]
-    const uint8_t* bs;  // B scale codes [Cop][Kp/32]
-    long long ldb, ldbs;
-    int Kp;             // multiple of 128
-    int mtiles, ntiles;
-    float* c;           // plain store epilogue: c[row][col]
+    const uint8_t* a;   // A = Q4(R) codes, step-major, rows = output channels
+    const uint8_t* as;  // A scale codes, step-major
+    const uint8_t* b;   // B = activation codes (FP4 deltas / FP8 cores), step-major
+    const uint8_t* bs;  // B scale codes, step-major
+    int nks;            // K steps (Kp / 128)
+    int mtiles, ntiles; // 256-row tiles of A and of B
+    float* c;           // plain store epilogue: c[b row][a row], leading dimension ldc
     long long ldc;
-    float* y;           // token epilogue: y[token][col]
+    float* y;           // token epilogue: y[token][channel], Co channels per row
     int Co;
-    Geom g;
+    int vec4;           // y rows are 16-byte aligned (Co % 4 == 0, y 16-byte aligned)
+    const int* stok;    // slot -> token (-1 for pad slots), Nslot_pad entries
+    int S;              // slots per cube
+    int kmax;           // last cube index
     const float* bias;  // per-cube core term [K_pad][ldbias]
     long long ldbias;
     const uint16_t* u;     // [Nslot_pad][rp]
@@ -73,13 +80,14 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
+// `base` must come from uniform_ptr.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff),
-                 "s"(uniform_ptr(base)) : "memory", "m0");
+                 "s"(base) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff),
-                 "s"(uniform_ptr(base)) : "memory", "m0");
+                 "s"(base) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
@@ -91,93 +99,156 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// XOR swizzles of 16-byte chunks within an LDS row.
-__device__ __forceinline__ int swz64(int row) { return (row >> 1) & 3; }   // 64-byte rows (4 chunks)
-__device__ __forceinline__ int swz128(int row) { return row & 7; }         // 128-byte rows (8 chunks)
-
-template <int AFMT, int OPSEL>
-__device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, AFMT, FMT_FP4, OPSEL, sa, OPSEL, sb);
-}
-
-// Tile of workgroup `bid` (see the file comment); returns false for the
-// padding workgroups beyond the tile count.
-__device__ __forceinline__ bool tile_of(int bid, int mt, int nt, int* tm, int* tn) {
+// Persistent schedule.  Workgroup b runs on XCD b & 7 (dispatch is
+// round-robin over the 8 XCDs) and takes the tiles of its XCD's share: XCD x
+// owns tile indices [x per, (x + 1) per), and its workgroups walk them with
+// stride G / 8, so the workgroups resident on one XCD at one time hold
+// consecutive indices.  Index v -> (channel tile, slot tile) in groups of GM
+// channel tiles x all slot tiles, column-major inside a group, so those
+// resident workgroups cover a compact block of 4 channel tiles x 8 slot
+// tiles and share their operand steps in the XCD's L2.
+struct TileWalk {
+    int x, y0, ystride, ylim, per, mt, nt;
+    __device__ int count() const { return y0 < ylim ? (ylim - y0 + ystride - 1) / ystride : 0; }
+    __device__ void coords(int it, int* tm, int* tn) const {
+        const int v = x * per + y0 + it * ystride;
+        constexpr int GM = 4;
+        const int grp = v / (GM * nt);
+        const int first = grp * GM;
+        const int gm = min(GM, mt - first);
+        const int within = v - grp * GM * nt;
+        *tm = first + within % gm;
+        *tn = within / gm;
+    }
+};
+__device__ __forceinline__ TileWalk tile_walk(int b, int G, int mt, int nt) {
+    TileWalk w;
     const int total = mt * nt;
-    const int per = (total + 7) / 8;
-    const int v = (bid & 7) * per + (bid >> 3);
-    if (v >= total) return false;
-    constexpr int GM = 4;
-    const int grp = v / (GM * nt);
-    const int first = grp * GM;
-    const int gm = min(GM, mt - first);
-    const int within = v - grp * GM * nt;
-    *tm = first + within % gm;
-    *tn = within / gm;
-    return true;
+    w.per = (total + 7) / 8;
+    w.x = b & 7;
+    w.y0 = b >> 3;
+    w.ystride = G >> 3;
+    w.ylim = min(w.per, total - w.x * w.per);
+    w.mt = mt;
+    w.nt = nt;
+    return w;
 }
 
-template <int AFMT, int EPI>
+// SMALLK: a K loop shorter than NS steps (the copy cursor may then run
+// ahead of the MFMAs' tile from a tile's first step on, or several tiles
+// ahead); that form recomputes the copy sources every step, the other one
+// only once per tile.
+template <int BFMT, int EPI, bool SMALLK>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
-    constexpr int AROW = AFMT == FMT_FP4 ? 64 : 128;            // A bytes per row per 128-wide K step
-    constexpr int A_BYTES = 256 * AROW;
-    constexpr int B_BYTES = 256 * 64;
-    constexpr int SA_OFF = A_BYTES + B_BYTES;
+    constexpr int BROW = BFMT == FMT_FP4 ? 64 : 128;         // B bytes per row per K step
+    constexpr int A_STEP = 256 * 64;                          // A bytes per tile step
+    constexpr int B_STEP = 256 * BROW;
+    constexpr int B_OFF = A_STEP;
+    constexpr int SA_OFF = B_OFF + B_STEP;
     constexpr int SB_OFF = SA_OFF + 1024;
     constexpr int STAGE = SB_OFF + 1024;
-    constexpr int NS = AFMT == FMT_FP4 ? 4 : 3;                // LDS stages in the ring
+    constexpr int NS = BFMT == FMT_FP4 ? 4 : 3;               // LDS stages in the ring
+    constexpr int APC = A_STEP / 1024 / 4;                    // 1 KB copies per wave: A
+    constexpr int BPC = B_STEP / 1024 / 4;                    //                       B
+    constexpr int DMAS = APC + BPC + 2;                       // copies per wave per stage
+    static_assert((NS - 3) * DMAS < 63, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
-    __shared__ long long rtok[EPI == EPI_TOKENS ? 256 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int g = lane >> 5, l32 = lane & 31;
-    int tm, tn;
-    if (!tile_of(blockIdx.x, p.mtiles, p.ntiles, &tm, &tn)) return;
-    const long long m0 = (long long)tm * 256, n0 = (long long)tn * 256;
-
-    if (EPI == EPI_TOKENS) {
-        long long slot = m0 + tid;
-        rtok[tid] = slot < p.g.Nslot ? slot_token(p.g, slot) : -1;
-    }
-
-    // ---- this lane's copy sources: uniform tile bases + per-lane 32-bit offsets.
-    // A: 256 rows x AROW bytes per stage = APC pieces of 1 KB per wave.
-    constexpr int APC = A_BYTES / 1024 / 4;       // pieces per wave (4 or 8)
-    constexpr int ACH = AROW / 16;                // 16-byte chunks per A row
-    constexpr int DMAS = APC + 4 + 2;             // copies per wave per stage
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t aoff[APC], boff[4];
-#pragma unroll
-    for (int j = 0; j < APC; ++j) {
-        int lin = (wv * APC + j) * 64 + lane;     // 16-byte chunk index within the stage
-        int row = lin / ACH, pc = lin % ACH;
-        int ch = AFMT == FMT_FP4 ? (pc ^ swz64(row)) : (pc ^ swz128(row));
-        aoff[j] = (uint32_t)(row * p.lda + ch * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int lin = (wv * 4 + j) * 64 + lane;
-        int row = lin >> 2, pc = lin & 3;
-        boff[j] = (uint32_t)(row * p.ldb + (pc ^ swz64(row)) * 16);
-    }
-    const uint32_t asoff = (uint32_t)((wv * 64 + lane) * p.ldas);
-    const uint32_t bsoff = (uint32_t)((wv * 64 + lane) * p.ldbs);
-    const uint8_t* abase = p.a + m0 * p.lda;
-    const uint8_t* bbase = p.b + n0 * p.ldb;
-    const uint8_t* asbase = p.as + m0 * p.ldas;
-    const uint8_t* bsbase = p.bs + n0 * p.ldbs;
-    const uint32_t lds0 = lds_addr(smem);
+    const TileWalk walk = tile_walk(blockIdx.x, gridDim.x, p.mtiles, p.ntiles);
+    const int ntiles = walk.count();
+    if (ntiles == 0) return;
+    const int nk = p.nks;
+    const int nsteps = ntiles * nk;
 
-    auto issue = [&](int kt, int buf) {
+    // Stagger: the eight XCDs start an eighth of a tile apart, so their
+    // epilogues (output stores) are spread over time instead of all CUs
+    // writing at once; the workgroups of one XCD stay in step, since they
+    // share operand steps in its L2.
+    {
+        const int phase = walk.x;
+        const long long wait = (long long)phase * nk * 160;
+        const long long t0 = (long long)clock64();
+        while ((long long)clock64() - t0 < wait) __builtin_amdgcn_s_sleep(8);
+    }
+
+    // ---- copies.  Global step s (over all of this workgroup's tiles) is
+    // K step s % nk of tile s / nk; the issue cursor walks them in order.
+    // Per-lane offsets are 32-bit; tile bases are uniform (scalar registers).
+    const uint32_t lds0 = lds_addr(smem);
+    const uint32_t va = (uint32_t)lane * 16 + wv * APC * 1024, vb = (uint32_t)lane * 16 + wv * BPC * 1024;
+    const uint32_t vs = (uint32_t)lane * 4 + wv * 256;
+    // The copy cursor (tile tf, K step kf) runs NS - 1 steps ahead of the
+    // MFMAs.  Past the last step it stays on it: those surplus copies land in
+    // buffers no step reads and keep the number of copies per step uniform.
+    // The step body must stay free of branches (the compiler would move the
+    // MFMAs across them), so the cursor advances by selects.
+    int tf = 0, kf = 0;
+    struct Src {
+        const uint8_t *a, *b, *as, *bs;
+    };
+    auto src_of = [&](int t, int k) {
+        int tm, tn;
+        walk.coords(t, &tm, &tn);
+        Src r;
+        r.a = (const uint8_t*)uniform_ptr(p.a + ((size_t)tm * p.nks + k) * A_STEP);
+        r.b = (const uint8_t*)uniform_ptr(p.b + ((size_t)tn * p.nks + k) * B_STEP);
+        r.as = (const uint8_t*)uniform_ptr(p.as + ((size_t)tm * p.nks + k) * 1024);
+        r.bs = (const uint8_t*)uniform_ptr(p.bs + ((size_t)tn * p.nks + k) * 1024);
+        return r;
+    };
+    // copy number j (0 .. DMAS - 1) of a step into LDS buffer buf
+    auto dma = [&](const Src& src, int buf, int j) {
         const uint32_t st = lds0 + buf * STAGE;
-#pragma unroll
-        for (int j = 0; j < APC; ++j) dma16(abase + (long long)kt * AROW, aoff[j], st + (wv * APC + j) * 1024);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(bbase + kt * 64, boff[j], st + A_BYTES + (wv * 4 + j) * 1024);
-        dma4(asbase + kt * 4, asoff, st + SA_OFF + wv * 256);
-        dma4(bsbase + kt * 4, bsoff, st + SB_OFF + wv * 256);
+        if (j < APC) {
+            dma16(src.a, va + j * 1024, st + (wv * APC + j) * 1024);
+        } else if (j < APC + BPC) {
+            const int jb = j - APC;
+            dma16(src.b, vb + jb * 1024, st + B_OFF + (wv * BPC + jb) * 1024);
+        } else if (j == APC + BPC) {
+            dma4(src.as, vs, st + SA_OFF + wv * 256);
+        } else {
+            dma4(src.bs, vs, st + SB_OFF + wv * 256);
+        }
+    };
+    // Cursor advance.  General form: recompute from (tf, kf).  Otherwise
+    // (nk >= NS) the cursor is in the MFMAs' tile it when that tile starts and
+    // wraps into tile it + 1 at step nk - NS: pointer increments inside a
+    // tile, and at the wrap the sources of the next tile's first step
+    // (prepared at the start of tile it in `nsrc`; for the last tile, its own
+    // last step with zero increments, `ninc` = 0).
+    Src src = src_of(0, 0), nsrc{};
+    int inc = 1, ninc = 1;
+    auto advance = [&]() {
+        const bool wrap = kf + 1 == nk;
+        const bool stay = wrap && tf + 1 == ntiles;
+        if constexpr (SMALLK) {
+            kf = stay ? kf : (wrap ? 0 : kf + 1);
+            tf = (wrap && !stay) ? tf + 1 : tf;
+            src = src_of(tf, kf);
+        } else {
+            kf = wrap ? 0 : kf + 1;
+            src.a = wrap ? nsrc.a : src.a + inc * A_STEP;
+            src.b = wrap ? nsrc.b : src.b + inc * B_STEP;
+            src.as = wrap ? nsrc.as : src.as + inc * 1024;
+            src.bs = wrap ? nsrc.bs : src.bs + inc * 1024;
+            inc = wrap ? ninc : inc;
+        }
+    };
+    auto prepare_next = [&](int it) {                  // tile it + 1 (or the clamp), for the cursor's wrap
+        if constexpr (!SMALLK) {
+            if (it + 1 < ntiles) {
+                nsrc = src_of(it + 1, 0);
+                ninc = 1;
+            } else {
+                nsrc = src_of(ntiles - 1, nk - 1);
+                ninc = 0;
+            }
+        }
     };
 
     v16f acc[4][4];
@@ -186,277 +257,264 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
 
-    // ---- low-rank branch first (registers are free here): acc = U L2 with
-    // 32x32x16 bf16 MFMAs over the padded rank; the K loop accumulates on top.
-    if (EPI == EPI_TOKENS) {
+    // ---- fragments of one 64-channel half step, byte addresses within a stage
+    const int arow0 = wr * 128 + l32;            // + 32 mi
+    const int brow0 = wc * 128 + l32;            // + 32 ni
+    const int asw = swz4(arow0);                 // the swizzles depend on row % 8 only
+    const int bsw = BFMT == FMT_FP4 ? swz4(brow0) : swz8(brow0);
+    struct Half {
+        uint4 a[4];
+        uint4 b[BFMT == FMT_FP4 ? 4 : 1];      // FP4 B fragments
+        v8i b8[BFMT == FMT_FP4 ? 1 : 4];       // FP8 B fragments (two 16-byte chunks each)
+        int sa[4], sb[4];
+    };
+    // LDS read number i (0 .. 15) of half kk's fragments, in the order of
+    // their first use by the MFMA sequence below: a0 b0 sa0 sb0 b1 sb1 b2 sb2
+    // b3 sb3 a1 sa1 a2 sa2 a3 sa3.
+    auto rd = [&](int buf, int kk, Half& F, int i) {
+        const uint8_t* st = smem + buf * STAGE;
+        auto rda = [&](int mi) { F.a[mi] = *(const uint4*)(st + (arow0 + 32 * mi) * 64 + (((2 * kk + g) ^ asw) << 4)); };
+        auto rdsa = [&](int mi) { F.sa[mi] = st[SA_OFF + (arow0 + 32 * mi) * 4 + 2 * kk + g]; };
+        auto rdsb = [&](int ni) { F.sb[ni] = st[SB_OFF + (brow0 + 32 * ni) * 4 + 2 * kk + g]; };
+        auto rdb = [&](int ni) {
+            const uint8_t* rowp = st + B_OFF + (brow0 + 32 * ni) * BROW;
+            if constexpr (BFMT == FMT_FP4) {
+                F.b[ni] = *(const uint4*)(rowp + (((2 * kk + g) ^ bsw) << 4));
+            } else {
+                const v4i lo = *(const v4i*)(rowp + (((4 * kk + g) ^ bsw) << 4));
+                const v4i hi = *(const v4i*)(rowp + (((4 * kk + 2 + g) ^ bsw) << 4));
+                F.b8[ni] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
+        switch (i) {
+            case 0: rda(0); break;
+            case 1: rdb(0); break;
+            case 2: rdsa(0); break;
+            case 3: rdsb(0); break;
+            case 4: rdb(1); break;
+            case 5: rdsb(1); break;
+            case 6: rdb(2); break;
+            case 7: rdsb(2); break;
+            case 8: rdb(3); break;
+            case 9: rdsb(3); break;
+            case 10: rda(1); break;
+            case 11: rdsa(1); break;
+            case 12: rda(2); break;
+            case 13: rdsa(2); break;
+            case 14: rda(3); break;
+            default: rdsa(3); break;
+        }
+    };
+    // MFMA number i (0 .. 15) of a half step: row block mi = i / 4, column block ni = i % 4
+    auto mma = [&](const Half& F, int i) {
+        const int mi = i >> 2, ni = i & 3;
+        const uint4 v = F.a[mi];
+        const v8i af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        v8i bf;
+        if constexpr (BFMT == FMT_FP4) {
+            const uint4 u = F.b[ni];
+            bf = (v8i){(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+        } else {
+            bf = F.b8[ni];
+        }
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[mi][ni], FMT_FP4, BFMT, 0, F.sa[mi], 0,
+                                                                      F.sb[ni]);
+    };
+
+    // ---- tile epilogue: acc[mi][ni][4 j + q] is channel m0 + wr 128 + 32 mi
+    // + 8 j + 4 g + q of B row n0 + wc 128 + 32 ni + l32.
+    auto epilogue = [&](int tm, int tn) {
+        const int m0 = tm * 256, n0 = tn * 256;
+        const int ch0 = m0 + wr * 128 + 4 * g;             // + 32 mi + 8 j
+        if (EPI == EPI_STORE) {
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                float* crow = p.c + (long long)(n0 + wc * 128 + 32 * ni + l32) * p.ldc + ch0;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const v16f& a = acc[mi][ni];
+                        *(float4*)(crow + 32 * mi + 8 * j) = make_float4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
+                    }
+            }
+            return;
+        }
+        // low-rank branch: acc += (U L2)^T with 32x32x16 bf16 MFMAs over the padded rank
         for (int kq = 0; kq < p.rp; kq += 16) {
-            v8bf ua[4], lb[4];
+            v8bf la[4], ub[4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
-                long long row = m0 + wr * 128 + l32 + 32 * mi;
-                ua[mi] = __builtin_bit_cast(v8bf, *(const uint4*)(p.u + row * p.rp + kq + 8 * g));
+                const long long ch = m0 + wr * 128 + l32 + 32 * mi;
+                la[mi] = __builtin_bit_cast(v8bf, *(const uint4*)(p.l2t + ch * p.rp + kq + 8 * g));
             }
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) {
-                long long col = n0 + wc * 128 + l32 + 32 * ni;
-                lb[ni] = __builtin_bit_cast(v8bf, *(const uint4*)(p.l2t + col * p.rp + kq + 8 * g));
+                const long long slot = n0 + wc * 128 + l32 + 32 * ni;
+                ub[ni] = __builtin_bit_cast(v8bf, *(const uint4*)(p.u + slot * p.rp + kq + 8 * g));
             }
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[mi], lb[ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[mi], ub[ni], acc[mi][ni], 0, 0, 0);
         }
-    }
-    // LDS fragment addresses (bytes within a stage)
-    const int arow0 = wr * 128 + l32;           // + 32 mi
-    const int brow0 = wc * 128 + l32;           // + 32 ni
-    const int sa_sw = AFMT == FMT_FP4 ? swz64(arow0) : swz128(arow0);
-    const int sb_sw = swz64(brow0);
-
-    // Fragments of one K step (both 64-wide halves), read from LDS one step
-    // ahead of their MFMAs into a second register set.
-    struct Frag {
-        uint4 a[2][4], a2[AFMT == FMT_FP4 ? 1 : 2][4], b[2][4];
-        uint32_t sa[4], sb[4];
-    };
-    auto load_frags = [&](int buf, Frag& F) {
-        const uint8_t* st = smem + buf * STAGE;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) F.sa[mi] = *(const uint32_t*)(st + SA_OFF + (arow0 + 32 * mi) * 4) >> (8 * g);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) F.sb[ni] = *(const uint32_t*)(st + SB_OFF + (brow0 + 32 * ni) * 4) >> (8 * g);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const uint8_t* rowp = st + (arow0 + 32 * mi) * AROW;
-                if constexpr (AFMT == FMT_FP4) {
-                    F.a[kk][mi] = *(const uint4*)(rowp + (((2 * kk + g) ^ sa_sw) << 4));
-                } else {
-                    F.a[kk][mi] = *(const uint4*)(rowp + (((4 * kk + g) ^ sa_sw) << 4));
-                    F.a2[kk][mi] = *(const uint4*)(rowp + (((4 * kk + 2 + g) ^ sa_sw) << 4));
-                }
-            }
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                F.b[kk][ni] = *(const uint4*)(st + A_BYTES + (brow0 + 32 * ni) * 64 + (((2 * kk + g) ^ sb_sw) << 4));
-        }
-    };
-    auto mfma_step = [&](const Frag& F) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const uint4 v = F.a[kk][mi];
-                v8i af;
-                if constexpr (AFMT == FMT_FP4) {
-                    af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                } else {
-                    const uint4 w = F.a2[kk][mi];
-                    af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, (int)w.x, (int)w.y, (int)w.z, (int)w.w};
-                }
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const uint4 u = F.b[kk][ni];
-                    const v8i bf = (v8i){(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-                    if (kk == 0)
-                        acc[mi][ni] = mfma32<AFMT, 0>(af, bf, acc[mi][ni], (int)F.sa[mi], (int)F.sb[ni]);
-                    else
-                        acc[mi][ni] = mfma32<AFMT, 2>(af, bf, acc[mi][ni], (int)F.sa[mi], (int)F.sb[ni]);
-                }
-            }
-    };
-
-    const int nk = p.Kp / 128;
-    if constexpr (AFMT == FMT_FP4) {
-        // ---- K loop over a ring of NS stages.  Step kt: copies for stage
-        // kt + NS - 1 go out (into the stage whose fragments were read at step
-        // kt - 2, long since consumed); wait for this wave's copies of stage
-        // kt + 1; barrier (now every wave's copies of kt + 1 have landed); read
-        // the fragments of kt + 1; run the MFMAs of kt from the fragments read
-        // one step earlier, so the MFMAs never wait for LDS.
-        for (int st = 0; st < NS - 1; ++st)
-            if (st < nk) issue(st, st);
-        if (nk >= NS - 1) wait_vm<(NS - 2) * DMAS>();   // stage 0 landed
-        else wait_vm<0>();
-        __syncthreads();
-        Frag F0, F1;
-        load_frags(0, F0);
-        auto step = [&](int kt, Frag& cur, Frag& nxt, auto STEADY) {
-            if constexpr (decltype(STEADY)::value) {
-                issue(kt + NS - 1, (kt + NS - 1) % NS);
-                wait_vm<(NS - 2) * DMAS>();              // stage kt + 1 landed; later ones may be in flight
-            } else {
-                if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-                wait_vm<0>();
-            }
-            __syncthreads();
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) load_frags((kt + 1) % NS, nxt);
-            mfma_step(cur);
-        };
-        int kt = 0;
-        for (; kt + NS < nk; kt += 2) {                 // steps kt and kt + 1 both issue copies
-            step(kt, F0, F1, std::true_type{});
-            step(kt + 1, F1, F0, std::true_type{});
-        }
-        for (; kt < nk; kt += 2) {                      // kt stays even: F0 always serves even steps
-            step(kt, F0, F1, std::false_type{});
-            if (kt + 1 < nk) step(kt + 1, F1, F0, std::false_type{});
-        }
-    } else {
-        // FP8 fragments are twice as wide, so a second register set does not
-        // fit beside 256 accumulators: read each step's fragments in the step.
-        // Step kt: copies for kt + NS - 1 out, fragments of kt read and MFMAs
-        // run, then wait for stage kt + 1 and barrier.
-        for (int st = 0; st < NS - 1; ++st)
-            if (st < nk) issue(st, st);
-        if (nk >= NS - 1) wait_vm<(NS - 2) * DMAS>();
-        else wait_vm<0>();
-        __syncthreads();
-        // one 64-wide K half at a time keeps only half the fragments live
-        auto compute = [&](int buf) {
-            const uint8_t* st = smem + buf * STAGE;
-            uint32_t sa[4], sb[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) sa[mi] = *(const uint32_t*)(st + SA_OFF + (arow0 + 32 * mi) * 4) >> (8 * g);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) sb[ni] = *(const uint32_t*)(st + SB_OFF + (brow0 + 32 * ni) * 4) >> (8 * g);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                v8i af[4], bf[4];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    const uint8_t* rowp = st + (arow0 + 32 * mi) * AROW;
-                    uint4 v0 = *(const uint4*)(rowp + (((4 * kk + g) ^ sa_sw) << 4));
-                    uint4 v1 = *(const uint4*)(rowp + (((4 * kk + 2 + g) ^ sa_sw) << 4));
-                    af[mi] = (v8i){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-                }
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    uint4 v = *(const uint4*)(st + A_BYTES + (brow0 + 32 * ni) * 64 + (((2 * kk + g) ^ sb_sw) << 4));
-                    bf[ni] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        if (kk == 0) acc[mi][ni] = mfma32<AFMT, 0>(af[mi], bf[ni], acc[mi][ni], (int)sa[mi], (int)sb[ni]);
-                        else acc[mi][ni] = mfma32<AFMT, 2>(af[mi], bf[ni], acc[mi][ni], (int)sa[mi], (int)sb[ni]);
-                    }
-            }
-        };
-        int kt = 0;
-        for (; kt + NS - 1 < nk; ++kt) {
-            issue(kt + NS - 1, (kt + NS - 1) % NS);
-            compute(kt % NS);
-            __builtin_amdgcn_sched_barrier(0);          // keep the MFMAs above the wait
-            wait_vm<(NS - 2) * DMAS>();
-            __syncthreads();
-        }
-        for (; kt < nk; ++kt) {
-            compute(kt % NS);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vm<0>();
-            __syncthreads();
-        }
-    }
-    __syncthreads();
-
-    if (EPI == EPI_STORE) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    long long row = m0 + wr * 128 + mi * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    long long col = n0 + wc * 128 + ni * 32 + l32;
-                    p.c[row * p.ldc + col] = acc[mi][ni][i];
-                }
-        return;
-    }
-
-    // ---- epilogue: y = acc + bias[cube], rows scattered to token order.
-    // The cube's core-term rows are staged in LDS, 64 slots (one 32-row MFMA
-    // block mi of each wave row) per phase, with the same register-free
-    // direct copies: one 1 KB row per wave instruction.
-    float* bl = (float*)smem;                              // [64 slots][256 columns]
-    const int S = p.g.S;
-    const long long kmax = p.g.K - 1;
-    auto bias_rows = [&](int mi) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int q = wv * 16 + j;                     // LDS row: wave row q / 32, row q % 32 of block mi
-            const long long slot = m0 + (q >> 5) * 128 + mi * 32 + (q & 31);
-            const long long k = min(slot / S, kmax);       // pad slots: any valid row, never stored
-            dma16(p.bias + k * p.ldbias + n0, (uint32_t)lane * 16, lds0 + q * 1024);
-        }
-    };
-    bias_rows(0);
-
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        wait_vm<0>();
-        __syncthreads();                                   // phase mi's rows have landed
-        long long yoff[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const long long t = rtok[wr * 128 + mi * 32 + 8 * (i >> 2) + 4 * g + (i & 3)];
-            yoff[i] = t < 0 ? -1 : t * (long long)p.Co + n0;
-        }
+        // y[token] = acc + core term of the token's cube (16-byte loads of the
+        // cube's row of the per-cube term, 16-byte stores into the token's row)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-            const int col = wc * 128 + ni * 32 + l32;
-            float bv[16];
+            const int slot = n0 + wc * 128 + 32 * ni + l32;
+            const int tok = p.stok[slot];
+            const int k = min(slot / p.S, p.kmax);          // pad slots: any valid row, never stored
+            const float* brow = p.bias + (long long)k * p.ldbias + ch0;
+            float4 bv[4][4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) bv[i] = bl[(wr * 32 + 8 * (i >> 2) + 4 * g + (i & 3)) * 256 + col];
-            if (n0 + col < p.Co) {
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (yoff[i] >= 0) p.y[yoff[i] + col] = acc[mi][ni][i] + bv[i];
-            }
+                for (int j = 0; j < 4; ++j) bv[mi][j] = *(const float4*)(brow + 32 * mi + 8 * j);
+            if (tok < 0) continue;
+            float* yrow = p.y + (long long)tok * p.Co;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v16f& a = acc[mi][ni];
+                    const float4 o = make_float4(a[4 * j] + bv[mi][j].x, a[4 * j + 1] + bv[mi][j].y,
+                                                 a[4 * j + 2] + bv[mi][j].z, a[4 * j + 3] + bv[mi][j].w);
+                    const int ch = ch0 + 32 * mi + 8 * j;
+                    if (p.vec4 && ch + 4 <= p.Co) {
+                        *(float4*)(yrow + ch) = o;
+                    } else {
+                        if (ch < p.Co) yrow[ch] = o.x;
+                        if (ch + 1 < p.Co) yrow[ch + 1] = o.y;
+                        if (ch + 2 < p.Co) yrow[ch + 2] = o.z;
+                        if (ch + 3 < p.Co) yrow[ch + 3] = o.w;
+                    }
+                }
         }
-        __syncthreads();                                   // every wave is done with phase mi's rows
-        if (mi < 3) bias_rows(mi + 1);
+    };
+
+    // ---- K loop over all global steps.  Step gs has two phases of 16 MFMAs,
+    // every MFMA followed by its companions (kept in place by scheduling
+    // barriers):
+    //   phase 1: MFMAs of half 0 of stage gs (fragments F0); companions read
+    //            half 1 of stage gs into F1;
+    //   then wait for this wave's copies of stage gs + 1 and barrier: all
+    //            copies of gs + 1 have landed, and every wave is done with
+    //            stage gs - 1, whose buffer takes the copies of gs + NS - 1;
+    //   phase 2: MFMAs of half 1 (F1); companions issue the copies of stage
+    //            gs + NS - 1 (possibly the next tile's) and read half 0 of
+    //            stage gs + 1 into F0.
+    // After the last step of a tile: wait for every copy in flight, then the
+    // epilogue (whose stores drain while the next tile runs), clear acc and
+    // read half 0 of the next tile's first stage.
+    // Fragments are read one phase before their MFMAs, so LDS latency hides
+    // behind 16 MFMAs.
+    for (int s = 0; s < NS - 1; ++s) {
+#pragma unroll
+        for (int j = 0; j < DMAS; ++j) dma(src, s, j);
+        advance();
+    }
+    wait_vm<(NS - 2) * DMAS>();                                // stage 0 landed
+    __syncthreads();
+    Half F0, F1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rd(0, 0, F0, i);
+    // Stage gs + 1 must have landed before the barrier of step gs.  Copies go
+    // out every step (past the end too), so normally NS - 3 later stages may
+    // still be in flight.  In a tile's first NS - 2 steps (after the first
+    // tile) stage gs + 1 was issued before the previous tile's epilogue, whose
+    // full wait already covered it; a loose count there lets the epilogue's
+    // stores stay in flight.  Half 0 of stage gs + 1 is read in every step,
+    // at a tile's last step too (it is the next tile's first stage).
+    int gs = 0;
+    for (int it = 0; it < ntiles; ++it) {
+        prepare_next(it);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
+        for (int ks = 0; ks < nk; ++ks, ++gs) {
+            const int cur = (unsigned)gs % NS, nxt = (unsigned)(gs + 1) % NS, fill = (unsigned)(gs + NS - 1) % NS;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mma(F0, i);
+                rd(cur, 1, F1, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Wait and barrier in one asm block (no branch for the compiler to
+            // move code across).  Every wave's reads of stage gs - 1 completed
+            // before its MFMAs of step gs - 1, so a bare barrier suffices; the
+            // memory clobber keeps the LDS reads below it.
+            const int loose = __builtin_amdgcn_readfirstlane((it > 0 && ks < NS - 2) ? 1 : 0);
+            asm volatile(
+                "s_cmp_eq_u32 %0, 0\n\t"
+                "s_cbranch_scc1 1f\n\t"
+                "s_waitcnt vmcnt(63)\n\t"
+                "s_branch 2f\n"
+                "1:\n\t"
+                "s_waitcnt vmcnt(%1)\n"
+                "2:\n\t"
+                "s_barrier" ::"s"(loose), "n"((NS - 3) * DMAS) : "memory", "scc");
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mma(F1, i);
+                if (i < DMAS) dma(src, fill, i);
+                rd(nxt, 0, F0, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            advance();
+        }
+        wait_vm<0>();
+        int tm, tn;
+        walk.coords(it, &tm, &tn);
+        epilogue(tm, tn);
     }
 }
 
-template <int AFMT, int EPI>
+// One persistent workgroup per CU (a multiple of 8, one share per XCD),
+// never more than the tiles need.
+static int persistent_grid(int total) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    int grid = max(8, cus / 8 * 8);
+    return min(grid, (total + 7) / 8 * 8);
+}
+
+template <int BFMT, int EPI>
 static hipError_t launch(const GemmArgs& a, hipStream_t st) {
-    int total = a.mtiles * a.ntiles;
-    int grid = (total + 7) / 8 * 8;
-    k_gemm<AFMT, EPI><<<grid, 256, 0, st>>>(a);
+    constexpr int NS = BFMT == FMT_FP4 ? 4 : 3;      // the kernel's LDS stages
+    const int grid = persistent_grid(a.mtiles * a.ntiles);
+    if (a.nks < NS) k_gemm<BFMT, EPI, true><<<grid, 256, 0, st>>>(a);
+    else k_gemm<BFMT, EPI, false><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t st) {
     GemmArgs d{};
-    d.b = w->rq;
-    d.bs = w->rs;
-    d.ldb = w->Kp / 2;
-    d.ldbs = w->Kp / 32;
-    d.Kp = (int)w->Kp;
-    d.ntiles = (int)(w->Cop / 256);
-    d.a = q->dq;
-    d.as = q->ds;
-    d.lda = q->Kp / 2;
-    d.ldas = q->Kp / 32;
-    d.mtiles = (int)(q->Nslot_pad / 256);
+    d.a = w->rq;
+    d.as = w->rs;
+    d.nks = (int)(w->Kp / 128);
+    d.mtiles = (int)(w->Cop / 256);
+    d.b = q->dq;
+    d.bs = q->ds;
+    d.ntiles = (int)(q->Nslot_pad / 256);
     d.y = y;
     d.Co = (int)w->Co;
-    d.g = q->g;
+    d.vec4 = (w->Co % 4 == 0) && ((uintptr_t)y % 16 == 0);
+    d.stok = q->stok;
+    d.S = q->g.S;
+    d.kmax = (int)(q->g.K - 1);
     d.u = q->u;
     d.l2t = w->l2t;
     d.rp = w->rp;
     // 1) per-cube core term bias[k] = Q8(core_k) Q4(R)
     GemmArgs c = d;
-    c.a = q->cq;
-    c.as = q->cs;
-    c.lda = q->Kp;
-    c.ldas = q->Kp / 32;
-    c.mtiles = (int)(q->K_pad / 256);
+    c.b = q->cq;
+    c.bs = q->cs;
+    c.ntiles = (int)(q->K_pad / 256);
     c.c = q->bias;
     c.ldc = w->Cop;
     hipError_t e = launch<FMT_FP8, EPI_STORE>(c, st);

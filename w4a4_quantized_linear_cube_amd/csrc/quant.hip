@@ -41,10 +41,10 @@ struct QuantArgs {
     int Ci, Kp, rp;
     int cubes_per_block;      // core_mode 0: whole cubes per workgroup
     int core_mode;            // 0: cores computed here; 1: read from coref
-    uint8_t* dq;              // [Nslot_pad][Kp/2]
-    uint8_t* ds;              // [Nslot_pad][Kp/32]
-    uint8_t* cq;              // [K_pad][Kp]
-    uint8_t* cs;              // [K_pad][Kp/32]
+    uint8_t* dq;              // Nslot_pad x Kp/2, step-major
+    uint8_t* ds;              // Nslot_pad x Kp/32, step-major
+    uint8_t* cq;              // K_pad x Kp, step-major
+    uint8_t* cs;              // K_pad x Kp/32, step-major
     uint16_t* u;              // [Nslot_pad][rp]
     const uint16_t* l1t;      // [rp][Kp]
     const float* coref;       // [K][Kp] (core_mode 1)
@@ -200,11 +200,10 @@ __global__ __launch_bounds__(QTHREADS) void k_quantize(QuantArgs a) {
                 int e = mx_exp_fp8(amax);
                 uint4 lo, hi;
                 encode_fp8x32(v, pow2f(e), lo, hi);
-                long long k = k_first + cr;
-                uint8_t* dst = a.cq + k * (long long)a.Kp + c0 + 32 * j;
-                *(uint4*)dst = lo;
-                *(uint4*)(dst + 16) = hi;
-                a.cs[k * (long long)(a.Kp / 32) + (c0 >> 5) + j] = (uint8_t)(e + 127);
+                const long long k = k_first + cr, G = (c0 >> 5) + j, nks = a.Kp / 128;
+                *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3), nks)) = lo;
+                *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + 1, nks)) = hi;
+                a.cs[off_scale(k, G, nks)] = (uint8_t)(e + 127);
             }
         }
 
@@ -222,9 +221,9 @@ __global__ __launch_bounds__(QTHREADS) void k_quantize(QuantArgs a) {
             }
             int e = mx_exp_fp4(amax);
             uint4 codes = encode_fp4x32(v, pow2f(e));
-            long long s = slot_of[r];
-            *(uint4*)(a.dq + s * (long long)(a.Kp / 2) + ((c0 + 32 * j) >> 1)) = codes;
-            a.ds[s * (long long)(a.Kp / 32) + (c0 >> 5) + j] = (uint8_t)(e + 127);
+            const long long s = slot_of[r], G = (c0 >> 5) + j, nks = a.Kp / 128;
+            *(uint4*)(a.dq + off_fp4(s, G, nks)) = codes;
+            a.ds[off_scale(s, G, nks)] = (uint8_t)(e + 127);
         }
         __syncthreads();
     }
@@ -285,8 +284,8 @@ struct CombineArgs {
     long long nblk;
     const float* part;
     float* coref;    // [K][Kp]
-    uint8_t* cq;     // [K_pad][Kp]
-    uint8_t* cs;     // [K_pad][Kp/32]
+    uint8_t* cq;     // K_pad x Kp, step-major
+    uint8_t* cs;     // K_pad x Kp/32, step-major
 };
 
 // core = fl32(sum of the block partials in block order / count), then FP8 codes.
@@ -321,10 +320,10 @@ __global__ __launch_bounds__(256) void k_core_combine(CombineArgs a) {
         int e = mx_exp_fp8(amax);
         uint4 lo, hi;
         encode_fp8x32(v, pow2f(e), lo, hi);
-        uint8_t* dst = a.cq + k * (long long)a.Kp + cg;
-        *(uint4*)dst = lo;
-        *(uint4*)(dst + 16) = hi;
-        a.cs[k * (long long)(a.Kp / 32) + (cg >> 5)] = (uint8_t)(e + 127);
+        const long long G = cg >> 5, nks = a.Kp / 128;
+        *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3), nks)) = lo;
+        *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + 1, nks)) = hi;
+        a.cs[off_scale(k, G, nks)] = (uint8_t)(e + 127);
     }
 }
 
@@ -342,10 +341,10 @@ __global__ __launch_bounds__(256) void k_residual(const WT* w, const uint16_t* l
     r[idx] = (float)(wv - p);
 }
 
-// MX-FP4 encode of rows: one (row, 32-group) per thread.
+// MX-FP4 encode of rows into the GEMM's step-major layout: one (row, 32-group) per thread.
 __global__ __launch_bounds__(256) void k_encode_fp4_rows(const float* src, long long rows, long long cols,
-                                                        long long ld_src, uint8_t* codes, long long ld_codes,
-                                                        uint8_t* scales, long long ld_scales) {
+                                                        long long ld_src, long long Kp, uint8_t* codes,
+                                                        uint8_t* scales) {
     long long ng = cols / 32;
     long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= rows * ng) return;
@@ -359,8 +358,14 @@ __global__ __launch_bounds__(256) void k_encode_fp4_rows(const float* src, long 
         amax = fmaxf(amax, fabsf(v[i]));
     }
     int e = mx_exp_fp4(amax);
-    *(uint4*)(codes + rrow * ld_codes + grp * 16) = encode_fp4x32(v, pow2f(e));
-    scales[rrow * ld_scales + grp] = (uint8_t)(e + 127);
+    *(uint4*)(codes + off_fp4(rrow, grp, Kp / 128)) = encode_fp4x32(v, pow2f(e));
+    scales[off_scale(rrow, grp, Kp / 128)] = (uint8_t)(e + 127);
+}
+
+// Slot -> token table of the GEMM epilogue (-1 for pad slots).
+__global__ __launch_bounds__(256) void k_slot_tokens(Geom g, int* stok, long long n) {
+    long long s = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (s < n) stok[s] = s < g.Nslot ? (int)slot_token(g, s) : -1;
 }
 
 // ------------------------------------------------------------ launchers ----
@@ -375,11 +380,11 @@ hipError_t launch_residual(const void* w_dev, int w_bf16, const uint16_t* l1_dev
     return hipGetLastError();
 }
 
-hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, int64_t ld_src, uint8_t* codes,
-                                  int64_t ld_codes, uint8_t* scales, int64_t ld_scales, hipStream_t st) {
+hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, int64_t ld_src, int64_t Kp,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t st) {
     long long n = rows * (cols / 32);
     unsigned blocks = (unsigned)((n + 255) / 256);
-    k_encode_fp4_rows<<<blocks, 256, 0, st>>>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales);
+    k_encode_fp4_rows<<<blocks, 256, 0, st>>>(src, rows, cols, ld_src, Kp, codes, scales);
     return hipGetLastError();
 }
 
@@ -417,6 +422,11 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
                                         : (unsigned)((g.Nslot + QROWS - 1) / QROWS);
     if (x_bf16) k_quantize<uint16_t><<<blocks, QTHREADS, 0, st>>>(a);
     else k_quantize<float><<<blocks, QTHREADS, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_slot_tokens(const Geom& g, int* stok, int64_t n, hipStream_t st) {
+    k_slot_tokens<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, stok, n);
     return hipGetLastError();
 }
 
