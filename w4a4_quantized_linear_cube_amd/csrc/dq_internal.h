@@ -35,10 +35,10 @@ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 //               element 2i in the low nibble of byte i) at (c ^ swz4(row));
 //   FP8 codes: 128 bytes per row step, chunk c (channels 16c .. 16c + 15)
 //               at (c ^ swz8(row));
-//   E8M0 scale codes: 4 bytes per row step, one per 32-channel group, in
-//               group order (no swizzle).
-__host__ __device__ inline int swz4(int r) { return (r >> 1) & 3; }
-__host__ __device__ inline int swz8(int r) { return r & 7; }
+//   E8M0 scale codes: one byte per row and 32-channel group, 1 KB per
+//               tile step, in the order given at off_scale.
+__host__ __device__ inline int swz4(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
+__host__ __device__ inline int swz8(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 // byte offset of FP4 group G (32 channels, 16 bytes) of a row
 __host__ __device__ inline size_t off_fp4(long long row, long long G, long long nks) {
     const int r = (int)(row & 255);
@@ -49,9 +49,14 @@ __host__ __device__ inline size_t off_fp8(long long row, long long ks, int c, lo
     const int r = (int)(row & 255);
     return ((size_t)((row >> 8) * nks + ks) * 256 + r) * 128 + (size_t)((c ^ swz8(r)) << 4);
 }
-// byte offset of the scale code of group G of a row
+// byte offset of the scale code of group G of a row.  A step's scale block
+// (256 rows x 4 groups, 1 KB) is ordered [row / 128][G % 2][row % 32]
+// [(row % 128) / 32][(G % 4) / 2], so the 8 codes one GEMM lane needs in a K
+// step (its four 32-row blocks x its two groups) are 8 consecutive bytes.
 __host__ __device__ inline size_t off_scale(long long row, long long G, long long nks) {
-    return ((size_t)((row >> 8) * nks + (G >> 2)) * 256 + (size_t)(row & 255)) * 4 + (size_t)(G & 3);
+    const int r = (int)(row & 255), gi = (int)(G & 3);
+    return ((size_t)((row >> 8) * nks + (G >> 2))) * 1024 +
+           (size_t)((((r >> 7) * 2 + (gi & 1)) * 32 + (r & 31)) * 8 + ((r >> 5) & 3) * 2 + (gi >> 1));
 }
 
 // Token grid and cube shape, with derived counts, as kernels see them.

@@ -62,8 +62,9 @@ struct GemmArgs {
     int rp;
 };
 
-constexpr int EPI_STORE = 0;
-constexpr int EPI_TOKENS = 1;
+constexpr int EPI_STORE = 0;      // plain fp32 stores c[b row][a row]
+constexpr int EPI_TOKENS = 1;     // low-rank branch + core term, rows scattered to token order
+constexpr int EPI_TOKENS_Q = 2;   // the same for cubes of a multiple of 4 slots, rank 32, 16-byte y rows
 
 // Direct global -> LDS copies (global_load_lds, saddr form): lane i copies
 // 16 (or 4) bytes from base + voff_i to LDS address m0 + 16 i (or 4 i), with
@@ -90,6 +91,21 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
                  "s"(base) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// load at a 32-bit byte offset from a base pointer
+template <class T>
+__device__ __forceinline__ T ld_off(const void* base, uint32_t off) {
+    return *(const T*)((const char*)base + off);
+}
+
+// value of lane J of each group of four lanes (DPP quad_perm broadcast)
+template <int J>
+__device__ __forceinline__ float4 quad_bcast(float4 v) {
+    auto b = [](float f) {   // quad_perm [J, J, J, J]
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, f), 0x55 * J, 0xF, 0xF, false));
+    };
+    return make_float4(b(v.x), b(v.y), b(v.z), b(v.w));
+}
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in
 // bits 15:14; expcnt 7 and lgkmcnt 15 mean no wait on those counters)
@@ -260,22 +276,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // ---- fragments of one 64-channel half step, byte addresses within a stage
     const int arow0 = wr * 128 + l32;            // + 32 mi
     const int brow0 = wc * 128 + l32;            // + 32 ni
-    const int asw = swz4(arow0);                 // the swizzles depend on row % 8 only
+    const int asw = swz4(arow0);                 // the swizzles depend on row % 16 only
     const int bsw = BFMT == FMT_FP4 ? swz4(brow0) : swz8(brow0);
+    // Scale codes: one 8-byte read per operand gives the lane's codes for the
+    // whole step (four 32-row blocks x two halves); code (block r, half kk) is
+    // byte 2 (r % 2) + kk of dword r / 2, selected by the MFMA's op_sel.
+    const int sa_off = SA_OFF + ((wr * 2 + g) * 32 + l32) * 8;
+    const int sb_off = SB_OFF + ((wc * 2 + g) * 32 + l32) * 8;
     struct Half {
         uint4 a[4];
         uint4 b[BFMT == FMT_FP4 ? 4 : 1];      // FP4 B fragments
         v8i b8[BFMT == FMT_FP4 ? 1 : 4];       // FP8 B fragments (two 16-byte chunks each)
-        int sa[4], sb[4];
+        uint2 sa, sb;
     };
-    // LDS read number i (0 .. 15) of half kk's fragments, in the order of
-    // their first use by the MFMA sequence below: a0 b0 sa0 sb0 b1 sb1 b2 sb2
-    // b3 sb3 a1 sa1 a2 sa2 a3 sa3.
+    // LDS read number i (0 .. 9) of half kk's fragments, in the order of
+    // their first use by the MFMA sequence below: a0 b0 sa sb b1 b2 b3 a1 a2 a3.
     auto rd = [&](int buf, int kk, Half& F, int i) {
         const uint8_t* st = smem + buf * STAGE;
         auto rda = [&](int mi) { F.a[mi] = *(const uint4*)(st + (arow0 + 32 * mi) * 64 + (((2 * kk + g) ^ asw) << 4)); };
-        auto rdsa = [&](int mi) { F.sa[mi] = st[SA_OFF + (arow0 + 32 * mi) * 4 + 2 * kk + g]; };
-        auto rdsb = [&](int ni) { F.sb[ni] = st[SB_OFF + (brow0 + 32 * ni) * 4 + 2 * kk + g]; };
         auto rdb = [&](int ni) {
             const uint8_t* rowp = st + B_OFF + (brow0 + 32 * ni) * BROW;
             if constexpr (BFMT == FMT_FP4) {
@@ -289,24 +307,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         switch (i) {
             case 0: rda(0); break;
             case 1: rdb(0); break;
-            case 2: rdsa(0); break;
-            case 3: rdsb(0); break;
+            case 2: F.sa = *(const uint2*)(st + sa_off); break;
+            case 3: F.sb = *(const uint2*)(st + sb_off); break;
             case 4: rdb(1); break;
-            case 5: rdsb(1); break;
-            case 6: rdb(2); break;
-            case 7: rdsb(2); break;
-            case 8: rdb(3); break;
-            case 9: rdsb(3); break;
-            case 10: rda(1); break;
-            case 11: rdsa(1); break;
-            case 12: rda(2); break;
-            case 13: rdsa(2); break;
-            case 14: rda(3); break;
-            default: rdsa(3); break;
+            case 5: rdb(2); break;
+            case 6: rdb(3); break;
+            case 7: rda(1); break;
+            case 8: rda(2); break;
+            default: rda(3); break;
         }
     };
-    // MFMA number i (0 .. 15) of a half step: row block mi = i / 4, column block ni = i % 4
-    auto mma = [&](const Half& F, int i) {
+    constexpr int NRD = 10;                      // LDS reads per half step
+    // MFMA number i (0 .. 15) of half kk: row block mi = i / 4, column block ni = i % 4
+    auto mma = [&](const Half& F, int kk, int i) {
         const int mi = i >> 2, ni = i & 3;
         const uint4 v = F.a[mi];
         const v8i af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
@@ -317,8 +330,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         } else {
             bf = F.b8[ni];
         }
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[mi][ni], FMT_FP4, BFMT, 0, F.sa[mi], 0,
-                                                                      F.sb[ni]);
+        const int sa = (mi >> 1) ? (int)F.sa.y : (int)F.sa.x, sb = (ni >> 1) ? (int)F.sb.y : (int)F.sb.x;
+        // op_sel operands must be constants: spell out the byte choices
+#define DQ_MFMA(OA, OB) acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[mi][ni], FMT_FP4, BFMT, OA, sa, OB, sb)
+        const int oa = 2 * (mi & 1) + kk, ob = 2 * (ni & 1) + kk;
+        switch (oa * 4 + ob) {
+            case 0: DQ_MFMA(0, 0); break;   case 1: DQ_MFMA(0, 1); break;   case 2: DQ_MFMA(0, 2); break;   case 3: DQ_MFMA(0, 3); break;
+            case 4: DQ_MFMA(1, 0); break;   case 5: DQ_MFMA(1, 1); break;   case 6: DQ_MFMA(1, 2); break;   case 7: DQ_MFMA(1, 3); break;
+            case 8: DQ_MFMA(2, 0); break;   case 9: DQ_MFMA(2, 1); break;   case 10: DQ_MFMA(2, 2); break;  case 11: DQ_MFMA(2, 3); break;
+            case 12: DQ_MFMA(3, 0); break;  case 13: DQ_MFMA(3, 1); break;  case 14: DQ_MFMA(3, 2); break;  default: DQ_MFMA(3, 3); break;
+        }
+#undef DQ_MFMA
     };
 
     // ---- tile epilogue: acc[mi][ni][4 j + q] is channel m0 + wr 128 + 32 mi
@@ -326,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     auto epilogue = [&](int tm, int tn) {
         const int m0 = tm * 256, n0 = tn * 256;
         const int ch0 = m0 + wr * 128 + 4 * g;             // + 32 mi + 8 j
-        if (EPI == EPI_STORE) {
+        if constexpr (EPI == EPI_STORE) {
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) {
                 float* crow = p.c + (long long)(n0 + wc * 128 + 32 * ni + l32) * p.ldc + ch0;
@@ -337,6 +359,80 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                         const v16f& a = acc[mi][ni];
                         *(float4*)(crow + 32 * mi + 8 * j) = make_float4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
                     }
+            }
+            return;
+        }
+        if constexpr (EPI == EPI_TOKENS_Q) {
+            // Every global load is issued before the first wait, so their
+            // latencies (and that of the copies still in flight) overlap: the
+            // slot -> token map, the core-term rows, the low-rank operands.
+            // Core term: a cube spans a multiple of 4 slots and tiles start at
+            // multiples of 256, so the four lanes of a quad hold slots of one
+            // cube; lane u of the quad loads the quarter of the cube's row
+            // that is piece (mi, u) of every lane's 16 pieces, and the quad
+            // exchanges the quarters by DPP broadcasts.
+            // (32-bit byte offsets from the uniform bases: one address register
+            // per row, the rest in the instructions' offset fields)
+            int tok[4];
+            float4 bq[4][4];
+            v8bf la[2][4], ub[2][4];
+            const int u4 = l32 & 3;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const int slot = n0 + wc * 128 + 32 * ni + l32;
+                tok[ni] = ld_off<int>(p.stok, (uint32_t)slot * 4);
+                const int k = min(slot / p.S, p.kmax);          // pad slots: any valid row, never stored
+                const uint32_t bo = ((uint32_t)k * (uint32_t)p.ldbias + (uint32_t)(ch0 + 8 * u4)) * 4;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) bq[ni][mi] = ld_off<float4>(p.bias, bo + 128 * mi);
+            }
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const uint32_t lo = ((uint32_t)(m0 + wr * 128 + l32 + 32 * mi) * 32 + 8 * g) * 2;
+                la[0][mi] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.l2t, lo));
+                la[1][mi] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.l2t, lo + 32));
+            }
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const uint32_t uo = ((uint32_t)(n0 + wc * 128 + l32 + 32 * ni) * 32 + 8 * g) * 2;
+                ub[0][ni] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.u, uo));
+                ub[1][ni] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.u, uo + 32));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // the copies of the next tile's first stages land before the next
+            // tile reads them (its first steps wait loosely)
+            wait_vm<0>();
+            // low-rank branch: acc += (U L2)^T, 32x32x16 bf16 MFMAs over the 32 ranks
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[h][mi], ub[h][ni], acc[mi][ni], 0, 0, 0);
+            // y[token] = acc + core term of the token's cube, 16-byte stores.
+            // The broadcasts run in every lane (a pad slot's lane still serves
+            // its quad); only the stores depend on the slot holding a token.
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const bool live = tok[ni] >= 0;
+                float* yrow = p.y + (long long)max(tok[ni], 0) * p.Co;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    float4 bv[4];
+                    bv[0] = quad_bcast<0>(bq[ni][mi]);     // piece (mi, j) comes from quad lane j
+                    bv[1] = quad_bcast<1>(bq[ni][mi]);
+                    bv[2] = quad_bcast<2>(bq[ni][mi]);
+                    bv[3] = quad_bcast<3>(bq[ni][mi]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const v16f& a = acc[mi][ni];
+                        const int ch = ch0 + 32 * mi + 8 * j;
+                        if (live && ch < p.Co)
+                            *(float4*)(yrow + ch) = make_float4(a[4 * j] + bv[j].x, a[4 * j + 1] + bv[j].y,
+                                                                a[4 * j + 2] + bv[j].z, a[4 * j + 3] + bv[j].w);
+                    }
+                }
             }
             return;
         }
@@ -419,7 +515,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     __syncthreads();
     Half F0, F1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rd(0, 0, F0, i);
+    for (int i = 0; i < NRD; ++i) rd(0, 0, F0, i);
     // Stage gs + 1 must have landed before the barrier of step gs.  Copies go
     // out every step (past the end too), so normally NS - 3 later stages may
     // still be in flight.  In a tile's first NS - 2 steps (after the first
@@ -438,8 +534,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             const int cur = (unsigned)gs % NS, nxt = (unsigned)(gs + 1) % NS, fill = (unsigned)(gs + NS - 1) % NS;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                mma(F0, i);
-                rd(cur, 1, F1, i);
+                mma(F0, 0, i);
+                if (i < NRD) rd(cur, 1, F1, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // Wait and barrier in one asm block (no branch for the compiler to
@@ -459,17 +555,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                mma(F1, i);
+                mma(F1, 1, i);
                 if (i < DMAS) dma(src, fill, i);
-                rd(nxt, 0, F0, i);
+                if (i < NRD) rd(nxt, 0, F0, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
             advance();
         }
-        wait_vm<0>();
+        if (EPI != EPI_TOKENS_Q) wait_vm<0>();   // that epilogue waits after issuing its loads
         int tm, tn;
         walk.coords(it, &tm, &tn);
         epilogue(tm, tn);
+        // The last step already read half 0 of the next tile's first stage
+        // (landed: its barrier covered it); reading it again here keeps those
+        // registers free during the epilogue.
+#pragma unroll
+        for (int i = 0; i < NRD; ++i) rd((unsigned)gs % NS, 0, F0, i);
     }
 }
 
@@ -522,6 +623,7 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t
     // 2) delta term + low-rank branch + the cube's core term -> y (token order)
     d.bias = q->bias;
     d.ldbias = w->Cop;
+    if (d.S % 4 == 0 && d.rp == 32 && d.vec4) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
     return launch<FMT_FP4, EPI_TOKENS>(d, st);
 }
 
