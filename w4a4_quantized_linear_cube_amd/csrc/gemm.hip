@@ -60,6 +60,7 @@ struct GemmArgs {
     const uint16_t* u;     // [Nslot_pad][rp]
     const uint16_t* l2t;   // [Cop][rp]
     int rp;
+    float* sink;        // 1 KB the token epilogue stores lanes without an output to (never read)
 };
 
 constexpr int EPI_STORE = 0;      // plain fp32 stores c[b row][a row]
@@ -343,22 +344,52 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #undef DQ_MFMA
     };
 
+    // ---- output transposition.  An accumulator block holds, per lane, 16
+    // channels of one B row in 16-byte pieces 8 channels apart, so direct
+    // stores would write 32 rows x 32 bytes per instruction.  Each wave
+    // passes its blocks through two 4 KB LDS buffers (32 rows x 128 bytes,
+    // pieces XOR-swizzled by row: conflict-free both ways) and reads them
+    // back as 8 rows x 128 contiguous bytes per instruction.  The buffers sit
+    // in the stage of the tile's last K step, which no wave reads after the
+    // epilogue's first barrier and no copy fills before the next tile's first
+    // barrier.
+    int tstage = 0;                                       // stage of the tile's last K step
+    auto tbuf = [&](int b) { return smem + tstage * STAGE + wv * 8192 + b * 4096; };
+    auto tput = [&](int b, const float4* o) {           // piece j of this lane's row l32 is channels 8 j + 4 g ..
+        uint8_t* t = tbuf(b) + l32 * 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(float4*)(t + (((2 * j + g) ^ ((l32 >> 1) & 7)) << 4)) = o[j];
+    };
+    auto tget = [&](int b, int i) {                     // row 8 i + lane / 8, channels 4 (lane % 8) ..
+        const int rr = 8 * i + (lane >> 3);
+        return *(const float4*)(tbuf(b) + rr * 128 + (((lane & 7) ^ ((rr >> 1) & 7)) << 4));
+    };
+
     // ---- tile epilogue: acc[mi][ni][4 j + q] is channel m0 + wr 128 + 32 mi
     // + 8 j + 4 g + q of B row n0 + wc 128 + 32 ni + l32.
     auto epilogue = [&](int tm, int tn) {
         const int m0 = tm * 256, n0 = tn * 256;
         const int ch0 = m0 + wr * 128 + 4 * g;             // + 32 mi + 8 j
         if constexpr (EPI == EPI_STORE) {
+            __syncthreads();                                // every wave is done with the last step's stage
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                float* crow = p.c + (long long)(n0 + wc * 128 + 32 * ni + l32) * p.ldc + ch0;
+            for (int b = 0; b < 17; ++b) {
+                if (b < 16) {                               // block b: mi = b % 4, ni = b / 4
+                    const v16f& a = acc[b & 3][b >> 2];
+                    float4 o[4];
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                    for (int j = 0; j < 4; ++j) o[j] = make_float4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
+                    tput(b & 1, o);
+                }
+                if (b > 0) {
+                    const int pb = b - 1, mi = pb & 3, ni = pb >> 2;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const v16f& a = acc[mi][ni];
-                        *(float4*)(crow + 32 * mi + 8 * j) = make_float4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 8 * i + (lane >> 3);
+                        const float4 v = tget(pb & 1, i);
+                        *(float4*)(p.c + (long long)(n0 + wc * 128 + 32 * ni + rr) * p.ldc + m0 + wr * 128 + 32 * mi + 4 * (lane & 7)) = v;
                     }
+                }
             }
             return;
         }
@@ -377,15 +408,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             float4 bq[4][4];
             v8bf la[2][4], ub[2][4];
             const int u4 = l32 & 3;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const int slot = n0 + wc * 128 + 32 * ni + l32;
-                tok[ni] = ld_off<int>(p.stok, (uint32_t)slot * 4);
-                const int k = min(slot / p.S, p.kmax);          // pad slots: any valid row, never stored
+            auto load_core = [&](int ni) {
+                const int k = min((n0 + wc * 128 + 32 * ni + l32) / p.S, p.kmax);   // pad slots: any valid row, never stored
                 const uint32_t bo = ((uint32_t)k * (uint32_t)p.ldbias + (uint32_t)(ch0 + 8 * u4)) * 4;
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) bq[ni][mi] = ld_off<float4>(p.bias, bo + 128 * mi);
-            }
+            };
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) tok[ni] = ld_off<int>(p.stok, (uint32_t)(n0 + wc * 128 + 32 * ni + l32) * 4);
+            load_core(0);                                   // rows of ni 2, 3 after the low-rank MFMAs
+            load_core(1);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 const uint32_t lo = ((uint32_t)(m0 + wr * 128 + l32 + 32 * mi) * 32 + 8 * g) * 2;
@@ -399,6 +431,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                 ub[1][ni] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.u, uo + 32));
             }
             __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();                                // every wave is done with the last step's stage
             // the copies of the next tile's first stages land before the next
             // tile reads them (its first steps wait loosely)
             wait_vm<0>();
@@ -410,27 +443,47 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[h][mi], ub[h][ni], acc[mi][ni], 0, 0, 0);
-            // y[token] = acc + core term of the token's cube, 16-byte stores.
-            // The broadcasts run in every lane (a pad slot's lane still serves
-            // its quad); only the stores depend on the slot holding a token.
+            load_core(2);
+            load_core(3);
+            __builtin_amdgcn_sched_barrier(0);
+            // y[token] = acc + core term of the token's cube, through the
+            // transposition buffers.  The broadcasts run in every lane (a pad
+            // slot's lane still serves its quad); a row is stored if its slot
+            // holds a token.
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const bool live = tok[ni] >= 0;
-                float* yrow = p.y + (long long)max(tok[ni], 0) * p.Co;
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    float4 bv[4];
+            for (int b = 0; b < 17; ++b) {
+                if (b < 16) {                               // block b: mi = b % 4, ni = b / 4
+                    const int mi = b & 3, ni = b >> 2;
+                    const v16f& a = acc[mi][ni];
+                    float4 bv[4], o[4];
                     bv[0] = quad_bcast<0>(bq[ni][mi]);     // piece (mi, j) comes from quad lane j
                     bv[1] = quad_bcast<1>(bq[ni][mi]);
                     bv[2] = quad_bcast<2>(bq[ni][mi]);
                     bv[3] = quad_bcast<3>(bq[ni][mi]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const v16f& a = acc[mi][ni];
-                        const int ch = ch0 + 32 * mi + 8 * j;
-                        if (live && ch < p.Co)
-                            *(float4*)(yrow + ch) = make_float4(a[4 * j] + bv[j].x, a[4 * j + 1] + bv[j].y,
-                                                                a[4 * j + 2] + bv[j].z, a[4 * j + 3] + bv[j].w);
+                    for (int j = 0; j < 4; ++j)
+                        o[j] = make_float4(a[4 * j] + bv[j].x, a[4 * j + 1] + bv[j].y, a[4 * j + 2] + bv[j].z,
+                                           a[4 * j + 3] + bv[j].w);
+                    tput(b & 1, o);
+                }
+                if (b > 0) {
+                    // rows 8 i + lane / 8 of block b - 1; every lane stores (a
+                    // lane whose row has no token, or whose channels lie past
+                    // Co, stores to the sink), so no branch splits the LDS
+                    // reads and their waits.
+                    const int pb = b - 1, mi = pb & 3, ni = pb >> 2;
+                    const int ch = m0 + wr * 128 + 32 * mi + 4 * (lane & 7);
+                    int t[4];
+                    float4 v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        t[i] = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) * 4, tok[ni]);   // token of row rr (lane rr)
+                        v[i] = tget(pb & 1, i);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float* dst = (t[i] >= 0 && ch < p.Co) ? p.y + (uint32_t)(t[i] * p.Co + ch) : p.sink + 4 * lane;
+                        *(float4*)dst = v[i];
                     }
                 }
             }
@@ -565,6 +618,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         if (EPI != EPI_TOKENS_Q) wait_vm<0>();   // that epilogue waits after issuing its loads
         int tm, tn;
         walk.coords(it, &tm, &tn);
+        tstage = (unsigned)(gs - 1) % NS;
         epilogue(tm, tn);
         // The last step already read half 0 of the next tile's first stage
         // (landed: its barrier covered it); reading it again here keeps those
@@ -611,6 +665,7 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t
     d.u = q->u;
     d.l2t = w->l2t;
     d.rp = w->rp;
+    d.sink = q->sink;
     // 1) per-cube core term bias[k] = Q8(core_k) Q4(R)
     GemmArgs c = d;
     c.b = q->cq;
@@ -623,7 +678,9 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t
     // 2) delta term + low-rank branch + the cube's core term -> y (token order)
     d.bias = q->bias;
     d.ldbias = w->Cop;
-    if (d.S % 4 == 0 && d.rp == 32 && d.vec4) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
+    // (32-bit element offsets into y and into the per-cube term)
+    const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
+    if (d.S % 4 == 0 && d.rp == 32 && d.vec4 && off32) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
     return launch<FMT_FP4, EPI_TOKENS>(d, st);
 }
 
