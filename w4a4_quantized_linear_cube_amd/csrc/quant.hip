@@ -8,32 +8,35 @@
 //   Q8(core), Q4(delta): MX, one E8M0 scale per 32 channels
 //   U_n     = bf16( bf16(x_n) L1 )   (fp32 MFMA accumulation)
 //
-// One workgroup owns up to 64 slot rows (whole cubes when a cube has at most
-// 64 tokens) and walks the channels in chunks: the chunk of X is staged in
-// LDS once (channel-contiguous, coalesced row segments) and then used three
-// times -- for the cube sums, for the deltas, and as the bf16 MFMA operand of
-// U -- so X is read from HBM exactly once.  Cubes of more than 64 tokens take
-// two extra small passes (64-token partial sums, then their ordered combine)
-// and X is read twice.
+// The pass works on blocks of 64 slot rows (whole cubes when a cube has at
+// most 64 tokens) and walks each block's channels in chunks: the chunk of X
+// is staged in LDS once (channel-contiguous, coalesced row segments) and then
+// used three times -- for the cube sums, for the deltas, and as the bf16 MFMA
+// operand of U -- so X is read from HBM exactly once.  Cubes of more than 64
+// tokens take two extra small passes (64-token partial sums, then their
+// ordered combine) and X is read twice.
+#include <algorithm>
 #include <type_traits>
 
 #include "dq_device.h"
 
 namespace dq {
 
-constexpr int QROWS = 64;          // slot rows per workgroup
-constexpr int QTHREADS = 256;      // wave 0: copies; wave 1: U; waves 2-3: quantizer
-constexpr int QROWB = 512;         // bytes of one row's channel chunk in LDS
-constexpr int QCHUNK = QROWS * QROWB;
-constexpr int QNBUF = 2;           // chunk buffers (two workgroups fit one CU)
+constexpr int QROWS = 64;                  // slot rows per block
+constexpr int QWAVES = 7;                  // wave 0: U; waves 1-2: copies; waves 3-6: quantizer
+constexpr int QTHREADS = QWAVES * 64;
+constexpr int QROWB = 256;                 // bytes of one row's channel chunk in LDS
+constexpr int QCHUNK = QROWS * QROWB;      // 16 KB
+constexpr int QDMA = QCHUNK / 2 / 1024;    // 1 KB X copies per copy wave per chunk
+constexpr int QKEEP = 4;                   // rows of a cube the quantizer keeps in registers
 
 template <typename XT> struct XTraits;
 template <> struct XTraits<float> {
-    static constexpr int CC = QROWB / 4;   // 128 channels per chunk
+    static constexpr int CC = QROWB / 4;   // 64 channels per chunk
     __device__ static float f(float v) { return v; }
 };
 template <> struct XTraits<uint16_t> {
-    static constexpr int CC = QROWB / 2;   // 256 channels per chunk
+    static constexpr int CC = QROWB / 2;   // 128 channels per chunk
     __device__ static float f(uint16_t v) { return bf16_to_f32(v); }
 };
 
@@ -42,6 +45,7 @@ struct QuantArgs {
     Geom g;
     int Ci, Kp, rp;
     int core_mode;            // 0: cores computed here (S <= 64); 1: read from coref
+    long long nblocks;        // 64-slot blocks
     uint8_t* dq;              // Nslot_pad x Kp/2, step-major
     uint8_t* ds;              // Nslot_pad x Kp/32, step-major
     uint8_t* cq;              // K_pad x Kp, step-major
@@ -49,109 +53,192 @@ struct QuantArgs {
     uint16_t* u;              // [Nslot_pad][rp]
     const uint16_t* l1t;      // [rp][Kp], zero beyond Ci
     const float* coref;       // [K][Kp] (core_mode 1)
-    const uint8_t* zero;      // QROWB zero bytes (source of absent rows and channels)
+    const uint8_t* zero;      // 256 zero bytes (source of absent rows and channels)
+    const int* stok;          // [Nslot_pad] token of each slot, -1 for pad slots
 };
 
-// LDS chunk layout: 16-byte chunk c of row r at r QROWB + ((c ^ (r & 15)) << 4);
-// the XOR makes both the quantizer's row reads and the MFMA's column reads
-// free of bank conflicts.
+// LDS chunk layout: 16-byte piece c of row r at r QROWB + ((c ^ (r & 15)) << 4);
+// the XOR makes the quantizer's row reads and the MFMA's column reads free of
+// bank conflicts.
 __device__ __forceinline__ int qoff(int r, int c) { return r * QROWB + ((c ^ (r & 15)) << 4); }
 
-// 32 channels (one group) of row r from a chunk buffer, as fp32
+// Block b: its first slot, first cube, rows and cubes.  Cubes of at most 64
+// tokens: whole cubes (64 / S of them); larger cubes: 64 slots.
+struct QBlock {
+    long long slot0, k_first;
+    int nrows, ncores;
+};
+__device__ __forceinline__ QBlock qblock(const QuantArgs& a, long long b) {
+    QBlock q;
+    if (a.core_mode == 0) {
+        const int cpb = QROWS / a.g.S;
+        q.k_first = b * cpb;
+        q.ncores = (int)min((long long)cpb, a.g.K - q.k_first);
+        q.slot0 = q.k_first * a.g.S;
+        q.nrows = q.ncores * a.g.S;
+    } else {
+        q.slot0 = b * QROWS;
+        q.nrows = (int)min((long long)QROWS, a.g.Nslot - q.slot0);
+        q.k_first = q.slot0 / a.g.S;
+        q.ncores = (int)((q.slot0 + q.nrows - 1) / a.g.S - q.k_first + 1);
+    }
+    return q;
+}
+
+// 8 channels (a quarter of a group) of row r from a chunk buffer, as fp32,
+// OR-ed with sgn: a pad row (zero bytes in the buffer) read with
+// sgn = 0x80000000 gives -0.0, which is an exact identity of IEEE addition
+// (x + -0 = x for every x, zeros included), so pad rows drop out of the
+// cube's sum in slot order without a branch.
 template <typename XT>
-__device__ __forceinline__ void qload(const uint8_t* buf, int r, int gc, float* v) {
+__device__ __forceinline__ void qload8(const uint8_t* buf, int r, int gc, int qq, uint32_t sgn, float* v) {
     if constexpr (sizeof(XT) == 2) {
+        const uint4 w = *(const uint4*)(buf + qoff(r, 4 * gc + qq));
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 w = *(const uint4*)(buf + qoff(r, 4 * gc + q));
-            const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[8 * q + 2 * i] = __uint_as_float(d[i] << 16);
-                v[8 * q + 2 * i + 1] = __uint_as_float(d[i] & 0xffff0000u);
-            }
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float((d[i] << 16) | sgn);
+            v[2 * i + 1] = __uint_as_float((d[i] & 0xffff0000u) | sgn);
         }
     } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float4 w = *(const float4*)(buf + qoff(r, 8 * gc + q));
-            v[4 * q] = w.x;
-            v[4 * q + 1] = w.y;
-            v[4 * q + 2] = w.z;
-            v[4 * q + 3] = w.w;
+        for (int h = 0; h < 2; ++h) {
+            const uint4 w = *(const uint4*)(buf + qoff(r, 8 * gc + 2 * qq + h));
+            v[4 * h] = __uint_as_float(w.x | sgn);
+            v[4 * h + 1] = __uint_as_float(w.y | sgn);
+            v[4 * h + 2] = __uint_as_float(w.z | sgn);
+            v[4 * h + 3] = __uint_as_float(w.w | sgn);
         }
     }
 }
 
-// One workgroup owns up to 64 slot rows (whole cubes when a cube has at most
-// 64 tokens) and walks the channels in chunks of 512 bytes per row.  Wave 0
-// copies each chunk of X straight into LDS (global_load_lds, one 16-byte
-// piece per lane, absent rows and channels from a zero page) one chunk ahead;
-// wave 1 accumulates U = bf16(X) L1 with 32x32x16 bf16 MFMAs; waves 2-3 run
-// one (cube, 32-channel group) per thread: the cube's core from its rows
-// (fp32 sum in slot order, then the division), the core's FP8 codes, and each
-// row's delta FP4 codes.  X is read from HBM exactly once.
-template <typename XT, int NCT>
-__global__ __launch_bounds__(QTHREADS, 2) void k_quantize(QuantArgs a) {
+// Ring depth: the copy waves keep (depth - 1) chunks in flight, at most 63
+// copies (the vmcnt range), in at most 150 KB of LDS.
+constexpr int qnbuf(int stage, int dmaw) {
+    return (1 + 63 / dmaw) < (150 * 1024 / stage) ? ((1 + 63 / dmaw) < 8 ? 1 + 63 / dmaw : 8)
+                                                  : ((150 * 1024 / stage) < 8 ? 150 * 1024 / stage : 8);
+}
+
+// maximum over the four lanes of a quad (DPP quad_perm exchanges)
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    return v;
+}
+
+// Persistent activation pass.  Workgroup w takes the 64-slot blocks w, w + G,
+// w + 2G, ... and walks each block's channels in chunks of 256 bytes per row;
+// the chunks of all its blocks form one stream.  Waves 1-2 copy chunks
+// straight into an LDS ring (global_load_lds, one 16-byte piece per lane,
+// absent rows and channels from a zero page) up to seven chunks ahead, across
+// block boundaries, together with the chunk's slice of L1; they issue nothing
+// else, so their copy counters track the ring exactly.  Wave 0 accumulates
+// U = bf16(X) L1 with 32x32x16 bf16 MFMAs from the stage and stores it after
+// a block's last chunk.  Waves 3-6 quantize: one
+// (cube, 32-channel group, quarter) per thread, the quad of a group's four
+// quarters sharing its maxima by DPP: the cube's core (fp32 sum in slot
+// order, then the division), its FP8 codes, each row's delta FP4 codes.
+// X is read from HBM exactly once.
+template <typename XT, int NCT, int CM>
+__global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
     constexpr int CC = XTraits<XT>::CC;
     constexpr int NGC = CC / 32;                     // groups per chunk
-    constexpr int EPC = 16 / (int)sizeof(XT);        // elements per 16-byte chunk
-    __shared__ __attribute__((aligned(1024))) uint8_t xbuf[QNBUF * QCHUNK];
-    __shared__ int tok_s[QROWS];
-    __shared__ int rb_s[QROWS], re_s[QROWS], cnt_s[QROWS];
+    constexpr int EPC = 16 / (int)sizeof(XT);        // elements per 16-byte piece
+    // L1 chunk (rank tile ct, row = rank, 2 CC bytes per row, pieces swizzled
+    // like X) follows the X chunk in each ring stage
+    constexpr int LROWB = 2 * CC;
+    constexpr int LNP = LROWB / 16;                  // 16-byte pieces per L1 row
+    constexpr int LRPC = 1024 / LROWB;               // L1 rows per 1 KB copy
+    constexpr int LDMA = NCT * 32 / LRPC / 2;        // L1 copies per copy wave per chunk
+    constexpr int QDMAW = QDMA + LDMA;               // copies per copy wave per chunk
+    constexpr int STAGE = QCHUNK + NCT * 32 * LROWB;
+    constexpr int QNBUF = qnbuf(STAGE, QDMAW);       // ring stages
+    __shared__ __attribute__((aligned(1024))) uint8_t xbuf[QNBUF * STAGE];
+    __shared__ int tok_s[2][QROWS];
+    __shared__ int4 meta_s[2][QROWS];   // per cube: first row, end row, present rows (bit j: row first + j), tokens
 
     const Geom& g = a.g;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-
-    // ---- rows and cubes of this workgroup
-    long long k_first, slot0;
-    int nrows, ncores;
-    if (a.core_mode == 0) {
-        const int cpb = QROWS / g.S;
-        k_first = (long long)blockIdx.x * cpb;
-        ncores = (int)min((long long)cpb, g.K - k_first);
-        slot0 = k_first * g.S;
-        nrows = ncores * g.S;
-    } else {
-        slot0 = (long long)blockIdx.x * QROWS;
-        nrows = (int)min((long long)QROWS, g.Nslot - slot0);
-        k_first = slot0 / g.S;
-        ncores = (int)((slot0 + nrows - 1) / g.S - k_first + 1);
-    }
-    if (tid < QROWS) {
-        const long long s = slot0 + tid;
-        tok_s[tid] = tid < nrows ? (int)slot_token(g, s) : -1;
-    }
-    if (tid < ncores) {
-        const long long k = k_first + tid;
-        rb_s[tid] = (int)max(0LL, k * g.S - slot0);
-        re_s[tid] = (int)min((long long)nrows, (k + 1) * g.S - slot0);
-        int ct, ch, cw;
-        cnt_s[tid] = cube_count(g, k, &ct, &ch, &cw);
-    }
-    __syncthreads();
-
     const int nchunks = (a.Ci + CC - 1) / CC;
+    const long long nmine = a.nblocks > (long long)blockIdx.x ? (a.nblocks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+    if (nmine == 0) return;
+    const long long total = nmine * nchunks;
     const uint32_t lds0 = (uint32_t)(uintptr_t)xbuf;
     const XT* __restrict__ x = (const XT*)a.x;
+    const int qtid = tid - 192;                      // quantizer thread (waves 3-6)
 
-    // wave 0: the 32 copies of chunk ci into buffer ci % QNBUF (two rows per
-    // copy; a lane of an absent row or channel reads the zero page)
-    auto issue = [&](int ci) {
-        const int c0 = ci * CC;
-        const uint32_t base = lds0 + (uint32_t)(ci % QNBUF) * QCHUNK;
-        int t[QROWS / 2];
+    // block metadata, double-buffered by block parity: token of each row;
+    // per cube its row range, which of its first 32 rows hold tokens, and its
+    // token count
+    auto fill_meta = [&](int mb, long long i) {
+        const QBlock B = qblock(a, blockIdx.x + i * gridDim.x);
+        if (qtid < QROWS) {
+            const int rb = qtid < B.ncores ? (int)max(0LL, (B.k_first + qtid) * g.S - B.slot0) : 0;
+            const int re = qtid < B.ncores ? (int)min((long long)B.nrows, (B.k_first + qtid + 1) * g.S - B.slot0) : 0;
+            int pm = 0;
+            for (int j = 0; j < 32 && rb + j < re; ++j) pm |= (a.stok[B.slot0 + rb + j] >= 0 ? 1 : 0) << j;
+            tok_s[mb][qtid] = qtid < B.nrows ? a.stok[B.slot0 + qtid] : -1;
+            int ct, ch, cw;
+            const int cnt = qtid < B.ncores ? cube_count(g, B.k_first + qtid, &ct, &ch, &cw) : 0;
+            meta_s[mb][qtid] = make_int4(rb, re, pm, cnt);
+        }
+    };
+    if (wave >= 3) fill_meta(0, 0);
+
+    // ---- copy waves: wave 1 rows 0-31, wave 2 rows 32-63 of each chunk; copy
+    // j covers rows 4 j .. 4 j + 3 of the wave's half (lane: row + lane / 16,
+    // piece lane % 16).  The cursor (block i_f, chunk c_f) runs past the end on
+    // zero-page copies into buffers no one reads, so every chunk step issues
+    // the same number of copies.
+    const int cw = __builtin_amdgcn_readfirstlane(wave - 1);
+    long long i_f = 0, s_f = 0;
+    int c_f = 0;
+    int tokr[QDMA];
+    // tokens of a block's rows: scalar loads (they count on lgkmcnt, so the
+    // copy counter keeps tracking the copies alone), then each lane picks its row
+    typedef const __attribute__((address_space(4))) int cint;
+    cint* stok_c = (cint*)(uintptr_t)a.stok;
+    auto load_toks = [&](long long i) {
+        int t[QDMA][4];
+        const QBlock Bn = qblock(a, blockIdx.x + min(i, nmine - 1) * gridDim.x);
 #pragma unroll
-        for (int j = 0; j < QROWS / 2; ++j) t[j] = tok_s[2 * j + (lane >> 5)];
+        for (int j = 0; j < QDMA; ++j)
 #pragma unroll
-        for (int j = 0; j < QROWS / 2; ++j) {
-            const int r = 2 * j + (lane >> 5);
-            const int ch = c0 + ((lane & 31) ^ (r & 15)) * EPC;   // first channel of the logical chunk at this position
-            const void* src = (t[j] >= 0 && ch < a.Ci) ? (const void*)(x + (long long)t[j] * a.Ci + ch)
-                                                       : (const void*)(a.zero + 16 * (lane & 31));
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base + j * 2 * QROWB), "v"(src)
+            for (int q = 0; q < 4; ++q) {
+                const int r = 32 * cw + 4 * j + q;
+                t[j][q] = (i < nmine && r < Bn.nrows) ? stok_c[Bn.slot0 + r] : -1;
+            }
+        const int sel = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < QDMA; ++j) tokr[j] = sel == 0 ? t[j][0] : sel == 1 ? t[j][1] : sel == 2 ? t[j][2] : t[j][3];
+    };
+    auto issue = [&]() {
+        const uint32_t stage = lds0 + (uint32_t)(s_f % QNBUF) * STAGE;
+        const uint32_t base = stage + cw * (QCHUNK / 2);
+        const int c0 = c_f * CC;
+#pragma unroll
+        for (int j = 0; j < QDMA; ++j) {
+            const int r = 32 * cw + 4 * j + (lane >> 4);
+            const int ch = c0 + ((lane & 15) ^ (r & 15)) * EPC;   // first channel of the logical piece at this position
+            const void* src = (tokr[j] >= 0 && ch < a.Ci) ? (const void*)(x + (long long)tokr[j] * a.Ci + ch)
+                                                          : (const void*)(a.zero + 16 * (lane & 15));
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(base + j * 1024)), "v"(src)
                          : "memory", "m0");
+        }
+        // L1 rows of the chunk (in bounds: l1t rows are Kp wide, zero past Ci)
+#pragma unroll
+        for (int j = 0; j < LDMA; ++j) {
+            const int lr = (cw * LDMA + j) * LRPC + lane / LNP;            // L1 row (rank) of this lane
+            const int pc = (lane % LNP) ^ (lr % LNP);                      // logical piece at this position
+            const uint16_t* src = a.l1t + (long long)lr * a.Kp + c0 + 8 * pc;
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(stage + QCHUNK + (cw * LDMA + j) * 1024)),
+                         "v"(src) : "memory", "m0");
+        }
+        ++s_f;
+        if (++c_f == nchunks) {
+            c_f = 0;
+            load_toks(++i_f);
         }
     };
     auto barrier = [&]() {
@@ -160,42 +247,46 @@ __global__ __launch_bounds__(QTHREADS, 2) void k_quantize(QuantArgs a) {
         asm volatile("" ::: "memory");
     };
 
-    // U accumulators (wave 1): two 32-row tiles x NCT 32-wide rank tiles
+    // ---- U accumulators (wave 0): two 32-row tiles x NCT 32-wide rank tiles
     v16f uacc[2][NCT > 0 ? NCT : 1];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < (NCT > 0 ? NCT : 1); ++j) uacc[i][j] = (v16f){};
-    // L1 fragments of rank tile ct for the chunk at channel c0 (16 channels per fragment)
-    constexpr int NL = NCT == 1 ? CC / 16 : 4;       // fragments per load batch
-    uint4 lcur[NL], lnext[NCT == 1 ? NL : 1];
-    auto load_l1 = [&](int c0, int ct, uint4* dst) {
-#pragma unroll
-        for (int q = 0; q < NL; ++q) {
-            const int c = c0 + 16 * q + 8 * (lane >> 5);
-            dst[q] = c < a.Kp ? *(const uint4*)(a.l1t + (long long)(ct * 32 + (lane & 31)) * a.Kp + c) : make_uint4(0u, 0u, 0u, 0u);
+
+    // The three roles run their own loops over the chunk stream, one barrier
+    // per chunk each: chunk s has landed and is visible at barrier s, and
+    // every wave is done with chunk s - 1, whose stage takes the copies of
+    // chunk s + QNBUF - 1.
+    if (wave == 1 || wave == 2) {
+        load_toks(0);
+        for (int k = 0; k < QNBUF - 1; ++k) issue();
+        for (long long s = 0; s < total; ++s) {
+            __builtin_amdgcn_s_waitcnt(((QNBUF - 2) * QDMAW & 15) | (((QNBUF - 2) * QDMAW >> 4) << 14) | 0x0F70);
+            barrier();
+            issue();
+        }
+        // the surplus copies land before the wave ends (no copy may write
+        // LDS after the workgroup has released it)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        return;
+    }
+    long long i = 0;      // block ordinal of chunk step s
+    int c = 0;            // chunk of step s within its block
+    QBlock B = qblock(a, blockIdx.x);
+    auto next_chunk = [&]() {
+        if (++c == nchunks) {
+            c = 0;
+            ++i;
+            if (i < nmine) B = qblock(a, blockIdx.x + i * gridDim.x);
         }
     };
-    if (NCT == 1 && wave == 1) load_l1(0, 0, lnext);
-
     if (wave == 0) {
-        issue(0);
-        if (nchunks > 1) issue(1);
-    }
-    for (int ci = 0; ci < nchunks; ++ci) {
-        const int c0 = ci * CC;
-        const uint8_t* buf = xbuf + (ci % QNBUF) * QCHUNK;
-        if (wave == 0) {
-            if (ci + 1 < nchunks) __builtin_amdgcn_s_waitcnt((32 & 15) | ((32 >> 4) << 14) | 0x0F70);   // chunk ci landed
-            else __builtin_amdgcn_s_waitcnt(0x0F70);
-        }
-        barrier();   // chunk ci visible to every wave
-
-        if (NCT > 0 && wave == 1) {
-            // ---- U += bf16(X chunk) L1 chunk.  L1 fragments come from global
-            // memory (L2-resident); with one rank tile they are loaded a chunk
-            // ahead, otherwise one tile's worth per batch.
-            const int kend = min(CC, a.Kp - c0);
+        for (long long s = 0; s < total; ++s, next_chunk()) {
+            barrier();
+            if constexpr (NCT == 0) continue;
+            const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
+            // ---- U += bf16(X chunk) L1 chunk, both operands from the stage
             auto a_frag = [&](int rt, int kk) {
                 const int r = rt * 32 + (lane & 31);
                 if constexpr (sizeof(XT) == 2) {
@@ -211,111 +302,143 @@ __global__ __launch_bounds__(QTHREADS, 2) void k_quantize(QuantArgs a) {
                     return v;
                 }
             };
-            if constexpr (NCT == 1) {
+            auto b_frag = [&](int ct, int kk) {
+                const int lr = ct * 32 + (lane & 31);
+                const int pc = kk / 8 + (lane >> 5);
+                return __builtin_bit_cast(v8bf, *(const uint4*)(buf + QCHUNK + lr * LROWB + ((pc ^ (lr % LNP)) << 4)));
+            };
+            // (Kp is a multiple of 128, so a chunk never passes it)
 #pragma unroll
-                for (int q = 0; q < CC / 16; ++q) lcur[q] = lnext[q];
-                if (ci + 1 < nchunks) load_l1(c0 + CC, 0, lnext);
+            for (int q = 0; q < CC / 16; ++q) {
 #pragma unroll
-                for (int q = 0; q < CC / 16; ++q) {
-                    if (16 * q < kend) {
-                        const v8bf bv = __builtin_bit_cast(v8bf, lcur[q]);
-                        uacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag(0, 16 * q), bv, uacc[0][0], 0, 0, 0);
-                        uacc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag(1, 16 * q), bv, uacc[1][0], 0, 0, 0);
-                    }
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const v8bf bv = b_frag(ct, 16 * q);
+                    uacc[0][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag(0, 16 * q), bv, uacc[0][ct], 0, 0, 0);
+                    uacc[1][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag(1, 16 * q), bv, uacc[1][ct], 0, 0, 0);
                 }
-            } else {
-                for (int kb = 0; kb < kend; kb += 16 * NL) {
+            }
+            if (c + 1 == nchunks) {
+                // ---- U -> bf16, slot order (rows of absent tokens were zero)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
-                        load_l1(c0 + kb, ct, lcur);
 #pragma unroll
-                        for (int q = 0; q < NL; ++q) {
-                            if (kb + 16 * q < kend) {
-                                const v8bf bv = __builtin_bit_cast(v8bf, lcur[q]);
-                                uacc[0][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag(0, kb + 16 * q), bv, uacc[0][ct], 0, 0, 0);
-                                uacc[1][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag(1, kb + 16 * q), bv, uacc[1][ct], 0, 0, 0);
-                            }
+                        for (int e = 0; e < 16; ++e) {
+                            const int row = rt * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                            if (row < B.nrows) a.u[(B.slot0 + row) * a.rp + ct * 32 + (lane & 31)] = bf16_rne(uacc[rt][ct][e]);
                         }
+                        uacc[rt][ct] = (v16f){};
                     }
-                }
-            }
-        } else if (wave >= 2) {
-            // ---- quantizer: one (cube, group) per thread
-            const long long nks = a.Kp / 128;
-            for (int t = tid - 128; t < ncores * NGC; t += 128) {
-                const int cr = t / NGC, gc = t - cr * NGC;
-                const long long G = (c0 >> 5) + gc;
-                if (G * 32 >= a.Ci) continue;
-                const int rb = rb_s[cr], re = re_s[cr];
-                const long long k = k_first + cr;
-                float core[32];
-                if (a.core_mode == 0) {
-                    bool first = true;
-                    for (int r = rb; r < re; ++r) {
-                        if (tok_s[r] < 0) continue;
-                        float v[32];
-                        qload<XT>(buf, r, gc, v);
-#pragma unroll
-                        for (int i = 0; i < 32; ++i) core[i] = first ? v[i] : core[i] + v[i];
-                        first = false;
-                    }
-                    const int cnt = cnt_s[cr];
-                    float amax = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) {
-                        core[i] = mean_div(core[i], cnt);
-                        amax = fmaxf(amax, fabsf(core[i]));
-                    }
-                    const int e = mx_exp_fp8(amax);
-                    uint4 lo, hi;
-                    encode_fp8x32(core, pow2f(e), lo, hi);
-                    *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3), nks)) = lo;
-                    *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + 1, nks)) = hi;
-                    a.cs[off_scale(k, G, nks)] = (uint8_t)(e + 127);
-                } else {
-                    const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float4 w = cp[q];
-                        core[4 * q] = w.x;
-                        core[4 * q + 1] = w.y;
-                        core[4 * q + 2] = w.z;
-                        core[4 * q + 3] = w.w;
-                    }
-                }
-                for (int r = rb; r < re; ++r) {
-                    if (tok_s[r] < 0) continue;
-                    float v[32];
-                    qload<XT>(buf, r, gc, v);
-                    float amax = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) {
-                        v[i] = v[i] - core[i];
-                        amax = fmaxf(amax, fabsf(v[i]));
-                    }
-                    const int e = mx_exp_fp4(amax);
-                    const long long s = slot0 + r;
-                    *(uint4*)(a.dq + off_fp4(s, G, nks)) = encode_fp4x32(v, pow2f(e));
-                    a.ds[off_scale(s, G, nks)] = (uint8_t)(e + 127);
-                }
             }
         }
-        barrier();   // every wave is done with buffer ci % QNBUF
-        if (wave == 0 && ci + QNBUF < nchunks) issue(ci + QNBUF);
+        return;
     }
-
-    // ---- U -> bf16, slot order (rows of absent tokens were zero)
-    if (wave == 1) {
+    // quantizer waves
+    for (long long s = 0; s < total; ++s, next_chunk()) {
+        barrier();
+        const int c0 = c * CC;
+        const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
+        const int mb = (int)(i & 1);
+        if (c == 0 && i + 1 < nmine) fill_meta(mb ^ 1, i + 1);   // the next block's metadata
+        // ---- quantizer: one (cube, group, quarter) per thread
+        const long long nks = a.Kp / 128;
+        const int ntask = B.ncores * NGC * 4;
+        // one task; FULL: the cube has at least QKEEP rows here (CM 0: S >= QKEEP),
+        // so the kept rows need no bound checks
+        auto task = [&](int t, auto full) {
+            constexpr bool FULL = decltype(full)::value;
+            const int qq = t & 3, pr = t >> 2;
+            const int cr = pr / NGC, gc = pr - cr * NGC;
+            const long long G = (c0 >> 5) + gc;
+            if (G * 32 >= a.Ci) return;                        // the same for the quad
+            const int4 md = meta_s[mb][cr];
+            const int rb = md.x, re = md.y, pm = md.z;
+            const int nr = CM == 0 ? g.S : re - rb;            // rows of the cube in this block
+            const long long k = B.k_first + cr;
+            float core[8], xr[QKEEP][8];                       // rows rb .. rb + QKEEP - 1 kept for the deltas
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+            for (int j = 0; j < QKEEP; ++j)
+                if (FULL || j < nr) qload8<XT>(buf, rb + j, gc, qq, ((pm >> j) & 1) ? 0u : 0x80000000u, xr[j]);
+            if constexpr (CM == 0) {
+                // fp32 sum of the present rows in slot order (pad rows read as
+                // -0.0 and drop out exactly), then the division
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
+                for (int e = 0; e < 8; ++e) core[e] = -0.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = rt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    if (row < nrows) a.u[(slot0 + row) * a.rp + ct * 32 + (lane & 31)] = bf16_rne(uacc[rt][ct][i]);
+                for (int j = 0; j < QKEEP; ++j)
+                    if (FULL || j < nr)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) core[e] += xr[j][e];
+                for (int r = rb + QKEEP; r < re; ++r) {
+                    float v[8];
+                    qload8<XT>(buf, r, gc, qq, tok_s[mb][r] >= 0 ? 0u : 0x80000000u, v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) core[e] += v[e];
                 }
+                const int cnt = md.w;
+                float amax = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    core[e] = mean_div(core[e], cnt);
+                    amax = fmaxf(amax, fabsf(core[e]));
+                }
+                amax = quad_max(amax);
+                const int ex = mx_exp_fp8(amax);
+                const float sc = pow2f(ex);
+                uint32_t d[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    v2s z = {0, 0};
+                    v2s p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, core[4 * h], core[4 * h + 1], sc, false);
+                    v2s q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, core[4 * h + 2], core[4 * h + 3], sc, true);
+                    d[h] = __builtin_bit_cast(uint32_t, q);
+                }
+                *(uint2*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + (qq >> 1), nks) + 8 * (qq & 1)) = make_uint2(d[0], d[1]);
+                if (qq == 0) a.cs[off_scale(k, G, nks)] = (uint8_t)(ex + 127);
+            } else {
+                const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32 + 8 * qq);
+                const float4 w0 = cp[0], w1 = cp[1];
+                core[0] = w0.x; core[1] = w0.y; core[2] = w0.z; core[3] = w0.w;
+                core[4] = w1.x; core[5] = w1.y; core[6] = w1.z; core[7] = w1.w;
             }
+            // Deltas of every row, pad rows included: their codes are never
+            // read back as a token's (the forward pass discards pad rows' outputs).
+            auto delta = [&](int r, const float* v) {
+                float dv[8];
+                float amax = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    dv[e] = v[e] - core[e];
+                    amax = fmaxf(amax, fabsf(dv[e]));
+                }
+                amax = quad_max(amax);
+                const int ex = mx_exp_fp4(amax);
+                const float sc = pow2f(ex);
+                uint32_t code = 0u;
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, dv[0], dv[1], sc, 0);
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, dv[2], dv[3], sc, 1);
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, dv[4], dv[5], sc, 2);
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, dv[6], dv[7], sc, 3);
+                const long long sl = B.slot0 + r;
+                *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code;
+                if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(ex + 127);
+            };
+#pragma unroll
+            for (int j = 0; j < QKEEP; ++j)
+                if (FULL || j < nr) delta(rb + j, xr[j]);
+            for (int r = rb + QKEEP; r < re; ++r) {
+                if (tok_s[mb][r] < 0) continue;
+                float v[8];
+                qload8<XT>(buf, r, gc, qq, 0u, v);
+                delta(r, v);
+            }
+        };
+        const bool full = (CM == 0 ? g.S : 0) >= QKEEP;
+        for (int t = qtid; t < ntask; t += 256) {
+            if (full) task(t, std::true_type{});
+            else task(t, std::false_type{});
+        }
     }
 }
 
@@ -493,12 +616,18 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
     a.l1t = w->l1t;
     a.coref = q->coref;
     a.zero = q->zero;
+    a.stok = q->stok;
     const long long cpb = QROWS / g.S;
-    unsigned blocks = q->core_mode == 0 ? (unsigned)((g.K + cpb - 1) / cpb) : (unsigned)((g.Nslot + QROWS - 1) / QROWS);
+    a.nblocks = q->core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const unsigned blocks = (unsigned)std::min<long long>(a.nblocks, cus);   // persistent: one workgroup per CU
     const int nct = q->rp / 32;
     auto go = [&](auto XT_, auto NCT_) {
         using XT = decltype(XT_);
-        k_quantize<XT, decltype(NCT_)::value><<<blocks, QTHREADS, 0, st>>>(a);
+        if (a.core_mode == 0) k_quantize<XT, decltype(NCT_)::value, 0><<<blocks, QTHREADS, 0, st>>>(a);
+        else k_quantize<XT, decltype(NCT_)::value, 1><<<blocks, QTHREADS, 0, st>>>(a);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
