@@ -39,24 +39,32 @@ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 //               tile step, in the order given at off_scale.
 __host__ __device__ inline int swz4(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
 __host__ __device__ inline int swz8(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
-// byte offset of FP4 group G (32 channels, 16 bytes) of a row
-__host__ __device__ inline size_t off_fp4(long long row, long long G, long long nks) {
-    const int r = (int)(row & 255);
-    return ((size_t)((row >> 8) * nks + (G >> 2)) * 256 + r) * 64 + (size_t)((((int)G & 3) ^ swz4(r)) << 4);
+// Offsets inside one tile step-block sequence: row r < 256 of its tile,
+// 32-bit (a tile of the largest operands spans well under 4 GB).
+// byte offset of FP4 group G (32 channels, 16 bytes) of tile row r
+__host__ __device__ inline uint32_t toff_fp4(int r, int G) {
+    return ((uint32_t)(G >> 2) * 256 + (uint32_t)r) * 64 + (uint32_t)(((G & 3) ^ swz4(r)) << 4);
 }
-// byte offset of 16-byte chunk c (channels 16c .. 16c + 15 of the row's step ks) of an FP8 row
-__host__ __device__ inline size_t off_fp8(long long row, long long ks, int c, long long nks) {
-    const int r = (int)(row & 255);
-    return ((size_t)((row >> 8) * nks + ks) * 256 + r) * 128 + (size_t)((c ^ swz8(r)) << 4);
+// byte offset of 16-byte chunk c (channels 16c .. 16c + 15 of K step ks) of FP8 tile row r
+__host__ __device__ inline uint32_t toff_fp8(int r, int ks, int c) {
+    return ((uint32_t)ks * 256 + (uint32_t)r) * 128 + (uint32_t)((c ^ swz8(r)) << 4);
 }
-// byte offset of the scale code of group G of a row.  A step's scale block
-// (256 rows x 4 groups, 1 KB) is ordered [row / 128][G % 2][row % 32]
+// byte offset of the scale code of group G of tile row r.  A step's scale
+// block (256 rows x 4 groups, 1 KB) is ordered [row / 128][G % 2][row % 32]
 // [(row % 128) / 32][(G % 4) / 2], so the 8 codes one GEMM lane needs in a K
 // step (its four 32-row blocks x its two groups) are 8 consecutive bytes.
+__host__ __device__ inline uint32_t toff_scale(int r, int G) {
+    return (uint32_t)(G >> 2) * 1024 + (uint32_t)((((r >> 7) * 2 + (G & 1)) * 32 + (r & 31)) * 8 + ((r >> 5) & 3) * 2 + ((G & 3) >> 1));
+}
+// the same for any row of a matrix of nks K steps
+__host__ __device__ inline size_t off_fp4(long long row, long long G, long long nks) {
+    return (size_t)(row >> 8) * (size_t)nks * 16384 + toff_fp4((int)(row & 255), (int)G);
+}
+__host__ __device__ inline size_t off_fp8(long long row, long long ks, int c, long long nks) {
+    return (size_t)(row >> 8) * (size_t)nks * 32768 + toff_fp8((int)(row & 255), (int)ks, c);
+}
 __host__ __device__ inline size_t off_scale(long long row, long long G, long long nks) {
-    const int r = (int)(row & 255), gi = (int)(G & 3);
-    return ((size_t)((row >> 8) * nks + (G >> 2))) * 1024 +
-           (size_t)((((r >> 7) * 2 + (gi & 1)) * 32 + (r & 31)) * 8 + ((r >> 5) & 3) * 2 + (gi >> 1));
+    return (size_t)(row >> 8) * (size_t)nks * 1024 + toff_scale((int)(row & 255), (int)G);
 }
 
 // Token grid and cube shape, with derived counts, as kernels see them.

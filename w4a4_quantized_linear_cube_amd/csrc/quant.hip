@@ -91,6 +91,40 @@ __device__ __forceinline__ QBlock qblock(const QuantArgs& a, long long b) {
 // (x + -0 = x for every x, zeros included), so pad rows drop out of the
 // cube's sum in slot order without a branch.
 template <typename XT>
+struct QRaw {
+    uint4 w[sizeof(XT) == 2 ? 1 : 2];
+};
+template <typename XT>
+__device__ __forceinline__ QRaw<XT> qraw8(const uint8_t* buf, int r, int gc, int qq) {
+    QRaw<XT> q;
+    if constexpr (sizeof(XT) == 2) {
+        q.w[0] = *(const uint4*)(buf + qoff(r, 4 * gc + qq));
+    } else {
+        q.w[0] = *(const uint4*)(buf + qoff(r, 8 * gc + 2 * qq));
+        q.w[1] = *(const uint4*)(buf + qoff(r, 8 * gc + 2 * qq + 1));
+    }
+    return q;
+}
+template <typename XT>
+__device__ __forceinline__ void qconv8(const QRaw<XT>& q, uint32_t sgn, float* v) {
+    if constexpr (sizeof(XT) == 2) {
+        const uint32_t d[4] = {q.w[0].x, q.w[0].y, q.w[0].z, q.w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float((d[i] << 16) | sgn);
+            v[2 * i + 1] = __uint_as_float((d[i] & 0xffff0000u) | sgn);
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v[4 * h] = __uint_as_float(q.w[h].x | sgn);
+            v[4 * h + 1] = __uint_as_float(q.w[h].y | sgn);
+            v[4 * h + 2] = __uint_as_float(q.w[h].z | sgn);
+            v[4 * h + 3] = __uint_as_float(q.w[h].w | sgn);
+        }
+    }
+}
+template <typename XT>
 __device__ __forceinline__ void qload8(const uint8_t* buf, int r, int gc, int qq, uint32_t sgn, float* v) {
     if constexpr (sizeof(XT) == 2) {
         const uint4 w = *(const uint4*)(buf + qoff(r, 4 * gc + qq));
@@ -344,8 +378,14 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
         // ---- quantizer: one (cube, group, quarter) per thread
         const long long nks = a.Kp / 128;
         const int ntask = B.ncores * NGC * 4;
-        // one task; FULL: the cube has at least QKEEP rows here (CM 0: S >= QKEEP),
-        // so the kept rows need no bound checks
+        // FULL: whole cubes of at least QKEEP rows with 64 % S == 0, so a
+        // block's rows (and its cubes) lie in one 256-row tile of the outputs
+        const bool full = CM == 0 && g.S >= QKEEP && 64 % g.S == 0;
+        uint8_t* const dq_t = a.dq + (size_t)(B.slot0 >> 8) * (size_t)nks * 16384;
+        uint8_t* const ds_t = a.ds + (size_t)(B.slot0 >> 8) * (size_t)nks * 1024;
+        uint8_t* const cq_t = a.cq + (size_t)(B.k_first >> 8) * (size_t)nks * 32768;
+        uint8_t* const cs_t = a.cs + (size_t)(B.k_first >> 8) * (size_t)nks * 1024;
+        // one task (FULL: the case above, so the kept rows need no bound checks)
         auto task = [&](int t, auto full) {
             constexpr bool FULL = decltype(full)::value;
             const int qq = t & 3, pr = t >> 2;
@@ -353,13 +393,17 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
             const long long G = (c0 >> 5) + gc;
             if (G * 32 >= a.Ci) return;                        // the same for the quad
             const int4 md = meta_s[mb][cr];
-            const int rb = md.x, re = md.y, pm = md.z;
+            const int rb = CM == 0 ? cr * g.S : md.x, re = CM == 0 ? rb + g.S : md.y, pm = md.z;   // CM 0: whole cubes
             const int nr = CM == 0 ? g.S : re - rb;            // rows of the cube in this block
             const long long k = B.k_first + cr;
             float core[8], xr[QKEEP][8];                       // rows rb .. rb + QKEEP - 1 kept for the deltas
+            QRaw<XT> raw[QKEEP];                               // all kept rows' LDS reads in flight together
 #pragma unroll
             for (int j = 0; j < QKEEP; ++j)
-                if (FULL || j < nr) qload8<XT>(buf, rb + j, gc, qq, ((pm >> j) & 1) ? 0u : 0x80000000u, xr[j]);
+                if (FULL || j < nr) raw[j] = qraw8<XT>(buf, rb + j, gc, qq);
+#pragma unroll
+            for (int j = 0; j < QKEEP; ++j)
+                if (FULL || j < nr) qconv8<XT>(raw[j], ((pm >> j) & 1) ? 0u : 0x80000000u, xr[j]);
             if constexpr (CM == 0) {
                 // fp32 sum of the present rows in slot order (pad rows read as
                 // -0.0 and drop out exactly), then the division
@@ -377,12 +421,17 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
                     for (int e = 0; e < 8; ++e) core[e] += v[e];
                 }
                 const int cnt = md.w;
+                if ((cnt & (cnt - 1)) == 0) {                  // exact power-of-two scaling
+                    const float rc = 1.0f / (float)cnt;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) core[e] *= rc;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) core[e] = __fdiv_rn(core[e], (float)cnt);
+                }
                 float amax = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    core[e] = mean_div(core[e], cnt);
-                    amax = fmaxf(amax, fabsf(core[e]));
-                }
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(core[e]));
                 amax = quad_max(amax);
                 const int ex = mx_exp_fp8(amax);
                 const float sc = pow2f(ex);
@@ -394,8 +443,14 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
                     v2s q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, core[4 * h + 2], core[4 * h + 3], sc, true);
                     d[h] = __builtin_bit_cast(uint32_t, q);
                 }
-                *(uint2*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + (qq >> 1), nks) + 8 * (qq & 1)) = make_uint2(d[0], d[1]);
-                if (qq == 0) a.cs[off_scale(k, G, nks)] = (uint8_t)(ex + 127);
+                if constexpr (FULL) {
+                    const int kt = (int)(B.k_first & 255) + cr;    // the block's cubes share one 256-cube tile
+                    *(uint2*)(cq_t + toff_fp8(kt, (int)(G >> 2), 2 * (int)(G & 3) + (qq >> 1)) + 8 * (qq & 1)) = make_uint2(d[0], d[1]);
+                    if (qq == 0) cs_t[toff_scale(kt, (int)G)] = (uint8_t)(ex + 127);
+                } else {
+                    *(uint2*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + (qq >> 1), nks) + 8 * (qq & 1)) = make_uint2(d[0], d[1]);
+                    if (qq == 0) a.cs[off_scale(k, G, nks)] = (uint8_t)(ex + 127);
+                }
             } else {
                 const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32 + 8 * qq);
                 const float4 w0 = cp[0], w1 = cp[1];
@@ -424,9 +479,44 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
                 *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code;
                 if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(ex + 127);
             };
+            if constexpr (FULL) {
+                // the kept rows together: their maxima, exponents and codes
+                // interleave; lane qq writes row qq's scale code
+                const int rt0 = (int)(B.slot0 & 255) + rb;          // the block's rows share one 256-row tile
+                float am[QKEEP];
+                uint32_t code[QKEEP];
+                int ex[QKEEP];
 #pragma unroll
-            for (int j = 0; j < QKEEP; ++j)
-                if (FULL || j < nr) delta(rb + j, xr[j]);
+                for (int j = 0; j < QKEEP; ++j) {
+                    am[j] = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        xr[j][e] = xr[j][e] - core[e];
+                        am[j] = fmaxf(am[j], fabsf(xr[j][e]));
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < QKEEP; ++j) am[j] = quad_max(am[j]);
+#pragma unroll
+                for (int j = 0; j < QKEEP; ++j) {
+                    ex[j] = mx_exp_fp4(am[j]);
+                    const float sc = pow2f(ex[j]);
+                    uint32_t w = 0u;
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][0], xr[j][1], sc, 0);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][2], xr[j][3], sc, 1);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][4], xr[j][5], sc, 2);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][6], xr[j][7], sc, 3);
+                    code[j] = w;
+                }
+#pragma unroll
+                for (int j = 0; j < QKEEP; ++j) *(uint32_t*)(dq_t + toff_fp4(rt0 + j, (int)G) + 4 * qq) = code[j];
+                const int exq = qq == 0 ? ex[0] : qq == 1 ? ex[1] : qq == 2 ? ex[2] : ex[3];
+                ds_t[toff_scale(rt0 + qq, (int)G)] = (uint8_t)(exq + 127);
+            } else {
+#pragma unroll
+                for (int j = 0; j < QKEEP; ++j)
+                    if (j < nr) delta(rb + j, xr[j]);
+            }
             for (int r = rb + QKEEP; r < re; ++r) {
                 if (tok_s[mb][r] < 0) continue;
                 float v[8];
@@ -434,7 +524,6 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
                 delta(r, v);
             }
         };
-        const bool full = (CM == 0 ? g.S : 0) >= QKEEP;
         for (int t = qtid; t < ntask; t += 256) {
             if (full) task(t, std::true_type{});
             else task(t, std::false_type{});
