@@ -7,9 +7,13 @@ broadcast, token-order fp32 output).  Prints one JSON line.
 
 value  = effective TOPS of the whole step, 2 N Ci Co / t_step (the dense
          layer's work; the method's own work differs, see 'work' below).
-roofline = the dominant kernel (the forward GEMM over the tokens): its
-         algorithmic flops per launch / its average duration from HIP events
-         on the launch stream, against the MFMA peak of its operand types.
+roofline = the dominant kernel, the delta GEMM (dq_delta_term: one launch of
+         the FP4 x FP4 scaled-MFMA GEMM over the slots, with the low-rank
+         branch, the core-term broadcast and the token-order stores in its
+         epilogue): algorithmic FP4 flops per launch, 2 N_slot Ci Co, / its
+         average duration from HIP events on the launch stream, against the
+         dense FP4 peak; traffic from the committed rocprofv3 counter summary
+         of the same kernel source, else null.
 cpu_baseline = the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -42,8 +46,8 @@ def parse():
     ap.add_argument("--x-seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the oracle's timed sample")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--copy-only-mib", type=int, default=0,
+                    help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
 
 
@@ -56,6 +60,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_only_mib:
+        nbytes = args.copy_only_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copies: 3 x {nbytes} bytes read and written", file=sys.stderr, flush=True)
+        return
 
     from w4a4_quantized_linear_cube_amd import dq, synth
 
@@ -85,7 +99,8 @@ def main():
     K = Tc * Hc * Wc
     S = t_ * h_ * w_
     dense_flops = 2.0 * N * Ci * Co
-    f_fp4 = 2.0 * N * Ci * Co            # delta term, one row per token
+    Nslot = K * S
+    f_fp4 = 2.0 * Nslot * Ci * Co        # delta term, one row per slot (pad slots of partial cubes included)
     f_fp8 = 2.0 * K * Ci * Co            # core term, one row per cube
     f_bf16 = 2.0 * N * r * (Ci + Co)     # low-rank branch
     xbytes = 2 if cfg.dtype == "bf16" else 4
@@ -96,45 +111,54 @@ def main():
         dq.dq_linear(weights, x, qa, y, stream)
     torch.cuda.synchronize()
 
-    # timed steps; per-phase events on the launch stream
-    t_quant, t_fwd = [], []
+    # timed steps (activation pass, core term, delta term: dq_linear's work);
+    # per-phase events on the launch stream
+    t_quant, t_core, t_delta = [], [], []
     start = ev()
     torch.cuda.synchronize()
     start.record(stream)
     marks = []
     for _ in range(args.steps):
-        a, b, c = ev(), ev(), ev()
+        a, b, c, d = ev(), ev(), ev(), ev()
         a.record(stream)
         dq.dq_quantize_act(weights, x, qa, stream)
         b.record(stream)
-        dq.dq_linear_forward(weights, qa, y, stream)
+        dq.dq_core_term(weights, qa, stream)
         c.record(stream)
-        marks.append((a, b, c))
+        dq.dq_delta_term(weights, qa, y, stream)
+        d.record(stream)
+        marks.append((a, b, c, d))
     end = ev()
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    for a, b, c in marks:
+    for a, b, c, d in marks:
         t_quant.append(a.elapsed_time(b))
-        t_fwd.append(b.elapsed_time(c))
+        t_core.append(b.elapsed_time(c))
+        t_delta.append(c.elapsed_time(d))
     ms_step = total_ms / args.steps
     q_ms = float(np.mean(t_quant))
-    f_ms = float(np.mean(t_fwd))
+    c_ms = float(np.mean(t_core))
+    d_ms = float(np.mean(t_delta))
+    f_ms = c_ms + d_ms
 
-    if args.copy_probe_mib:
-        nbytes = args.copy_probe_mib << 20
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy probe: {nbytes} bytes read, {nbytes} bytes written", file=sys.stderr, flush=True)
+    # device-to-device copy rate (the practical ceiling of the activation pass)
+    cbytes = 1 << 30
+    csrc = torch.empty(cbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    c0, c1 = ev(), ev()
+    c0.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
 
     value = dense_flops / (ms_step * 1e-3) / 1e12
-    fwd_flops = f_fp4 + f_fp8 + f_bf16
-    t_min_fwd = f_fp4 / PEAK_FP4 + f_fp8 / PEAK_FP8 + f_bf16 / PEAK_BF16
-    peak_mix = fwd_flops / t_min_fwd
-    achieved = fwd_flops / (f_ms * 1e-3)
+    achieved = f_fp4 / (d_ms * 1e-3)
+    traffic = committed_traffic(args.config, cube)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -169,20 +193,48 @@ def main():
             "algorithmic_bytes": int(quant_bytes),
             "GBps": round(quant_bytes / (q_ms * 1e-3) / 1e9, 1),
             "pct_hbm": round(100 * quant_bytes / (q_ms * 1e-3) / PEAK_HBM, 2),
+            "copy_GBps": round(copy_gbps, 1),
+            "pct_copy": round(100 * quant_bytes / (q_ms * 1e-3) / 1e9 / copy_gbps, 2),
+        },
+        "core_term": {
+            "ms": round(c_ms, 4),
+            "fp8_tflops": round(f_fp8 / (c_ms * 1e-3) / 1e12, 2),
+            "pct_fp8_peak": round(100 * f_fp8 / (c_ms * 1e-3) / PEAK_FP8, 2),
         },
         "roofline": {
-            "kernel": "forward GEMMs (core term + delta term + low-rank branch + store)",
+            "kernel": "delta GEMM (dq_delta_term: FP4 x FP4 scaled MFMA over the slots; low-rank branch, "
+                      "core-term broadcast and token-order stores in the epilogue)",
             "bound": "mfma",
             "achieved": round(achieved / 1e12, 2),
-            "peak": round(peak_mix / 1e12, 2),
+            "peak": round(PEAK_FP4 / 1e12, 2),
             "unit": "TFLOP/s",
-            "frac": round(achieved / peak_mix, 4),
-            "traffic": None,
+            "frac": round(achieved / PEAK_FP4, 4),
+            "traffic": traffic,
+            "ms": round(d_ms, 4),
             "work": {"fp4_flops": f_fp4, "fp8_flops": f_fp8, "bf16_flops": f_bf16},
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def committed_traffic(config, cube):
+    """HBM bytes per launch of the delta GEMM from the committed counter
+    summary (profiles/delta_gemm_<config>_traffic.json: FETCH_SIZE and
+    WRITE_SIZE per dispatch, each scaled by the same counter's reading for a
+    plain copy of known size), if it was taken on this workload and on the
+    current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"delta_gemm_{config}_traffic.json")
+    src = os.path.join(ROOT, "w4a4_quantized_linear_cube_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_hip_sha256") != digest or list(rec.get("cube", [])) != list(cube):
+        return None
+    return rec.get("traffic_bytes")
 
 
 def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):

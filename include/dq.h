@@ -142,6 +142,20 @@ dq_status dq_quantize_act(const dq_weights* w, const void* x_dev, dq_dtype dt, d
  * in `q` by the last dq_quantize_act.  Asynchronous on `stream`. */
 dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
 
+/* The two halves of dq_linear_forward, in its order, for callers that time
+ * or schedule them separately.
+ * dq_core_term: the per-cube core term Q8(core_k) Q4(R) (the pages'
+ *   "dynamic token bias", one row per cube, 关键设计 4), fp32, into the
+ *   workspace `q`.
+ * dq_delta_term: Q4(delta_n) Q4(R) + U[n] L2, plus the core term of token
+ *   n's cube as left in `q` by the last dq_core_term, written to y_dev
+ *   [N][Co] fp32 in token order (every element written).
+ * Same arguments, errors and asynchrony as dq_linear_forward; calling
+ * dq_delta_term without dq_core_term after a dq_quantize_act reads a stale
+ * core term (not detected). */
+dq_status dq_core_term(const dq_weights* w, dq_qact* q, void* stream);
+dq_status dq_delta_term(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
+
 /* dq_quantize_act followed by dq_linear_forward on the same stream. */
 dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, float* y_dev, void* stream);
 

@@ -223,6 +223,25 @@ def test_two_runs_bit_identical(dqm):
         assert np.array_equal(outs[0][1][k], outs[1][1][k]), k
 
 
+
+def test_forward_halves_match_forward(dqm):
+    """dq_core_term then dq_delta_term is dq_linear_forward (the same launches)."""
+    _say("case forward halves")
+    T, H, W, Ci, Co = 4, 10, 12, 256, 512
+    x = synth.make_activation(T, H, W, Ci, seed=15, dtype="bf16", n_outliers=4).to(DEV)
+    wt = synth.make_weight(Ci, Co, seed=16, dtype="bf16")
+    l1, l2 = _random_factors(Ci, Co, 32, 19)
+    weights = dqm.dq_prepare_weights_lowrank(wt, l1, l2)
+    qa = dqm.dq_qact_create(weights, (T, H, W, 1, 2, 2))
+    dqm.dq_quantize_act(weights, x, qa)
+    y1 = torch.full((T * H * W, Co), float("nan"), device=DEV)
+    y2 = torch.full((T * H * W, Co), float("nan"), device=DEV)
+    dqm.dq_linear_forward(weights, qa, y1)
+    dqm.dq_core_term(weights, qa)
+    dqm.dq_delta_term(weights, qa, y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+
 def test_library_svd_path(dqm):
     """dq_prepare_weights: the host SVD factors meet Eckart-Young, and R / Q4(R)
     follow from them (R = fl32(W - L1 L2) within one rounding; codes decode to

@@ -62,6 +62,8 @@ def test_argument_errors_before_any_device_work(lib):
     _expect(lib.dq_qact_create(None, dq.Geom(2, 2, 2, 1, 1, 1), ctypes.byref(h)), 1, lib)
     _expect(lib.dq_quantize_act(None, None, 0, None, None), 1, lib)
     _expect(lib.dq_linear_forward(None, None, None, None), 1, lib)
+    _expect(lib.dq_core_term(None, None, None), 1, lib)
+    _expect(lib.dq_delta_term(None, None, None, None), 1, lib)
     _expect(lib.dq_lowrank_factors(P(w), 0, 96, 64, -1, 0, P(l1), P(l2)), 1, lib)
     _expect(lib.dq_lowrank_factors(P(w), 0, 0, 64, 1, 0, P(l1), P(l2)), 2, lib)
 

@@ -401,17 +401,29 @@ dq_status dq_quantize_act(const dq_weights* w, const void* x_dev, dq_dtype dt, d
     return DQ_OK;
 }
 
-dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {
+static dq_status forward_parts(const dq_weights* w, dq_qact* q, float* y_dev, int parts, void* stream) {
     g_last_error.clear();
     dq_status st = check_pair(w, q);
     if (st != DQ_OK) return st;
-    if (!y_dev) return fail(DQ_ERR_INVALID_ARG, "y_dev is NULL");
+    if ((parts & dq::FWD_DELTA) && !y_dev) return fail(DQ_ERR_INVALID_ARG, "y_dev is NULL");
     if (((uintptr_t)y_dev) % 4 != 0) return fail(DQ_ERR_INVALID_ARG, "y_dev must be 4-byte aligned");
     DeviceGuard dg(q->device);
     if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
-    hipError_t e = launch_forward(w, q, y_dev, (hipStream_t)stream);
+    hipError_t e = launch_forward(w, q, y_dev, parts, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return DQ_OK;
+}
+
+dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {
+    return forward_parts(w, q, y_dev, dq::FWD_CORE | dq::FWD_DELTA, stream);
+}
+
+dq_status dq_core_term(const dq_weights* w, dq_qact* q, void* stream) {
+    return forward_parts(w, q, nullptr, dq::FWD_CORE, stream);
+}
+
+dq_status dq_delta_term(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {
+    return forward_parts(w, q, y_dev, dq::FWD_DELTA, stream);
 }
 
 dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, float* y_dev, void* stream) {

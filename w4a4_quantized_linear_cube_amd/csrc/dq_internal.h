@@ -124,6 +124,7 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
 hipError_t launch_slot_tokens(const Geom& g, int* stok, int64_t n, hipStream_t st);
 
 // ---- launchers (gemm.hip) ----
-hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t st);
+constexpr int FWD_CORE = 1, FWD_DELTA = 2;   // parts of the forward pass
+hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, hipStream_t st);
 
 }  // namespace dq

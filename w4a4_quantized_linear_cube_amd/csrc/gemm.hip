@@ -647,7 +647,7 @@ static hipError_t launch(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t st) {
+hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, hipStream_t st) {
     GemmArgs d{};
     d.a = w->rq;
     d.as = w->rs;
@@ -666,22 +666,27 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, hipStream_t
     d.l2t = w->l2t;
     d.rp = w->rp;
     d.sink = q->sink;
-    // 1) per-cube core term bias[k] = Q8(core_k) Q4(R)
-    GemmArgs c = d;
-    c.b = q->cq;
-    c.bs = q->cs;
-    c.ntiles = (int)(q->K_pad / 256);
-    c.c = q->bias;
-    c.ldc = w->Cop;
-    hipError_t e = launch<FMT_FP8, EPI_STORE>(c, st);
-    if (e != hipSuccess) return e;
-    // 2) delta term + low-rank branch + the cube's core term -> y (token order)
-    d.bias = q->bias;
-    d.ldbias = w->Cop;
-    // (32-bit element offsets into y and into the per-cube term)
-    const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
-    if (d.S % 4 == 0 && d.rp == 32 && d.vec4 && off32) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
-    return launch<FMT_FP4, EPI_TOKENS>(d, st);
+    if (parts & FWD_CORE) {
+        // per-cube core term bias[k] = Q8(core_k) Q4(R)
+        GemmArgs c = d;
+        c.b = q->cq;
+        c.bs = q->cs;
+        c.ntiles = (int)(q->K_pad / 256);
+        c.c = q->bias;
+        c.ldc = w->Cop;
+        hipError_t e = launch<FMT_FP8, EPI_STORE>(c, st);
+        if (e != hipSuccess) return e;
+    }
+    if (parts & FWD_DELTA) {
+        // delta term + low-rank branch + the cube's core term -> y (token order)
+        d.bias = q->bias;
+        d.ldbias = w->Cop;
+        // (32-bit element offsets into y and into the per-cube term)
+        const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
+        if (d.S % 4 == 0 && d.rp == 32 && d.vec4 && off32) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
+        return launch<FMT_FP4, EPI_TOKENS>(d, st);
+    }
+    return hipSuccess;
 }
 
 }  // namespace dq

@@ -24,7 +24,7 @@ STATUS = {0: "DQ_OK", 1: "DQ_ERR_INVALID_ARG", 2: "DQ_ERR_SHAPE", 3: "DQ_ERR_UNS
 EXPORTS = ("dq_last_error", "dq_status_str", "dq_lowrank_factors", "dq_prepare_weights_lowrank",
            "dq_prepare_weights", "dq_weights_destroy", "dq_weights_info", "dq_weights_export",
            "dq_qact_create", "dq_qact_destroy", "dq_qact_info", "dq_quantize_act", "dq_linear_forward",
-           "dq_linear", "dq_qact_export")
+           "dq_core_term", "dq_delta_term", "dq_linear", "dq_qact_export")
 
 
 class DQError(RuntimeError):
@@ -66,6 +66,8 @@ def load():
         "dq_qact_info": ([P, P, P, P], ctypes.c_int),
         "dq_quantize_act": ([P, P, ctypes.c_int, P, P], ctypes.c_int),
         "dq_linear_forward": ([P, P, P, P], ctypes.c_int),
+        "dq_core_term": ([P, P, P], ctypes.c_int),
+        "dq_delta_term": ([P, P, P, P], ctypes.c_int),
         "dq_linear": ([P, P, ctypes.c_int, P, P, P], ctypes.c_int),
         "dq_qact_export": ([P, P, P, P, P, P, P], ctypes.c_int),
     }
@@ -197,6 +199,14 @@ def dq_quantize_act(w: Weights, x, q: QAct, stream=None):
 
 def dq_linear_forward(w: Weights, q: QAct, y, stream=None):
     _check(load().dq_linear_forward(w.handle, q.handle, _ptr(y), _stream(stream)), "dq_linear_forward")
+
+
+def dq_core_term(w: Weights, q: QAct, stream=None):
+    _check(load().dq_core_term(w.handle, q.handle, _stream(stream)), "dq_core_term")
+
+
+def dq_delta_term(w: Weights, q: QAct, y, stream=None):
+    _check(load().dq_delta_term(w.handle, q.handle, _ptr(y), _stream(stream)), "dq_delta_term")
 
 
 def dq_linear(w: Weights, x, q: QAct, y, stream=None):
