@@ -387,7 +387,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                     for (int i = 0; i < 4; ++i) {
                         const int rr = 8 * i + (lane >> 3);
                         const float4 v = tget(pb & 1, i);
-                        *(float4*)(p.c + (long long)(n0 + wc * 128 + 32 * ni + rr) * p.ldc + m0 + wr * 128 + 32 * mi + 4 * (lane & 7)) = v;
+                        __builtin_nontemporal_store(__builtin_bit_cast(v4f, v),   // read once, by the delta GEMM
+                                                    (v4f*)(p.c + (long long)(n0 + wc * 128 + 32 * ni + rr) * p.ldc + m0 + wr * 128 + 32 * mi + 4 * (lane & 7)));
                     }
                 }
             }
@@ -412,7 +413,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                 const int k = min((n0 + wc * 128 + 32 * ni + l32) / p.S, p.kmax);   // pad slots: any valid row, never stored
                 const uint32_t bo = ((uint32_t)k * (uint32_t)p.ldbias + (uint32_t)(ch0 + 8 * u4)) * 4;
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) bq[ni][mi] = ld_off<float4>(p.bias, bo + 128 * mi);
+                for (int mi = 0; mi < 4; ++mi)   // each element is read once: no cache allocation
+                    bq[ni][mi] = __builtin_bit_cast(float4, __builtin_nontemporal_load((const v4f*)((const char*)p.bias + bo + 128 * mi)));
             };
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) tok[ni] = ld_off<int>(p.stok, (uint32_t)(n0 + wc * 128 + 32 * ni + l32) * 4);
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float* dst = (t[i] >= 0 && ch < p.Co) ? p.y + (uint32_t)(t[i] * p.Co + ch) : p.sink + 4 * lane;
-                        *(float4*)dst = v[i];
+                        __builtin_nontemporal_store(__builtin_bit_cast(v4f, v[i]), (v4f*)dst);   // y is not read back
                     }
                 }
             }
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                                                  a[4 * j + 2] + bv[mi][j].z, a[4 * j + 3] + bv[mi][j].w);
                     const int ch = ch0 + 32 * mi + 8 * j;
                     if (p.vec4 && ch + 4 <= p.Co) {
-                        *(float4*)(yrow + ch) = o;
+                        __builtin_nontemporal_store(__builtin_bit_cast(v4f, o), (v4f*)(yrow + ch));
                     } else {
                         if (ch < p.Co) yrow[ch] = o.x;
                         if (ch + 1 < p.Co) yrow[ch + 1] = o.y;
