@@ -23,8 +23,6 @@
 namespace dq {
 
 constexpr int QROWS = 64;                  // slot rows per block
-constexpr int QWAVES = 7;                  // wave 0: U; waves 1-2: copies; waves 3-6: quantizer
-constexpr int QTHREADS = QWAVES * 64;
 constexpr int QROWB = 256;                 // bytes of one row's channel chunk in LDS
 constexpr int QCHUNK = QROWS * QROWB;      // 16 KB
 constexpr int QDMA = QCHUNK / 2 / 1024;    // 1 KB X copies per copy wave per chunk
@@ -146,12 +144,29 @@ __device__ __forceinline__ void qload8(const uint8_t* buf, int r, int gc, int qq
     }
 }
 
-// Ring depth: the copy waves keep (depth - 1) chunks in flight, at most 63
-// copies (the vmcnt range), in at most 150 KB of LDS.
-constexpr int qnbuf(int stage, int dmaw) {
-    return (1 + 63 / dmaw) < (150 * 1024 / stage) ? ((1 + 63 / dmaw) < 8 ? 1 + 63 / dmaw : 8)
-                                                  : ((150 * 1024 / stage) < 8 ? 150 * 1024 / stage : 8);
+// Ring depth for sp chunks per barrier: at most (depth - sp) chunks of
+// copies outstanding (63, the vmcnt range), at most 150 KB of LDS, at most 8.
+constexpr int qnbuf(int stage, int dmaw, int sp) {
+    const int a = sp + 63 / dmaw, b = 150 * 1024 / stage;
+    return a < b ? (a < 8 ? a : 8) : (b < 8 ? b : 8);
 }
+
+// Geometry of the activation pass for input type XT and NCT 32-wide rank
+// tiles: channels per chunk, LDS stage (X chunk + L1 slice), copies per copy
+// wave per chunk, chunks per barrier, ring depth, waves (wave 0: U; waves
+// 1-2: copies; then one quantizer group of four waves per chunk of a period).
+template <typename XT, int NCT>
+struct QCfg {
+    static constexpr int CC = XTraits<XT>::CC;
+    static constexpr int LROWB = 2 * CC;
+    static constexpr int LRPC = 1024 / LROWB;
+    static constexpr int LDMA = NCT * 32 / LRPC / 2;
+    static constexpr int QDMAW = QDMA + LDMA;
+    static constexpr int STAGE = QCHUNK + NCT * 32 * LROWB;
+    static constexpr int SP = qnbuf(STAGE, QDMAW, 2) >= 5 ? 2 : 1;
+    static constexpr int NB = qnbuf(STAGE, QDMAW, SP);
+    static constexpr int THREADS = (3 + 4 * SP) * 64;
+};
 
 // maximum over the four lanes of a quad (DPP quad_perm exchanges)
 __device__ __forceinline__ float quad_max(float v) {
@@ -174,7 +189,7 @@ __device__ __forceinline__ float quad_max(float v) {
 // order, then the division), its FP8 codes, each row's delta FP4 codes.
 // X is read from HBM exactly once.
 template <typename XT, int NCT, int CM>
-__global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
+__global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantArgs a) {
     constexpr int CC = XTraits<XT>::CC;
     constexpr int NGC = CC / 32;                     // groups per chunk
     constexpr int EPC = 16 / (int)sizeof(XT);        // elements per 16-byte piece
@@ -186,10 +201,14 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
     constexpr int LDMA = NCT * 32 / LRPC / 2;        // L1 copies per copy wave per chunk
     constexpr int QDMAW = QDMA + LDMA;               // copies per copy wave per chunk
     constexpr int STAGE = QCHUNK + NCT * 32 * LROWB;
-    constexpr int QNBUF = qnbuf(STAGE, QDMAW);       // ring stages
+    // chunks per barrier: two when the ring is deep enough (each quantizer
+    // group then has two chunk periods for its chunk), else one
+    constexpr int SP = QCfg<XT, NCT>::SP;
+    constexpr int QNBUF = QCfg<XT, NCT>::NB;         // ring stages
+    static_assert(QNBUF >= 2 * SP, "ring too shallow");
     __shared__ __attribute__((aligned(1024))) uint8_t xbuf[QNBUF * STAGE];
-    __shared__ int tok_s[2][QROWS];
-    __shared__ int4 meta_s[2][QROWS];   // per cube: first row, end row, present rows (bit j: row first + j), tokens
+    __shared__ int tok_s[2][2][QROWS];              // [group][buffer]
+    __shared__ int4 meta_s[2][2][QROWS];            // per cube: first row, end row, present rows (bit j: row first + j), tokens
 
     const Geom& g = a.g;
     const int tid = threadIdx.x;
@@ -200,25 +219,27 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
     const long long total = nmine * nchunks;
     const uint32_t lds0 = (uint32_t)(uintptr_t)xbuf;
     const XT* __restrict__ x = (const XT*)a.x;
-    const int qtid = tid - 192;                      // quantizer thread (waves 3-6)
+    const int qgrp = (wave - 3) >> 2;                // quantizer group (waves 3-6, 7-10)
+    const int qtid = tid - 192 - 256 * qgrp;         // thread within the group
 
-    // block metadata, double-buffered by block parity: token of each row;
-    // per cube its row range, which of its first 32 rows hold tokens, and its
-    // token count
+    // block metadata of a quantizer group, double-buffered: token of each
+    // row; per cube its row range, which of its first 32 rows hold tokens,
+    // and its token count
     auto fill_meta = [&](int mb, long long i) {
         const QBlock B = qblock(a, blockIdx.x + i * gridDim.x);
+        int* const tok_s_ = tok_s[qgrp][mb];
+        int4* const meta_s_ = meta_s[qgrp][mb];
         if (qtid < QROWS) {
             const int rb = qtid < B.ncores ? (int)max(0LL, (B.k_first + qtid) * g.S - B.slot0) : 0;
             const int re = qtid < B.ncores ? (int)min((long long)B.nrows, (B.k_first + qtid + 1) * g.S - B.slot0) : 0;
             int pm = 0;
             for (int j = 0; j < 32 && rb + j < re; ++j) pm |= (a.stok[B.slot0 + rb + j] >= 0 ? 1 : 0) << j;
-            tok_s[mb][qtid] = qtid < B.nrows ? a.stok[B.slot0 + qtid] : -1;
+            tok_s_[qtid] = qtid < B.nrows ? a.stok[B.slot0 + qtid] : -1;
             int ct, ch, cw;
             const int cnt = qtid < B.ncores ? cube_count(g, B.k_first + qtid, &ct, &ch, &cw) : 0;
-            meta_s[mb][qtid] = make_int4(rb, re, pm, cnt);
+            meta_s_[qtid] = make_int4(rb, re, pm, cnt);
         }
     };
-    if (wave >= 3) fill_meta(0, 0);
 
     // ---- copy waves: wave 1 rows 0-31, wave 2 rows 32-63 of each chunk; copy
     // j covers rows 4 j .. 4 j + 3 of the wave's half (lane: row + lane / 16,
@@ -289,16 +310,22 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
         for (int j = 0; j < (NCT > 0 ? NCT : 1); ++j) uacc[i][j] = (v16f){};
 
     // The three roles run their own loops over the chunk stream, one barrier
-    // per chunk each: chunk s has landed and is visible at barrier s, and
-    // every wave is done with chunk s - 1, whose stage takes the copies of
-    // chunk s + QNBUF - 1.
+    // per period of SP chunks: chunks SP u .. SP u + SP - 1 have landed and
+    // are visible at barrier u, and every wave is done with the previous
+    // period's chunks, whose stages take the copies of chunks
+    // SP u + QNBUF - SP .. SP u + QNBUF - 1.  Quantizer group q takes chunk
+    // SP u + q.
+    const long long nsteps = (total + SP - 1) / SP;   // barrier periods
     if (wave == 1 || wave == 2) {
         load_toks(0);
-        for (int k = 0; k < QNBUF - 1; ++k) issue();
-        for (long long s = 0; s < total; ++s) {
-            __builtin_amdgcn_s_waitcnt(((QNBUF - 2) * QDMAW & 15) | (((QNBUF - 2) * QDMAW >> 4) << 14) | 0x0F70);
+        for (int k = 0; k < QNBUF - SP; ++k) issue();
+        for (long long u = 0; u < nsteps; ++u) {
+            // chunks SP u .. SP u + SP - 1 landed: later copies in flight
+            constexpr int LATER = (QNBUF - 2 * SP) * QDMAW;
+            __builtin_amdgcn_s_waitcnt((LATER & 15) | ((LATER >> 4) << 14) | 0x0F70);
             barrier();
-            issue();
+#pragma unroll
+            for (int k = 0; k < SP; ++k) issue();
         }
         // the surplus copies land before the wave ends (no copy may write
         // LDS after the workgroup has released it)
@@ -317,7 +344,7 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
     };
     if (wave == 0) {
         for (long long s = 0; s < total; ++s, next_chunk()) {
-            barrier();
+            if (s % SP == 0) barrier();
             if constexpr (NCT == 0) continue;
             const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
             // ---- U += bf16(X chunk) L1 chunk, both operands from the stage
@@ -366,15 +393,20 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
                     }
             }
         }
+        // barriers of the periods after the last chunk's (none: total chunks
+        // fill nsteps periods, the last one possibly partly)
         return;
     }
-    // quantizer waves
-    for (long long s = 0; s < total; ++s, next_chunk()) {
+    // quantizer groups: group q takes chunks q, q + SP, q + 2 SP, ...
+    for (int k = 0; k < qgrp; ++k) next_chunk();
+    int mb = 0;                                      // the group's metadata buffer of its current block
+    if (qgrp < total) fill_meta(0, i);
+    for (long long u = 0; u < nsteps; ++u) {
         barrier();
+        const long long s = SP * u + qgrp;
+        if (s >= total) continue;
         const int c0 = c * CC;
         const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
-        const int mb = (int)(i & 1);
-        if (c == 0 && i + 1 < nmine) fill_meta(mb ^ 1, i + 1);   // the next block's metadata
         // ---- quantizer: one (cube, group, quarter) per thread
         const long long nks = a.Kp / 128;
         const int ntask = B.ncores * NGC * 4;
@@ -392,7 +424,7 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
             const int cr = pr / NGC, gc = pr - cr * NGC;
             const long long G = (c0 >> 5) + gc;
             if (G * 32 >= a.Ci) return;                        // the same for the quad
-            const int4 md = meta_s[mb][cr];
+            const int4 md = meta_s[qgrp][mb][cr];
             const int rb = CM == 0 ? cr * g.S : md.x, re = CM == 0 ? rb + g.S : md.y, pm = md.z;   // CM 0: whole cubes
             const int nr = CM == 0 ? g.S : re - rb;            // rows of the cube in this block
             const long long k = B.k_first + cr;
@@ -416,7 +448,7 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
                         for (int e = 0; e < 8; ++e) core[e] += xr[j][e];
                 for (int r = rb + QKEEP; r < re; ++r) {
                     float v[8];
-                    qload8<XT>(buf, r, gc, qq, tok_s[mb][r] >= 0 ? 0u : 0x80000000u, v);
+                    qload8<XT>(buf, r, gc, qq, tok_s[qgrp][mb][r] >= 0 ? 0u : 0x80000000u, v);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) core[e] += v[e];
                 }
@@ -518,7 +550,7 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
                     if (j < nr) delta(rb + j, xr[j]);
             }
             for (int r = rb + QKEEP; r < re; ++r) {
-                if (tok_s[mb][r] < 0) continue;
+                if (tok_s[qgrp][mb][r] < 0) continue;
                 float v[8];
                 qload8<XT>(buf, r, gc, qq, 0u, v);
                 delta(r, v);
@@ -527,6 +559,15 @@ __global__ __launch_bounds__(QTHREADS, 1) void k_quantize(QuantArgs a) {
         for (int t = qtid; t < ntask; t += 256) {
             if (full) task(t, std::true_type{});
             else task(t, std::false_type{});
+        }
+        // the group's next chunk; a new block's metadata goes to the other
+        // buffer now and is read after the next barrier
+        const long long i_prev = i;
+#pragma unroll
+        for (int k = 0; k < SP; ++k) next_chunk();
+        if (i != i_prev && i < nmine) {
+            mb ^= 1;
+            fill_meta(mb, i);
         }
     }
 }
@@ -715,8 +756,9 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
     const int nct = q->rp / 32;
     auto go = [&](auto XT_, auto NCT_) {
         using XT = decltype(XT_);
-        if (a.core_mode == 0) k_quantize<XT, decltype(NCT_)::value, 0><<<blocks, QTHREADS, 0, st>>>(a);
-        else k_quantize<XT, decltype(NCT_)::value, 1><<<blocks, QTHREADS, 0, st>>>(a);
+        constexpr int THREADS = QCfg<XT, decltype(NCT_)::value>::THREADS;
+        if (a.core_mode == 0) k_quantize<XT, decltype(NCT_)::value, 0><<<blocks, THREADS, 0, st>>>(a);
+        else k_quantize<XT, decltype(NCT_)::value, 1><<<blocks, THREADS, 0, st>>>(a);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
