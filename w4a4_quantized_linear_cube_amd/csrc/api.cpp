@@ -356,7 +356,7 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
         (e = dalloc(&q->bias, (size_t)(q->K_pad * q->Cop), &q->bytes)) != hipSuccess ||
         (e = dalloc(&q->stok, (size_t)q->Nslot_pad, &q->bytes)) != hipSuccess ||
         (e = dalloc(&q->zero, (size_t)512, &q->bytes)) != hipSuccess ||
-        (e = dalloc(&q->sink, (size_t)256, &q->bytes)) != hipSuccess)
+        (e = dalloc(&q->sink, (size_t)512, &q->bytes)) != hipSuccess)
         return hip_fail(e, "hipMalloc workspace");
     if ((e = launch_slot_tokens(q->g, q->stok, q->Nslot_pad, nullptr)) != hipSuccess) return hip_fail(e, "slot table");
     if (q->core_mode == 1) {

@@ -105,7 +105,7 @@ struct dq_qact {
     float* bias = nullptr;     // [K_pad][Cop]       per-cube core term Q8(core) Q4(R)
     int* stok = nullptr;       // [Nslot_pad]        token of each slot, -1 for pad slots
     uint8_t* zero = nullptr;   // [512]              zero bytes (copy source of absent rows)
-    float* sink = nullptr;     // [256]              target of the GEMM's discarded 16-byte stores
+    float* sink = nullptr;     // [512]              target of the GEMM's discarded 16-byte stores
     float* coref = nullptr;    // [K][Kp]            fp32 cores (core_mode 1)
     float* part = nullptr;     // [K*nblk][Kp]       fp32 block partials (core_mode 1)
     size_t bytes = 0;

@@ -60,12 +60,12 @@ struct GemmArgs {
     const uint16_t* u;     // [Nslot_pad][rp]
     const uint16_t* l2t;   // [Cop][rp]
     int rp;
-    float* sink;        // 1 KB the token epilogue stores lanes without an output to (never read)
+    float* sink;        // 2 KB the token epilogue stores lanes without an output to (never read)
 };
 
 constexpr int EPI_STORE = 0;      // plain fp32 stores c[b row][a row]
 constexpr int EPI_TOKENS = 1;     // low-rank branch + core term, rows scattered to token order
-constexpr int EPI_TOKENS_Q = 2;   // the same for cubes of a multiple of 4 slots, rank 32, 16-byte y rows
+constexpr int EPI_TOKENS_Q = 2;   // the same for cubes of a multiple of 4 slots, rank 32, Co a multiple of 256
 
 // Direct global -> LDS copies (global_load_lds, saddr form): lane i copies
 // 16 (or 4) bytes from base + voff_i to LDS address m0 + 16 i (or 4 i), with
@@ -99,11 +99,14 @@ __device__ __forceinline__ T ld_off(const void* base, uint32_t off) {
     return *(const T*)((const char*)base + off);
 }
 
-// value of lane J of each group of four lanes (DPP quad_perm broadcast)
+// value of lane J of each group of four lanes (DPP quad_perm broadcast).
+// quad_perm never reads outside the quad, so the fill value (0, with
+// bound_ctrl) is never used; being the identity of an add, it lets the
+// compiler fold the broadcast into the add that consumes it (v_add_f32_dpp).
 template <int J>
 __device__ __forceinline__ float4 quad_bcast(float4 v) {
     auto b = [](float f) {   // quad_perm [J, J, J, J]
-        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, f), 0x55 * J, 0xF, 0xF, false));
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, f), 0x55 * J, 0xF, 0xF, true));
     };
     return make_float4(b(v.x), b(v.y), b(v.z), b(v.w));
 }
@@ -168,7 +171,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     constexpr int APC = A_STEP / 1024 / 4;                    // 1 KB copies per wave: A
     constexpr int BPC = B_STEP / 1024 / 4;                    //                       B
     constexpr int DMAS = APC + BPC + 2;                       // copies per wave per stage
-    static_assert((NS - 3) * DMAS < 63, "vmcnt range");
+    static_assert((NS - 2) * DMAS < 63, "vmcnt range");
+    // With four stages a stage's copies go out in two halves: H1 of them in
+    // phase 2 of one step, the rest in phase 1 of the next, so the copy
+    // stream (and the wait to issue it) is spread over the whole step.
+    constexpr bool SPLIT = NS >= 4;
+    constexpr int H1 = SPLIT ? DMAS / 2 : DMAS;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
     const int tid = threadIdx.x;
@@ -451,7 +459,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             // y[token] = acc + core term of the token's cube, through the
             // transposition buffers.  The broadcasts run in every lane (a pad
             // slot's lane still serves its quad); a row is stored if its slot
-            // holds a token.
+            // holds a token.  (Co is a multiple of 256 here: every channel of
+            // the tile exists.)
+            const int chq = m0 + wr * 128 + 4 * (lane & 7);   // this lane's channels after the transposition (+ 32 mi)
+            float* rowp[4];
 #pragma unroll
             for (int b = 0; b < 17; ++b) {
                 if (b < 16) {                               // block b: mi = b % 4, ni = b / 4
@@ -469,23 +480,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                     tput(b & 1, o);
                 }
                 if (b > 0) {
-                    // rows 8 i + lane / 8 of block b - 1; every lane stores (a
-                    // lane whose row has no token, or whose channels lie past
-                    // Co, stores to the sink), so no branch splits the LDS
-                    // reads and their waits.
+                    // rows 8 i + lane / 8 of block b - 1.  A row's destination
+                    // (its token's y row, or the sink for a slot without a
+                    // token) is the same for the four blocks of one ni: found
+                    // once, at mi = 0, and offset by 32 mi channels (the
+                    // stores' immediate offsets).  Every lane stores, so no
+                    // branch splits the LDS reads and their waits.
                     const int pb = b - 1, mi = pb & 3, ni = pb >> 2;
-                    const int ch = m0 + wr * 128 + 32 * mi + 4 * (lane & 7);
-                    int t[4];
-                    float4 v[4];
+                    if (mi == 0) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        t[i] = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) * 4, tok[ni]);   // token of row rr (lane rr)
-                        v[i] = tget(pb & 1, i);
+                        for (int i = 0; i < 4; ++i) {
+                            const int t = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) * 4, tok[ni]);   // token of row rr (lane rr)
+                            float* yrow = p.y + (uint32_t)(t * p.Co + chq);
+                            rowp[i] = t >= 0 ? yrow : p.sink + 4 * lane;
+                        }
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float* dst = (t[i] >= 0 && ch < p.Co) ? p.y + (uint32_t)(t[i] * p.Co + ch) : p.sink + 4 * lane;
-                        __builtin_nontemporal_store(__builtin_bit_cast(v4f, v[i]), (v4f*)dst);   // y is not read back
+                        const float4 v = tget(pb & 1, i);
+                        __builtin_nontemporal_store(__builtin_bit_cast(v4f, v), (v4f*)(rowp[i] + 32 * mi));   // y is not read back
                     }
                 }
             }
@@ -561,23 +574,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // read half 0 of the next tile's first stage.
     // Fragments are read one phase before their MFMAs, so LDS latency hides
     // behind 16 MFMAs.
+    // Prologue: stages 0 .. NS - 2 (the last of them only its first half
+    // when split; the cursor then stays on it).
     for (int s = 0; s < NS - 1; ++s) {
+        const bool half = SPLIT && s == NS - 2;
 #pragma unroll
-        for (int j = 0; j < DMAS; ++j) dma(src, s, j);
-        advance();
+        for (int j = 0; j < DMAS; ++j)
+            if (!half || j < H1) dma(src, s, j);
+        if (!half) advance();
     }
-    wait_vm<(NS - 2) * DMAS>();                                // stage 0 landed
+    wait_vm<(NS - 2) * DMAS - (DMAS - H1)>();                  // stage 0 landed
     __syncthreads();
     Half F0, F1;
 #pragma unroll
     for (int i = 0; i < NRD; ++i) rd(0, 0, F0, i);
     // Stage gs + 1 must have landed before the barrier of step gs.  Copies go
     // out every step (past the end too), so normally NS - 3 later stages may
-    // still be in flight.  In a tile's first NS - 2 steps (after the first
-    // tile) stage gs + 1 was issued before the previous tile's epilogue, whose
-    // full wait already covered it; a loose count there lets the epilogue's
-    // stores stay in flight.  Half 0 of stage gs + 1 is read in every step,
-    // at a tile's last step too (it is the next tile's first stage).
+    // still be in flight (split: the copies issued after stage gs + 1's last
+    // half are the two halves of stage gs + 2, the same count).  In a tile's
+    // first NS - 2 steps (split: NS - 3) after the first tile, stage gs + 1
+    // was issued in full before the previous tile's epilogue, whose full wait
+    // already covered it; a loose count there lets the epilogue's stores stay
+    // in flight.  Half 0 of stage gs + 1 is read in every step, at a tile's
+    // last step too (it is the next tile's first stage).
     int gs = 0;
     for (int it = 0; it < ntiles; ++it) {
         prepare_next(it);
@@ -587,17 +606,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
         for (int ks = 0; ks < nk; ++ks, ++gs) {
             const int cur = (unsigned)gs % NS, nxt = (unsigned)(gs + 1) % NS, fill = (unsigned)(gs + NS - 1) % NS;
+            const int fillp = (unsigned)(gs + NS - 2) % NS;   // the cursor's stage in phase 1 (its second half)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 mma(F0, 0, i);
                 if (i < NRD) rd(cur, 1, F1, i);
+                if (SPLIT && i < DMAS - H1) dma(src, fillp, H1 + i);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if constexpr (SPLIT) advance();
             // Wait and barrier in one asm block (no branch for the compiler to
             // move code across).  Every wave's reads of stage gs - 1 completed
             // before its MFMAs of step gs - 1, so a bare barrier suffices; the
             // memory clobber keeps the LDS reads below it.
-            const int loose = __builtin_amdgcn_readfirstlane((it > 0 && ks < NS - 2) ? 1 : 0);
+            const int loose = __builtin_amdgcn_readfirstlane((it > 0 && ks < NS - 2 - (SPLIT ? 1 : 0)) ? 1 : 0);
             asm volatile(
                 "s_cmp_eq_u32 %0, 0\n\t"
                 "s_cbranch_scc1 1f\n\t"
@@ -611,11 +633,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 mma(F1, 1, i);
-                if (i < DMAS) dma(src, fill, i);
+                if (i < H1) dma(src, fill, i);
                 if (i < NRD) rd(nxt, 0, F0, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            advance();
+            if constexpr (!SPLIT) advance();
         }
         if (EPI != EPI_TOKENS_Q) wait_vm<0>();   // that epilogue waits after issuing its loads
         int tm, tn;
@@ -685,7 +707,7 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
         d.ldbias = w->Cop;
         // (32-bit element offsets into y and into the per-cube term)
         const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
-        if (d.S % 4 == 0 && d.rp == 32 && d.vec4 && off32) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
+        if (d.S % 4 == 0 && d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
         return launch<FMT_FP4, EPI_TOKENS>(d, st);
     }
     return hipSuccess;
