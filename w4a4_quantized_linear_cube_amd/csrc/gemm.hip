@@ -177,6 +177,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // stream (and the wait to issue it) is spread over the whole step.
     constexpr bool SPLIT = NS >= 4;
     constexpr int H1 = SPLIT ? DMAS / 2 : DMAS;
+    // Split copies sit after every third MFMA of a phase (phase 1 from MFMA
+    // 0, phase 2 from MFMA 2), which measured faster than issuing them after
+    // consecutive MFMAs; unsplit, copy j follows MFMA j.
+    static_assert(!SPLIT || (3 * (DMAS - H1 - 1) < 16 && 2 + 3 * (H1 - 1) < 16), "copy slots");
+    auto p1_copy = [](int i) { return SPLIT && i % 3 == 0 && i / 3 < DMAS - H1 ? H1 + i / 3 : -1; };
+    auto p2_copy = [](int i) { return SPLIT ? (i >= 2 && (i - 2) % 3 == 0 && (i - 2) / 3 < H1 ? (i - 2) / 3 : -1) : (i < H1 ? i : -1); };
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
     const int tid = threadIdx.x;
@@ -611,7 +617,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             for (int i = 0; i < 16; ++i) {
                 mma(F0, 0, i);
                 if (i < NRD) rd(cur, 1, F1, i);
-                if (SPLIT && i < DMAS - H1) dma(src, fillp, H1 + i);
+                if (p1_copy(i) >= 0) dma(src, fillp, p1_copy(i));
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (SPLIT) advance();
@@ -633,7 +639,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 mma(F1, 1, i);
-                if (i < H1) dma(src, fill, i);
+                if (p2_copy(i) >= 0) dma(src, fill, p2_copy(i));
                 if (i < NRD) rd(nxt, 0, F0, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
