@@ -368,6 +368,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // epilogue's first barrier and no copy fills before the next tile's first
     // barrier.
     int tstage = 0;                                       // stage of the tile's last K step
+
+    // ---- core-term rows of the token epilogue.  A cube spans a multiple of
+    // 4 slots and tiles start at multiples of 256, so the four lanes of a quad
+    // hold slots of one cube; lane u of the quad loads the quarter of the
+    // cube's row that is piece (mi, u) of every lane's 16 pieces, and the
+    // epilogue exchanges the quarters by DPP broadcasts.  They are loaded
+    // CORE_AHEAD steps before the tile's K loop ends (at its start if K is
+    // shorter): issued ahead of the last steps' copies, they have landed when
+    // the epilogue starts instead of queueing behind those copies.
+    // (32-bit byte offsets from the uniform base: one address register per
+    // row, the rest in the instructions' offset fields; each element is read
+    // once, so the loads allocate no cache lines.)
+    constexpr int CORE_AHEAD = 6;
+    float4 bq[4][4];
+    auto load_core = [&](int tm, int tn) {
+        const uint32_t chq0 = (uint32_t)(tm * 256 + wr * 128 + 4 * g + 8 * (l32 & 3));
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int k = min((tn * 256 + wc * 128 + 32 * ni + l32) / p.S, p.kmax);   // pad slots: any valid row, never stored
+            const uint32_t bo = ((uint32_t)k * (uint32_t)p.ldbias + chq0) * 4;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                bq[ni][mi] = __builtin_bit_cast(float4, __builtin_nontemporal_load((const v4f*)((const char*)p.bias + bo + 128 * mi)));
+        }
+    };
     auto tbuf = [&](int b) { return smem + tstage * STAGE + wv * 8192 + b * 4096; };
     auto tput = [&](int b, const float4* o) {           // piece j of this lane's row l32 is channels 8 j + 4 g ..
         uint8_t* t = tbuf(b) + l32 * 128;
@@ -411,29 +436,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         if constexpr (EPI == EPI_TOKENS_Q) {
             // Every global load is issued before the first wait, so their
             // latencies (and that of the copies still in flight) overlap: the
-            // slot -> token map, the core-term rows, the low-rank operands.
-            // Core term: a cube spans a multiple of 4 slots and tiles start at
-            // multiples of 256, so the four lanes of a quad hold slots of one
-            // cube; lane u of the quad loads the quarter of the cube's row
-            // that is piece (mi, u) of every lane's 16 pieces, and the quad
-            // exchanges the quarters by DPP broadcasts.
+            // slot -> token map and the low-rank operands (the core-term rows,
+            // bq, were loaded during the K loop).
             // (32-bit byte offsets from the uniform bases: one address register
             // per row, the rest in the instructions' offset fields)
             int tok[4];
-            float4 bq[4][4];
             v8bf la[2][4], ub[2][4];
-            const int u4 = l32 & 3;
-            auto load_core = [&](int ni) {
-                const int k = min((n0 + wc * 128 + 32 * ni + l32) / p.S, p.kmax);   // pad slots: any valid row, never stored
-                const uint32_t bo = ((uint32_t)k * (uint32_t)p.ldbias + (uint32_t)(ch0 + 8 * u4)) * 4;
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)   // each element is read once: no cache allocation
-                    bq[ni][mi] = __builtin_bit_cast(float4, __builtin_nontemporal_load((const v4f*)((const char*)p.bias + bo + 128 * mi)));
-            };
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) tok[ni] = ld_off<int>(p.stok, (uint32_t)(n0 + wc * 128 + 32 * ni + l32) * 4);
-            load_core(0);                                   // rows of ni 2, 3 after the low-rank MFMAs
-            load_core(1);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 const uint32_t lo = ((uint32_t)(m0 + wr * 128 + l32 + 32 * mi) * 32 + 8 * g) * 2;
@@ -459,8 +469,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[h][mi], ub[h][ni], acc[mi][ni], 0, 0, 0);
-            load_core(2);
-            load_core(3);
             __builtin_amdgcn_sched_barrier(0);
             // y[token] = acc + core term of the token's cube, through the
             // transposition buffers.  The broadcasts run in every lane (a pad
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
-        for (int ks = 0; ks < nk; ++ks, ++gs) {
+        auto kstep = [&](int ks) __attribute__((always_inline)) {
             const int cur = (unsigned)gs % NS, nxt = (unsigned)(gs + 1) % NS, fill = (unsigned)(gs + NS - 1) % NS;
             const int fillp = (unsigned)(gs + NS - 2) % NS;   // the cursor's stage in phase 1 (its second half)
 #pragma unroll
@@ -644,7 +652,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (!SPLIT) advance();
+        };
+        int ks = 0;
+        if constexpr (EPI == EPI_TOKENS_Q) {
+            for (; ks < nk - CORE_AHEAD; ++ks, ++gs) kstep(ks);
+            int tm, tn;
+            walk.coords(it, &tm, &tn);
+            load_core(tm, tn);
         }
+        for (; ks < nk; ++ks, ++gs) kstep(ks);
         if (EPI != EPI_TOKENS_Q) wait_vm<0>();   // that epilogue waits after issuing its loads
         int tm, tn;
         walk.coords(it, &tm, &tn);
