@@ -175,6 +175,32 @@ __device__ __forceinline__ float quad_max(float v) {
     return v;
 }
 
+// maximum over a row of 16 lanes (quad exchanges, then the half-row and row
+// mirrors: lane i meets lane 7 - i, then lane 15 - i)
+__device__ __forceinline__ float row16_max(float v) {
+    v = quad_max(v);
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+// channels ch, ch + 1 (ch even, chunk-relative) of row r as raw bits, and
+// as fp32 OR-ed with sgn (see qconv8: pad rows read as -0.0)
+template <typename XT>
+__device__ __forceinline__ uint2 qraw2(const uint8_t* buf, int r, int ch) {
+    constexpr int EPC = 16 / (int)sizeof(XT);
+    const uint8_t* pc = buf + qoff(r, ch / EPC) + (ch % EPC) * (int)sizeof(XT);
+    if constexpr (sizeof(XT) == 2) return make_uint2(*(const uint32_t*)pc, 0u);
+    else return *(const uint2*)pc;
+}
+template <typename XT>
+__device__ __forceinline__ float2 qconv2(uint2 d, uint32_t sgn) {
+    if constexpr (sizeof(XT) == 2)
+        return make_float2(__uint_as_float((d.x << 16) | sgn), __uint_as_float((d.x & 0xffff0000u) | sgn));
+    else
+        return make_float2(__uint_as_float(d.x | sgn), __uint_as_float(d.y | sgn));
+}
+
 // Persistent activation pass.  Workgroup w takes the 64-slot blocks w, w + G,
 // w + 2G, ... and walks each block's channels in chunks of 256 bytes per row;
 // the chunks of all its blocks form one stream.  Waves 1-2 copy chunks
@@ -188,6 +214,16 @@ __device__ __forceinline__ float quad_max(float v) {
 // quarters sharing its maxima by DPP: the cube's core (fp32 sum in slot
 // order, then the division), its FP8 codes, each row's delta FP4 codes.
 // X is read from HBM exactly once.
+//
+// CM selects how a chunk's quantizer work is split:
+//   0: one pass; each (cube, group, quarter) thread also codes the cube's
+//      rows (blocks of 16 or more cubes: every thread has a cube);
+//   2: two phases for blocks of at most 8 cubes (cubes of 8 to 64 tokens):
+//      the (cube, group, quarter) threads write the fp32 core to LDS, a
+//      second barrier per period follows, and then every thread of the
+//      group codes (row, group, quarter) deltas;
+//   1: the same two phases with the cores of cubes of more than 64 tokens
+//      read from a pass before this one.
 template <typename XT, int NCT, int CM>
 __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantArgs a) {
     constexpr int CC = XTraits<XT>::CC;
@@ -209,6 +245,10 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     __shared__ __attribute__((aligned(1024))) uint8_t xbuf[QNBUF * STAGE];
     __shared__ int tok_s[2][2][QROWS];              // [group][buffer]
     __shared__ int4 meta_s[2][2][QROWS];            // per cube: first row, end row, present rows (bit j: row first + j), tokens
+    constexpr bool TWO = CM != 0;                    // two phases, two barriers per period
+    constexpr int TCUBES = 8;                        // cubes per block in the two-phase forms
+    __shared__ float core_s[TWO ? SP : 1][TWO ? TCUBES : 1][TWO ? CC : 1];   // fp32 cores of the group's chunk
+    __shared__ uint64_t pres_s[2][2];               // [group][buffer]: bit r = row r holds a token
 
     const Geom& g = a.g;
     const int tid = threadIdx.x;
@@ -230,11 +270,16 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
         int* const tok_s_ = tok_s[qgrp][mb];
         int4* const meta_s_ = meta_s[qgrp][mb];
         if (qtid < QROWS) {
+            // (the group's first wave: one row per lane; the ballot gives
+            // every row's presence, so no cube walks its rows in memory)
+            const int tk = qtid < B.nrows ? a.stok[B.slot0 + qtid] : -1;
+            tok_s_[qtid] = tk;
+            const uint64_t pres = __ballot(tk >= 0);
+            if (qtid == 0) pres_s[qgrp][mb] = pres;
             const int rb = qtid < B.ncores ? (int)max(0LL, (B.k_first + qtid) * g.S - B.slot0) : 0;
             const int re = qtid < B.ncores ? (int)min((long long)B.nrows, (B.k_first + qtid + 1) * g.S - B.slot0) : 0;
-            int pm = 0;
-            for (int j = 0; j < 32 && rb + j < re; ++j) pm |= (a.stok[B.slot0 + rb + j] >= 0 ? 1 : 0) << j;
-            tok_s_[qtid] = qtid < B.nrows ? a.stok[B.slot0 + qtid] : -1;
+            const int n = re - rb;                             // rows of the cube in this block
+            const int pm = n <= 0 ? 0 : (int)(uint32_t)((pres >> rb) & (n >= 32 ? 0xffffffffull : ((1ull << n) - 1)));
             int ct, ch, cw;
             const int cnt = qtid < B.ncores ? cube_count(g, B.k_first + qtid, &ct, &ch, &cw) : 0;
             meta_s_[qtid] = make_int4(rb, re, pm, cnt);
@@ -326,6 +371,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             barrier();
 #pragma unroll
             for (int k = 0; k < SP; ++k) issue();
+            if constexpr (TWO) barrier();
         }
         // the surplus copies land before the wave ends (no copy may write
         // LDS after the workgroup has released it)
@@ -344,7 +390,10 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     };
     if (wave == 0) {
         for (long long s = 0; s < total; ++s, next_chunk()) {
-            if (s % SP == 0) barrier();
+            if (s % SP == 0) {
+                barrier();
+                if constexpr (TWO) barrier();
+            }
             if constexpr (NCT == 0) continue;
             const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
             // ---- U += bf16(X chunk) L1 chunk, both operands from the stage
@@ -401,6 +450,156 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     for (int k = 0; k < qgrp; ++k) next_chunk();
     int mb = 0;                                      // the group's metadata buffer of its current block
     if (qgrp < total) fill_meta(0, i);
+    if constexpr (TWO) {
+        const long long nks = a.Kp / 128;
+        for (long long u = 0; u < nsteps; ++u) {
+            barrier();
+            const long long s = SP * u + qgrp;
+            const bool have = s < total;
+            const int c0 = c * CC;
+            const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
+            float(*const cs_)[CC] = core_s[qgrp];
+            // ---- phase 1: the cores.  CM 2: one (cube, channel pair) per
+            // thread, 16 lanes per 32-channel group; CM 1: one (cube, group,
+            // quarter) per thread copies the precomputed core.
+            if constexpr (CM == 2) {
+                const int ntask = B.ncores * (CC / 2);     // a multiple of 16: groups stay whole
+                const uint64_t pres = pres_s[qgrp][mb];
+                for (int t = qtid; have && t < ntask; t += 256) {
+                    const int cr = t / (CC / 2), ch = 2 * (t - cr * (CC / 2));
+                    if (c0 + ch >= a.Ci) continue;             // the same for the group's 16 lanes
+                    const long long k = B.k_first + cr;
+                    const int rb = cr * g.S, re = rb + g.S, cnt = meta_s[qgrp][mb][cr].w;
+                    // fp32 sum of the present rows in slot order (pad rows read as
+                    // -0.0 and drop out exactly); sixteen rows' loads in flight
+                    float s0 = -0.0f, s1 = -0.0f;
+                    int r = rb;
+                    for (; r + 16 <= re; r += 16) {
+                        uint2 raw[16];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) raw[j] = qraw2<XT>(buf, r + j, ch);
+                        __builtin_amdgcn_sched_barrier(0);     // all sixteen reads issued before the first use
+                        const uint32_t absent = ~(uint32_t)(pres >> r);   // bit j: row r + j has no token
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const float2 v = qconv2<XT>(raw[j], (absent << (31 - j)) & 0x80000000u);
+                            s0 += v.x;
+                            s1 += v.y;
+                        }
+                    }
+                    if (r + 8 <= re) {                     // cubes of 8 to 15 rows (or the rest of one)
+                        uint2 raw[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) raw[j] = qraw2<XT>(buf, r + j, ch);
+                        __builtin_amdgcn_sched_barrier(0);
+                        const uint32_t absent = ~(uint32_t)(pres >> r);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float2 v = qconv2<XT>(raw[j], (absent << (31 - j)) & 0x80000000u);
+                            s0 += v.x;
+                            s1 += v.y;
+                        }
+                        r += 8;
+                    }
+                    for (; r < re; ++r) {
+                        const float2 v = qconv2<XT>(qraw2<XT>(buf, r, ch), ((pres >> r) & 1) ? 0u : 0x80000000u);
+                        s0 += v.x;
+                        s1 += v.y;
+                    }
+                    if ((cnt & (cnt - 1)) == 0) {                  // exact power-of-two scaling
+                        const float rc = 1.0f / (float)cnt;
+                        s0 *= rc;
+                        s1 *= rc;
+                    } else {
+                        s0 = __fdiv_rn(s0, (float)cnt);
+                        s1 = __fdiv_rn(s1, (float)cnt);
+                    }
+                    const float amax = row16_max(fmaxf(fabsf(s0), fabsf(s1)));
+                    const int ex = mx_exp_fp8(amax);
+                    v2s z = {0, 0};
+                    const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false);
+                    const int gch = c0 + ch;                       // channel within the row
+                    *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) =
+                        (uint16_t)__builtin_bit_cast(uint32_t, cd);
+                    if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
+                    *(float2*)&cs_[cr][ch] = make_float2(s0, s1);
+                }
+            } else {
+                const int ntask = B.ncores * NGC * 4;
+                if (have && qtid < ntask) {
+                    const int qq = qtid & 3, pr = qtid >> 2;
+                    const int cr = pr / NGC, gc = pr - cr * NGC;
+                    const long long G = (c0 >> 5) + gc;
+                    if (G * 32 < a.Ci) {
+                        const long long k = B.k_first + cr;
+                        const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32 + 8 * qq);
+                        *(float4*)&cs_[cr][gc * 32 + qq * 8] = cp[0];
+                        *(float4*)&cs_[cr][gc * 32 + qq * 8 + 4] = cp[1];
+                    }
+                }
+            }
+            barrier();                                         // the group's cores are in LDS
+            // ---- phase 2: the deltas, one (row, group, quarter) per thread
+            if (have) {
+                const uint64_t pres = pres_s[qgrp][mb];
+                // every task computed first in straight-line code (absent rows
+                // and channels read zeros from the stage and index a written or
+                // stale core row in bounds), then the stores, predicated, so the
+                // tasks' LDS reads and DPP maxima interleave and quads stay whole
+                constexpr int NT2 = QROWS * NGC * 4 / 256;
+                uint32_t code[NT2];
+                int exq[NT2];
+                bool live[NT2];
+#pragma unroll
+                for (int n = 0; n < NT2; ++n) {
+                    const int t = qtid + 256 * n;
+                    const int qq = t & 3, pr = t >> 2;
+                    const int r = pr / NGC, gc = pr - r * NGC;
+                    const long long G = (c0 >> 5) + gc;
+                    live[n] = G * 32 < a.Ci && ((pres >> r) & 1);   // (pres has no bit for rows past the block)
+                    const int cr = CM == 1 ? (int)((B.slot0 + r) / g.S - B.k_first) : r / g.S;
+                    float v[8];
+                    qload8<XT>(buf, r, gc, qq, 0u, v);
+                    const float4 k0 = *(const float4*)&cs_[cr][gc * 32 + qq * 8];
+                    const float4 k1 = *(const float4*)&cs_[cr][gc * 32 + qq * 8 + 4];
+                    const float core[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                    float dv[8];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        dv[e] = v[e] - core[e];
+                        amax = fmaxf(amax, fabsf(dv[e]));
+                    }
+                    amax = quad_max(amax);
+                    exq[n] = mx_exp_fp4(amax);
+                    const float sc = pow2f(exq[n]);
+                    uint32_t w = 0u;
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[0], dv[1], sc, 0);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[2], dv[3], sc, 1);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[4], dv[5], sc, 2);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[6], dv[7], sc, 3);
+                    code[n] = w;
+                }
+#pragma unroll
+                for (int n = 0; n < NT2; ++n) {
+                    if (!live[n]) continue;
+                    const int t = qtid + 256 * n;
+                    const int qq = t & 3, pr = t >> 2;
+                    const int r = pr / NGC, gc = pr - r * NGC;
+                    const long long G = (c0 >> 5) + gc, sl = B.slot0 + r;
+                    *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
+                    if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
+                }
+                const long long i_prev = i;
+#pragma unroll
+                for (int k = 0; k < SP; ++k) next_chunk();
+                if (i != i_prev && i < nmine) {
+                    mb ^= 1;
+                    fill_meta(mb, i);
+                }
+            }
+        }
+    } else {
     for (long long u = 0; u < nsteps; ++u) {
         barrier();
         const long long s = SP * u + qgrp;
@@ -425,8 +624,8 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             const long long G = (c0 >> 5) + gc;
             if (G * 32 >= a.Ci) return;                        // the same for the quad
             const int4 md = meta_s[qgrp][mb][cr];
-            const int rb = CM == 0 ? cr * g.S : md.x, re = CM == 0 ? rb + g.S : md.y, pm = md.z;   // CM 0: whole cubes
-            const int nr = CM == 0 ? g.S : re - rb;            // rows of the cube in this block
+            const int rb = CM != 1 ? cr * g.S : md.x, re = CM != 1 ? rb + g.S : md.y, pm = md.z;   // whole cubes unless CM 1
+            const int nr = CM != 1 ? g.S : re - rb;            // rows of the cube in this block
             const long long k = B.k_first + cr;
             float core[8], xr[QKEEP][8];                       // rows rb .. rb + QKEEP - 1 kept for the deltas
             QRaw<XT> raw[QKEEP];                               // all kept rows' LDS reads in flight together
@@ -570,6 +769,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             fill_meta(mb, i);
         }
     }
+    }
 }
 
 // ---- cubes of more than 64 tokens: fp32 partial sums of 64-token blocks
@@ -581,14 +781,18 @@ struct PartialArgs {
     float* part;   // [K*nblk][Kp]
 };
 
+// One workgroup per (cube, 64-token block) and 256 x EPT channels; each
+// thread sums EPT channels (one 16-byte load per token) over the block's
+// tokens in order, eight tokens' loads in flight.
 template <typename XT>
 __global__ __launch_bounds__(256) void k_core_partial(PartialArgs a) {
+    constexpr int EPT = 16 / (int)sizeof(XT);      // channels per thread
     const Geom& g = a.g;
     long long kb = blockIdx.x;
     long long k = kb / a.nblk;
     long long b = kb - k * a.nblk;
-    int c = blockIdx.y * 256 + threadIdx.x;
-    if (c >= a.Ci) return;
+    const int c = (blockIdx.y * 256 + threadIdx.x) * EPT;
+    if (c >= a.Ci) return;                         // Ci is a multiple of 32: all EPT channels or none
     int ct, ch, cw;
     int cnt = cube_count(g, k, &ct, &ch, &cw);
     long long j0 = b * CORE_BLOCK;
@@ -596,14 +800,51 @@ __global__ __launch_bounds__(256) void k_core_partial(PartialArgs a) {
     int j1 = (int)min((long long)cnt, j0 + CORE_BLOCK);
     long long kw = k % g.Wc, kh = (k / g.Wc) % g.Hc, kt = k / ((long long)g.Wc * g.Hc);
     const XT* x = (const XT*)a.x;
-    float s = 0.0f;
-    for (int j = (int)j0; j < j1; ++j) {   // j-th present token, lexicographic in the clipped cube
-        int dw = j % cw, dh = (j / cw) % ch, dt = j / (cw * ch);
-        long long n = ((kt * g.t + dt) * g.H + kh * g.h + dh) * g.W + kw * g.w + dw;
-        float v = XTraits<XT>::f(x[n * a.Ci + c]);
-        s = (j == j0) ? v : s + v;
+    // tokens j0 .. j1 - 1 of the cube (lexicographic in the clipped cube),
+    // summed in order per channel (the first one starts the sum)
+    int dw = (int)(j0 % cw), dh = (int)((j0 / cw) % ch), dt = (int)(j0 / (cw * ch));
+    const long long n0 = ((kt * g.t) * g.H + kh * g.h) * g.W + kw * g.w;   // token (0, 0, 0) of the cube
+    float s[EPT];
+    for (int j = (int)j0; j < j1; j += 8) {
+        uint4 raw[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (j + q < j1) {
+                const long long n = n0 + ((long long)dt * g.H + dh) * g.W + dw;
+                raw[q] = *(const uint4*)(x + n * a.Ci + c);
+                if (++dw == cw) {
+                    dw = 0;
+                    if (++dh == ch) {
+                        dh = 0;
+                        ++dt;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (j + q >= j1) continue;
+            float v[EPT];
+            if constexpr (sizeof(XT) == 2) {
+                const uint32_t d[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = __uint_as_float(d[e] << 16);
+                    v[2 * e + 1] = __uint_as_float(d[e] & 0xffff0000u);
+                }
+            } else {
+                v[0] = __uint_as_float(raw[q].x);
+                v[1] = __uint_as_float(raw[q].y);
+                v[2] = __uint_as_float(raw[q].z);
+                v[3] = __uint_as_float(raw[q].w);
+            }
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) s[e] = (j + q == j0) ? v[e] : s[e] + v[e];
+        }
     }
-    a.part[kb * a.Kp + c] = s;
+    float* out = a.part + kb * a.Kp + c;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) *(float4*)(out + e) = make_float4(s[e], s[e + 1], s[e + 2], s[e + 3]);
 }
 
 struct CombineArgs {
@@ -629,7 +870,14 @@ __global__ __launch_bounds__(256) void k_core_combine(CombineArgs a) {
     if (c < a.Ci) {
         const float* p = a.part + k * a.nblk * a.Kp + c;
         float s = p[0];
-        for (int b = 1; b < nb; ++b) s = s + p[(long long)b * a.Kp];
+        for (int b = 1; b < nb; b += 16) {               // in block order, sixteen loads in flight
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = b + q < nb ? p[(long long)(b + q) * a.Kp] : 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (b + q < nb) s = s + v[q];
+        }
         core = mean_div(s, cnt);
         a.coref[k * a.Kp + c] = core;
     }
@@ -720,7 +968,8 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
     const Geom& g = q->g;
     if (q->core_mode == 1) {
         PartialArgs pa{x, g, (int)q->Ci, (int)q->Kp, q->nblk, q->part};
-        dim3 grid((unsigned)(g.K * q->nblk), (unsigned)((q->Ci + 255) / 256));
+        const int ept = x_bf16 ? 8 : 4;                // channels per thread (16-byte loads)
+        dim3 grid((unsigned)(g.K * q->nblk), (unsigned)((q->Ci + 256 * ept - 1) / (256 * ept)));
         if (x_bf16) k_core_partial<uint16_t><<<grid, 256, 0, st>>>(pa);
         else k_core_partial<float><<<grid, 256, 0, st>>>(pa);
         hipError_t e = hipGetLastError();
@@ -754,11 +1003,16 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
         cus = 256;
     const unsigned blocks = (unsigned)std::min<long long>(a.nblocks, cus);   // persistent: one workgroup per CU
     const int nct = q->rp / 32;
+    // one-pass quantizer for blocks of 16 or more cubes (every thread of a
+    // group has a cube); two phases for blocks of at most 8 (cubes of 8 to 64
+    // tokens) and for cubes of more than 64 tokens
+    const int cm = a.core_mode == 1 ? 1 : (cpb <= 8 ? 2 : 0);
     auto go = [&](auto XT_, auto NCT_) {
         using XT = decltype(XT_);
         constexpr int THREADS = QCfg<XT, decltype(NCT_)::value>::THREADS;
-        if (a.core_mode == 0) k_quantize<XT, decltype(NCT_)::value, 0><<<blocks, THREADS, 0, st>>>(a);
-        else k_quantize<XT, decltype(NCT_)::value, 1><<<blocks, THREADS, 0, st>>>(a);
+        if (cm == 0) k_quantize<XT, decltype(NCT_)::value, 0><<<blocks, THREADS, 0, st>>>(a);
+        else if (cm == 1) k_quantize<XT, decltype(NCT_)::value, 1><<<blocks, THREADS, 0, st>>>(a);
+        else k_quantize<XT, decltype(NCT_)::value, 2><<<blocks, THREADS, 0, st>>>(a);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
