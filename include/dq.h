@@ -152,7 +152,10 @@ dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void*
  *   [N][Co] fp32 in token order (every element written).
  * Same arguments, errors and asynchrony as dq_linear_forward; calling
  * dq_delta_term without dq_core_term after a dq_quantize_act reads a stale
- * core term (not detected). */
+ * core term (not detected).
+ * Cubes of one token (t = h = w = 1): every delta is exactly zero, so
+ * dq_delta_term alone computes y = Q8(x_n) Q4(R) + U[n] L2 in one FP8 GEMM
+ * and dq_core_term does nothing. */
 dq_status dq_core_term(const dq_weights* w, dq_qact* q, void* stream);
 dq_status dq_delta_term(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
 

@@ -544,12 +544,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             const int slot = n0 + wc * 128 + 32 * ni + l32;
             const int tok = p.stok[slot];
             const int k = min(slot / p.S, p.kmax);          // pad slots: any valid row, never stored
-            const float* brow = p.bias + (long long)k * p.ldbias + ch0;
             float4 bv[4][4];
+            if (p.bias) {
+                const float* brow = p.bias + (long long)k * p.ldbias + ch0;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bv[mi][j] = *(const float4*)(brow + 32 * mi + 8 * j);
+                    for (int j = 0; j < 4; ++j) bv[mi][j] = *(const float4*)(brow + 32 * mi + 8 * j);
+            } else {                                        // no per-cube term
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bv[mi][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
             if (tok < 0) continue;
             float* yrow = p.y + (long long)tok * p.Co;
 #pragma unroll
@@ -656,9 +663,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         int ks = 0;
         if constexpr (EPI == EPI_TOKENS_Q) {
             for (; ks < nk - CORE_AHEAD; ++ks, ++gs) kstep(ks);
-            int tm, tn;
-            walk.coords(it, &tm, &tn);
-            load_core(tm, tn);
+            if (p.bias) {
+                int tm, tn;
+                walk.coords(it, &tm, &tn);
+                load_core(tm, tn);
+            } else {                                       // no per-cube term: add zeros
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bq[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
         for (; ks < nk; ++ks, ++gs) kstep(ks);
         if (EPI != EPI_TOKENS_Q) wait_vm<0>();   // that epilogue waits after issuing its loads
@@ -712,6 +726,21 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
     d.l2t = w->l2t;
     d.rp = w->rp;
     d.sink = q->sink;
+    // (32-bit element offsets into y and into the per-cube term)
+    const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
+    if (q->g.S == 1) {
+        // One-token cubes: every delta is x - x = 0 exactly, so y = Q8(x) Q4(R)
+        // + U L2, one FP8 GEMM over the cubes (cube k is slot k) with the token
+        // epilogue and no per-cube term.  It is the delta half's work; the
+        // core half has nothing to do.
+        if (!(parts & FWD_DELTA)) return hipSuccess;
+        d.b = q->cq;
+        d.bs = q->cs;
+        d.ntiles = (int)(q->K_pad / 256);
+        d.bias = nullptr;
+        if (d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0) return launch<FMT_FP8, EPI_TOKENS_Q>(d, st);
+        return launch<FMT_FP8, EPI_TOKENS>(d, st);
+    }
     if (parts & FWD_CORE) {
         // per-cube core term bias[k] = Q8(core_k) Q4(R)
         GemmArgs c = d;
@@ -727,8 +756,6 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
         // delta term + low-rank branch + the cube's core term -> y (token order)
         d.bias = q->bias;
         d.ldbias = w->Cop;
-        // (32-bit element offsets into y and into the per-cube term)
-        const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
         if (d.S % 4 == 0 && d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
         return launch<FMT_FP4, EPI_TOKENS>(d, st);
     }
