@@ -15,6 +15,10 @@ roofline = the dominant kernel, the delta GEMM (dq_delta_term: one launch of
          dense FP4 peak; traffic from the committed rocprofv3 counter summary
          of the same kernel source, else null.
 cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+
+--sweep instead prints one JSON line per cube shape of the config's list
+(e.g. --config ffn_down_720p --sweep: 1x1x1, 1x2x2, 2x2x2, 1x4x4 and one
+global cube) with the step time, effective TOPS and the three phases.
 """
 from __future__ import annotations
 
@@ -46,9 +50,93 @@ def parse():
     ap.add_argument("--x-seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the oracle's timed sample")
+    ap.add_argument("--sweep", action="store_true", help="one JSON line per cube shape of the config")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
+
+
+def time_steps(dq, weights, x, qa, y, stream, steps, warmup):
+    """Mean ms per step and per phase (activation pass, core term, delta
+    term) over `steps` timed steps, HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        dq.dq_linear(weights, x, qa, y, stream)
+    torch.cuda.synchronize()
+    start, end = ev(), ev()
+    start.record(stream)
+    marks = []
+    for _ in range(steps):
+        a, b, c, d = ev(), ev(), ev(), ev()
+        a.record(stream)
+        dq.dq_quantize_act(weights, x, qa, stream)
+        b.record(stream)
+        dq.dq_core_term(weights, qa, stream)
+        c.record(stream)
+        dq.dq_delta_term(weights, qa, y, stream)
+        d.record(stream)
+        marks.append((a, b, c, d))
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    q_ms = float(np.mean([a.elapsed_time(b) for a, b, c, d in marks]))
+    c_ms = float(np.mean([b.elapsed_time(c) for a, b, c, d in marks]))
+    d_ms = float(np.mean([c.elapsed_time(d) for a, b, c, d in marks]))
+    return ms_step, q_ms, c_ms, d_ms
+
+
+def work(cfg, cube):
+    """Sizes of the method's work for a cube shape: cubes, slots, flops of
+    each GEMM, the activation pass's algorithmic bytes."""
+    t_, h_, w_ = cube
+    Tc, Hc, Wc = -(-cfg.T // t_), -(-cfg.H // h_), -(-cfg.W // w_)
+    K = Tc * Hc * Wc
+    S = t_ * h_ * w_
+    N, Ci, Co, r = cfg.N, cfg.Ci, cfg.Co, cfg.rank
+    xbytes = 2 if cfg.dtype == "bf16" else 4
+    return {
+        "K": K, "S": S, "Nslot": K * S,
+        "dense": 2.0 * N * Ci * Co,
+        "fp4": 2.0 * K * S * Ci * Co,        # delta term, one row per slot (pad slots of partial cubes included)
+        "fp8": 2.0 * K * Ci * Co,            # core term, one row per cube
+        "bf16": 2.0 * N * r * (Ci + Co),     # low-rank branch
+        "quant_bytes": N * Ci * xbytes * (2 if S > 64 else 1) + N * Ci * (0.5 + 1 / 32) + K * Ci * (1 + 1 / 32) + 2 * N * r,
+    }
+
+
+def sweep(args, cfg, dq, torch):
+    """One JSON line per cube shape of the config (same weights, same X)."""
+    wt = synth_mod().config_weight(cfg)
+    weights = dq.dq_prepare_weights(wt, cfg.rank, seed=cfg.w_seed, device=0)
+    x = synth_mod().make_activation(cfg.T, cfg.H, cfg.W, cfg.Ci, seed=cfg.x_seeds[0], dtype=cfg.dtype,
+                                    n_outliers=cfg.n_outliers, device="cuda")
+    y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for cube in cfg.cubes:
+        qa = dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + tuple(cube))
+        ms, q_ms, c_ms, d_ms = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
+        wk = work(cfg, cube)
+        one = wk["S"] == 1          # one-token cubes: the delta term is one FP8 GEMM over the cubes
+        rec = {
+            "config": cfg.name, "cube": list(cube), "cubes": wk["K"], "slots": wk["Nslot"],
+            "ms_per_step": round(ms, 4), "effective_tops": round(wk["dense"] / (ms * 1e-3) / 1e12, 2),
+            "quantize": {"ms": round(q_ms, 4), "GBps": round(wk["quant_bytes"] / (q_ms * 1e-3) / 1e9, 1)},
+            "core_term": {"ms": round(c_ms, 4)} if one else
+                         {"ms": round(c_ms, 4), "fp8_tflops": round(wk["fp8"] / (c_ms * 1e-3) / 1e12, 1)},
+            "delta_term": {"ms": round(d_ms, 4), "fp8_tflops": round(wk["fp8"] / (d_ms * 1e-3) / 1e12, 1)} if one else
+                          {"ms": round(d_ms, 4), "fp4_tflops": round(wk["fp4"] / (d_ms * 1e-3) / 1e12, 1)},
+        }
+        print(json.dumps(rec), flush=True)
+        torch.cuda.synchronize()
+        del qa                      # frees the cube shape's buffers
+
+
+def synth_mod():
+    from w4a4_quantized_linear_cube_amd import synth
+    return synth
 
 
 def main():
@@ -78,6 +166,9 @@ def main():
         __graft_entry__.build()
     dq.load()
     cfg = synth.CONFIGS[args.config]
+    if args.sweep:
+        sweep(args, cfg, dq, torch)
+        return
     cube = tuple(int(v) for v in args.cube.split(",")) if args.cube else cfg.cubes[0]
     xseed = cfg.x_seeds[0] if args.x_seed is None else args.x_seed
     T, H, W, Ci, Co, r = cfg.T, cfg.H, cfg.W, cfg.Ci, cfg.Co, cfg.rank
@@ -95,52 +186,15 @@ def main():
 
     # derived sizes of the method's work
     t_, h_, w_ = cube
-    Tc, Hc, Wc = -(-T // t_), -(-H // h_), -(-W // w_)
-    K = Tc * Hc * Wc
-    S = t_ * h_ * w_
-    dense_flops = 2.0 * N * Ci * Co
-    Nslot = K * S
-    f_fp4 = 2.0 * Nslot * Ci * Co        # delta term, one row per slot (pad slots of partial cubes included)
-    f_fp8 = 2.0 * K * Ci * Co            # core term, one row per cube
-    f_bf16 = 2.0 * N * r * (Ci + Co)     # low-rank branch
-    xbytes = 2 if cfg.dtype == "bf16" else 4
-    quant_bytes = N * Ci * xbytes * (2 if S > 64 else 1) + N * Ci * (0.5 + 1 / 32) + K * Ci * (1 + 1 / 32) + 2 * N * r
-
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    for _ in range(args.warmup):
-        dq.dq_linear(weights, x, qa, y, stream)
-    torch.cuda.synchronize()
+    wk = work(cfg, cube)
+    K, S = wk["K"], wk["S"]
+    dense_flops, f_fp4, f_fp8, f_bf16, quant_bytes = wk["dense"], wk["fp4"], wk["fp8"], wk["bf16"], wk["quant_bytes"]
 
     # timed steps (activation pass, core term, delta term: dq_linear's work);
     # per-phase events on the launch stream
-    t_quant, t_core, t_delta = [], [], []
-    start = ev()
-    torch.cuda.synchronize()
-    start.record(stream)
-    marks = []
-    for _ in range(args.steps):
-        a, b, c, d = ev(), ev(), ev(), ev()
-        a.record(stream)
-        dq.dq_quantize_act(weights, x, qa, stream)
-        b.record(stream)
-        dq.dq_core_term(weights, qa, stream)
-        c.record(stream)
-        dq.dq_delta_term(weights, qa, y, stream)
-        d.record(stream)
-        marks.append((a, b, c, d))
-    end = ev()
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    for a, b, c, d in marks:
-        t_quant.append(a.elapsed_time(b))
-        t_core.append(b.elapsed_time(c))
-        t_delta.append(c.elapsed_time(d))
-    ms_step = total_ms / args.steps
-    q_ms = float(np.mean(t_quant))
-    c_ms = float(np.mean(t_core))
-    d_ms = float(np.mean(t_delta))
+    ms_step, q_ms, c_ms, d_ms = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
     f_ms = c_ms + d_ms
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
     # device-to-device copy rate (the practical ceiling of the activation pass)
     cbytes = 1 << 30

@@ -293,7 +293,7 @@ def _oracle_weight(cfg):
     return _WEIGHT_CACHE[cfg.name]
 
 
-def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=512):
+def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=512, versus_direct=False):
     T, H, W = cfg.T, cfg.H, cfg.W
     g = cubes.Geometry(T, H, W, *cube)
     _say(f"case {cfg.name} cube {cube} seed {xseed}: generating")
@@ -333,6 +333,20 @@ def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=5
     err, row = _check_y(y.cpu().numpy()[q["tokens"]], yo, bound)
     _say(f"{cfg.name} cube {cube} seed {xseed}: codes bit-exact on {len(ids)} cubes; "
          f"Y rel err {err:.2e} worst row {row:.2e} on {len(q['tokens'])} tokens")
+    if versus_direct:
+        # output error against the exact X W (fp64) on 128 of the sampled
+        # tokens: delta W4A4 (the GPU output) and direct W4A4 of X (oracle:
+        # the same R, rank and MX rule, X quantized per token without a core)
+        t = q["tokens"][:128]
+        ex = layer.exact_output(xf[t], synth.to_f32_numpy(wt))
+        e_dq = layer.rel_fro(y.cpu().numpy()[t], ex)
+        e_dir = layer.rel_fro(layer.direct_output(xf[t], q["U"][:128], l2, rc, rs), ex)
+        _say(f"{cfg.name} cube {cube}: error vs exact X W on {len(t)} tokens: delta W4A4 {e_dq:.3e}, "
+             f"direct W4A4 {e_dir:.3e} (ratio {e_dq / e_dir:.3f})")
+        # the core removes shared content before the 4-bit step (关键设计 3):
+        # never worse than direct W4A4 beyond noise (a single global cube is
+        # the degenerate case, about equal)
+        assert e_dq <= 1.02 * e_dir, (e_dq, e_dir)
 
 
 def test_attn14b_projection_sampled(dqm):
@@ -349,4 +363,4 @@ def test_ffn_up_720p_sampled(dqm):
 @pytest.mark.parametrize("cube", synth.CONFIGS["ffn_down_720p"].cubes, ids=lambda c: "x".join(map(str, c)))
 def test_ffn_down_720p_sampled(dqm, cube):
     cfg = synth.CONFIGS["ffn_down_720p"]
-    _full_size_case(dqm, cfg, cube, cfg.x_seeds[0], check_weights=(cube == (1, 2, 2)), n_cubes=24)
+    _full_size_case(dqm, cfg, cube, cfg.x_seeds[0], check_weights=(cube == (1, 2, 2)), n_cubes=24, versus_direct=True)
