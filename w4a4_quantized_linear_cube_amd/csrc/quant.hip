@@ -465,7 +465,11 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             if constexpr (CM == 2) {
                 const int ntask = B.ncores * (CC / 2);     // a multiple of 16: groups stay whole
                 const uint64_t pres = pres_s[qgrp][mb];
-                for (int t = qtid; have && t < ntask; t += 256) {
+                // the second group's tasks start at its third wave, so the two
+                // groups' first tasks (all of them when a block has one cube)
+                // run on different SIMDs (waves go round-robin over the four)
+                const int tq = (qtid + 128 * qgrp) & 255;
+                for (int t = tq; have && t < ntask; t += 256) {
                     const int cr = t / (CC / 2), ch = 2 * (t - cr * (CC / 2));
                     if (c0 + ch >= a.Ci) continue;             // the same for the group's 16 lanes
                     const long long k = B.k_first + cr;
