@@ -180,6 +180,7 @@ EDGE = [
     (1, 1, 3, (1, 1, 2), 32, 8, 8, "f32"),         # three tokens
     (2, 16, 16, (1, 4, 4), 512, 256, 32, "bf16"),  # 16-token cubes, several tiles in every dim
     (3, 7, 10, (1, 2, 2), 512, 512, 32, "bf16"),   # 4-token cubes, clipped, pad slots, two channel tiles
+    (3, 6, 8, (1, 4, 4), 96, 64, 16, "f32"),        # fp32 input, one wave per 16-token cube (clipped), a partial chunk
     (21, 4, 6, (4, 1, 4), 64, 64, 16, "bf16"),     # the pages' small tile t4 h1 w4 on 21 frames
     (21, 4, 16, (4, 2, 8), 64, 64, 16, "bf16"),    # the pages' large tile t4 h2 w8
 ]

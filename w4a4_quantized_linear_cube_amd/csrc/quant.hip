@@ -217,13 +217,16 @@ __device__ __forceinline__ float2 qconv2(uint2 d, uint32_t sgn) {
 //
 // CM selects how a chunk's quantizer work is split:
 //   0: one pass; each (cube, group, quarter) thread also codes the cube's
-//      rows (blocks of 16 or more cubes: every thread has a cube);
-//   2: two phases for blocks of at most 8 cubes (cubes of 8 to 64 tokens):
+//      rows (blocks of 7 or more cubes);
+//   2: two phases for blocks of at most 3 cubes (cubes of 17 to 64 tokens):
 //      the (cube, group, quarter) threads write the fp32 core to LDS, a
 //      second barrier per period follows, and then every thread of the
 //      group codes (row, group, quarter) deltas;
 //   1: the same two phases with the cores of cubes of more than 64 tokens
-//      read from a pass before this one.
+//      read from a pass before this one;
+//   3: one pass with one wave per cube, for blocks of 4 to 6 cubes (cubes
+//      of 10 to 16 tokens): the core by channel pairs, then the cube's
+//      (row, group, quarter) deltas, both on the same wave.
 template <typename XT, int NCT, int CM>
 __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantArgs a) {
     constexpr int CC = XTraits<XT>::CC;
@@ -245,9 +248,10 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     __shared__ __attribute__((aligned(1024))) uint8_t xbuf[QNBUF * STAGE];
     __shared__ int tok_s[2][2][QROWS];              // [group][buffer]
     __shared__ int4 meta_s[2][2][QROWS];            // per cube: first row, end row, present rows (bit j: row first + j), tokens
-    constexpr bool TWO = CM != 0;                    // two phases, two barriers per period
+    constexpr bool TWO = CM == 1 || CM == 2;         // two phases, two barriers per period
     constexpr int TCUBES = 8;                        // cubes per block in the two-phase forms
-    __shared__ float core_s[TWO ? SP : 1][TWO ? TCUBES : 1][TWO ? CC : 1];   // fp32 cores of the group's chunk
+    constexpr bool CORES = CM != 0;                  // fp32 cores of the group's chunk in LDS
+    __shared__ float core_s[CORES ? SP : 1][CORES ? TCUBES : 1][CORES ? CC : 1];
     __shared__ uint64_t pres_s[2][2];               // [group][buffer]: bit r = row r holds a token
 
     const Geom& g = a.g;
@@ -759,9 +763,119 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 delta(r, v);
             }
         };
-        for (int t = qtid; t < ntask; t += 256) {
-            if (full) task(t, std::true_type{});
-            else task(t, std::false_type{});
+        if constexpr (CM == 3) {
+            // one wave per cube (4 to 8 cubes per block, 1 or 2 per wave):
+            // the wave's lanes take channel pairs for the cube's core, write
+            // it to LDS, and then take (row, group, quarter) delta tasks of
+            // the same cube; the core passes between lanes of one wave only
+            // (LDS operations of a wave complete in order), so no barrier
+            const int wq = qtid >> 6;                      // wave within the group
+            const uint64_t pres = pres_s[qgrp][mb];
+            float(*const cs_)[CC] = core_s[qgrp];
+            for (int cr = wq; cr < B.ncores; cr += 4) {    // wave-uniform
+                const long long k = B.k_first + cr;
+                const int rb = cr * g.S, S = g.S;
+                // core: channels ch, ch + 1 of the chunk, rows in slot order
+                // (pad rows add -0.0: exact), every row's read in flight
+                const int ch = 2 * lane;
+                float s0 = -0.0f, s1 = -0.0f;
+                int r = 0;
+                for (; r + 8 <= S; r += 8) {
+                    uint2 raw[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) raw[j] = qraw2<XT>(buf, rb + r + j, ch);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const uint32_t absent = ~(uint32_t)(pres >> (rb + r));
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float2 v = qconv2<XT>(raw[j], (absent << (31 - j)) & 0x80000000u);
+                        s0 += v.x;
+                        s1 += v.y;
+                    }
+                }
+                for (; r < S; ++r) {
+                    const float2 v = qconv2<XT>(qraw2<XT>(buf, rb + r, ch), ((pres >> (rb + r)) & 1) ? 0u : 0x80000000u);
+                    s0 += v.x;
+                    s1 += v.y;
+                }
+                const int cnt = meta_s[qgrp][mb][cr].w;
+                if ((cnt & (cnt - 1)) == 0) {              // exact power-of-two scaling
+                    const float rc = 1.0f / (float)cnt;
+                    s0 *= rc;
+                    s1 *= rc;
+                } else {
+                    s0 = __fdiv_rn(s0, (float)cnt);
+                    s1 = __fdiv_rn(s1, (float)cnt);
+                }
+                {
+                    const float amax = row16_max(fmaxf(fabsf(s0), fabsf(s1)));   // 16 lanes: one 32-channel group
+                    const int ex = mx_exp_fp8(amax);
+                    v2s z = {0, 0};
+                    const uint16_t cd = (uint16_t)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false));
+                    // (fp32 chunks have CC = 64 channels: lanes 32-63 store
+                    // nothing; the conditions hold for whole 16-lane groups)
+                    const int gch = c0 + ch;               // channel within the row
+                    if (ch < CC) {
+                        if (gch < a.Ci) {
+                            *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) = cd;
+                            if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
+                        }
+                        *(float2*)&cs_[cr][ch] = make_float2(s0, s1);
+                    }
+                }
+                // deltas: (row, group, quarter) tasks of this cube, computed
+                // side by side, stores predicated (absent rows and channels
+                // read zeros and in-bounds rows; quads stay whole)
+                constexpr int NTW = (16 * NGC * 4 + 63) / 64;   // tasks per lane for cubes of up to 16 rows
+                uint32_t code[NTW];
+                int exq[NTW];
+                bool live[NTW];
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) {
+                    const int t = lane + 64 * n;
+                    const int qq = t & 3, pr = t >> 2;
+                    const int j = pr / NGC, gc = pr - j * NGC;
+                    const int rr = min(rb + j, QROWS - 1);
+                    const long long G = (c0 >> 5) + gc;
+                    live[n] = j < S && G * 32 < a.Ci && ((pres >> rr) & 1);
+                    float v[8];
+                    qload8<XT>(buf, rr, gc, qq, 0u, v);
+                    const float4 k0 = *(const float4*)&cs_[cr][gc * 32 + qq * 8];
+                    const float4 k1 = *(const float4*)&cs_[cr][gc * 32 + qq * 8 + 4];
+                    const float core[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                    float dv[8];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        dv[e] = v[e] - core[e];
+                        amax = fmaxf(amax, fabsf(dv[e]));
+                    }
+                    amax = quad_max(amax);
+                    exq[n] = mx_exp_fp4(amax);
+                    const float sc = pow2f(exq[n]);
+                    uint32_t w = 0u;
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[0], dv[1], sc, 0);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[2], dv[3], sc, 1);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[4], dv[5], sc, 2);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[6], dv[7], sc, 3);
+                    code[n] = w;
+                }
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) {
+                    if (!live[n]) continue;
+                    const int t = lane + 64 * n;
+                    const int qq = t & 3, pr = t >> 2;
+                    const int j = pr / NGC, gc = pr - j * NGC;
+                    const long long G = (c0 >> 5) + gc, sl = B.slot0 + rb + j;
+                    *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
+                    if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
+                }
+            }
+        } else {
+            for (int t = qtid; t < ntask; t += 256) {
+                if (full) task(t, std::true_type{});
+                else task(t, std::false_type{});
+            }
         }
         // the group's next chunk; a new block's metadata goes to the other
         // buffer now and is read after the next barrier
@@ -1007,16 +1121,19 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
         cus = 256;
     const unsigned blocks = (unsigned)std::min<long long>(a.nblocks, cus);   // persistent: one workgroup per CU
     const int nct = q->rp / 32;
-    // one-pass quantizer for blocks of 16 or more cubes (every thread of a
-    // group has a cube); two phases for blocks of at most 8 (cubes of 8 to 64
-    // tokens) and for cubes of more than 64 tokens
-    const int cm = a.core_mode == 1 ? 1 : (cpb <= 8 ? 2 : 0);
+    // one-pass quantizer for blocks of 7 or more cubes (a thread per (cube,
+    // group, quarter)); a wave per cube for blocks of 4 to 6; two phases for
+    // blocks of at most 3 and for cubes of more than 64 tokens (measured on
+    // the 720p FFN layers: 8 cubes per block one-pass 0.43 ms, two-phase
+    // 0.45, wave per cube 0.48; 4 cubes per block 0.79, 0.46, 0.41)
+    const int cm = a.core_mode == 1 ? 1 : (cpb <= 3 ? 2 : (cpb <= 6 ? 3 : 0));
     auto go = [&](auto XT_, auto NCT_) {
         using XT = decltype(XT_);
         constexpr int THREADS = QCfg<XT, decltype(NCT_)::value>::THREADS;
         if (cm == 0) k_quantize<XT, decltype(NCT_)::value, 0><<<blocks, THREADS, 0, st>>>(a);
         else if (cm == 1) k_quantize<XT, decltype(NCT_)::value, 1><<<blocks, THREADS, 0, st>>>(a);
-        else k_quantize<XT, decltype(NCT_)::value, 2><<<blocks, THREADS, 0, st>>>(a);
+        else if (cm == 2) k_quantize<XT, decltype(NCT_)::value, 2><<<blocks, THREADS, 0, st>>>(a);
+        else k_quantize<XT, decltype(NCT_)::value, 3><<<blocks, THREADS, 0, st>>>(a);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
