@@ -222,8 +222,9 @@ __device__ __forceinline__ float2 qconv2(uint2 d, uint32_t sgn) {
 //      the (cube, group, quarter) threads write the fp32 core to LDS, a
 //      second barrier per period follows, and then every thread of the
 //      group codes (row, group, quarter) deltas;
-//   1: the same two phases with the cores of cubes of more than 64 tokens
-//      read from a pass before this one;
+//   1: cubes of more than 64 tokens: their cores come from a pass before
+//      this one, and every thread of the group codes (row, group, quarter)
+//      deltas reading them (one barrier per period);
 //   3: one pass with one wave per cube, for blocks of 4 to 6 cubes (cubes
 //      of 10 to 16 tokens): the core by channel pairs, then the cube's
 //      (row, group, quarter) deltas, both on the same wave.
@@ -248,10 +249,11 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     __shared__ __attribute__((aligned(1024))) uint8_t xbuf[QNBUF * STAGE];
     __shared__ int tok_s[2][2][QROWS];              // [group][buffer]
     __shared__ int4 meta_s[2][2][QROWS];            // per cube: first row, end row, present rows (bit j: row first + j), tokens
-    constexpr bool TWO = CM == 1 || CM == 2;         // two phases, two barriers per period
+    constexpr bool TWO = CM == 1 || CM == 2;         // (row, group, quarter) delta tasks over the whole group
+    constexpr bool BAR2 = CM == 2;                   // phase 1 in the quantizers: two barriers per period
     constexpr int TCUBES = 8;                        // cubes per block in the two-phase forms
-    constexpr bool CORES = CM != 0;                  // fp32 cores of the group's chunk in LDS
-    __shared__ float core_s[CORES ? SP : 1][CORES ? TCUBES : 1][CORES ? CC : 1];
+    constexpr bool CORES = CM >= 2;                  // fp32 cores of the group's chunk in LDS
+    __shared__ float core_s[CORES ? SP : 1][CORES ? TCUBES : 1][CC];
     __shared__ uint64_t pres_s[2][2];               // [group][buffer]: bit r = row r holds a token
 
     const Geom& g = a.g;
@@ -375,7 +377,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             barrier();
 #pragma unroll
             for (int k = 0; k < SP; ++k) issue();
-            if constexpr (TWO) barrier();
+            if constexpr (BAR2) barrier();
         }
         // the surplus copies land before the wave ends (no copy may write
         // LDS after the workgroup has released it)
@@ -396,7 +398,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
         for (long long s = 0; s < total; ++s, next_chunk()) {
             if (s % SP == 0) {
                 barrier();
-                if constexpr (TWO) barrier();
+                if constexpr (BAR2) barrier();
             }
             if constexpr (NCT == 0) continue;
             const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
@@ -463,9 +465,9 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             const int c0 = c * CC;
             const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
             float(*const cs_)[CC] = core_s[qgrp];
-            // ---- phase 1: the cores.  CM 2: one (cube, channel pair) per
-            // thread, 16 lanes per 32-channel group; CM 1: one (cube, group,
-            // quarter) per thread copies the precomputed core.
+            // ---- phase 1 (CM 2): the cores, one (cube, channel pair) per
+            // thread, 16 lanes per 32-channel group.  (CM 1 reads the cores
+            // from the earlier pass in phase 2 and has no phase 1.)
             if constexpr (CM == 2) {
                 const int ntask = B.ncores * (CC / 2);     // a multiple of 16: groups stay whole
                 const uint64_t pres = pres_s[qgrp][mb];
@@ -532,21 +534,8 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
                     *(float2*)&cs_[cr][ch] = make_float2(s0, s1);
                 }
-            } else {
-                const int ntask = B.ncores * NGC * 4;
-                if (have && qtid < ntask) {
-                    const int qq = qtid & 3, pr = qtid >> 2;
-                    const int cr = pr / NGC, gc = pr - cr * NGC;
-                    const long long G = (c0 >> 5) + gc;
-                    if (G * 32 < a.Ci) {
-                        const long long k = B.k_first + cr;
-                        const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32 + 8 * qq);
-                        *(float4*)&cs_[cr][gc * 32 + qq * 8] = cp[0];
-                        *(float4*)&cs_[cr][gc * 32 + qq * 8 + 4] = cp[1];
-                    }
-                }
+                barrier();                                     // the group's cores are in LDS
             }
-            barrier();                                         // the group's cores are in LDS
             // ---- phase 2: the deltas, one (row, group, quarter) per thread
             if (have) {
                 const uint64_t pres = pres_s[qgrp][mb];
@@ -565,11 +554,21 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const int r = pr / NGC, gc = pr - r * NGC;
                     const long long G = (c0 >> 5) + gc;
                     live[n] = G * 32 < a.Ci && ((pres >> r) & 1);   // (pres has no bit for rows past the block)
-                    const int cr = CM == 1 ? (int)((B.slot0 + r) / g.S - B.k_first) : r / g.S;
                     float v[8];
                     qload8<XT>(buf, r, gc, qq, 0u, v);
-                    const float4 k0 = *(const float4*)&cs_[cr][gc * 32 + qq * 8];
-                    const float4 k1 = *(const float4*)&cs_[cr][gc * 32 + qq * 8 + 4];
+                    float4 k0, k1;
+                    if constexpr (CM == 1) {
+                        // the cube's core row from the earlier pass (clamped for
+                        // rows past the last slot; columns stay below Kp)
+                        const long long k = min((B.slot0 + r) / g.S, g.K - 1);
+                        const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32 + 8 * qq);
+                        k0 = cp[0];
+                        k1 = cp[1];
+                    } else {
+                        const int cr = r / g.S;
+                        k0 = *(const float4*)&cs_[cr][gc * 32 + qq * 8];
+                        k1 = *(const float4*)&cs_[cr][gc * 32 + qq * 8 + 4];
+                    }
                     const float core[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
                     float dv[8];
                     float amax = 0.0f;
