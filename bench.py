@@ -103,7 +103,10 @@ def work(cfg, cube):
         "fp4": 2.0 * K * S * Ci * Co,        # delta term, one row per slot (pad slots of partial cubes included)
         "fp8": 2.0 * K * Ci * Co,            # core term, one row per cube
         "bf16": 2.0 * N * r * (Ci + Co),     # low-rank branch
-        "quant_bytes": N * Ci * xbytes * (2 if S > 64 else 1) + N * Ci * (0.5 + 1 / 32) + K * Ci * (1 + 1 / 32) + 2 * N * r,
+        # X once (twice for cubes of more than 64 tokens), delta codes and scales
+        # (not stored for one-token cubes: all zero), core codes and scales, U
+        "quant_bytes": N * Ci * xbytes * (2 if S > 64 else 1) + (0 if S == 1 else N * Ci * (0.5 + 1 / 32))
+                       + K * Ci * (1 + 1 / 32) + 2 * N * r,
     }
 
 

@@ -165,7 +165,9 @@ dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact
 /* Copy the state of the last dq_quantize_act to the host in canonical token
  * order (any pointer may be NULL): delta codes [N][Ci/2], delta scale codes
  * [N][Ci/32], core codes [K][Ci] (FP8 E4M3), core scale codes [K][Ci/32],
- * U [N][rank] bf16 bits.  Synchronises `stream` first. */
+ * U [N][rank] bf16 bits.  Synchronises `stream` first.  With one-token
+ * cubes (t = h = w = 1) every delta is exactly zero: its codes and scale
+ * codes are reported as 0 (the activation pass does not store them). */
 dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscales_host, uint8_t* ccodes_host,
                          uint8_t* cscales_host, uint16_t* u_host, void* stream);
 

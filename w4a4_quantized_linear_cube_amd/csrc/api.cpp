@@ -444,14 +444,21 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
     const int64_t Ci = q->Ci, Kp = q->Kp;
     try {
         std::vector<uint8_t> buf;
-        if (dcodes_host) {
+        // One-token cubes: every delta is x - x = +0 exactly, coded 0 with
+        // scale code 0 (2^-127); the activation pass does not store them.
+        const bool zero_deltas = g.S == 1;
+        if (dcodes_host && zero_deltas) {
+            std::memset(dcodes_host, 0, (size_t)(g.N * (Ci / 2)));
+        } else if (dcodes_host) {
             if ((e = fetch_all(q->dq, (size_t)(q->Nslot_pad * Kp / 2), buf)) != hipSuccess) return hip_fail(e, "copy delta codes");
             for (long long s = 0; s < g.Nslot; ++s) {
                 long long t = host_slot_token(g, s);
                 if (t >= 0) unstep_fp4(buf, s, Ci, Kp, dcodes_host + t * (Ci / 2));
             }
         }
-        if (dscales_host) {
+        if (dscales_host && zero_deltas) {
+            std::memset(dscales_host, 0, (size_t)(g.N * (Ci / 32)));
+        } else if (dscales_host) {
             if ((e = fetch_all(q->ds, (size_t)(q->Nslot_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy delta scales");
             for (long long s = 0; s < g.Nslot; ++s) {
                 long long t = host_slot_token(g, s);

@@ -750,7 +750,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 for (int j = 0; j < QKEEP; ++j) *(uint32_t*)(dq_t + toff_fp4(rt0 + j, (int)G) + 4 * qq) = code[j];
                 const int exq = qq == 0 ? ex[0] : qq == 1 ? ex[1] : qq == 2 ? ex[2] : ex[3];
                 ds_t[toff_scale(rt0 + qq, (int)G)] = (uint8_t)(exq + 127);
-            } else {
+            } else if (g.S > 1) {                           // one-token cubes: every delta is 0, not stored
 #pragma unroll
                 for (int j = 0; j < QKEEP; ++j)
                     if (j < nr) delta(rb + j, xr[j]);
