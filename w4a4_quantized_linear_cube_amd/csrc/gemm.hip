@@ -196,17 +196,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     const int nk = p.nks;
     const int nsteps = ntiles * nk;
 
-    // Stagger: the eight XCDs start an eighth of a tile apart, so their
-    // epilogues (output stores) are spread over time instead of all CUs
-    // writing at once; the workgroups of one XCD stay in step, since they
-    // share operand steps in its L2.
-    {
-        const int phase = walk.x;
-        const long long wait = (long long)phase * nk * 160;
-        const long long t0 = (long long)clock64();
-        while ((long long)clock64() - t0 < wait) __builtin_amdgcn_s_sleep(8);
-    }
-
     // ---- copies.  Global step s (over all of this workgroup's tiles) is
     // K step s % nk of tile s / nk; the issue cursor walks them in order.
     // Per-lane offsets are 32-bit; tile bases are uniform (scalar registers).

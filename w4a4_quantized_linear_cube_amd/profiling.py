@@ -38,13 +38,24 @@ def summarize_trace(d: str, out: str, cmd: str) -> None:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(files[0])))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    # Per-dispatch durations (DIR/*_kernel_trace.csv) give the median, which
+    # the first dispatches (clock still ramping) do not move.
+    durs = defaultdict(list)
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            durs[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+
+    def median_us(name):
+        v = sorted(durs.get(name, []))
+        return f"{v[len(v) // 2] / 1e3:.1f}" if v else "-"
+
     lines = ["# Kernel trace: " + os.path.splitext(os.path.basename(out))[0], "",
              "Command (from the repository root on the GPU box):", "", "```", cmd, "```", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | total (ms) |",
-             "|---|---|---|---|---|---|"]
+             "| kernel | calls | average (us) | median (us) | min (us) | max (us) | total (ms) |",
+             "|---|---|---|---|---|---|---|"]
     for r in rows[:12]:
         lines.append(f"| `{_short(r['Name'])[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{median_us(r['Name'])} | {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.2f} |")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
