@@ -19,6 +19,9 @@ cpu_baseline = the CPU oracle on a bounded sample of the same workload.
 --sweep instead prints one JSON line per cube shape of the config's list
 (e.g. --config ffn_down_720p --sweep: 1x1x1, 1x2x2, 2x2x2, 1x4x4 and one
 global cube) with the step time, effective TOPS and the three phases.
+--schedule prints the same for the timestep-aware cube sizes (4x1x4, then
+4x2x8), and one line for a whole denoising run of the layer that switches
+between them.
 """
 from __future__ import annotations
 
@@ -51,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the oracle's timed sample")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per cube shape of the config")
+    ap.add_argument("--schedule", action="store_true",
+                    help="the timestep-aware cube schedule (4x1x4 early, 4x2x8 after) on the config's layer")
+    ap.add_argument("--denoise-steps", type=int, default=10, help="denoising steps of one --schedule run")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
@@ -92,20 +98,27 @@ def work(cfg, cube):
     """Sizes of the method's work for a cube shape: cubes, slots, flops of
     each GEMM, the activation pass's algorithmic bytes."""
     t_, h_, w_ = cube
-    Tc, Hc, Wc = -(-cfg.T // t_), -(-cfg.H // h_), -(-cfg.W // w_)
-    K = Tc * Hc * Wc
+    Hc, Wc = -(-cfg.H // h_), -(-cfg.W // w_)
     S = t_ * h_ * w_
     N, Ci, Co, r = cfg.N, cfg.Ci, cfg.Co, cfg.rank
     xbytes = 2 if cfg.dtype == "bf16" else 4
+    # frame segments: the whole frame groups, then the last T % t frames as
+    # cubes of T % t frames (no pad slots for the missing frames)
+    T0 = cfg.T - cfg.T % t_
+    segs = [(T0, t_)] + ([(cfg.T - T0, cfg.T - T0)] if T0 < cfg.T else [])
+    K = sum(-(-Ts // ts) * Hc * Wc for Ts, ts in segs)
+    Nslot = sum(-(-Ts // ts) * Hc * Wc * ts * h_ * w_ for Ts, ts in segs)
+    # X once (twice in a segment of cubes of more than 64 tokens)
+    xreads = sum(Ts * cfg.H * cfg.W * (2 if ts * h_ * w_ > 64 else 1) for Ts, ts in segs)
     return {
-        "K": K, "S": S, "Nslot": K * S,
+        "K": K, "S": S, "Nslot": Nslot,
         "dense": 2.0 * N * Ci * Co,
-        "fp4": 2.0 * K * S * Ci * Co,        # delta term, one row per slot (pad slots of partial cubes included)
+        "fp4": 2.0 * Nslot * Ci * Co,        # delta term, one row per slot (pad slots of clipped cubes included)
         "fp8": 2.0 * K * Ci * Co,            # core term, one row per cube
         "bf16": 2.0 * N * r * (Ci + Co),     # low-rank branch
-        # X once (twice for cubes of more than 64 tokens), delta codes and scales
-        # (not stored for one-token cubes: all zero), core codes and scales, U
-        "quant_bytes": N * Ci * xbytes * (2 if S > 64 else 1) + (0 if S == 1 else N * Ci * (0.5 + 1 / 32))
+        # X, delta codes and scales (not stored for one-token cubes: all
+        # zero), core codes and scales, U
+        "quant_bytes": xreads * Ci * xbytes + (0 if S == 1 else N * Ci * (0.5 + 1 / 32))
                        + K * Ci * (1 + 1 / 32) + 2 * N * r,
     }
 
@@ -120,21 +133,73 @@ def sweep(args, cfg, dq, torch):
     stream = torch.cuda.current_stream()
     for cube in cfg.cubes:
         qa = dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + tuple(cube))
-        ms, q_ms, c_ms, d_ms = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
-        wk = work(cfg, cube)
-        one = wk["S"] == 1          # one-token cubes: the delta term is one FP8 GEMM over the cubes
-        rec = {
-            "config": cfg.name, "cube": list(cube), "cubes": wk["K"], "slots": wk["Nslot"],
-            "ms_per_step": round(ms, 4), "effective_tops": round(wk["dense"] / (ms * 1e-3) / 1e12, 2),
-            "quantize": {"ms": round(q_ms, 4), "GBps": round(wk["quant_bytes"] / (q_ms * 1e-3) / 1e9, 1)},
-            "core_term": {"ms": round(c_ms, 4)} if one else
-                         {"ms": round(c_ms, 4), "fp8_tflops": round(wk["fp8"] / (c_ms * 1e-3) / 1e12, 1)},
-            "delta_term": {"ms": round(d_ms, 4), "fp8_tflops": round(wk["fp8"] / (d_ms * 1e-3) / 1e12, 1)} if one else
-                          {"ms": round(d_ms, 4), "fp4_tflops": round(wk["fp4"] / (d_ms * 1e-3) / 1e12, 1)},
-        }
-        print(json.dumps(rec), flush=True)
+        timing = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
+        print(json.dumps(shape_record(cfg, cube, *timing)), flush=True)
         torch.cuda.synchronize()
         del qa                      # frees the cube shape's buffers
+
+
+def shape_record(cfg, cube, ms, q_ms, c_ms, d_ms):
+    """One cube shape's step time, split by phase, with its rates."""
+    wk = work(cfg, cube)
+    one = wk["S"] == 1          # one-token cubes: the delta term is one FP8 GEMM over the cubes
+    return {
+        "config": cfg.name, "cube": list(cube), "cubes": wk["K"], "slots": wk["Nslot"],
+        "ms_per_step": round(ms, 4), "effective_tops": round(wk["dense"] / (ms * 1e-3) / 1e12, 2),
+        "quantize": {"ms": round(q_ms, 4), "GBps": round(wk["quant_bytes"] / (q_ms * 1e-3) / 1e9, 1)},
+        "core_term": {"ms": round(c_ms, 4)} if one else
+                     {"ms": round(c_ms, 4), "fp8_tflops": round(wk["fp8"] / (c_ms * 1e-3) / 1e12, 1)},
+        "delta_term": {"ms": round(d_ms, 4), "fp8_tflops": round(wk["fp8"] / (d_ms * 1e-3) / 1e12, 1)} if one else
+                      {"ms": round(d_ms, 4), "fp4_tflops": round(wk["fp4"] / (d_ms * 1e-3) / 1e12, 1)},
+    }
+
+
+# Timestep-aware cube sizes (DeltaQuant notes, 损失函数/训练策略): 16-token
+# cubes (t4 h1 w4) for the first 25-30 % of the denoising steps (high noise,
+# the steps that matter most for quality), 64-token cubes (t4 h2 w8) for the
+# rest.  30 % here.
+SCHEDULE_SHAPES = ((4, 1, 4), (4, 2, 8))
+SCHEDULE_EARLY = 0.3
+
+
+def schedule(args, cfg, dq, torch):
+    """The cube schedule on one layer: a JSON line per cube shape, then one
+    for a whole denoising run of the layer (the shape switches after the
+    early steps; both handles stay allocated, so switching costs nothing)."""
+    wt = synth_mod().config_weight(cfg)
+    weights = dq.dq_prepare_weights(wt, cfg.rank, seed=cfg.w_seed, device=0)
+    x = synth_mod().make_activation(cfg.T, cfg.H, cfg.W, cfg.Ci, seed=cfg.x_seeds[0], dtype=cfg.dtype,
+                                    n_outliers=cfg.n_outliers, device="cuda")
+    y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    qas = [dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + s) for s in SCHEDULE_SHAPES]
+    recs = []
+    for s, qa in zip(SCHEDULE_SHAPES, qas):
+        recs.append(shape_record(cfg, s, *time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)))
+        print(json.dumps(recs[-1]), flush=True)
+    n = args.denoise_steps
+    n_early = max(1, min(n, round(SCHEDULE_EARLY * n)))
+    plan = [qas[0]] * n_early + [qas[1]] * (n - n_early)
+    for qa in plan:                 # warm-up: one run
+        dq.dq_linear(weights, x, qa, y, stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    runs = max(1, args.steps // n)
+    start.record(stream)
+    for _ in range(runs):
+        for qa in plan:
+            dq.dq_linear(weights, x, qa, y, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_call = start.elapsed_time(end) / (runs * n)
+    dense = work(cfg, SCHEDULE_SHAPES[0])["dense"]
+    print(json.dumps({
+        "config": cfg.name, "schedule": [["x".join(map(str, SCHEDULE_SHAPES[0])), n_early],
+                                         ["x".join(map(str, SCHEDULE_SHAPES[1])), n - n_early]],
+        "denoise_steps": n, "runs": runs, "ms_per_layer_call": round(ms_call, 4),
+        "effective_tops": round(dense / (ms_call * 1e-3) / 1e12, 2),
+        "predicted_ms_per_layer_call": round((n_early * recs[0]["ms_per_step"] + (n - n_early) * recs[1]["ms_per_step"]) / n, 4),
+    }), flush=True)
 
 
 def synth_mod():
@@ -171,6 +236,9 @@ def main():
     cfg = synth.CONFIGS[args.config]
     if args.sweep:
         sweep(args, cfg, dq, torch)
+        return
+    if args.schedule:
+        schedule(args, cfg, dq, torch)
         return
     cube = tuple(int(v) for v in args.cube.split(",")) if args.cube else cfg.cubes[0]
     xseed = cfg.x_seeds[0] if args.x_seed is None else args.x_seed

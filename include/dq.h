@@ -116,7 +116,10 @@ dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2
 /* Workspace for activations of one geometry: delta codes and scales, core
  * codes and scales, U = bf16(bf16(X) L1), and (for cube shapes that need it)
  * the per-cube core term.  Owns its device buffers (sized from the geometry,
- * Ci, Co and the rank of `w`); free with dq_qact_destroy.  Errors:
+ * Ci, Co and the rank of `w`); free with dq_qact_destroy.  When t does not
+ * divide T, the cubes of the last, clipped frame group (T % t frames) are laid
+ * out as a grid of their own: the same cubes, tokens, sums and codes, without
+ * rows for the missing frames, so the forward does no work for them.  Errors:
  * DQ_ERR_SHAPE for an invalid geometry or size overflow. */
 dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out);
 void dq_qact_destroy(dq_qact* q);

@@ -183,6 +183,8 @@ EDGE = [
     (3, 6, 8, (1, 4, 4), 96, 64, 16, "f32"),        # fp32 input, one wave per 16-token cube (clipped), a partial chunk
     (21, 4, 6, (4, 1, 4), 64, 64, 16, "bf16"),     # the pages' small tile t4 h1 w4 on 21 frames
     (21, 4, 16, (4, 2, 8), 64, 64, 16, "bf16"),    # the pages' large tile t4 h2 w8
+    (5, 6, 8, (2, 2, 2), 256, 256, 32, "bf16"),    # last frame alone: second frame segment at row 256
+    (9, 8, 16, (4, 2, 4), 256, 512, 32, "bf16"),   # second frame segment after four tiles of 32-token cubes
 ]
 
 
@@ -359,6 +361,18 @@ def test_attn14b_projection_sampled(dqm):
 def test_ffn_up_720p_sampled(dqm):
     cfg = synth.CONFIGS["ffn_up_720p"]
     _full_size_case(dqm, cfg, cfg.cubes[0], cfg.x_seeds[0], check_weights=True)
+
+
+@pytest.mark.parametrize("cube,step", [((4, 1, 4), 0), ((4, 2, 8), 1)], ids=["4x1x4", "4x2x8"])
+def test_ffn_up_720p_schedule_shapes(dqm, cube, step):
+    """The timestep-aware cube sizes (DeltaQuant notes, 损失函数/训练策略) at
+    full size: 16-token cubes early in denoising (one quantizer wave per cube),
+    64-token cubes later (the two-phase quantizer), each on its own synthetic
+    timestep's activations; codes bit-exact on sampled cubes, Y within the
+    bound, and delta W4A4 no worse than direct W4A4."""
+    cfg = synth.CONFIGS["ffn_up_720p"]
+    _full_size_case(dqm, cfg, cube, cfg.x_seeds[0] + step, check_weights=False, n_cubes=24 // (1 + step),
+                    versus_direct=True)
 
 
 @pytest.mark.parametrize("cube", synth.CONFIGS["ffn_down_720p"].cubes, ids=lambda c: "x".join(map(str, c)))

@@ -4,6 +4,7 @@
 // the low-rank factors.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <limits>
@@ -341,11 +342,33 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
     q->rp = w->rp;
     q->rank = w->rank;
     q->g = Geom{G.T, G.H, G.W, G.t, G.h, G.w, Tc, Hc, Wc, (int)S, (long long)N, (long long)K, (long long)Nslot};
-    q->Nslot_pad = round_up(Nslot, MPAD);
-    q->K_pad = round_up(K, MPAD);
-    q->core_mode = S <= 64 ? 0 : 1;
-    q->nblk = (S + CORE_BLOCK - 1) / CORE_BLOCK;
-    if (!mul_ok(q->Nslot_pad, q->Kp, lim) || !mul_ok(q->K_pad, q->Cop, lim) || !mul_ok(K * q->nblk, q->Kp, lim))
+    // frame segments: whole frame groups, then the clipped last group (if any)
+    const int T0 = G.T - G.T % G.t;                  // >= t, since t <= T
+    const int segT[2] = {T0, G.T - T0}, segt[2] = {G.t, G.T - T0};
+    q->nseg = T0 < G.T ? 2 : 1;
+    int64_t row = 0, krow = 0, tok = 0, kk = 0, max_partials = 0;
+    for (int i = 0; i < q->nseg; ++i) {
+        dq_segment& sg = q->seg[i];
+        const int tc = (segT[i] + segt[i] - 1) / segt[i];
+        const int64_t Ks = (int64_t)tc * Hc * Wc, Ss = (int64_t)segt[i] * G.h * G.w;
+        const int64_t Ns = (int64_t)segT[i] * G.H * G.W;
+        sg.g = Geom{segT[i], G.H, G.W, segt[i], G.h, G.w, tc, Hc, Wc, (int)Ss, (long long)Ns, (long long)Ks,
+                    (long long)(Ks * Ss)};
+        sg.tok0 = tok;
+        sg.k0 = kk;
+        sg.row0 = row;
+        sg.krow0 = krow;
+        sg.core_mode = Ss <= 64 ? 0 : 1;
+        sg.nblk = (Ss + CORE_BLOCK - 1) / CORE_BLOCK;
+        if (sg.core_mode == 1) max_partials = std::max(max_partials, Ks * sg.nblk);
+        tok += Ns;
+        kk += Ks;
+        row += round_up(Ks * Ss, MPAD);
+        krow += round_up(Ks, MPAD);
+    }
+    q->Nslot_pad = row;
+    q->K_pad = krow;
+    if (!mul_ok(q->Nslot_pad, q->Kp, lim) || !mul_ok(q->K_pad, q->Cop, lim) || !mul_ok(max_partials, q->Kp, lim))
         return fail(DQ_ERR_SHAPE, "workspace too large");
     hipError_t e;
     if ((e = dalloc(&q->dq, (size_t)(q->Nslot_pad * q->Kp / 2), &q->bytes)) != hipSuccess ||
@@ -358,10 +381,15 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
         (e = dalloc(&q->zero, (size_t)512, &q->bytes)) != hipSuccess ||
         (e = dalloc(&q->sink, (size_t)512, &q->bytes)) != hipSuccess)
         return hip_fail(e, "hipMalloc workspace");
-    if ((e = launch_slot_tokens(q->g, q->stok, q->Nslot_pad, nullptr)) != hipSuccess) return hip_fail(e, "slot table");
-    if (q->core_mode == 1) {
-        if ((e = dalloc(&q->coref, (size_t)(K * q->Kp), &q->bytes)) != hipSuccess ||
-            (e = dalloc(&q->part, (size_t)(K * q->nblk * q->Kp), &q->bytes)) != hipSuccess)
+    for (int i = 0; i < q->nseg; ++i) {
+        const dq_segment& sg = q->seg[i];
+        const int64_t rows = (i + 1 < q->nseg ? q->seg[i + 1].row0 : q->Nslot_pad) - sg.row0;
+        if ((e = launch_slot_tokens(sg.g, sg.tok0, q->stok + sg.row0, rows, nullptr)) != hipSuccess)
+            return hip_fail(e, "slot table");
+    }
+    if (max_partials > 0) {
+        if ((e = dalloc(&q->coref, (size_t)(q->K_pad * q->Kp), &q->bytes)) != hipSuccess ||
+            (e = dalloc(&q->part, (size_t)(max_partials * q->Kp), &q->bytes)) != hipSuccess)
             return hip_fail(e, "hipMalloc workspace");
     }
     if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "workspace init");
@@ -442,6 +470,20 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
     if (e != hipSuccess) return hip_fail(e, "stream synchronize");
     const Geom& g = q->g;
     const int64_t Ci = q->Ci, Kp = q->Kp;
+    // (slot row, token) of every token, and the row of every cube
+    auto each_slot = [&](auto&& fn) {
+        for (int i = 0; i < q->nseg; ++i) {
+            const dq_segment& sg = q->seg[i];
+            for (long long s = 0; s < sg.g.Nslot; ++s) {
+                const long long t = host_slot_token(sg.g, s);
+                if (t >= 0) fn(sg.row0 + s, sg.tok0 + t);
+            }
+        }
+    };
+    auto cube_row = [&](long long k) {
+        const dq_segment& sg = q->seg[q->nseg > 1 && k >= q->seg[1].k0 ? 1 : 0];
+        return sg.krow0 + (k - sg.k0);
+    };
     try {
         std::vector<uint8_t> buf;
         // One-token cubes: every delta is x - x = +0 exactly, coded 0 with
@@ -451,35 +493,26 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
             std::memset(dcodes_host, 0, (size_t)(g.N * (Ci / 2)));
         } else if (dcodes_host) {
             if ((e = fetch_all(q->dq, (size_t)(q->Nslot_pad * Kp / 2), buf)) != hipSuccess) return hip_fail(e, "copy delta codes");
-            for (long long s = 0; s < g.Nslot; ++s) {
-                long long t = host_slot_token(g, s);
-                if (t >= 0) unstep_fp4(buf, s, Ci, Kp, dcodes_host + t * (Ci / 2));
-            }
+            each_slot([&](long long s, long long t) { unstep_fp4(buf, s, Ci, Kp, dcodes_host + t * (Ci / 2)); });
         }
         if (dscales_host && zero_deltas) {
             std::memset(dscales_host, 0, (size_t)(g.N * (Ci / 32)));
         } else if (dscales_host) {
             if ((e = fetch_all(q->ds, (size_t)(q->Nslot_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy delta scales");
-            for (long long s = 0; s < g.Nslot; ++s) {
-                long long t = host_slot_token(g, s);
-                if (t >= 0) unstep_scales(buf, s, Ci, Kp, dscales_host + t * (Ci / 32));
-            }
+            each_slot([&](long long s, long long t) { unstep_scales(buf, s, Ci, Kp, dscales_host + t * (Ci / 32)); });
         }
         if (ccodes_host) {
             if ((e = fetch_all(q->cq, (size_t)(q->K_pad * Kp), buf)) != hipSuccess) return hip_fail(e, "copy core codes");
-            for (long long k = 0; k < g.K; ++k) unstep_fp8(buf, k, Ci, Kp, ccodes_host + k * Ci);
+            for (long long k = 0; k < g.K; ++k) unstep_fp8(buf, cube_row(k), Ci, Kp, ccodes_host + k * Ci);
         }
         if (cscales_host) {
             if ((e = fetch_all(q->cs, (size_t)(q->K_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy core scales");
-            for (long long k = 0; k < g.K; ++k) unstep_scales(buf, k, Ci, Kp, cscales_host + k * (Ci / 32));
+            for (long long k = 0; k < g.K; ++k) unstep_scales(buf, cube_row(k), Ci, Kp, cscales_host + k * (Ci / 32));
         }
         if (u_host && q->rank > 0) {
-            if ((e = fetch_all(q->u, (size_t)(g.Nslot * q->rp * 2), buf)) != hipSuccess) return hip_fail(e, "copy U");
+            if ((e = fetch_all(q->u, (size_t)(q->Nslot_pad * q->rp * 2), buf)) != hipSuccess) return hip_fail(e, "copy U");
             const uint16_t* ub = (const uint16_t*)buf.data();
-            for (long long s = 0; s < g.Nslot; ++s) {
-                long long t = host_slot_token(g, s);
-                if (t >= 0) std::memcpy(u_host + t * q->rank, ub + s * q->rp, (size_t)q->rank * 2);
-            }
+            each_slot([&](long long s, long long t) { std::memcpy(u_host + t * q->rank, ub + s * q->rp, (size_t)q->rank * 2); });
         }
     } catch (const std::bad_alloc&) {
         return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");

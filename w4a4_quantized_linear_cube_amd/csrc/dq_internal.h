@@ -89,14 +89,30 @@ struct dq_weights {
     size_t bytes = 0;
 };
 
+// Frame segments.  Frames are the slowest token axis, so when t does not
+// divide T the clipped cubes of the last frame group form a regular grid of
+// their own: frames [0, T - T % t) with t x h x w cubes and the last T % t
+// frames with (T % t) x h x w cubes.  The two segments hold the same cubes,
+// tokens and slot order within each cube as the full grid, but the second
+// needs no pad slots for the missing frames.  Segment i's slot rows start at
+// row0, its cube rows (core codes, per-cube term) at krow0, both multiples of
+// 256 (GEMM tiles); its tokens are tok0 + its own token numbers, its cubes
+// k0 + its own cube numbers.
+struct dq_segment {
+    dq::Geom g{};
+    int64_t tok0 = 0, k0 = 0, row0 = 0, krow0 = 0;
+    int core_mode = 0;         // 0: cores inside the activation pass (S <= 64); 1: separate passes
+    int64_t nblk = 0;          // 64-token blocks per cube (core_mode 1)
+};
+
 struct dq_qact {
     int device = 0;
     int64_t Ci = 0, Co = 0, Kp = 0, Cop = 0;
     int rp = 0, rank = 0;
-    dq::Geom g{};
+    dq::Geom g{};              // the full token grid and cube shape
+    int nseg = 1;
+    dq_segment seg[2]{};
     int64_t Nslot_pad = 0, K_pad = 0;
-    int core_mode = 0;         // 0: cores inside the activation pass (S <= 64); 1: separate passes
-    int64_t nblk = 0;          // 64-token blocks per cube (core_mode 1)
     uint8_t* dq = nullptr;     // Nslot_pad x Kp/2   delta codes, slot order, step-major
     uint8_t* ds = nullptr;     // Nslot_pad x Kp/32  delta scale codes, step-major
     uint8_t* cq = nullptr;     // K_pad x Kp         core FP8 codes, step-major
@@ -106,8 +122,8 @@ struct dq_qact {
     int* stok = nullptr;       // [Nslot_pad]        token of each slot, -1 for pad slots
     uint8_t* zero = nullptr;   // [512]              zero bytes (copy source of absent rows)
     float* sink = nullptr;     // [512]              target of the GEMM's discarded 16-byte stores
-    float* coref = nullptr;    // [K][Kp]            fp32 cores (core_mode 1)
-    float* part = nullptr;     // [K*nblk][Kp]       fp32 block partials (core_mode 1)
+    float* coref = nullptr;    // [K_pad][Kp]        fp32 cores (segments of core_mode 1), cube rows
+    float* part = nullptr;     // [K*nblk][Kp]       fp32 block partials (core_mode 1; the segments take turns)
     size_t bytes = 0;
 };
 
@@ -121,7 +137,7 @@ hipError_t launch_residual(const void* w_dev, int w_bf16, const uint16_t* l1_dev
 hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, int64_t ld_src, int64_t Kp,
                                   uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qact* q, hipStream_t st);
-hipError_t launch_slot_tokens(const Geom& g, int* stok, int64_t n, hipStream_t st);
+hipError_t launch_slot_tokens(const Geom& g, int64_t tok0, int* stok, int64_t n, hipStream_t st);
 
 // ---- launchers (gemm.hip) ----
 constexpr int FWD_CORE = 1, FWD_DELTA = 2;   // parts of the forward pass

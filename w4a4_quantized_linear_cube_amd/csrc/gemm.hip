@@ -53,8 +53,10 @@ struct GemmArgs {
     int Co;
     int vec4;           // y rows are 16-byte aligned (Co % 4 == 0, y 16-byte aligned)
     const int* stok;    // slot -> token (-1 for pad slots), Nslot_pad entries
-    int S;              // slots per cube
-    int kmax;           // last cube index
+    int S;              // slots per cube (rows below split)
+    int split;          // first slot row of the second frame segment (its cube rows from ksplit,
+    int S2, ksplit;     //   S2 slots per cube); past the last row if there is one segment
+    int kmax;           // last cube row
     const float* bias;  // per-cube core term [K_pad][ldbias]
     long long ldbias;
     const uint16_t* u;     // [Nslot_pad][rp]
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     int tstage = 0;                                       // stage of the tile's last K step
 
     // ---- core-term rows of the token epilogue.  A cube spans a multiple of
-    // 4 slots and tiles start at multiples of 256, so the four lanes of a quad
+    // 4 slots and tiles and frame segments start at multiples of 256 rows, so the four lanes of a quad
     // hold slots of one cube; lane u of the quad loads the quarter of the
     // cube's row that is piece (mi, u) of every lane's 16 pieces, and the
     // epilogue exchanges the quarters by DPP broadcasts.  They are loaded
@@ -370,12 +372,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // row, the rest in the instructions' offset fields; each element is read
     // once, so the loads allocate no cache lines.)
     constexpr int CORE_AHEAD = 6;
+    // cube row of slot row sl (pad slots: some valid row, never stored)
+    auto cube_row = [&](int sl) {
+        const int k = sl < p.split ? sl / p.S : p.ksplit + (sl - p.split) / p.S2;
+        return min(k, p.kmax);
+    };
     float4 bq[4][4];
     auto load_core = [&](int tm, int tn) {
         const uint32_t chq0 = (uint32_t)(tm * 256 + wr * 128 + 4 * g + 8 * (l32 & 3));
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-            const int k = min((tn * 256 + wc * 128 + 32 * ni + l32) / p.S, p.kmax);   // pad slots: any valid row, never stored
+            const int k = cube_row(tn * 256 + wc * 128 + 32 * ni + l32);
             const uint32_t bo = ((uint32_t)k * (uint32_t)p.ldbias + chq0) * 4;
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         for (int ni = 0; ni < 4; ++ni) {
             const int slot = n0 + wc * 128 + 32 * ni + l32;
             const int tok = p.stok[slot];
-            const int k = min(slot / p.S, p.kmax);          // pad slots: any valid row, never stored
+            const int k = cube_row(slot);
             float4 bv[4][4];
             if (p.bias) {
                 const float* brow = p.bias + (long long)k * p.ldbias + ch0;
@@ -709,8 +716,11 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
     d.Co = (int)w->Co;
     d.vec4 = (w->Co % 4 == 0) && ((uintptr_t)y % 16 == 0);
     d.stok = q->stok;
-    d.S = q->g.S;
-    d.kmax = (int)(q->g.K - 1);
+    d.S = q->seg[0].g.S;
+    d.split = q->nseg > 1 ? (int)q->seg[1].row0 : (int)q->Nslot_pad;
+    d.S2 = q->seg[q->nseg - 1].g.S;
+    d.ksplit = (int)q->seg[q->nseg - 1].krow0;
+    d.kmax = (int)(q->K_pad - 1);
     d.u = q->u;
     d.l2t = w->l2t;
     d.rp = w->rp;
@@ -745,7 +755,8 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
         // delta term + low-rank branch + the cube's core term -> y (token order)
         d.bias = q->bias;
         d.ldbias = w->Cop;
-        if (d.S % 4 == 0 && d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
+        if (d.S % 4 == 0 && d.S2 % 4 == 0 && d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0)
+            return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
         return launch<FMT_FP4, EPI_TOKENS>(d, st);
     }
     return hipSuccess;

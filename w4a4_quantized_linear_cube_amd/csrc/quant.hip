@@ -1056,9 +1056,12 @@ __global__ __launch_bounds__(256) void k_encode_fp4_rows(const float* src, long 
 }
 
 // Slot -> token table of the GEMM epilogue (-1 for pad slots).
-__global__ __launch_bounds__(256) void k_slot_tokens(Geom g, int* stok, long long n) {
+__global__ __launch_bounds__(256) void k_slot_tokens(Geom g, long long tok0, int* stok, long long n) {
     long long s = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (s < n) stok[s] = s < g.Nslot ? (int)slot_token(g, s) : -1;
+    if (s < n) {
+        const long long t = s < g.Nslot ? slot_token(g, s) : -1;
+        stok[s] = t >= 0 ? (int)(tok0 + t) : -1;
+    }
 }
 
 // ------------------------------------------------------------ launchers ----
@@ -1081,40 +1084,49 @@ hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, 
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qact* q, hipStream_t st) {
-    const Geom& g = q->g;
-    if (q->core_mode == 1) {
-        PartialArgs pa{x, g, (int)q->Ci, (int)q->Kp, q->nblk, q->part};
+// One frame segment: its geometry, and the buffers advanced to its first slot
+// row and first cube row (whole 256-row tiles of the step-major layouts).
+static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, int x_bf16, dq_qact* q,
+                                          const dq_segment& sg, hipStream_t st) {
+    const Geom& g = sg.g;
+    const size_t nks = (size_t)(q->Kp / 128);
+    uint8_t* const cq = q->cq + (size_t)(sg.krow0 / 256) * nks * 32768;
+    uint8_t* const cs = q->cs + (size_t)(sg.krow0 / 256) * nks * 1024;
+    float* const coref = q->coref ? q->coref + sg.krow0 * q->Kp : nullptr;
+    if (sg.core_mode == 1) {
+        // (the partial-sum pass finds tokens from the segment's own grid)
+        const void* xs = (const char*)x + (size_t)sg.tok0 * (size_t)q->Ci * (x_bf16 ? 2 : 4);
+        PartialArgs pa{xs, g, (int)q->Ci, (int)q->Kp, sg.nblk, q->part};
         const int ept = x_bf16 ? 8 : 4;                // channels per thread (16-byte loads)
-        dim3 grid((unsigned)(g.K * q->nblk), (unsigned)((q->Ci + 256 * ept - 1) / (256 * ept)));
+        dim3 grid((unsigned)(g.K * sg.nblk), (unsigned)((q->Ci + 256 * ept - 1) / (256 * ept)));
         if (x_bf16) k_core_partial<uint16_t><<<grid, 256, 0, st>>>(pa);
         else k_core_partial<float><<<grid, 256, 0, st>>>(pa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        CombineArgs ca{g, (int)q->Ci, (int)q->Kp, q->nblk, q->part, q->coref, q->cq, q->cs};
+        CombineArgs ca{g, (int)q->Ci, (int)q->Kp, sg.nblk, q->part, coref, cq, cs};
         dim3 grid2((unsigned)g.K, (unsigned)((q->Ci + 255) / 256));
         k_core_combine<<<grid2, 256, 0, st>>>(ca);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     QuantArgs a{};
-    a.x = x;
+    a.x = x;                                           // rows by token number, through the slot table
     a.g = g;
     a.Ci = (int)q->Ci;
     a.Kp = (int)q->Kp;
     a.rp = q->rp;
-    a.core_mode = q->core_mode;
-    a.dq = q->dq;
-    a.ds = q->ds;
-    a.cq = q->cq;
-    a.cs = q->cs;
-    a.u = q->u;
+    a.core_mode = sg.core_mode;
+    a.dq = q->dq + (size_t)(sg.row0 / 256) * nks * 16384;
+    a.ds = q->ds + (size_t)(sg.row0 / 256) * nks * 1024;
+    a.cq = cq;
+    a.cs = cs;
+    a.u = q->u + sg.row0 * q->rp;
     a.l1t = w->l1t;
-    a.coref = q->coref;
+    a.coref = coref;
     a.zero = q->zero;
-    a.stok = q->stok;
+    a.stok = q->stok + sg.row0;
     const long long cpb = QROWS / g.S;
-    a.nblocks = q->core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;
+    a.nblocks = sg.core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
@@ -1153,8 +1165,16 @@ hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qa
     return hipGetLastError();
 }
 
-hipError_t launch_slot_tokens(const Geom& g, int* stok, int64_t n, hipStream_t st) {
-    k_slot_tokens<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, stok, n);
+hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qact* q, hipStream_t st) {
+    for (int i = 0; i < q->nseg; ++i) {
+        hipError_t e = launch_quantize_segment(w, x, x_bf16, q, q->seg[i], st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_slot_tokens(const Geom& g, int64_t tok0, int* stok, int64_t n, hipStream_t st) {
+    k_slot_tokens<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, tok0, stok, n);
     return hipGetLastError();
 }
 
