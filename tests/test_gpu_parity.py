@@ -184,6 +184,7 @@ EDGE = [
     (21, 4, 6, (4, 1, 4), 64, 64, 16, "bf16"),     # the pages' small tile t4 h1 w4 on 21 frames
     (21, 4, 16, (4, 2, 8), 64, 64, 16, "bf16"),    # the pages' large tile t4 h2 w8
     (5, 6, 8, (2, 2, 2), 256, 256, 32, "bf16"),    # last frame alone: second frame segment at row 256
+    (4, 6, 10, (2, 2, 2), 128, 96, 16, "f32"),     # fp32 input, 8-token cubes (eight lanes per group)
     (9, 8, 16, (4, 2, 4), 256, 512, 32, "bf16"),   # second frame segment after four tiles of 32-token cubes
 ]
 

@@ -144,6 +144,32 @@ __device__ __forceinline__ void qload8(const uint8_t* buf, int r, int gc, int qq
     }
 }
 
+// channels 4 e .. 4 e + 3 (e < 8) of group gc of row r: raw bits (bf16: an
+// 8-byte half of a piece; fp32: a whole piece), and as fp32 OR-ed with sgn
+template <typename XT>
+__device__ __forceinline__ uint4 qraw4(const uint8_t* buf, int r, int gc, int e) {
+    if constexpr (sizeof(XT) == 2) {
+        const uint2 w = *(const uint2*)(buf + qoff(r, 4 * gc + (e >> 1)) + 8 * (e & 1));
+        return make_uint4(w.x, w.y, 0u, 0u);
+    } else {
+        return *(const uint4*)(buf + qoff(r, 8 * gc + e));
+    }
+}
+template <typename XT>
+__device__ __forceinline__ void qconv4(uint4 q, uint32_t sgn, float* v) {
+    if constexpr (sizeof(XT) == 2) {
+        v[0] = __uint_as_float((q.x << 16) | sgn);
+        v[1] = __uint_as_float((q.x & 0xffff0000u) | sgn);
+        v[2] = __uint_as_float((q.y << 16) | sgn);
+        v[3] = __uint_as_float((q.y & 0xffff0000u) | sgn);
+    } else {
+        v[0] = __uint_as_float(q.x | sgn);
+        v[1] = __uint_as_float(q.y | sgn);
+        v[2] = __uint_as_float(q.z | sgn);
+        v[3] = __uint_as_float(q.w | sgn);
+    }
+}
+
 // Ring depth for sp chunks per barrier: at most (depth - sp) chunks of
 // copies outstanding (63, the vmcnt range), at most 150 KB of LDS, at most 8.
 constexpr int qnbuf(int stage, int dmaw, int sp) {
@@ -181,6 +207,14 @@ __device__ __forceinline__ float row16_max(float v) {
     v = quad_max(v);
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+// maximum over an aligned group of 8 lanes (quad exchanges, then the
+// half-row mirror: lane i meets lane 7 - i)
+__device__ __forceinline__ float oct_max(float v) {
+    v = quad_max(v);
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
     return v;
 }
 
@@ -227,7 +261,10 @@ __device__ __forceinline__ float2 qconv2(uint2 d, uint32_t sgn) {
 //      deltas reading them (one barrier per period);
 //   3: one pass with one wave per cube, for blocks of 4 to 6 cubes (cubes
 //      of 10 to 16 tokens): the core by channel pairs, then the cube's
-//      (row, group, quarter) deltas, both on the same wave.
+//      (row, group, quarter) deltas, both on the same wave;
+//   4: one pass for cubes of exactly 8 tokens: one (cube, group, eighth)
+//      per thread (4 channels, 8 lanes per group), all 8 rows kept in
+//      registers, so the block's 8 cubes fill the group's 256 threads.
 template <typename XT, int NCT, int CM>
 __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantArgs a) {
     constexpr int CC = XTraits<XT>::CC;
@@ -252,7 +289,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     constexpr bool TWO = CM == 1 || CM == 2;         // (row, group, quarter) delta tasks over the whole group
     constexpr bool BAR2 = CM == 2;                   // phase 1 in the quantizers: two barriers per period
     constexpr int TCUBES = 8;                        // cubes per block in the two-phase forms
-    constexpr bool CORES = CM >= 2;                  // fp32 cores of the group's chunk in LDS
+    constexpr bool CORES = CM == 2 || CM == 3;       // fp32 cores of the group's chunk in LDS
     __shared__ float core_s[CORES ? SP : 1][CORES ? TCUBES : 1][CC];
     __shared__ uint64_t pres_s[2][2];               // [group][buffer]: bit r = row r holds a token
 
@@ -870,6 +907,80 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
                 }
             }
+        } else if constexpr (CM == 4) {
+            // cubes of 8 rows, whole in the block (64 of its slots, one
+            // 256-row tile of the outputs): one (cube, group, eighth) per thread
+            for (int t = qtid; t < B.ncores * NGC * 8; t += 256) {
+                const int e = t & 7, pr = t >> 3;
+                const int cr = pr / NGC, gc = pr - cr * NGC;
+                const long long G = (c0 >> 5) + gc;
+                if (G * 32 >= a.Ci) continue;                  // the same for the 8 lanes
+                const int rb = cr * 8, pm = meta_s[qgrp][mb][cr].z;
+                uint4 raw[8];
+                float xr[8][4], core[4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) raw[j] = qraw4<XT>(buf, rb + j, gc, e);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qconv4<XT>(raw[j], ((pm >> j) & 1) ? 0u : 0x80000000u, xr[j]);
+                // fp32 sum of the present rows in slot order (pad rows read as
+                // -0.0 and drop out exactly), then the division
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    core[q] = -0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) core[q] += xr[j][q];
+                }
+                const int cnt = meta_s[qgrp][mb][cr].w;
+                if ((cnt & (cnt - 1)) == 0) {                  // exact power-of-two scaling
+                    const float rc = 1.0f / (float)cnt;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) core[q] *= rc;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) core[q] = __fdiv_rn(core[q], (float)cnt);
+                }
+                const int kt = (int)(B.k_first & 255) + cr;    // the block's cubes share one 256-cube tile
+                {
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fabsf(core[q]));
+                    const int ex = mx_exp_fp8(oct_max(amax));
+                    const float sc = pow2f(ex);
+                    v2s z = {0, 0};
+                    const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, core[0], core[1], sc, false);
+                    const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, core[2], core[3], sc, true);
+                    *(uint32_t*)(cq_t + toff_fp8(kt, (int)(G >> 2), 2 * (int)(G & 3) + (e >> 2)) + 4 * (e & 3)) =
+                        __builtin_bit_cast(uint32_t, cd);
+                    if (e == 0) cs_t[toff_scale(kt, (int)G)] = (uint8_t)(ex + 127);
+                }
+                // deltas of the 8 rows (pad rows too: never read back as a
+                // token's); lane e writes row e's scale code
+                const int rt0 = (int)(B.slot0 & 255) + rb;     // the block's rows share one 256-row tile
+                float am[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    am[j] = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        xr[j][q] = xr[j][q] - core[q];
+                        am[j] = fmaxf(am[j], fabsf(xr[j][q]));
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) am[j] = oct_max(am[j]);
+                int exs = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int ex = mx_exp_fp4(am[j]);
+                    const float sc = pow2f(ex);
+                    uint32_t w = 0u;
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][0], xr[j][1], sc, 0);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][2], xr[j][3], sc, 1);
+                    *(uint16_t*)(dq_t + toff_fp4(rt0 + j, (int)G) + 2 * e) = (uint16_t)w;
+                    exs = e == j ? ex : exs;
+                }
+                ds_t[toff_scale(rt0 + e, (int)G)] = (uint8_t)(exs + 127);
+            }
         } else {
             for (int t = qtid; t < ntask; t += 256) {
                 if (full) task(t, std::true_type{});
@@ -1133,18 +1244,20 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
     const unsigned blocks = (unsigned)std::min<long long>(a.nblocks, cus);   // persistent: one workgroup per CU
     const int nct = q->rp / 32;
     // one-pass quantizer for blocks of 7 or more cubes (a thread per (cube,
-    // group, quarter)); a wave per cube for blocks of 4 to 6; two phases for
-    // blocks of at most 3 and for cubes of more than 64 tokens (measured on
-    // the 720p FFN layers: 8 cubes per block one-pass 0.43 ms, two-phase
-    // 0.45, wave per cube 0.48; 4 cubes per block 0.79, 0.46, 0.41)
-    const int cm = a.core_mode == 1 ? 1 : (cpb <= 3 ? 2 : (cpb <= 6 ? 3 : 0));
+    // group, quarter)), with eighths instead of quarters for 8-token cubes;
+    // a wave per cube for blocks of 4 to 6; two phases for blocks of at most
+    // 3 and for cubes of more than 64 tokens (measured on the 720p FFN
+    // layers: 8 cubes per block one-pass 0.43-0.48 ms, eighths 0.35,
+    // two-phase 0.45, wave per cube 0.48; 4 cubes per block 0.79, 0.46, 0.41)
+    const int cm = a.core_mode == 1 ? 1 : (g.S == 8 ? 4 : (cpb <= 3 ? 2 : (cpb <= 6 ? 3 : 0)));
     auto go = [&](auto XT_, auto NCT_) {
         using XT = decltype(XT_);
         constexpr int THREADS = QCfg<XT, decltype(NCT_)::value>::THREADS;
         if (cm == 0) k_quantize<XT, decltype(NCT_)::value, 0><<<blocks, THREADS, 0, st>>>(a);
         else if (cm == 1) k_quantize<XT, decltype(NCT_)::value, 1><<<blocks, THREADS, 0, st>>>(a);
         else if (cm == 2) k_quantize<XT, decltype(NCT_)::value, 2><<<blocks, THREADS, 0, st>>>(a);
-        else k_quantize<XT, decltype(NCT_)::value, 3><<<blocks, THREADS, 0, st>>>(a);
+        else if (cm == 3) k_quantize<XT, decltype(NCT_)::value, 3><<<blocks, THREADS, 0, st>>>(a);
+        else k_quantize<XT, decltype(NCT_)::value, 4><<<blocks, THREADS, 0, st>>>(a);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
