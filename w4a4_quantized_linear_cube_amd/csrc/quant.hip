@@ -506,13 +506,64 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             // thread, 16 lanes per 32-channel group.  (CM 1 reads the cores
             // from the earlier pass in phase 2 and has no phase 1.)
             if constexpr (CM == 2) {
-                const int ntask = B.ncores * (CC / 2);     // a multiple of 16: groups stay whole
                 const uint64_t pres = pres_s[qgrp][mb];
                 // the second group's tasks start at its third wave, so the two
                 // groups' first tasks (all of them when a block has one cube)
                 // run on different SIMDs (waves go round-robin over the four)
                 const int tq = (qtid + 128 * qgrp) & 255;
-                for (int t = tq; have && t < ntask; t += 256) {
+                // blocks of one cube: one (cube, channel) per thread, 32 lanes
+                // per group (the sums are chains in slot order, so a channel
+                // is the finest split; pairs would keep one wave per group
+                // busy).  With more cubes, pairs (fewer instructions per
+                // channel) already spread over the SIMDs.
+                const int nsingle = have && B.ncores * CC <= 128 ? B.ncores * CC : 0;
+                for (int t = tq; t < nsingle; t += 256) {
+                    const int cr = t / CC, ch = t - cr * CC;
+                    if (c0 + ch >= a.Ci) continue;             // the same for the group's 32 lanes
+                    const long long k = B.k_first + cr;
+                    const int rb = cr * g.S, re = rb + g.S, cnt = meta_s[qgrp][mb][cr].w;
+                    // fp32 sum of the present rows in slot order (pad rows read as
+                    // -0.0 and drop out exactly); sixteen rows' loads in flight
+                    const uint8_t* const pc = buf + (ch % EPC) * (int)sizeof(XT);
+                    const int pch = ch / EPC;
+                    auto raw1 = [&](int r) -> uint32_t {
+                        if constexpr (sizeof(XT) == 2) return (uint32_t)*(const uint16_t*)(pc + qoff(r, pch)) << 16;
+                        else return *(const uint32_t*)(pc + qoff(r, pch));
+                    };
+                    float s0 = -0.0f;
+                    int r = rb;
+                    // (a cube with all its tokens needs no pad-row masks)
+                    const uint32_t full = cnt == g.S ? 0xffffffffu : 0u;
+                    for (; r + 16 <= re; r += 16) {
+                        uint32_t raw[16];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) raw[j] = raw1(r + j);
+                        __builtin_amdgcn_sched_barrier(0);     // all sixteen reads issued before the first use
+                        if (full) {
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) s0 += __uint_as_float(raw[j]);
+                        } else {
+                            const uint32_t absent = ~(uint32_t)(pres >> r);   // bit j: row r + j has no token
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) s0 += __uint_as_float(raw[j] | ((absent << (31 - j)) & 0x80000000u));
+                        }
+                    }
+                    for (; r < re; ++r) s0 += __uint_as_float(raw1(r) | (((pres >> r) & 1) ? 0u : 0x80000000u));
+                    if ((cnt & (cnt - 1)) == 0) s0 *= 1.0f / (float)cnt;   // exact power-of-two scaling
+                    else s0 = __fdiv_rn(s0, (float)cnt);
+                    float amax = row16_max(fabsf(s0));
+                    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, amax), 0x401F)));   // lane ^ 16
+                    const int ex = mx_exp_fp8(amax);
+                    v2s z = {0, 0};
+                    const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, 0.0f, pow2f(ex), false);
+                    const int gch = c0 + ch;                       // channel within the row
+                    *(uint8_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) =
+                        (uint8_t)__builtin_bit_cast(uint32_t, cd);
+                    if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
+                    cs_[cr][ch] = s0;
+                }
+                const int ntask = have && !nsingle ? B.ncores * (CC / 2) : 0;   // a multiple of 16: groups stay whole
+                for (int t = tq; t < ntask; t += 256) {
                     const int cr = t / (CC / 2), ch = 2 * (t - cr * (CC / 2));
                     if (c0 + ch >= a.Ci) continue;             // the same for the group's 16 lanes
                     const long long k = B.k_first + cr;
@@ -521,17 +572,27 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     // -0.0 and drop out exactly); sixteen rows' loads in flight
                     float s0 = -0.0f, s1 = -0.0f;
                     int r = rb;
+                    const uint32_t full = cnt == g.S ? 0xffffffffu : 0u;   // all tokens: no pad-row masks
                     for (; r + 16 <= re; r += 16) {
                         uint2 raw[16];
 #pragma unroll
                         for (int j = 0; j < 16; ++j) raw[j] = qraw2<XT>(buf, r + j, ch);
                         __builtin_amdgcn_sched_barrier(0);     // all sixteen reads issued before the first use
-                        const uint32_t absent = ~(uint32_t)(pres >> r);   // bit j: row r + j has no token
+                        if (full) {
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const float2 v = qconv2<XT>(raw[j], (absent << (31 - j)) & 0x80000000u);
-                            s0 += v.x;
-                            s1 += v.y;
+                            for (int j = 0; j < 16; ++j) {
+                                const float2 v = qconv2<XT>(raw[j], 0u);
+                                s0 += v.x;
+                                s1 += v.y;
+                            }
+                        } else {
+                            const uint32_t absent = ~(uint32_t)(pres >> r);   // bit j: row r + j has no token
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) {
+                                const float2 v = qconv2<XT>(raw[j], (absent << (31 - j)) & 0x80000000u);
+                                s0 += v.x;
+                                s1 += v.y;
+                            }
                         }
                     }
                     if (r + 8 <= re) {                     // cubes of 8 to 15 rows (or the rest of one)
@@ -816,17 +877,28 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 const int ch = 2 * lane;
                 float s0 = -0.0f, s1 = -0.0f;
                 int r = 0;
+                const int cnt = meta_s[qgrp][mb][cr].w;
+                const uint32_t full = cnt == S ? 0xffffffffu : 0u;   // all tokens: no pad-row masks
                 for (; r + 8 <= S; r += 8) {
                     uint2 raw[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) raw[j] = qraw2<XT>(buf, rb + r + j, ch);
                     __builtin_amdgcn_sched_barrier(0);
-                    const uint32_t absent = ~(uint32_t)(pres >> (rb + r));
+                    if (full) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float2 v = qconv2<XT>(raw[j], (absent << (31 - j)) & 0x80000000u);
-                        s0 += v.x;
-                        s1 += v.y;
+                        for (int j = 0; j < 8; ++j) {
+                            const float2 v = qconv2<XT>(raw[j], 0u);
+                            s0 += v.x;
+                            s1 += v.y;
+                        }
+                    } else {
+                        const uint32_t absent = ~(uint32_t)(pres >> (rb + r));
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float2 v = qconv2<XT>(raw[j], (absent << (31 - j)) & 0x80000000u);
+                            s0 += v.x;
+                            s1 += v.y;
+                        }
                     }
                 }
                 for (; r < S; ++r) {
@@ -834,7 +906,6 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     s0 += v.x;
                     s1 += v.y;
                 }
-                const int cnt = meta_s[qgrp][mb][cr].w;
                 if ((cnt & (cnt - 1)) == 0) {              // exact power-of-two scaling
                     const float rc = 1.0f / (float)cnt;
                     s0 *= rc;
