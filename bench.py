@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--schedule", action="store_true",
                     help="the timestep-aware cube schedule (4x1x4 early, 4x2x8 after) on the config's layer")
     ap.add_argument("--denoise-steps", type=int, default=10, help="denoising steps of one --schedule run")
+    ap.add_argument("--core-group", type=int, default=32, choices=(32, 64),
+                    help="channels per FP8 exponent of the cores (64: the pages' group size)")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
@@ -132,7 +134,7 @@ def sweep(args, cfg, dq, torch):
     y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     for cube in cfg.cubes:
-        qa = dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + tuple(cube))
+        qa = dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + tuple(cube), core_group=args.core_group)
         timing = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
         print(json.dumps(shape_record(cfg, cube, *timing)), flush=True)
         torch.cuda.synchronize()
@@ -172,7 +174,7 @@ def schedule(args, cfg, dq, torch):
                                     n_outliers=cfg.n_outliers, device="cuda")
     y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
-    qas = [dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + s) for s in SCHEDULE_SHAPES]
+    qas = [dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + s, core_group=args.core_group) for s in SCHEDULE_SHAPES]
     recs = []
     for s, qa in zip(SCHEDULE_SHAPES, qas):
         recs.append(shape_record(cfg, s, *time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)))
@@ -249,7 +251,7 @@ def main():
 
     wt = synth.config_weight(cfg)
     weights = dq.dq_prepare_weights(wt, r, seed=cfg.w_seed, device=0)
-    qa = dq.dq_qact_create(weights, (T, H, W) + cube)
+    qa = dq.dq_qact_create(weights, (T, H, W) + cube, core_group=args.core_group)
     x = synth.make_activation(T, H, W, Ci, seed=xseed, dtype=cfg.dtype, n_outliers=cfg.n_outliers, device="cuda")
     y = torch.empty(N, Co, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -306,6 +308,7 @@ def main():
             "workload": f"{cfg.name}: X {N}x{Ci} ({T}x{H}x{W} tokens) {cfg.dtype} -> Y {N}x{Co} fp32, "
                         f"cube {t_}x{h_}x{w_}, rank {r}",
             "tokens": N, "Ci": Ci, "Co": Co, "cube": list(cube), "rank": r, "cubes": K,
+            "core_group": args.core_group,
         },
         "pct_fp4_peak_step": round(100 * dense_flops / (ms_step * 1e-3) / PEAK_FP4, 2),
         "forward": {

@@ -15,7 +15,8 @@ import numpy as np
 from . import cubes, mx
 
 
-def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray, cube_ids=None, tokens=None) -> dict:
+def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray, cube_ids=None, tokens=None,
+                        core_group: int = 32) -> dict:
     """What the activation pass produces, for the given cubes (all by default).
 
     Cores are always formed from every token of a cube; deltas and U are
@@ -24,7 +25,8 @@ def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray,
 
     Returns a dict with
       cube_ids [k]; tokens [n] (ascending);
-      core [k, Ci] fp32; core_codes [k, Ci] and core_scales [k, Ci/32] (FP8);
+      core [k, Ci] fp32; core_codes [k, Ci] and core_scales [k, Ci/32] (FP8,
+      one exponent per core_group channels: 32, or the pages' 64);
       delta [n, Ci] fp32; delta_codes [n, Ci/2] packed and delta_scales
       [n, Ci/32] (FP4); U [n, r] bf16 bits.
     """
@@ -41,7 +43,7 @@ def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray,
     row_of_cube = np.full(g.K, -1, dtype=np.int64)
     row_of_cube[ids] = np.arange(len(ids))
     delta = cubes.cube_delta(x32, core, g, tokens, row_of_cube)
-    core_codes, core_scales = mx.mx_quantize(core, "fp8")
+    core_codes, core_scales = mx.mx_quantize(core, "fp8", core_group)
     d_codes, d_scales = mx.mx_quantize(delta, "fp4")
     out = dict(cube_ids=ids, tokens=tokens, row_of_cube=row_of_cube, core=core,
                core_codes=core_codes, core_scales=core_scales, delta=delta,

@@ -77,21 +77,27 @@ def round_to_grid(v: np.ndarray, mags: np.ndarray) -> np.ndarray:
     return idx.astype(np.uint8)
 
 
-def mx_quantize(x32: np.ndarray, fmt: str):
+def mx_quantize(x32: np.ndarray, fmt: str, scale_group: int = GROUP):
     """MX-quantize fp32 values along the last axis in groups of 32.
 
     Returns (codes uint8 [..., C] one code per element, scale codes uint8
     [..., C/32]).  Each group: e = mx_exponent(max|x|), element code =
     round_to_grid(x / 2^e) with the sign bit copied from x.
+
+    scale_group = 64 takes e from the maximum over each 64 consecutive
+    channels (the pages' per-group FP8 core, group size 64: 损失函数/训练策略)
+    and stores it as the scale code of both of its 32-channel blocks.
     """
     mags, qmax, sign_shift = _FORMATS[fmt]
     x32 = np.asarray(x32, dtype=np.float32)
     C = x32.shape[-1]
     if C % GROUP:
         raise ValueError("channel count must be a multiple of 32")
+    if scale_group not in (GROUP, 2 * GROUP) or C % scale_group:
+        raise ValueError("scale group must be 32 or 64 and divide the channel count")
     g = x32.reshape(x32.shape[:-1] + (C // GROUP, GROUP))
-    amax = np.abs(g).max(axis=-1)
-    e = mx_exponent(amax, qmax)
+    gs = x32.reshape(x32.shape[:-1] + (C // scale_group, scale_group))
+    e = np.repeat(mx_exponent(np.abs(gs).max(axis=-1), qmax), scale_group // GROUP, axis=-1)
     v = g.astype(np.float64) * np.ldexp(1.0, -e)[..., None]     # exact
     idx = round_to_grid(v, mags)
     codes = idx | (np.signbit(g).astype(np.uint8) << sign_shift)

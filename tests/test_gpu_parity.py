@@ -110,7 +110,7 @@ def _check_y(y, yo, bound=None):
     return err, row
 
 
-def _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed, wseed, svd="oracle", n_out=4, w_out=2):
+def _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed, wseed, svd="oracle", n_out=4, w_out=2, core_group=32):
     x = synth.make_activation(T, H, W, Ci, seed=xseed, dtype=dtype, n_outliers=n_out)
     wt = synth.make_weight(Ci, Co, seed=wseed, dtype=dtype, outlier_rows=w_out)
     xf, wf = synth.to_f32_numpy(x), synth.to_f32_numpy(wt)
@@ -119,17 +119,19 @@ def _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed, wseed, svd="oracle", 
     else:
         l1, l2 = _random_factors(Ci, Co, rank, wseed + 1)
     weights = dqm.dq_prepare_weights_lowrank(wt, l1 if rank else None, l2 if rank else None, device=0)
-    qa = dqm.dq_qact_create(weights, (T, H, W) + tuple(cube))
+    qa = dqm.dq_qact_create(weights, (T, H, W) + tuple(cube), core_group=core_group)
     xd = x.to(DEV)
     y = torch.full((T * H * W, Co), float("nan"), dtype=torch.float32, device=DEV)
     dqm.dq_linear(weights, xd, qa, y)
     torch.cuda.synchronize()
-    return dict(x=xf, wt=wf, l1=l1, l2=l2, weights=weights, qa=qa, y=y.cpu().numpy(), g=cubes.Geometry(T, H, W, *cube))
+    return dict(x=xf, wt=wf, l1=l1, l2=l2, weights=weights, qa=qa, y=y.cpu().numpy(), g=cubes.Geometry(T, H, W, *cube),
+                core_group=core_group)
 
 
 def _full_compare(dqm, L):
     got = dqm.dq_qact_export(L["qa"])
-    q = layer.quantize_activation(L["x"], L["g"], L["l1"] if L["l1"].shape[1] else None)
+    q = layer.quantize_activation(L["x"], L["g"], L["l1"] if L["l1"].shape[1] else None,
+                                  core_group=L.get("core_group", 32))
     assert np.array_equal(got["core_codes"], q["core_codes"]), "core codes"
     assert np.array_equal(got["core_scales"], q["core_scales"]), "core scales"
     assert np.array_equal(got["delta_scales"], q["delta_scales"]), "delta scales"
@@ -198,6 +200,43 @@ def test_edge_cases(dqm, case):
                n_out=min(4, Ci // 16))
     err, row = _full_compare(dqm, L)
     _say(f"edge {case}: rel err {err:.2e} worst row {row:.2e}")
+
+
+# group-64 cores (one FP8 exponent per 64 channels), through every form of
+# the activation pass: one-pass (4-token cubes), eighths (8), wave per cube
+# (16), two phases with channel pairs (32) and single channels (64), the
+# partial-sum pass (cubes of more than 64 tokens), one-token cubes
+CORE64 = [
+    (3, 7, 10, (1, 2, 2), 256, 256, 32, "bf16"),
+    (2, 5, 6, (1, 2, 2), 128, 64, 16, "f32"),
+    (4, 6, 10, (2, 2, 2), 256, 96, 16, "bf16"),
+    (3, 6, 8, (1, 4, 4), 128, 64, 16, "bf16"),
+    (3, 8, 8, (2, 4, 4), 128, 64, 16, "bf16"),
+    (5, 7, 9, (4, 4, 4), 192, 64, 16, "bf16"),
+    (5, 7, 9, (4, 4, 4), 128, 64, 16, "f32"),
+    (3, 9, 10, (3, 9, 10), 128, 48, 16, "bf16"),
+    (2, 6, 6, (1, 1, 1), 128, 64, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CORE64, ids=[f"{c[0]}x{c[1]}x{c[2]}_c{'x'.join(map(str, c[3]))}_ci{c[4]}_{c[7]}"
+                                              for c in CORE64])
+def test_core_group_64(dqm, case):
+    T, H, W, cube, Ci, Co, rank, dtype = case
+    _say(f"case core group 64 {case}")
+    L = _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed=T * 100 + Ci + 64, wseed=Co + 9,
+               n_out=min(4, Ci // 16), core_group=64)
+    err, row = _full_compare(dqm, L)
+    _say(f"core group 64 {case}: rel err {err:.2e} worst row {row:.2e}")
+
+
+def test_core_group_errors(dqm):
+    wt = synth.make_weight(96, 64, seed=3, dtype="f32")
+    weights = dqm.dq_prepare_weights_lowrank(wt, None, None)
+    with pytest.raises(dqm.DQError, match="DQ_ERR_SHAPE"):
+        dqm.dq_qact_create(weights, (2, 2, 2, 1, 1, 1), core_group=64)      # 64 does not divide Ci = 96
+    with pytest.raises(dqm.DQError, match="DQ_ERR_INVALID_ARG"):
+        dqm.dq_qact_create(weights, (2, 2, 2, 1, 1, 1), core_group=48)
 
 
 def test_wan1p3b_projection_full(dqm):

@@ -156,6 +156,41 @@ def test_mx_quantize_group_scale_and_zero():
     assert np.all(np.abs(deq[0, :32] - x[0, :32]) <= 2.0 ** -1)             # half the top spacing of 2^e * {4, 6}
 
 
+def test_mx_quantize_scale_group_64():
+    """One exponent per 64 channels (the pages' group-64 FP8 core), pinned by
+    properties of the definition: the exponent grows with the maximum, so the
+    shared scale code is the larger of the two 32-channel codes; the half that
+    sets it is coded exactly as with 32-channel groups; every element of the
+    other half takes the nearest FP8 value times the shared scale (brute force
+    over all 256 codes, ties to the even code); equal halves change nothing."""
+    rng = np.random.default_rng(64)
+    x = (rng.standard_normal((6, 256)) * np.exp(rng.uniform(-4, 4, (6, 256)))).astype(np.float32)
+    x[2, 64:128] *= 1e-3                                  # one half far below its partner
+    c32, s32 = mx.mx_quantize(x, "fp8")
+    c64, s64 = mx.mx_quantize(x, "fp8", 64)
+    pair = np.maximum(s32[:, 0::2], s32[:, 1::2])
+    assert np.array_equal(s64[:, 0::2], pair) and np.array_equal(s64[:, 1::2], pair)
+    assert np.any(s32 != s64)                             # the case is not degenerate
+    vals = np.array([mx.fp8_decode_magnitude(c & 0x7F) * (-1.0 if c & 0x80 else 1.0) for c in range(256)])
+    valid = np.isfinite(vals)
+    for r in range(x.shape[0]):
+        for b in range(x.shape[1] // 32):
+            blk = slice(32 * b, 32 * b + 32)
+            if s64[r, b] == s32[r, b]:
+                assert np.array_equal(c64[r, blk], c32[r, blk])
+            scale = 2.0 ** (int(s64[r, b]) - 127)
+            for i in range(32 * b, 32 * b + 32):
+                err = np.where(valid, np.abs(vals * scale - float(x[r, i])), np.inf)
+                best = np.flatnonzero(err == err.min())
+                assert int(c64[r, i]) in best, (r, i)
+                if len(best) > 1:                         # a tie: the even mantissa
+                    assert (int(c64[r, i]) & 1) == 0, (r, i)
+    same = np.tile(x[:, :32], (1, 2))                     # equal halves
+    assert np.array_equal(mx.mx_quantize(same, "fp8", 64)[0], mx.mx_quantize(same, "fp8")[0])
+    with pytest.raises(ValueError):
+        mx.mx_quantize(x[:, :96], "fp8", 64)
+
+
 def test_pack_nibble_order():
     codes = np.array([[1, 2, 3, 4, 0xF, 0x8]], dtype=np.uint8)
     assert list(mx.pack_fp4(codes)[0]) == [0x21, 0x43, 0x8F]

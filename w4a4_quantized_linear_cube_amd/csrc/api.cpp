@@ -312,10 +312,16 @@ dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2
 }
 
 dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
+    return dq_qact_create_ex(w, geom, 32, out);
+}
+
+dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, dq_qact** out) {
     g_last_error.clear();
     if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    if (core_group != 32 && core_group != 64) return fail(DQ_ERR_INVALID_ARG, "core_group must be 32 or 64");
+    if (w->Ci % core_group != 0) return fail(DQ_ERR_SHAPE, "core_group must divide Ci");
     const dq_geom& G = geom;
     if (G.T < 1 || G.H < 1 || G.W < 1) return fail(DQ_ERR_SHAPE, "T, H, W must be >= 1");
     if (G.t < 1 || G.t > G.T || G.h < 1 || G.h > G.H || G.w < 1 || G.w > G.W)
@@ -342,6 +348,7 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
     q->rp = w->rp;
     q->rank = w->rank;
     q->g = Geom{G.T, G.H, G.W, G.t, G.h, G.w, Tc, Hc, Wc, (int)S, (long long)N, (long long)K, (long long)Nslot};
+    q->core_group = core_group;
     // frame segments: whole frame groups, then the clipped last group (if any)
     const int T0 = G.T - G.T % G.t;                  // >= t, since t <= T
     const int segT[2] = {T0, G.T - T0}, segt[2] = {G.t, G.T - T0};

@@ -53,6 +53,7 @@ struct QuantArgs {
     const float* coref;       // [K][Kp] (core_mode 1)
     const uint8_t* zero;      // 256 zero bytes (source of absent rows and channels)
     const int* stok;          // [Nslot_pad] token of each slot, -1 for pad slots
+    int core_g64;             // cores: one exponent per 64 channels (the maximum of two 32-channel groups)
 };
 
 // LDS chunk layout: 16-byte piece c of row r at r QROWB + ((c ^ (r & 15)) << 4);
@@ -216,6 +217,21 @@ __device__ __forceinline__ float oct_max(float v) {
     v = quad_max(v);
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
     return v;
+}
+
+// The maximum of a 64-channel core group from those of its two 32-channel
+// halves, when their lanes are `d` apart in aligned blocks of 2 d lanes: the
+// half-row mirror (d = 4), the row mirror (d = 8), a swizzle (d = 16) or a
+// permute (d = 32).  Unchanged for 32-channel groups.
+template <int D>
+__device__ __forceinline__ float core_pair_max(float m, int g64) {
+    if (!g64) return m;
+    int o;
+    if constexpr (D == 4) o = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x141, 0xF, 0xF, false);
+    else if constexpr (D == 8) o = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x140, 0xF, 0xF, false);
+    else if constexpr (D == 16) o = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x401F);
+    else o = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32) << 2), __builtin_bit_cast(int, m));
+    return fmaxf(m, __builtin_bit_cast(float, o));
 }
 
 // channels ch, ch + 1 (ch even, chunk-relative) of row r as raw bits, and
@@ -553,7 +569,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     else s0 = __fdiv_rn(s0, (float)cnt);
                     float amax = row16_max(fabsf(s0));
                     amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, amax), 0x401F)));   // lane ^ 16
-                    const int ex = mx_exp_fp8(amax);
+                    const int ex = mx_exp_fp8(core_pair_max<32>(amax, a.core_g64));
                     v2s z = {0, 0};
                     const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, 0.0f, pow2f(ex), false);
                     const int gch = c0 + ch;                       // channel within the row
@@ -623,7 +639,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                         s1 = __fdiv_rn(s1, (float)cnt);
                     }
                     const float amax = row16_max(fmaxf(fabsf(s0), fabsf(s1)));
-                    const int ex = mx_exp_fp8(amax);
+                    const int ex = mx_exp_fp8(core_pair_max<16>(amax, a.core_g64));
                     v2s z = {0, 0};
                     const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false);
                     const int gch = c0 + ch;                       // channel within the row
@@ -768,7 +784,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 float amax = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(core[e]));
-                amax = quad_max(amax);
+                amax = core_pair_max<4>(quad_max(amax), a.core_g64);
                 const int ex = mx_exp_fp8(amax);
                 const float sc = pow2f(ex);
                 uint32_t d[2];
@@ -916,7 +932,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 }
                 {
                     const float amax = row16_max(fmaxf(fabsf(s0), fabsf(s1)));   // 16 lanes: one 32-channel group
-                    const int ex = mx_exp_fp8(amax);
+                    const int ex = mx_exp_fp8(core_pair_max<16>(amax, a.core_g64));
                     v2s z = {0, 0};
                     const uint16_t cd = (uint16_t)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false));
                     // (fp32 chunks have CC = 64 channels: lanes 32-63 store
@@ -1015,7 +1031,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     float amax = 0.0f;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fabsf(core[q]));
-                    const int ex = mx_exp_fp8(oct_max(amax));
+                    const int ex = mx_exp_fp8(core_pair_max<8>(oct_max(amax), a.core_g64));
                     const float sc = pow2f(ex);
                     v2s z = {0, 0};
                     const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, core[0], core[1], sc, false);
@@ -1154,6 +1170,7 @@ struct CombineArgs {
     float* coref;    // [K][Kp]
     uint8_t* cq;     // K_pad x Kp, step-major
     uint8_t* cs;     // K_pad x Kp/32, step-major
+    int core_g64;    // one exponent per 64 channels
 };
 
 // core = fl32(sum of the block partials in block order / count), then FP8 codes.
@@ -1192,6 +1209,9 @@ __global__ __launch_bounds__(256) void k_core_combine(CombineArgs a) {
             v[i] = tile[32 * j + i];
             amax = fmaxf(amax, fabsf(v[i]));
         }
+        if (a.core_g64)                                 // the other half of the 64-channel group
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(tile[32 * (j ^ 1) + i]));
         int e = mx_exp_fp8(amax);
         uint4 lo, hi;
         encode_fp8x32(v, pow2f(e), lo, hi);
@@ -1285,7 +1305,7 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
         else k_core_partial<float><<<grid, 256, 0, st>>>(pa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        CombineArgs ca{g, (int)q->Ci, (int)q->Kp, sg.nblk, q->part, coref, cq, cs};
+        CombineArgs ca{g, (int)q->Ci, (int)q->Kp, sg.nblk, q->part, coref, cq, cs, q->core_group == 64};
         dim3 grid2((unsigned)g.K, (unsigned)((q->Ci + 255) / 256));
         k_core_combine<<<grid2, 256, 0, st>>>(ca);
         e = hipGetLastError();
@@ -1307,6 +1327,7 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
     a.coref = coref;
     a.zero = q->zero;
     a.stok = q->stok + sg.row0;
+    a.core_g64 = q->core_group == 64;
     const long long cpb = QROWS / g.S;
     a.nblocks = sg.core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;
     int dev = 0, cus = 0;

@@ -23,7 +23,7 @@ STATUS = {0: "DQ_OK", 1: "DQ_ERR_INVALID_ARG", 2: "DQ_ERR_SHAPE", 3: "DQ_ERR_UNS
 # every entry point declared in include/dq.h
 EXPORTS = ("dq_last_error", "dq_status_str", "dq_lowrank_factors", "dq_prepare_weights_lowrank",
            "dq_prepare_weights", "dq_weights_destroy", "dq_weights_info", "dq_weights_export",
-           "dq_qact_create", "dq_qact_destroy", "dq_qact_info", "dq_quantize_act", "dq_linear_forward",
+           "dq_qact_create", "dq_qact_create_ex", "dq_qact_destroy", "dq_qact_info", "dq_quantize_act", "dq_linear_forward",
            "dq_core_term", "dq_delta_term", "dq_linear", "dq_qact_export")
 
 
@@ -62,6 +62,7 @@ def load():
         "dq_weights_info": ([P, P, P, P, P], ctypes.c_int),
         "dq_weights_export": ([P, P, P, P, P, P], ctypes.c_int),
         "dq_qact_create": ([P, Geom, PP], ctypes.c_int),
+        "dq_qact_create_ex": ([P, Geom, I32, PP], ctypes.c_int),
         "dq_qact_destroy": ([P], None),
         "dq_qact_info": ([P, P, P, P], ctypes.c_int),
         "dq_quantize_act": ([P, P, ctypes.c_int, P, P], ctypes.c_int),
@@ -187,9 +188,14 @@ def dq_weights_export(w: Weights) -> dict:
     return out
 
 
-def dq_qact_create(w: Weights, geom: Sequence[int]) -> QAct:
+def dq_qact_create(w: Weights, geom: Sequence[int], core_group: int = 32) -> QAct:
+    """Workspace for a (T, H, W, t, h, w) geometry; core_group 64 gives the
+    cores one scale per 64 channels (dq_qact_create_ex)."""
     h = ctypes.c_void_p()
-    _check(load().dq_qact_create(w.handle, Geom(*geom), ctypes.byref(h)), "dq_qact_create")
+    if core_group == 32:
+        _check(load().dq_qact_create(w.handle, Geom(*geom), ctypes.byref(h)), "dq_qact_create")
+    else:
+        _check(load().dq_qact_create_ex(w.handle, Geom(*geom), core_group, ctypes.byref(h)), "dq_qact_create_ex")
     return QAct(h, w, geom)
 
 
