@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--denoise-steps", type=int, default=10, help="denoising steps of one --schedule run")
     ap.add_argument("--core-group", type=int, default=32, choices=(32, 64),
                     help="channels per FP8 exponent of the cores (64: the pages' group size)")
+    ap.add_argument("--core-bits", type=int, default=8, choices=(8, 4),
+                    help="MX-FP8 cores (the pages' choice) or MX-FP4 cores (the 4-bit point of their ablation)")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
@@ -96,7 +98,7 @@ def time_steps(dq, weights, x, qa, y, stream, steps, warmup):
     return ms_step, q_ms, c_ms, d_ms
 
 
-def work(cfg, cube):
+def work(cfg, cube, core_bits=8):
     """Sizes of the method's work for a cube shape: cubes, slots, flops of
     each GEMM, the activation pass's algorithmic bytes."""
     t_, h_, w_ = cube
@@ -116,12 +118,12 @@ def work(cfg, cube):
         "K": K, "S": S, "Nslot": Nslot,
         "dense": 2.0 * N * Ci * Co,
         "fp4": 2.0 * Nslot * Ci * Co,        # delta term, one row per slot (pad slots of clipped cubes included)
-        "fp8": 2.0 * K * Ci * Co,            # core term, one row per cube
+        "fp8": 2.0 * K * Ci * Co,            # core term, one row per cube (FP8, or FP4 cores)
         "bf16": 2.0 * N * r * (Ci + Co),     # low-rank branch
         # X, delta codes and scales (not stored for one-token cubes: all
         # zero), core codes and scales, U
         "quant_bytes": xreads * Ci * xbytes + (0 if S == 1 else N * Ci * (0.5 + 1 / 32))
-                       + K * Ci * (1 + 1 / 32) + 2 * N * r,
+                       + K * Ci * (core_bits / 8 + 1 / 32) + 2 * N * r,
     }
 
 
@@ -134,24 +136,25 @@ def sweep(args, cfg, dq, torch):
     y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     for cube in cfg.cubes:
-        qa = dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + tuple(cube), core_group=args.core_group)
+        qa = dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + tuple(cube), core_group=args.core_group, core_bits=args.core_bits)
         timing = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
-        print(json.dumps(shape_record(cfg, cube, *timing)), flush=True)
+        print(json.dumps(shape_record(cfg, cube, *timing, core_bits=args.core_bits)), flush=True)
         torch.cuda.synchronize()
         del qa                      # frees the cube shape's buffers
 
 
-def shape_record(cfg, cube, ms, q_ms, c_ms, d_ms):
+def shape_record(cfg, cube, ms, q_ms, c_ms, d_ms, core_bits=8):
     """One cube shape's step time, split by phase, with its rates."""
-    wk = work(cfg, cube)
-    one = wk["S"] == 1          # one-token cubes: the delta term is one FP8 GEMM over the cubes
+    wk = work(cfg, cube, core_bits)
+    one = wk["S"] == 1          # one-token cubes: the delta term is one GEMM over the cubes (FP8 or FP4 cores)
+    ck = f"fp{core_bits}_tflops"
     return {
         "config": cfg.name, "cube": list(cube), "cubes": wk["K"], "slots": wk["Nslot"],
         "ms_per_step": round(ms, 4), "effective_tops": round(wk["dense"] / (ms * 1e-3) / 1e12, 2),
         "quantize": {"ms": round(q_ms, 4), "GBps": round(wk["quant_bytes"] / (q_ms * 1e-3) / 1e9, 1)},
         "core_term": {"ms": round(c_ms, 4)} if one else
-                     {"ms": round(c_ms, 4), "fp8_tflops": round(wk["fp8"] / (c_ms * 1e-3) / 1e12, 1)},
-        "delta_term": {"ms": round(d_ms, 4), "fp8_tflops": round(wk["fp8"] / (d_ms * 1e-3) / 1e12, 1)} if one else
+                     {"ms": round(c_ms, 4), ck: round(wk["fp8"] / (c_ms * 1e-3) / 1e12, 1)},
+        "delta_term": {"ms": round(d_ms, 4), ck: round(wk["fp8"] / (d_ms * 1e-3) / 1e12, 1)} if one else
                       {"ms": round(d_ms, 4), "fp4_tflops": round(wk["fp4"] / (d_ms * 1e-3) / 1e12, 1)},
     }
 
@@ -174,10 +177,11 @@ def schedule(args, cfg, dq, torch):
                                     n_outliers=cfg.n_outliers, device="cuda")
     y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
-    qas = [dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + s, core_group=args.core_group) for s in SCHEDULE_SHAPES]
+    qas = [dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + s, core_group=args.core_group, core_bits=args.core_bits) for s in SCHEDULE_SHAPES]
     recs = []
     for s, qa in zip(SCHEDULE_SHAPES, qas):
-        recs.append(shape_record(cfg, s, *time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)))
+        recs.append(shape_record(cfg, s, *time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup),
+                                 core_bits=args.core_bits))
         print(json.dumps(recs[-1]), flush=True)
     n = args.denoise_steps
     n_early = max(1, min(n, round(SCHEDULE_EARLY * n)))
@@ -251,7 +255,7 @@ def main():
 
     wt = synth.config_weight(cfg)
     weights = dq.dq_prepare_weights(wt, r, seed=cfg.w_seed, device=0)
-    qa = dq.dq_qact_create(weights, (T, H, W) + cube, core_group=args.core_group)
+    qa = dq.dq_qact_create(weights, (T, H, W) + cube, core_group=args.core_group, core_bits=args.core_bits)
     x = synth.make_activation(T, H, W, Ci, seed=xseed, dtype=cfg.dtype, n_outliers=cfg.n_outliers, device="cuda")
     y = torch.empty(N, Co, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -259,7 +263,7 @@ def main():
 
     # derived sizes of the method's work
     t_, h_, w_ = cube
-    wk = work(cfg, cube)
+    wk = work(cfg, cube, args.core_bits)
     K, S = wk["K"], wk["S"]
     dense_flops, f_fp4, f_fp8, f_bf16, quant_bytes = wk["dense"], wk["fp4"], wk["fp8"], wk["bf16"], wk["quant_bytes"]
 
@@ -302,13 +306,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 (deltas, R) + mxfp8 (cores) + bf16 (low rank), fp32 accumulate",
+        "dtype": f"mxfp4 (deltas, R) + mxfp{args.core_bits} (cores) + bf16 (low rank), fp32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: X {N}x{Ci} ({T}x{H}x{W} tokens) {cfg.dtype} -> Y {N}x{Co} fp32, "
                         f"cube {t_}x{h_}x{w_}, rank {r}",
             "tokens": N, "Ci": Ci, "Co": Co, "cube": list(cube), "rank": r, "cubes": K,
-            "core_group": args.core_group,
+            "core_group": args.core_group, "core_bits": args.core_bits,
         },
         "pct_fp4_peak_step": round(100 * dense_flops / (ms_step * 1e-3) / PEAK_FP4, 2),
         "forward": {
@@ -326,8 +330,8 @@ def main():
         },
         "core_term": {
             "ms": round(c_ms, 4),
-            "fp8_tflops": round(f_fp8 / (c_ms * 1e-3) / 1e12, 2),
-            "pct_fp8_peak": round(100 * f_fp8 / (c_ms * 1e-3) / PEAK_FP8, 2),
+            f"fp{args.core_bits}_tflops": round(f_fp8 / (c_ms * 1e-3) / 1e12, 2),
+            f"pct_fp{args.core_bits}_peak": round(100 * f_fp8 / (c_ms * 1e-3) / (PEAK_FP8 if args.core_bits == 8 else PEAK_FP4), 2),
         },
         "roofline": {
             "kernel": "delta GEMM (dq_delta_term: FP4 x FP4 scaled MFMA over the slots; low-rank branch, "

@@ -123,15 +123,21 @@ dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2
  * DQ_ERR_SHAPE for an invalid geometry or size overflow. */
 dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out);
 
-/* dq_qact_create with a choice of the cores' scale group: core_group = 32
- * (one E8M0 scale per 32-channel MX block, as dq_qact_create) or 64 (the
- * pages' per-group FP8 core with group size 64, DeltaQuant notes
- * 损失函数/训练策略: one exponent from the maximum over 64 consecutive
- * channels, stored as the scale code of both of its 32-channel blocks; the
- * GEMMs read the same layout).  Deltas keep groups of 32.  Errors:
- * DQ_ERR_INVALID_ARG for another core_group, DQ_ERR_SHAPE when core_group does
- * not divide Ci, and those of dq_qact_create. */
-dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, dq_qact** out);
+/* dq_qact_create with a choice of how cores are quantized.
+ *   core_group = 32: one E8M0 scale per 32-channel MX block (as
+ *     dq_qact_create); 64: the pages' per-group core with group size 64
+ *     (DeltaQuant notes, 损失函数/训练策略): one exponent from the maximum
+ *     over 64 consecutive channels, stored as the scale code of both of its
+ *     32-channel blocks.
+ *   core_bits = 8: MX-FP8 (E4M3) cores, the pages' choice; 4: MX-FP4 (E2M1)
+ *     cores, the 4-bit point of the pages' core-precision ablation (消融实验);
+ *     the core GEMM then runs FP4 x FP4.
+ * Deltas keep MX-FP4 with groups of 32.  dq_qact_export reports core codes one
+ * per byte in either format.  Errors: DQ_ERR_INVALID_ARG for another
+ * core_group or core_bits, DQ_ERR_SHAPE when core_group does not divide Ci,
+ * and those of dq_qact_create. */
+dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, int32_t core_bits,
+                            dq_qact** out);
 void dq_qact_destroy(dq_qact* q);
 
 /* Sizes of a workspace (any pointer may be NULL): tokens N, cubes K, and the

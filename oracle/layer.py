@@ -16,7 +16,7 @@ from . import cubes, mx
 
 
 def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray, cube_ids=None, tokens=None,
-                        core_group: int = 32) -> dict:
+                        core_group: int = 32, core_bits: int = 8) -> dict:
     """What the activation pass produces, for the given cubes (all by default).
 
     Cores are always formed from every token of a cube; deltas and U are
@@ -26,7 +26,9 @@ def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray,
     Returns a dict with
       cube_ids [k]; tokens [n] (ascending);
       core [k, Ci] fp32; core_codes [k, Ci] and core_scales [k, Ci/32] (FP8,
-      one exponent per core_group channels: 32, or the pages' 64);
+      or FP4 for core_bits = 4, the 4-bit point of the pages' core-precision
+      ablation; one exponent per core_group channels: 32, or the pages' 64);
+      core_fmt;
       delta [n, Ci] fp32; delta_codes [n, Ci/2] packed and delta_scales
       [n, Ci/32] (FP4); U [n, r] bf16 bits.
     """
@@ -43,10 +45,11 @@ def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray,
     row_of_cube = np.full(g.K, -1, dtype=np.int64)
     row_of_cube[ids] = np.arange(len(ids))
     delta = cubes.cube_delta(x32, core, g, tokens, row_of_cube)
-    core_codes, core_scales = mx.mx_quantize(core, "fp8", core_group)
+    core_fmt = {8: "fp8", 4: "fp4"}[core_bits]
+    core_codes, core_scales = mx.mx_quantize(core, core_fmt, core_group)
     d_codes, d_scales = mx.mx_quantize(delta, "fp4")
     out = dict(cube_ids=ids, tokens=tokens, row_of_cube=row_of_cube, core=core,
-               core_codes=core_codes, core_scales=core_scales, delta=delta,
+               core_codes=core_codes, core_scales=core_scales, core_fmt=core_fmt, delta=delta,
                delta_codes=mx.pack_fp4(d_codes), delta_scales=d_scales)
     if l1_bits is not None:
         out["U"] = low_rank_down(x32[tokens], l1_bits)
@@ -73,7 +76,7 @@ def forward(q: dict, g: cubes.Geometry, r_codes: np.ndarray, r_scales: np.ndarra
     sel = slice(None) if rows is None else np.asarray(rows)
     tokens = q["tokens"][sel]
     rdq = mx.mx_dequantize(mx.unpack_fp4(r_codes), r_scales, "fp4").T          # [Ci][Co]
-    core_dq = mx.mx_dequantize(q["core_codes"], q["core_scales"], "fp8")      # [k][Ci]
+    core_dq = mx.mx_dequantize(q["core_codes"], q["core_scales"], q.get("core_fmt", "fp8"))   # [k][Ci]
     delta_dq = mx.mx_dequantize(mx.unpack_fp4(q["delta_codes"][sel]), q["delta_scales"][sel], "fp4")
     lr = mx.bf16_bits_to_f64(q["U"][sel]) @ mx.bf16_bits_to_f64(l2_bits)
     core_rows = q["row_of_cube"][cubes.cube_of_token(g, tokens)]

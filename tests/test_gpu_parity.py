@@ -81,7 +81,7 @@ def _abs_bound(q, g, rc, rs, l2_bits, x_rows, l1_bits):
     Ci = rc.shape[1] * 2
     r = l2_bits.shape[0]
     rdq = np.abs(mx.mx_dequantize(mx.unpack_fp4(rc), rs, "fp4")).T
-    core_abs = np.abs(mx.mx_dequantize(q["core_codes"], q["core_scales"], "fp8"))
+    core_abs = np.abs(mx.mx_dequantize(q["core_codes"], q["core_scales"], q.get("core_fmt", "fp8")))
     delta_abs = np.abs(mx.mx_dequantize(mx.unpack_fp4(q["delta_codes"]), q["delta_scales"], "fp4"))
     rows = q["row_of_cube"][cubes.cube_of_token(g, q["tokens"])]
     blocks = Ci // 64 + 4
@@ -110,7 +110,8 @@ def _check_y(y, yo, bound=None):
     return err, row
 
 
-def _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed, wseed, svd="oracle", n_out=4, w_out=2, core_group=32):
+def _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed, wseed, svd="oracle", n_out=4, w_out=2, core_group=32,
+           core_bits=8):
     x = synth.make_activation(T, H, W, Ci, seed=xseed, dtype=dtype, n_outliers=n_out)
     wt = synth.make_weight(Ci, Co, seed=wseed, dtype=dtype, outlier_rows=w_out)
     xf, wf = synth.to_f32_numpy(x), synth.to_f32_numpy(wt)
@@ -119,19 +120,19 @@ def _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed, wseed, svd="oracle", 
     else:
         l1, l2 = _random_factors(Ci, Co, rank, wseed + 1)
     weights = dqm.dq_prepare_weights_lowrank(wt, l1 if rank else None, l2 if rank else None, device=0)
-    qa = dqm.dq_qact_create(weights, (T, H, W) + tuple(cube), core_group=core_group)
+    qa = dqm.dq_qact_create(weights, (T, H, W) + tuple(cube), core_group=core_group, core_bits=core_bits)
     xd = x.to(DEV)
     y = torch.full((T * H * W, Co), float("nan"), dtype=torch.float32, device=DEV)
     dqm.dq_linear(weights, xd, qa, y)
     torch.cuda.synchronize()
     return dict(x=xf, wt=wf, l1=l1, l2=l2, weights=weights, qa=qa, y=y.cpu().numpy(), g=cubes.Geometry(T, H, W, *cube),
-                core_group=core_group)
+                core_group=core_group, core_bits=core_bits)
 
 
 def _full_compare(dqm, L):
     got = dqm.dq_qact_export(L["qa"])
     q = layer.quantize_activation(L["x"], L["g"], L["l1"] if L["l1"].shape[1] else None,
-                                  core_group=L.get("core_group", 32))
+                                  core_group=L.get("core_group", 32), core_bits=L.get("core_bits", 8))
     assert np.array_equal(got["core_codes"], q["core_codes"]), "core codes"
     assert np.array_equal(got["core_scales"], q["core_scales"]), "core scales"
     assert np.array_equal(got["delta_scales"], q["delta_scales"]), "delta scales"
@@ -230,6 +231,19 @@ def test_core_group_64(dqm, case):
     _say(f"core group 64 {case}: rel err {err:.2e} worst row {row:.2e}")
 
 
+# 4-bit cores (the 4-bit point of the pages' core-precision ablation), through
+# the same forms; the last case combines them with group-64 scales
+@pytest.mark.parametrize("case", CORE64, ids=[f"{c[0]}x{c[1]}x{c[2]}_c{'x'.join(map(str, c[3]))}_ci{c[4]}_{c[7]}"
+                                              for c in CORE64])
+def test_core_fp4(dqm, case):
+    T, H, W, cube, Ci, Co, rank, dtype = case
+    _say(f"case fp4 cores {case}")
+    L = _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed=T * 100 + Ci + 4, wseed=Co + 11,
+               n_out=min(4, Ci // 16), core_bits=4, core_group=64 if cube == (2, 2, 2) else 32)
+    err, row = _full_compare(dqm, L)
+    _say(f"fp4 cores {case}: rel err {err:.2e} worst row {row:.2e}")
+
+
 def test_core_group_errors(dqm):
     wt = synth.make_weight(96, 64, seed=3, dtype="f32")
     weights = dqm.dq_prepare_weights_lowrank(wt, None, None)
@@ -237,6 +251,8 @@ def test_core_group_errors(dqm):
         dqm.dq_qact_create(weights, (2, 2, 2, 1, 1, 1), core_group=64)      # 64 does not divide Ci = 96
     with pytest.raises(dqm.DQError, match="DQ_ERR_INVALID_ARG"):
         dqm.dq_qact_create(weights, (2, 2, 2, 1, 1, 1), core_group=48)
+    with pytest.raises(dqm.DQError, match="DQ_ERR_INVALID_ARG"):
+        dqm.dq_qact_create(weights, (2, 2, 2, 1, 1, 1), core_bits=6)
 
 
 def test_wan1p3b_projection_full(dqm):

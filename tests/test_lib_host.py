@@ -60,7 +60,7 @@ def test_argument_errors_before_any_device_work(lib):
     _expect(lib.dq_prepare_weights_lowrank(P(w), 0, 96, 64, 8, None, P(l2), 0, ctypes.byref(h)), 1, lib)
     # workspace for a null weight, and null handles for the hot calls
     _expect(lib.dq_qact_create(None, dq.Geom(2, 2, 2, 1, 1, 1), ctypes.byref(h)), 1, lib)
-    _expect(lib.dq_qact_create_ex(None, dq.Geom(2, 2, 2, 1, 1, 1), 64, ctypes.byref(h)), 1, lib)
+    _expect(lib.dq_qact_create_ex(None, dq.Geom(2, 2, 2, 1, 1, 1), 64, 8, ctypes.byref(h)), 1, lib)
     _expect(lib.dq_quantize_act(None, None, 0, None, None), 1, lib)
     _expect(lib.dq_linear_forward(None, None, None, None), 1, lib)
     _expect(lib.dq_core_term(None, None, None), 1, lib)

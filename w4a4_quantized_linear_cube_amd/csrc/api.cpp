@@ -312,15 +312,17 @@ dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2
 }
 
 dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
-    return dq_qact_create_ex(w, geom, 32, out);
+    return dq_qact_create_ex(w, geom, 32, 8, out);
 }
 
-dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, dq_qact** out) {
+dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, int32_t core_bits,
+                            dq_qact** out) {
     g_last_error.clear();
     if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
     if (core_group != 32 && core_group != 64) return fail(DQ_ERR_INVALID_ARG, "core_group must be 32 or 64");
+    if (core_bits != 8 && core_bits != 4) return fail(DQ_ERR_INVALID_ARG, "core_bits must be 8 or 4");
     if (w->Ci % core_group != 0) return fail(DQ_ERR_SHAPE, "core_group must divide Ci");
     const dq_geom& G = geom;
     if (G.T < 1 || G.H < 1 || G.W < 1) return fail(DQ_ERR_SHAPE, "T, H, W must be >= 1");
@@ -349,6 +351,7 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
     q->rank = w->rank;
     q->g = Geom{G.T, G.H, G.W, G.t, G.h, G.w, Tc, Hc, Wc, (int)S, (long long)N, (long long)K, (long long)Nslot};
     q->core_group = core_group;
+    q->core_bits = core_bits;
     // frame segments: whole frame groups, then the clipped last group (if any)
     const int T0 = G.T - G.T % G.t;                  // >= t, since t <= T
     const int segT[2] = {T0, G.T - T0}, segt[2] = {G.t, G.T - T0};
@@ -510,7 +513,15 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
         }
         if (ccodes_host) {
             if ((e = fetch_all(q->cq, (size_t)(q->K_pad * Kp), buf)) != hipSuccess) return hip_fail(e, "copy core codes");
-            for (long long k = 0; k < g.K; ++k) unstep_fp8(buf, cube_row(k), Ci, Kp, ccodes_host + k * Ci);
+            if (q->core_bits == 4) {                      // packed nibbles -> one code per byte
+                std::vector<uint8_t> row((size_t)(Ci / 2));
+                for (long long k = 0; k < g.K; ++k) {
+                    unstep_fp4(buf, cube_row(k), Ci, Kp, row.data());
+                    for (int64_t c = 0; c < Ci; ++c) ccodes_host[k * Ci + c] = (uint8_t)((row[c / 2] >> (4 * (c & 1))) & 15);
+                }
+            } else {
+                for (long long k = 0; k < g.K; ++k) unstep_fp8(buf, cube_row(k), Ci, Kp, ccodes_host + k * Ci);
+            }
         }
         if (cscales_host) {
             if ((e = fetch_all(q->cs, (size_t)(q->K_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy core scales");

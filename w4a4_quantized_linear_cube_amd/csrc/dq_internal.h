@@ -110,7 +110,8 @@ struct dq_qact {
     int64_t Ci = 0, Co = 0, Kp = 0, Cop = 0;
     int rp = 0, rank = 0;
     dq::Geom g{};              // the full token grid and cube shape
-    int core_group = 32;       // channels per exponent of the FP8 cores (32 or 64)
+    int core_group = 32;       // channels per exponent of the cores (32 or 64)
+    int core_bits = 8;         // cores as MX-FP8 (8) or MX-FP4 (4, the FP4 layout in cq)
     int nseg = 1;
     dq_segment seg[2]{};
     int64_t Nslot_pad = 0, K_pad = 0;

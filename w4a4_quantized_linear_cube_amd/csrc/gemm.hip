@@ -729,26 +729,30 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
     const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
     if (q->g.S == 1) {
         // One-token cubes: every delta is x - x = 0 exactly, so y = Q8(x) Q4(R)
-        // + U L2, one FP8 GEMM over the cubes (cube k is slot k) with the token
-        // epilogue and no per-cube term.  It is the delta half's work; the
+        // + U L2 (Q4(x) for 4-bit cores), one GEMM over the cubes (cube k is
+        // slot k) with the token epilogue and no per-cube term.  It is the delta half's work; the
         // core half has nothing to do.
         if (!(parts & FWD_DELTA)) return hipSuccess;
         d.b = q->cq;
         d.bs = q->cs;
         d.ntiles = (int)(q->K_pad / 256);
         d.bias = nullptr;
+        if (q->core_bits == 4) {
+            if (d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0) return launch<FMT_FP4, EPI_TOKENS_Q>(d, st);
+            return launch<FMT_FP4, EPI_TOKENS>(d, st);
+        }
         if (d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0) return launch<FMT_FP8, EPI_TOKENS_Q>(d, st);
         return launch<FMT_FP8, EPI_TOKENS>(d, st);
     }
     if (parts & FWD_CORE) {
-        // per-cube core term bias[k] = Q8(core_k) Q4(R)
+        // per-cube core term bias[k] = Q8(core_k) Q4(R) (Q4(core_k) for 4-bit cores)
         GemmArgs c = d;
         c.b = q->cq;
         c.bs = q->cs;
         c.ntiles = (int)(q->K_pad / 256);
         c.c = q->bias;
         c.ldc = w->Cop;
-        hipError_t e = launch<FMT_FP8, EPI_STORE>(c, st);
+        hipError_t e = q->core_bits == 4 ? launch<FMT_FP4, EPI_STORE>(c, st) : launch<FMT_FP8, EPI_STORE>(c, st);
         if (e != hipSuccess) return e;
     }
     if (parts & FWD_DELTA) {

@@ -54,6 +54,7 @@ struct QuantArgs {
     const uint8_t* zero;      // 256 zero bytes (source of absent rows and channels)
     const int* stok;          // [Nslot_pad] token of each slot, -1 for pad slots
     int core_g64;             // cores: one exponent per 64 channels (the maximum of two 32-channel groups)
+    int core_fp4;             // cores as MX-FP4 (the FP4 layout in cq) instead of MX-FP8
 };
 
 // LDS chunk layout: 16-byte piece c of row r at r QROWB + ((c ^ (r & 15)) << 4);
@@ -569,12 +570,20 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     else s0 = __fdiv_rn(s0, (float)cnt);
                     float amax = row16_max(fabsf(s0));
                     amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, amax), 0x401F)));   // lane ^ 16
-                    const int ex = mx_exp_fp8(core_pair_max<32>(amax, a.core_g64));
-                    v2s z = {0, 0};
-                    const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, 0.0f, pow2f(ex), false);
+                    const float cmax = core_pair_max<32>(amax, a.core_g64);
+                    const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const int gch = c0 + ch;                       // channel within the row
-                    *(uint8_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) =
-                        (uint8_t)__builtin_bit_cast(uint32_t, cd);
+                    if (a.core_fp4) {
+                        // a channel pair's two nibbles meet in its even lane
+                        const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0xB1, 0xF, 0xF, false));
+                        const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s0, s1, pow2f(ex), 0);
+                        if ((ch & 1) == 0) *(uint8_t*)(a.cq + off_fp4(k, gch >> 5, nks) + ((gch & 31) >> 1)) = (uint8_t)w;
+                    } else {
+                        v2s z = {0, 0};
+                        const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, 0.0f, pow2f(ex), false);
+                        *(uint8_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) =
+                            (uint8_t)__builtin_bit_cast(uint32_t, cd);
+                    }
                     if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
                     cs_[cr][ch] = s0;
                 }
@@ -639,12 +648,18 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                         s1 = __fdiv_rn(s1, (float)cnt);
                     }
                     const float amax = row16_max(fmaxf(fabsf(s0), fabsf(s1)));
-                    const int ex = mx_exp_fp8(core_pair_max<16>(amax, a.core_g64));
-                    v2s z = {0, 0};
-                    const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false);
+                    const float cmax = core_pair_max<16>(amax, a.core_g64);
+                    const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const int gch = c0 + ch;                       // channel within the row
-                    *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) =
-                        (uint16_t)__builtin_bit_cast(uint32_t, cd);
+                    if (a.core_fp4) {
+                        *(uint8_t*)(a.cq + off_fp4(k, gch >> 5, nks) + ((gch & 31) >> 1)) =
+                            (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s0, s1, pow2f(ex), 0);
+                    } else {
+                        v2s z = {0, 0};
+                        const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false);
+                        *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) =
+                            (uint16_t)__builtin_bit_cast(uint32_t, cd);
+                    }
                     if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
                     *(float2*)&cs_[cr][ch] = make_float2(s0, s1);
                 }
@@ -785,8 +800,17 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(core[e]));
                 amax = core_pair_max<4>(quad_max(amax), a.core_g64);
-                const int ex = mx_exp_fp8(amax);
+                const int ex = a.core_fp4 ? mx_exp_fp4(amax) : mx_exp_fp8(amax);
                 const float sc = pow2f(ex);
+                if (a.core_fp4) {
+                    uint32_t w = 0u;
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[0], core[1], sc, 0);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[2], core[3], sc, 1);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[4], core[5], sc, 2);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[6], core[7], sc, 3);
+                    *(uint32_t*)(a.cq + off_fp4(k, G, nks) + 4 * qq) = w;
+                    if (qq == 0) a.cs[off_scale(k, G, nks)] = (uint8_t)(ex + 127);
+                } else {
                 uint32_t d[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -802,6 +826,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 } else {
                     *(uint2*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + (qq >> 1), nks) + 8 * (qq & 1)) = make_uint2(d[0], d[1]);
                     if (qq == 0) a.cs[off_scale(k, G, nks)] = (uint8_t)(ex + 127);
+                }
                 }
             } else {
                 const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32 + 8 * qq);
@@ -932,15 +957,19 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 }
                 {
                     const float amax = row16_max(fmaxf(fabsf(s0), fabsf(s1)));   // 16 lanes: one 32-channel group
-                    const int ex = mx_exp_fp8(core_pair_max<16>(amax, a.core_g64));
+                    const float cmax = core_pair_max<16>(amax, a.core_g64);
+                    const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     v2s z = {0, 0};
-                    const uint16_t cd = (uint16_t)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false));
+                    const uint16_t cd = a.core_fp4
+                        ? (uint16_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s0, s1, pow2f(ex), 0)
+                        : (uint16_t)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s0, s1, pow2f(ex), false));
                     // (fp32 chunks have CC = 64 channels: lanes 32-63 store
                     // nothing; the conditions hold for whole 16-lane groups)
                     const int gch = c0 + ch;               // channel within the row
                     if (ch < CC) {
                         if (gch < a.Ci) {
-                            *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) = cd;
+                            if (a.core_fp4) *(uint8_t*)(a.cq + off_fp4(k, gch >> 5, nks) + ((gch & 31) >> 1)) = (uint8_t)cd;
+                            else *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) = cd;
                             if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
                         }
                         *(float2*)&cs_[cr][ch] = make_float2(s0, s1);
@@ -1031,13 +1060,21 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     float amax = 0.0f;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fabsf(core[q]));
-                    const int ex = mx_exp_fp8(core_pair_max<8>(oct_max(amax), a.core_g64));
+                    const float cmax = core_pair_max<8>(oct_max(amax), a.core_g64);
+                    const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const float sc = pow2f(ex);
-                    v2s z = {0, 0};
-                    const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, core[0], core[1], sc, false);
-                    const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, core[2], core[3], sc, true);
-                    *(uint32_t*)(cq_t + toff_fp8(kt, (int)(G >> 2), 2 * (int)(G & 3) + (e >> 2)) + 4 * (e & 3)) =
-                        __builtin_bit_cast(uint32_t, cd);
+                    if (a.core_fp4) {
+                        uint32_t w = 0u;
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[0], core[1], sc, 0);
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[2], core[3], sc, 1);
+                        *(uint16_t*)(a.cq + off_fp4(B.k_first + cr, G, nks) + 2 * e) = (uint16_t)w;
+                    } else {
+                        v2s z = {0, 0};
+                        const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, core[0], core[1], sc, false);
+                        const v2s cd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, core[2], core[3], sc, true);
+                        *(uint32_t*)(cq_t + toff_fp8(kt, (int)(G >> 2), 2 * (int)(G & 3) + (e >> 2)) + 4 * (e & 3)) =
+                            __builtin_bit_cast(uint32_t, cd);
+                    }
                     if (e == 0) cs_t[toff_scale(kt, (int)G)] = (uint8_t)(ex + 127);
                 }
                 // deltas of the 8 rows (pad rows too: never read back as a
@@ -1171,6 +1208,7 @@ struct CombineArgs {
     uint8_t* cq;     // K_pad x Kp, step-major
     uint8_t* cs;     // K_pad x Kp/32, step-major
     int core_g64;    // one exponent per 64 channels
+    int core_fp4;    // MX-FP4 cores (FP4 layout in cq)
 };
 
 // core = fl32(sum of the block partials in block order / count), then FP8 codes.
@@ -1212,12 +1250,18 @@ __global__ __launch_bounds__(256) void k_core_combine(CombineArgs a) {
         if (a.core_g64)                                 // the other half of the 64-channel group
 #pragma unroll
             for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(tile[32 * (j ^ 1) + i]));
-        int e = mx_exp_fp8(amax);
-        uint4 lo, hi;
-        encode_fp8x32(v, pow2f(e), lo, hi);
         const long long G = cg >> 5, nks = a.Kp / 128;
-        *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3), nks)) = lo;
-        *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + 1, nks)) = hi;
+        int e;
+        if (a.core_fp4) {
+            e = mx_exp_fp4(amax);
+            *(uint4*)(a.cq + off_fp4(k, G, nks)) = encode_fp4x32(v, pow2f(e));
+        } else {
+            e = mx_exp_fp8(amax);
+            uint4 lo, hi;
+            encode_fp8x32(v, pow2f(e), lo, hi);
+            *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3), nks)) = lo;
+            *(uint4*)(a.cq + off_fp8(k, G >> 2, 2 * (int)(G & 3) + 1, nks)) = hi;
+        }
         a.cs[off_scale(k, G, nks)] = (uint8_t)(e + 127);
     }
 }
@@ -1293,6 +1337,7 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
     const Geom& g = sg.g;
     const size_t nks = (size_t)(q->Kp / 128);
     uint8_t* const cq = q->cq + (size_t)(sg.krow0 / 256) * nks * 32768;
+    uint8_t* const cq4 = q->cq + (size_t)(sg.krow0 / 256) * nks * 16384;   // FP4 cores: 16 KB per tile step
     uint8_t* const cs = q->cs + (size_t)(sg.krow0 / 256) * nks * 1024;
     float* const coref = q->coref ? q->coref + sg.krow0 * q->Kp : nullptr;
     if (sg.core_mode == 1) {
@@ -1305,7 +1350,8 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
         else k_core_partial<float><<<grid, 256, 0, st>>>(pa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        CombineArgs ca{g, (int)q->Ci, (int)q->Kp, sg.nblk, q->part, coref, cq, cs, q->core_group == 64};
+        CombineArgs ca{g, (int)q->Ci, (int)q->Kp, sg.nblk, q->part, coref, q->core_bits == 4 ? cq4 : cq, cs,
+                       q->core_group == 64, q->core_bits == 4};
         dim3 grid2((unsigned)g.K, (unsigned)((q->Ci + 255) / 256));
         k_core_combine<<<grid2, 256, 0, st>>>(ca);
         e = hipGetLastError();
@@ -1328,6 +1374,8 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
     a.zero = q->zero;
     a.stok = q->stok + sg.row0;
     a.core_g64 = q->core_group == 64;
+    a.core_fp4 = q->core_bits == 4;
+    if (a.core_fp4) a.cq = cq4;
     const long long cpb = QROWS / g.S;
     a.nblocks = sg.core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;
     int dev = 0, cus = 0;

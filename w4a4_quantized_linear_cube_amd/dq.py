@@ -62,7 +62,7 @@ def load():
         "dq_weights_info": ([P, P, P, P, P], ctypes.c_int),
         "dq_weights_export": ([P, P, P, P, P, P], ctypes.c_int),
         "dq_qact_create": ([P, Geom, PP], ctypes.c_int),
-        "dq_qact_create_ex": ([P, Geom, I32, PP], ctypes.c_int),
+        "dq_qact_create_ex": ([P, Geom, I32, I32, PP], ctypes.c_int),
         "dq_qact_destroy": ([P], None),
         "dq_qact_info": ([P, P, P, P], ctypes.c_int),
         "dq_quantize_act": ([P, P, ctypes.c_int, P, P], ctypes.c_int),
@@ -188,14 +188,16 @@ def dq_weights_export(w: Weights) -> dict:
     return out
 
 
-def dq_qact_create(w: Weights, geom: Sequence[int], core_group: int = 32) -> QAct:
+def dq_qact_create(w: Weights, geom: Sequence[int], core_group: int = 32, core_bits: int = 8) -> QAct:
     """Workspace for a (T, H, W, t, h, w) geometry; core_group 64 gives the
-    cores one scale per 64 channels (dq_qact_create_ex)."""
+    cores one scale per 64 channels, core_bits 4 MX-FP4 cores
+    (dq_qact_create_ex)."""
     h = ctypes.c_void_p()
-    if core_group == 32:
+    if core_group == 32 and core_bits == 8:
         _check(load().dq_qact_create(w.handle, Geom(*geom), ctypes.byref(h)), "dq_qact_create")
     else:
-        _check(load().dq_qact_create_ex(w.handle, Geom(*geom), core_group, ctypes.byref(h)), "dq_qact_create_ex")
+        _check(load().dq_qact_create_ex(w.handle, Geom(*geom), core_group, core_bits, ctypes.byref(h)),
+               "dq_qact_create_ex")
     return QAct(h, w, geom)
 
 
