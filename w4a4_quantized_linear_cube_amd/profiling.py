@@ -4,9 +4,14 @@
         kernel-trace statistics (DIR/*_kernel_stats.csv) -> markdown table
     python -m w4a4_quantized_linear_cube_amd.profiling counters RUN_FETCH RUN_WRITE COPY_FETCH COPY_WRITE
             --copy-bytes B --config NAME --cube t,h,w --out OUT.json --cmd "..."
-        FETCH_SIZE / WRITE_SIZE per dispatch of the delta GEMM, each scaled by
-        the same counter's reading for plain device copies of known size
-        (B bytes read and B bytes written in total), -> HBM bytes per launch
+        FETCH_SIZE / WRITE_SIZE per dispatch of the delta GEMM (and of the
+        activation pass and the core GEMM), each scaled by the same counter's
+        reading for plain device copies of known size (B bytes read and B
+        bytes written in total), -> HBM bytes per launch
+    python -m w4a4_quantized_linear_cube_amd.profiling mfma RUN OUT.md --cmd "..."
+        SQ_INSTS_VALU_MFMA_MOPS_{F6F4,F8,BF16}, SQ_VALU_MFMA_BUSY_CYCLES and
+        GRBM_GUI_ACTIVE per dispatch of each kernel -> MFMA flops executed and
+        MFMA utilisation (busy cycles per SIMD / active cycles per XCD)
 
 The counter JSON records the SHA-256 of gemm.hip; bench.py reports its
 traffic only while the kernel source is unchanged.
@@ -24,7 +29,10 @@ from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 DELTA_KERNEL = re.compile(r"k_gemm<4, [12], ")     # the delta GEMM (FP4 B operand, token epilogue)
-CORE_KERNEL = re.compile(r"k_gemm<0, 0, ")
+CORE_KERNEL = re.compile(r"k_gemm<[04], 0, ")     # the core GEMM (FP8 or FP4 cores, plain-store epilogue)
+QUANT_KERNEL = re.compile(r"k_quantize<")
+SIMDS = 1024                                     # 256 CUs x 4 SIMDs
+XCDS = 8                                         # GRBM_GUI_ACTIVE comes summed over the XCDs
 COPY_KERNEL = re.compile(r"copyBuffer")
 
 
@@ -61,14 +69,29 @@ def summarize_trace(d: str, out: str, cmd: str) -> None:
     print("\n".join(lines))
 
 
-def _counter_per_dispatch(d: str, counter: str, pattern) -> list:
-    """Sum of `counter` over the instances of each matching dispatch."""
-    per = defaultdict(float)
+def _counter_per_dispatch(d: str, counter: str, pattern, reduce="sum") -> list:
+    """Sum (or max) of `counter` over the instances of each matching dispatch."""
+    per = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != counter or not pattern.search(r["Kernel_Name"]):
                 continue
-            per[(f, r["Dispatch_Id"])] += float(r["Counter_Value"])
+            k, v = (f, r["Dispatch_Id"]), float(r["Counter_Value"])
+            per[k] = (per.get(k, 0.0) + v) if reduce == "sum" else max(per.get(k, v), v)
+    return list(per.values())
+
+
+def _mean(v):
+    return sum(v) / len(v) if v else None
+
+
+def _durations_ns(d: str, pattern) -> list:
+    """End - start timestamp of each matching dispatch (one counter's rows)."""
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if pattern.search(r["Kernel_Name"]):
+                per[(f, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     return list(per.values())
 
 
@@ -96,8 +119,44 @@ def summarize_counters(run_fetch, run_write, copy_fetch, copy_write, copy_bytes,
         "gemm_hip_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
         "command": cmd,
     }
+    # the other two kernels of the step, from the same runs
+    others = {}
+    for name, pat in (("activation pass (k_quantize)", QUANT_KERNEL), ("core GEMM (k_gemm, plain-store epilogue)", CORE_KERNEL)):
+        f = _mean(_counter_per_dispatch(run_fetch, "FETCH_SIZE", pat))
+        w = _mean(_counter_per_dispatch(run_write, "WRITE_SIZE", pat))
+        if f is not None and w is not None:
+            others[name] = {"fetch_bytes": int(f * 1024 * f_scale), "write_bytes": int(w * 1024 * w_scale),
+                            "traffic_bytes": int(f * 1024 * f_scale + w * 1024 * w_scale)}
+    rec["other_kernels"] = others
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec, indent=1))
+
+
+def summarize_mfma(run: str, out: str, cmd: str) -> None:
+    lines = ["# MFMA counters: " + os.path.splitext(os.path.basename(out))[0], "",
+             "Command (from the repository root on the GPU box):", "", "```", cmd, "```", "",
+             "Per dispatch, averaged over the dispatches of each kernel (counter runs serialise dispatches).  "
+             "MFMA flops = MOPS x 512.  GRBM_GUI_ACTIVE comes summed over the %d XCDs: active cycles = it / %d, "
+             "clock = active cycles / dispatch duration.  MFMA utilisation = (SQ_VALU_MFMA_BUSY_CYCLES / %d SIMDs) / "
+             "active cycles: the share of the kernel's cycles the average SIMD's matrix core is busy." % (XCDS, XCDS, SIMDS), "",
+             "| kernel | dispatches | duration (us) | clock (GHz) | MFMA TFLOP F6F4 | MFMA TFLOP F8 | MFMA TFLOP BF16 | busy cycles / SIMD | active cycles | MFMA utilisation |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, pat in (("delta GEMM (k_gemm, token epilogue)", DELTA_KERNEL), ("core GEMM (k_gemm, plain store)", CORE_KERNEL),
+                      ("activation pass (k_quantize)", QUANT_KERNEL)):
+        m4 = _counter_per_dispatch(run, "SQ_INSTS_VALU_MFMA_MOPS_F6F4", pat)
+        m8 = _counter_per_dispatch(run, "SQ_INSTS_VALU_MFMA_MOPS_F8", pat)
+        mb = _counter_per_dispatch(run, "SQ_INSTS_VALU_MFMA_MOPS_BF16", pat)
+        busy = _counter_per_dispatch(run, "SQ_VALU_MFMA_BUSY_CYCLES", pat)
+        act = _counter_per_dispatch(run, "GRBM_GUI_ACTIVE", pat, reduce="max")
+        if not act:
+            continue
+        b, a = _mean(busy), _mean(act) / XCDS
+        dur = _mean(_durations_ns(run, pat))
+        lines.append(f"| {name} | {len(act)} | {dur / 1e3:.1f} | {a / dur:.2f} | {_mean(m4) * 512 / 1e12:.3f} | "
+                     f"{_mean(m8) * 512 / 1e12:.3f} | {_mean(mb) * 512 / 1e12:.4f} | {b / SIMDS:.0f} | {a:.0f} | "
+                     f"{100 * b / SIMDS / a:.1f} % |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main(argv):
@@ -115,6 +174,15 @@ def main(argv):
         ap.add_argument("--cmd", required=True)
         a = ap.parse_args(argv[1:])
         summarize_counters(*a.dirs, a.copy_bytes, a.config, [int(v) for v in a.cube.split(",")], a.out, a.cmd)
+        return
+    if len(argv) >= 3 and argv[0] == "mfma":
+        import argparse
+        ap = argparse.ArgumentParser()
+        ap.add_argument("run")
+        ap.add_argument("out")
+        ap.add_argument("--cmd", required=True)
+        a = ap.parse_args(argv[1:])
+        summarize_mfma(a.run, a.out, a.cmd)
         return
     raise SystemExit(__doc__)
 
