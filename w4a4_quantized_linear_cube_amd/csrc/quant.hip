@@ -716,15 +716,26 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[6], dv[7], sc, 3);
                     code[n] = w;
                 }
+                // blocks of exactly 64 slots start at multiples of 64: their
+                // rows lie in one 256-row tile (32-bit offsets)
+                const bool tile64 = B.nrows == 64 && (B.slot0 & 63) == 0;
+                uint8_t* const dq_t = a.dq + (size_t)(B.slot0 >> 8) * (size_t)nks * 16384;
+                uint8_t* const ds_t = a.ds + (size_t)(B.slot0 >> 8) * (size_t)nks * 1024;
 #pragma unroll
                 for (int n = 0; n < NT2; ++n) {
                     if (!live[n]) continue;
                     const int t = qtid + 256 * n;
                     const int qq = t & 3, pr = t >> 2;
                     const int r = pr / NGC, gc = pr - r * NGC;
-                    const long long G = (c0 >> 5) + gc, sl = B.slot0 + r;
-                    *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
-                    if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
+                    if (tile64) {
+                        const int G = (c0 >> 5) + gc, rt = (int)(B.slot0 & 255) + r;
+                        *(uint32_t*)(dq_t + toff_fp4(rt, G) + 4 * qq) = code[n];
+                        if (qq == 0) ds_t[toff_scale(rt, G)] = (uint8_t)(exq[n] + 127);
+                    } else {
+                        const long long G = (c0 >> 5) + gc, sl = B.slot0 + r;
+                        *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
+                        if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
+                    }
                 }
                 const long long i_prev = i;
 #pragma unroll
@@ -750,6 +761,8 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
         const bool full = CM == 0 && g.S >= QKEEP && 64 % g.S == 0;
         uint8_t* const dq_t = a.dq + (size_t)(B.slot0 >> 8) * (size_t)nks * 16384;
         uint8_t* const ds_t = a.ds + (size_t)(B.slot0 >> 8) * (size_t)nks * 1024;
+        // blocks of exactly 64 slots start at multiples of 64: their rows lie in one 256-row tile
+        const bool tile64 = B.ncores * g.S == 64 && (B.slot0 & 63) == 0;
         uint8_t* const cq_t = a.cq + (size_t)(B.k_first >> 8) * (size_t)nks * 32768;
         uint8_t* const cs_t = a.cs + (size_t)(B.k_first >> 8) * (size_t)nks * 1024;
         // one task (FULL: the case above, so the kept rows need no bound checks)
@@ -1018,9 +1031,15 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const int t = lane + 64 * n;
                     const int qq = t & 3, pr = t >> 2;
                     const int j = pr / NGC, gc = pr - j * NGC;
-                    const long long G = (c0 >> 5) + gc, sl = B.slot0 + rb + j;
-                    *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
-                    if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
+                    if (tile64) {                              // 32-bit offsets in the block's tile
+                        const int G = (c0 >> 5) + gc, rt = (int)(B.slot0 & 255) + rb + j;
+                        *(uint32_t*)(dq_t + toff_fp4(rt, G) + 4 * qq) = code[n];
+                        if (qq == 0) ds_t[toff_scale(rt, G)] = (uint8_t)(exq[n] + 127);
+                    } else {
+                        const long long G = (c0 >> 5) + gc, sl = B.slot0 + rb + j;
+                        *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
+                        if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
+                    }
                 }
             }
         } else if constexpr (CM == 4) {
