@@ -47,7 +47,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps first (20: the GPU clock ramps up after the host-side weight preparation)")
     ap.add_argument("--config", default="ffn_up_720p")
     ap.add_argument("--cube", default=None, help="t,h,w (default: the config's first cube)")
     ap.add_argument("--x-seed", type=int, default=None)
