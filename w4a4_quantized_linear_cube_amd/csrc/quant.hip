@@ -1124,6 +1124,48 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 }
                 ds_t[toff_scale(rt0 + e, (int)G)] = (uint8_t)(exs + 127);
             }
+        } else if (CM == 0 && g.S == 1) {
+            // one-token cubes: the core is the token itself (x / 1, exact) and
+            // every delta is 0 (not stored); one (row, group, quarter) per
+            // thread codes the row, stores through the block's 256-row tile
+            // (its 64 cubes start at a multiple of 64)
+            for (int t = qtid; t < ntask; t += 256) {
+                const int qq = t & 3, pr = t >> 2;
+                const int cr = pr / NGC, gc = pr - cr * NGC;
+                const int G = (c0 >> 5) + gc;
+                if (G * 32 >= a.Ci) continue;                  // the same for the quad
+                float v[8];
+                qload8<XT>(buf, cr, gc, qq, 0u, v);
+                float amax = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+                amax = core_pair_max<4>(quad_max(amax), a.core_g64);
+                const int kt = (int)(B.k_first & 255) + cr;
+                if (a.core_fp4) {
+                    const int ex = mx_exp_fp4(amax);
+                    const float sc = pow2f(ex);
+                    uint32_t w = 0u;
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], sc, 0);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], sc, 1);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
+                    *(uint32_t*)(a.cq + off_fp4(B.k_first + cr, G, nks) + 4 * qq) = w;
+                    if (qq == 0) cs_t[toff_scale(kt, G)] = (uint8_t)(ex + 127);
+                } else {
+                    const int ex = mx_exp_fp8(amax);
+                    const float sc = pow2f(ex);
+                    uint32_t d[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        v2s z = {0, 0};
+                        v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, v[4 * h], v[4 * h + 1], sc, false);
+                        v2s hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v[4 * h + 2], v[4 * h + 3], sc, true);
+                        d[h] = __builtin_bit_cast(uint32_t, hi);
+                    }
+                    *(uint2*)(cq_t + toff_fp8(kt, G >> 2, 2 * (G & 3) + (qq >> 1)) + 8 * (qq & 1)) = make_uint2(d[0], d[1]);
+                    if (qq == 0) cs_t[toff_scale(kt, G)] = (uint8_t)(ex + 127);
+                }
+            }
         } else {
             for (int t = qtid; t < ntask; t += 256) {
                 if (full) task(t, std::true_type{});
