@@ -189,6 +189,7 @@ EDGE = [
     (5, 6, 8, (2, 2, 2), 256, 256, 32, "bf16"),    # last frame alone: second frame segment at row 256
     (4, 6, 10, (2, 2, 2), 128, 96, 16, "f32"),     # fp32 input, 8-token cubes (eight lanes per group)
     (9, 8, 16, (4, 2, 4), 256, 512, 32, "bf16"),   # second frame segment after four tiles of 32-token cubes
+    (5, 9, 10, (4, 9, 10), 64, 48, 16, "f32"),     # both frame segments with cubes of more than 64 tokens, fp32 input
 ]
 
 
