@@ -59,8 +59,8 @@ def parse():
     ap.add_argument("--denoise-steps", type=int, default=10, help="denoising steps of one --schedule run")
     ap.add_argument("--core-group", type=int, default=32, choices=(32, 64),
                     help="channels per FP8 exponent of the cores (64: the pages' group size)")
-    ap.add_argument("--core-bits", type=int, default=8, choices=(8, 4),
-                    help="MX-FP8 cores (the pages' choice) or MX-FP4 cores (the 4-bit point of their ablation)")
+    ap.add_argument("--core-bits", type=int, default=8, choices=(8, 4, 16),
+                    help="MX-FP8 cores (the pages' choice), MX-FP4 or bf16 cores (the 4- and 16-bit points of their ablation)")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
@@ -147,7 +147,7 @@ def shape_record(cfg, cube, ms, q_ms, c_ms, d_ms, core_bits=8):
     """One cube shape's step time, split by phase, with its rates."""
     wk = work(cfg, cube, core_bits)
     one = wk["S"] == 1          # one-token cubes: the delta term is one GEMM over the cubes (FP8 or FP4 cores)
-    ck = f"fp{core_bits}_tflops"
+    ck = ("bf16" if core_bits == 16 else f"fp{core_bits}") + "_tflops"
     return {
         "config": cfg.name, "cube": list(cube), "cubes": wk["K"], "slots": wk["Nslot"],
         "ms_per_step": round(ms, 4), "effective_tops": round(wk["dense"] / (ms * 1e-3) / 1e12, 2),
@@ -270,6 +270,7 @@ def main():
     # timed steps (activation pass, core term, delta term: dq_linear's work);
     # per-phase events on the launch stream
     ms_step, q_ms, c_ms, d_ms = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
+    ctype = "bf16" if args.core_bits == 16 else f"fp{args.core_bits}"      # the core GEMM's input type
     f_ms = c_ms + d_ms
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -306,7 +307,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"mxfp4 (deltas, R) + mxfp{args.core_bits} (cores) + bf16 (low rank), fp32 accumulate",
+        "dtype": f"mxfp4 (deltas, R) + {'bf16' if args.core_bits == 16 else 'mxfp%d' % args.core_bits} (cores) + bf16 (low rank), fp32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: X {N}x{Ci} ({T}x{H}x{W} tokens) {cfg.dtype} -> Y {N}x{Co} fp32, "
@@ -330,8 +331,8 @@ def main():
         },
         "core_term": {
             "ms": round(c_ms, 4),
-            f"fp{args.core_bits}_tflops": round(f_fp8 / (c_ms * 1e-3) / 1e12, 2),
-            f"pct_fp{args.core_bits}_peak": round(100 * f_fp8 / (c_ms * 1e-3) / (PEAK_FP8 if args.core_bits == 8 else PEAK_FP4), 2),
+            f"{ctype}_tflops": round(f_fp8 / (c_ms * 1e-3) / 1e12, 2),
+            f"pct_{ctype}_peak": round(100 * f_fp8 / (c_ms * 1e-3) / {8: PEAK_FP8, 4: PEAK_FP4, 16: PEAK_BF16}[args.core_bits], 2),
         },
         "roofline": {
             "kernel": "delta GEMM (dq_delta_term: FP4 x FP4 scaled MFMA over the slots; low-rank branch, "

@@ -27,8 +27,9 @@ def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray,
       cube_ids [k]; tokens [n] (ascending);
       core [k, Ci] fp32; core_codes [k, Ci] and core_scales [k, Ci/32] (FP8,
       or FP4 for core_bits = 4, the 4-bit point of the pages' core-precision
-      ablation; one exponent per core_group channels: 32, or the pages' 64);
-      core_fmt;
+      ablation; one exponent per core_group channels: 32, or the pages' 64;
+      for core_bits = 16 the bf16 bits of the core, round to nearest even,
+      and no scales); core_fmt;
       delta [n, Ci] fp32; delta_codes [n, Ci/2] packed and delta_scales
       [n, Ci/32] (FP4); U [n, r] bf16 bits.
     """
@@ -45,8 +46,11 @@ def quantize_activation(x32: np.ndarray, g: cubes.Geometry, l1_bits: np.ndarray,
     row_of_cube = np.full(g.K, -1, dtype=np.int64)
     row_of_cube[ids] = np.arange(len(ids))
     delta = cubes.cube_delta(x32, core, g, tokens, row_of_cube)
-    core_fmt = {8: "fp8", 4: "fp4"}[core_bits]
-    core_codes, core_scales = mx.mx_quantize(core, core_fmt, core_group)
+    core_fmt = {8: "fp8", 4: "fp4", 16: "bf16"}[core_bits]
+    if core_fmt == "bf16":
+        core_codes, core_scales = mx.f32_to_bf16_bits(core), None
+    else:
+        core_codes, core_scales = mx.mx_quantize(core, core_fmt, core_group)
     d_codes, d_scales = mx.mx_quantize(delta, "fp4")
     out = dict(cube_ids=ids, tokens=tokens, row_of_cube=row_of_cube, core=core,
                core_codes=core_codes, core_scales=core_scales, core_fmt=core_fmt, delta=delta,
@@ -76,7 +80,7 @@ def forward(q: dict, g: cubes.Geometry, r_codes: np.ndarray, r_scales: np.ndarra
     sel = slice(None) if rows is None else np.asarray(rows)
     tokens = q["tokens"][sel]
     rdq = mx.mx_dequantize(mx.unpack_fp4(r_codes), r_scales, "fp4").T          # [Ci][Co]
-    core_dq = mx.mx_dequantize(q["core_codes"], q["core_scales"], q.get("core_fmt", "fp8"))   # [k][Ci]
+    core_dq = core_values(q)                                                        # [k][Ci]
     delta_dq = mx.mx_dequantize(mx.unpack_fp4(q["delta_codes"][sel]), q["delta_scales"][sel], "fp4")
     lr = mx.bf16_bits_to_f64(q["U"][sel]) @ mx.bf16_bits_to_f64(l2_bits)
     core_rows = q["row_of_cube"][cubes.cube_of_token(g, tokens)]
@@ -84,6 +88,14 @@ def forward(q: dict, g: cubes.Geometry, r_codes: np.ndarray, r_scales: np.ndarra
 
 
 # ------------------------------------------------------------ sanity ----
+def core_values(q: dict) -> np.ndarray:
+    """The quantized cores' values in fp64 (exact), whatever their format."""
+    fmt = q.get("core_fmt", "fp8")
+    if fmt == "bf16":
+        return mx.bf16_bits_to_f64(q["core_codes"])
+    return mx.mx_dequantize(q["core_codes"], q["core_scales"], fmt)
+
+
 def exact_output(x32_rows: np.ndarray, wt32: np.ndarray) -> np.ndarray:
     """X W in fp64 (W = wt32^T)."""
     return np.asarray(x32_rows, dtype=np.float64) @ np.asarray(wt32, dtype=np.float64).T

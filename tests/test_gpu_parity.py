@@ -81,7 +81,7 @@ def _abs_bound(q, g, rc, rs, l2_bits, x_rows, l1_bits):
     Ci = rc.shape[1] * 2
     r = l2_bits.shape[0]
     rdq = np.abs(mx.mx_dequantize(mx.unpack_fp4(rc), rs, "fp4")).T
-    core_abs = np.abs(mx.mx_dequantize(q["core_codes"], q["core_scales"], q.get("core_fmt", "fp8")))
+    core_abs = np.abs(layer.core_values(q))
     delta_abs = np.abs(mx.mx_dequantize(mx.unpack_fp4(q["delta_codes"]), q["delta_scales"], "fp4"))
     rows = q["row_of_cube"][cubes.cube_of_token(g, q["tokens"])]
     blocks = Ci // 64 + 4
@@ -134,7 +134,8 @@ def _full_compare(dqm, L):
     q = layer.quantize_activation(L["x"], L["g"], L["l1"] if L["l1"].shape[1] else None,
                                   core_group=L.get("core_group", 32), core_bits=L.get("core_bits", 8))
     assert np.array_equal(got["core_codes"], q["core_codes"]), "core codes"
-    assert np.array_equal(got["core_scales"], q["core_scales"]), "core scales"
+    if q["core_scales"] is not None:
+        assert np.array_equal(got["core_scales"], q["core_scales"]), "core scales"
     assert np.array_equal(got["delta_scales"], q["delta_scales"]), "delta scales"
     assert np.array_equal(got["delta_codes"], q["delta_codes"]), "delta codes"
     r = lowrank.residual(L["wt"], L["l1"], L["l2"])
@@ -243,6 +244,20 @@ def test_core_fp4(dqm, case):
                n_out=min(4, Ci // 16), core_bits=4, core_group=64 if cube == (2, 2, 2) else 32)
     err, row = _full_compare(dqm, L)
     _say(f"fp4 cores {case}: rel err {err:.2e} worst row {row:.2e}")
+
+
+# bf16 cores (the 16-bit point of the pages' core-precision ablation: the
+# cores rounded to bf16, the core term a library bf16 GEMM against Q4(R)),
+# through every form of the activation pass
+@pytest.mark.parametrize("case", CORE64, ids=[f"{c[0]}x{c[1]}x{c[2]}_c{'x'.join(map(str, c[3]))}_ci{c[4]}_{c[7]}"
+                                              for c in CORE64])
+def test_core_bf16(dqm, case):
+    T, H, W, cube, Ci, Co, rank, dtype = case
+    _say(f"case bf16 cores {case}")
+    L = _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed=T * 100 + Ci + 16, wseed=Co + 13,
+               n_out=min(4, Ci // 16), core_bits=16)
+    err, row = _full_compare(dqm, L)
+    _say(f"bf16 cores {case}: rel err {err:.2e} worst row {row:.2e}")
 
 
 def test_core_group_errors(dqm):

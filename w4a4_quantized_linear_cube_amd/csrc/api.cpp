@@ -13,6 +13,8 @@
 #include <string>
 #include <vector>
 
+#include <rocblas/rocblas.h>
+
 #include "dq.h"
 #include "dq_internal.h"
 
@@ -99,6 +101,9 @@ void free_qact(dq_qact* q) {
     (void)hipFree(q->bias);
     (void)hipFree(q->coref);
     (void)hipFree(q->part);
+    (void)hipFree(q->cbf);
+    (void)hipFree(q->rbf);
+    if (q->blas) (void)rocblas_destroy_handle((rocblas_handle)q->blas);
     delete q;
 }
 
@@ -322,7 +327,7 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
     *out = nullptr;
     if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
     if (core_group != 32 && core_group != 64) return fail(DQ_ERR_INVALID_ARG, "core_group must be 32 or 64");
-    if (core_bits != 8 && core_bits != 4) return fail(DQ_ERR_INVALID_ARG, "core_bits must be 8 or 4");
+    if (core_bits != 8 && core_bits != 4 && core_bits != 16) return fail(DQ_ERR_INVALID_ARG, "core_bits must be 8, 4 or 16");
     if (w->Ci % core_group != 0) return fail(DQ_ERR_SHAPE, "core_group must divide Ci");
     const dq_geom& G = geom;
     if (G.T < 1 || G.H < 1 || G.W < 1) return fail(DQ_ERR_SHAPE, "T, H, W must be >= 1");
@@ -402,6 +407,16 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
             (e = dalloc(&q->part, (size_t)(max_partials * q->Kp), &q->bytes)) != hipSuccess)
             return hip_fail(e, "hipMalloc workspace");
     }
+    if (core_bits == 16) {                          // bf16 cores: Q4(R) as bf16 and a library GEMM
+        if ((e = dalloc(&q->cbf, (size_t)(q->K_pad * q->Kp), &q->bytes)) != hipSuccess ||
+            (e = dalloc(&q->rbf, (size_t)(q->Cop * q->Kp), &q->bytes)) != hipSuccess)
+            return hip_fail(e, "hipMalloc workspace");
+        if ((e = launch_decode_fp4_bf16(w->rq, w->rs, q->Cop, q->Kp, q->rbf, nullptr)) != hipSuccess)
+            return hip_fail(e, "decode Q4(R)");
+        rocblas_handle h = nullptr;
+        if (rocblas_create_handle(&h) != rocblas_status_success) return fail(DQ_ERR_DEVICE, "rocblas_create_handle failed");
+        q->blas = h;
+    }
     if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "workspace init");
     *out = guard.release();
     return DQ_OK;
@@ -447,6 +462,21 @@ static dq_status forward_parts(const dq_weights* w, dq_qact* q, float* y_dev, in
     if (((uintptr_t)y_dev) % 4 != 0) return fail(DQ_ERR_INVALID_ARG, "y_dev must be 4-byte aligned");
     DeviceGuard dg(q->device);
     if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    if (q->core_bits == 16 && (parts & dq::FWD_CORE)) {
+        // bf16 cores: per-cube term [K_pad][Cop] = cores [K_pad][Kp] x (Q4(R) as bf16 [Cop][Kp])^T, fp32
+        // accumulation and output (column-major: term^T = R_bf16 (transposed view) x cores^T)
+        rocblas_handle h = (rocblas_handle)q->blas;
+        const float one = 1.0f, zero = 0.0f;
+        if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success ||
+            rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)q->Cop,
+                            (rocblas_int)q->K_pad, (rocblas_int)q->Kp, &one, q->rbf, rocblas_datatype_bf16_r,
+                            (rocblas_int)q->Kp, q->cbf, rocblas_datatype_bf16_r, (rocblas_int)q->Kp, &zero, q->bias,
+                            rocblas_datatype_f32_r, (rocblas_int)q->Cop, q->bias, rocblas_datatype_f32_r,
+                            (rocblas_int)q->Cop, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) !=
+                rocblas_status_success)
+            return fail(DQ_ERR_DEVICE, "bf16 core GEMM failed");
+        parts &= ~dq::FWD_CORE;
+    }
     hipError_t e = launch_forward(w, q, y_dev, parts, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return DQ_OK;
@@ -511,7 +541,11 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
             if ((e = fetch_all(q->ds, (size_t)(q->Nslot_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy delta scales");
             each_slot([&](long long s, long long t) { unstep_scales(buf, s, Ci, Kp, dscales_host + t * (Ci / 32)); });
         }
-        if (ccodes_host) {
+        if (ccodes_host && q->core_bits == 16) {            // bf16 bits, two bytes per value
+            if ((e = fetch_all(q->cbf, (size_t)(q->K_pad * Kp * 2), buf)) != hipSuccess) return hip_fail(e, "copy cores");
+            for (long long k = 0; k < g.K; ++k)
+                std::memcpy(ccodes_host + k * Ci * 2, &buf[(size_t)(cube_row(k) * Kp * 2)], (size_t)(Ci * 2));
+        } else if (ccodes_host) {
             if ((e = fetch_all(q->cq, (size_t)(q->K_pad * Kp), buf)) != hipSuccess) return hip_fail(e, "copy core codes");
             if (q->core_bits == 4) {                      // packed nibbles -> one code per byte
                 std::vector<uint8_t> row((size_t)(Ci / 2));
@@ -523,7 +557,7 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
                 for (long long k = 0; k < g.K; ++k) unstep_fp8(buf, cube_row(k), Ci, Kp, ccodes_host + k * Ci);
             }
         }
-        if (cscales_host) {
+        if (cscales_host && q->core_bits != 16) {
             if ((e = fetch_all(q->cs, (size_t)(q->K_pad * Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy core scales");
             for (long long k = 0; k < g.K; ++k) unstep_scales(buf, cube_row(k), Ci, Kp, cscales_host + k * (Ci / 32));
         }

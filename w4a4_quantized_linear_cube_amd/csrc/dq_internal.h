@@ -111,7 +111,10 @@ struct dq_qact {
     int rp = 0, rank = 0;
     dq::Geom g{};              // the full token grid and cube shape
     int core_group = 32;       // channels per exponent of the cores (32 or 64)
-    int core_bits = 8;         // cores as MX-FP8 (8) or MX-FP4 (4, the FP4 layout in cq)
+    int core_bits = 8;         // cores as MX-FP8 (8), MX-FP4 (4, the FP4 layout in cq) or bf16 (16, in cbf)
+    uint16_t* cbf = nullptr;   // [K_pad][Kp]        bf16 cores (core_bits 16)
+    uint16_t* rbf = nullptr;   // [Cop][Kp]          Q4(R) decoded to bf16 (core_bits 16)
+    void* blas = nullptr;      // rocBLAS handle of the bf16 core GEMM (core_bits 16)
     int nseg = 1;
     dq_segment seg[2]{};
     int64_t Nslot_pad = 0, K_pad = 0;
@@ -140,6 +143,8 @@ hipError_t launch_encode_fp4_rows(const float* src, int64_t rows, int64_t cols, 
                                   uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t launch_quantize(const dq_weights* w, const void* x, int x_bf16, dq_qact* q, hipStream_t st);
 hipError_t launch_slot_tokens(const Geom& g, int64_t tok0, int* stok, int64_t n, hipStream_t st);
+hipError_t launch_decode_fp4_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t Kp, uint16_t* out,
+                                  hipStream_t st);
 
 // ---- launchers (gemm.hip) ----
 constexpr int FWD_CORE = 1, FWD_DELTA = 2;   // parts of the forward pass

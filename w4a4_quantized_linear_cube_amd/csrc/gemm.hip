@@ -730,7 +730,7 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
     d.sink = q->sink;
     // (32-bit element offsets into y and into the per-cube term)
     const bool off32 = q->g.N * w->Co < (1ll << 31) && q->K_pad * w->Cop * 4 < (1ll << 32);
-    if (q->g.S == 1) {
+    if (q->g.S == 1 && q->core_bits != 16) {
         // One-token cubes: every delta is x - x = 0 exactly, so y = Q8(x) Q4(R)
         // + U L2 (Q4(x) for 4-bit cores), one GEMM over the cubes (cube k is
         // slot k) with the token epilogue and no per-cube term.  It is the delta half's work; the

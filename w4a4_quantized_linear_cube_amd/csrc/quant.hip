@@ -55,7 +55,11 @@ struct QuantArgs {
     const int* stok;          // [Nslot_pad] token of each slot, -1 for pad slots
     int core_g64;             // cores: one exponent per 64 channels (the maximum of two 32-channel groups)
     int core_fp4;             // cores as MX-FP4 (the FP4 layout in cq) instead of MX-FP8
+    uint16_t* cbf;            // bf16 cores [K][Kp] row-major (16-bit cores), else null
 };
+
+// bf16 bits of n consecutive core values (n = 2, 4, 8), packed for one store
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) { return (uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16); }
 
 // LDS chunk layout: 16-byte piece c of row r at r QROWB + ((c ^ (r & 15)) << 4);
 // the XOR makes the quantizer's row reads and the MFMA's column reads free of
@@ -573,6 +577,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const float cmax = core_pair_max<32>(amax, a.core_g64);
                     const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const int gch = c0 + ch;                       // channel within the row
+                    if (a.cbf) a.cbf[k * a.Kp + gch] = bf16_rne(s0);
                     if (a.core_fp4) {
                         // a channel pair's two nibbles meet in its even lane
                         const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0xB1, 0xF, 0xF, false));
@@ -651,6 +656,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const float cmax = core_pair_max<16>(amax, a.core_g64);
                     const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const int gch = c0 + ch;                       // channel within the row
+                    if (a.cbf) *(uint32_t*)(a.cbf + k * a.Kp + gch) = bf16x2(s0, s1);
                     if (a.core_fp4) {
                         *(uint8_t*)(a.cq + off_fp4(k, gch >> 5, nks) + ((gch & 31) >> 1)) =
                             (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s0, s1, pow2f(ex), 0);
@@ -815,6 +821,9 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 amax = core_pair_max<4>(quad_max(amax), a.core_g64);
                 const int ex = a.core_fp4 ? mx_exp_fp4(amax) : mx_exp_fp8(amax);
                 const float sc = pow2f(ex);
+                if (a.cbf)
+                    *(uint4*)(a.cbf + k * a.Kp + G * 32 + 8 * qq) = make_uint4(bf16x2(core[0], core[1]), bf16x2(core[2], core[3]),
+                                                                            bf16x2(core[4], core[5]), bf16x2(core[6], core[7]));
                 if (a.core_fp4) {
                     uint32_t w = 0u;
                     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[0], core[1], sc, 0);
@@ -981,6 +990,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const int gch = c0 + ch;               // channel within the row
                     if (ch < CC) {
                         if (gch < a.Ci) {
+                            if (a.cbf) *(uint32_t*)(a.cbf + k * a.Kp + gch) = bf16x2(s0, s1);
                             if (a.core_fp4) *(uint8_t*)(a.cq + off_fp4(k, gch >> 5, nks) + ((gch & 31) >> 1)) = (uint8_t)cd;
                             else *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) = cd;
                             if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
@@ -1082,6 +1092,8 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const float cmax = core_pair_max<8>(oct_max(amax), a.core_g64);
                     const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const float sc = pow2f(ex);
+                    if (a.cbf)
+                        *(uint2*)(a.cbf + (B.k_first + cr) * a.Kp + G * 32 + 4 * e) = make_uint2(bf16x2(core[0], core[1]), bf16x2(core[2], core[3]));
                     if (a.core_fp4) {
                         uint32_t w = 0u;
                         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[0], core[1], sc, 0);
@@ -1141,6 +1153,9 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
                 amax = core_pair_max<4>(quad_max(amax), a.core_g64);
                 const int kt = (int)(B.k_first & 255) + cr;
+                if (a.cbf)
+                    *(uint4*)(a.cbf + (B.k_first + cr) * a.Kp + G * 32 + 8 * qq) = make_uint4(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]),
+                                                                                         bf16x2(v[4], v[5]), bf16x2(v[6], v[7]));
                 if (a.core_fp4) {
                     const int ex = mx_exp_fp4(amax);
                     const float sc = pow2f(ex);
@@ -1270,6 +1285,7 @@ struct CombineArgs {
     uint8_t* cs;     // K_pad x Kp/32, step-major
     int core_g64;    // one exponent per 64 channels
     int core_fp4;    // MX-FP4 cores (FP4 layout in cq)
+    uint16_t* cbf;   // bf16 cores [K][Kp] (16-bit cores), else null
 };
 
 // core = fl32(sum of the block partials in block order / count), then FP8 codes.
@@ -1312,6 +1328,11 @@ __global__ __launch_bounds__(256) void k_core_combine(CombineArgs a) {
 #pragma unroll
             for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(tile[32 * (j ^ 1) + i]));
         const long long G = cg >> 5, nks = a.Kp / 128;
+        if (a.cbf)
+#pragma unroll
+            for (int i = 0; i < 32; i += 8)
+                *(uint4*)(a.cbf + k * a.Kp + cg + i) = make_uint4(bf16x2(v[i], v[i + 1]), bf16x2(v[i + 2], v[i + 3]),
+                                                                  bf16x2(v[i + 4], v[i + 5]), bf16x2(v[i + 6], v[i + 7]));
         int e;
         if (a.core_fp4) {
             e = mx_exp_fp4(amax);
@@ -1360,6 +1381,38 @@ __global__ __launch_bounds__(256) void k_encode_fp4_rows(const float* src, long 
     int e = mx_exp_fp4(amax);
     *(uint4*)(codes + off_fp4(rrow, grp, Kp / 128)) = encode_fp4x32(v, pow2f(e));
     scales[off_scale(rrow, grp, Kp / 128)] = (uint8_t)(e + 127);
+}
+
+// Q4(R) decoded to bf16 (exact: an FP4 value times a power of two), row-major
+// [rows][Kp], for the bf16-core ablation's library GEMM.  One (row, 32-group)
+// per thread.
+__global__ __launch_bounds__(256) void k_decode_fp4_bf16(const uint8_t* codes, const uint8_t* scales, long long rows,
+                                                        long long Kp, uint16_t* out) {
+    const long long ng = Kp / 32, idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * ng) return;
+    const long long r = idx / ng, G = idx - r * ng, nks = Kp / 128;
+    const uint4 w = *(const uint4*)(codes + off_fp4(r, G, nks));
+    const float sc = ldexpf(1.0f, (int)scales[off_scale(r, G, nks)] - 127);
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+    constexpr float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    uint32_t o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t byte = (d[i >> 2] >> (8 * (i & 3))) & 255u;
+        const float lo = ((byte & 8u) ? -1.0f : 1.0f) * mag[byte & 7u] * sc;
+        const float hi = ((byte & 128u) ? -1.0f : 1.0f) * mag[(byte >> 4) & 7u] * sc;
+        o[i] = bf16x2(lo, hi);
+    }
+    uint4* dst = (uint4*)(out + r * Kp + G * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+}
+
+hipError_t launch_decode_fp4_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t Kp, uint16_t* out,
+                                  hipStream_t st) {
+    const long long n = rows * (Kp / 32);
+    k_decode_fp4_bf16<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(codes, scales, rows, Kp, out);
+    return hipGetLastError();
 }
 
 // Slot -> token table of the GEMM epilogue (-1 for pad slots).
@@ -1412,7 +1465,7 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         CombineArgs ca{g, (int)q->Ci, (int)q->Kp, sg.nblk, q->part, coref, q->core_bits == 4 ? cq4 : cq, cs,
-                       q->core_group == 64, q->core_bits == 4};
+                       q->core_group == 64, q->core_bits == 4, q->cbf ? q->cbf + sg.krow0 * q->Kp : nullptr};
         dim3 grid2((unsigned)g.K, (unsigned)((q->Ci + 255) / 256));
         k_core_combine<<<grid2, 256, 0, st>>>(ca);
         e = hipGetLastError();
@@ -1436,6 +1489,7 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
     a.stok = q->stok + sg.row0;
     a.core_g64 = q->core_group == 64;
     a.core_fp4 = q->core_bits == 4;
+    a.cbf = q->cbf ? q->cbf + sg.krow0 * q->Kp : nullptr;
     if (a.core_fp4) a.cq = cq4;
     const long long cpb = QROWS / g.S;
     a.nblocks = sg.core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;

@@ -135,10 +135,11 @@ class Weights:
 class QAct:
     """Owns a dq_qact handle (keeps its weights alive)."""
 
-    def __init__(self, handle: ctypes.c_void_p, weights: Weights, geom: Tuple[int, ...]):
+    def __init__(self, handle: ctypes.c_void_p, weights: Weights, geom: Tuple[int, ...], core_bits: int = 8):
         self.handle = handle
         self.weights = weights
         self.geom = tuple(geom)
+        self.core_bits = core_bits
         N, K, nb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
         _check(load().dq_qact_info(handle, ctypes.byref(N), ctypes.byref(K), ctypes.byref(nb)), "dq_qact_info")
         self.N, self.K, self.device_bytes = N.value, K.value, nb.value
@@ -198,7 +199,7 @@ def dq_qact_create(w: Weights, geom: Sequence[int], core_group: int = 32, core_b
     else:
         _check(load().dq_qact_create_ex(w.handle, Geom(*geom), core_group, core_bits, ctypes.byref(h)),
                "dq_qact_create_ex")
-    return QAct(h, w, geom)
+    return QAct(h, w, geom, core_bits)
 
 
 def dq_quantize_act(w: Weights, x, q: QAct, stream=None):
@@ -224,10 +225,13 @@ def dq_linear(w: Weights, x, q: QAct, y, stream=None):
 def dq_qact_export(q: QAct, stream=None) -> dict:
     w = q.weights
     N, K, Ci, r = q.N, q.K, w.Ci, w.rank
+    bf16 = q.core_bits == 16                      # bf16 cores: their bits, no scales
     out = dict(delta_codes=np.zeros((N, Ci // 2), np.uint8), delta_scales=np.zeros((N, Ci // 32), np.uint8),
-               core_codes=np.zeros((K, Ci), np.uint8), core_scales=np.zeros((K, Ci // 32), np.uint8),
+               core_codes=np.zeros((K, Ci), np.uint16 if bf16 else np.uint8),
+               core_scales=None if bf16 else np.zeros((K, Ci // 32), np.uint8),
                U=np.zeros((N, r), np.uint16))
     _check(load().dq_qact_export(q.handle, _ptr(out["delta_codes"]), _ptr(out["delta_scales"]),
-                                 _ptr(out["core_codes"]), _ptr(out["core_scales"]), _ptr(out["U"]), _stream(stream)),
+                                 _ptr(out["core_codes"]), _ptr(out["core_scales"]) if not bf16 else None, _ptr(out["U"]),
+                                 _stream(stream)),
            "dq_qact_export")
     return out
