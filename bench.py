@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--cube", default=None, help="t,h,w (default: the config's first cube)")
     ap.add_argument("--x-seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-tokens", type=int, default=24576, help="tokens in the oracle's timed sample (about 10 s of host work)")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per cube shape of the config")
     ap.add_argument("--schedule", action="store_true",
                     help="the timestep-aware cube schedule (4x1x4 early, 4x2x8 after) on the config's layer")
