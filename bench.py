@@ -121,9 +121,10 @@ def work(cfg, cube, core_bits=8):
         "fp8": 2.0 * K * Ci * Co,            # core term, one row per cube (FP8, or FP4 cores)
         "bf16": 2.0 * N * r * (Ci + Co),     # low-rank branch
         # X, delta codes and scales (not stored for one-token cubes: all
-        # zero), core codes and scales, U
+        # zero), core codes and scales (bf16 cores: their bf16 rows and the
+        # FP8 codes, which the pass writes as well), U
         "quant_bytes": xreads * Ci * xbytes + (0 if S == 1 else N * Ci * (0.5 + 1 / 32))
-                       + K * Ci * (core_bits / 8 + 1 / 32) + 2 * N * r,
+                       + K * Ci * ((2 + 1) if core_bits == 16 else core_bits / 8) + K * Ci / 32 + 2 * N * r,
     }
 
 
