@@ -511,6 +511,10 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
         return;
     }
     // quantizer groups: group q takes chunks q, q + SP, q + 2 SP, ...
+    // Their waves issue ahead of the U and copy waves sharing their SIMDs
+    // (those have slack: they wait at the barriers), so a period ends when
+    // the quantizers' work does (2-5 % faster on the 720p FFN layers).
+    __builtin_amdgcn_s_setprio(1);
     for (int k = 0; k < qgrp; ++k) next_chunk();
     int mb = 0;                                      // the group's metadata buffer of its current block
     if (qgrp < total) fill_meta(0, i);
