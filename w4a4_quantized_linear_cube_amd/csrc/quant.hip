@@ -520,6 +520,27 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     if (qgrp < total) fill_meta(0, i);
     if constexpr (TWO) {
         const long long nks = a.Kp / 128;
+        constexpr int NT2 = QROWS * NGC * 4 / 256;   // (row, group, quarter) delta tasks per thread
+        // CM 1: the cores of the group's next chunk, loaded from the earlier
+        // pass's rows one period ahead (they land during the barrier wait
+        // instead of stalling the chunk); rows past the last slot clamp to a
+        // valid cube and columns stay below Kp
+        float4 kn[CM == 1 ? NT2 : 1][2];
+        auto load_cores = [&]() {
+            if constexpr (CM == 1) {
+#pragma unroll
+                for (int n = 0; n < NT2; ++n) {
+                    const int t = qtid + 256 * n;
+                    const int qq = t & 3, pr = t >> 2;
+                    const int r = pr / NGC, gc = pr - r * NGC;
+                    const long long k = min((B.slot0 + r) / g.S, g.K - 1);
+                    const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + (c * CC + gc * 32) + 8 * qq);
+                    kn[n][0] = cp[0];
+                    kn[n][1] = cp[1];
+                }
+            }
+        };
+        if (qgrp < total) load_cores();
         for (long long u = 0; u < nsteps; ++u) {
             barrier();
             const long long s = SP * u + qgrp;
@@ -682,7 +703,6 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 // and channels read zeros from the stage and index a written or
                 // stale core row in bounds), then the stores, predicated, so the
                 // tasks' LDS reads and DPP maxima interleave and quads stay whole
-                constexpr int NT2 = QROWS * NGC * 4 / 256;
                 uint32_t code[NT2];
                 int exq[NT2];
                 bool live[NT2];
@@ -697,12 +717,8 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     qload8<XT>(buf, r, gc, qq, 0u, v);
                     float4 k0, k1;
                     if constexpr (CM == 1) {
-                        // the cube's core row from the earlier pass (clamped for
-                        // rows past the last slot; columns stay below Kp)
-                        const long long k = min((B.slot0 + r) / g.S, g.K - 1);
-                        const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + G * 32 + 8 * qq);
-                        k0 = cp[0];
-                        k1 = cp[1];
+                        k0 = kn[n][0];                         // loaded one period ahead
+                        k1 = kn[n][1];
                     } else {
                         const int cr = r / g.S;
                         k0 = *(const float4*)&cs_[cr][gc * 32 + qq * 8];
@@ -754,6 +770,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     mb ^= 1;
                     fill_meta(mb, i);
                 }
+                load_cores();
             }
         }
     } else {
