@@ -1322,7 +1322,15 @@ __global__ __launch_bounds__(256) void k_core_combine(CombineArgs a) {
     if (c < a.Ci) {
         const float* p = a.part + k * a.nblk * a.Kp + c;
         float s = p[0];
-        for (int b = 1; b < nb; b += 16) {               // in block order, sixteen loads in flight
+        int b = 1;
+        for (; b + 64 <= nb; b += 64) {                   // in block order, 64 loads in flight (large cubes)
+            float v[64];
+#pragma unroll
+            for (int q = 0; q < 64; ++q) v[q] = p[(long long)(b + q) * a.Kp];
+#pragma unroll
+            for (int q = 0; q < 64; ++q) s = s + v[q];
+        }
+        for (; b < nb; b += 16) {                         // the rest, sixteen loads in flight
             float v[16];
 #pragma unroll
             for (int q = 0; q < 16; ++q) v[q] = b + q < nb ? p[(long long)(b + q) * a.Kp] : 0.0f;
