@@ -134,9 +134,11 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
 def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (nearest, ties to even), returned as uint16 bits.
 
-    Written as rounding the value to 8 significant bits: frexp gives
-    x = m 2^k with m in [0.5, 1); rint(m 2^8) is the 8-bit significand
-    rounded with ties to even.  Finite, normal-range inputs only.
+    bf16 keeps fp32's exponent range with 8 significant bits: for
+    x = m 2^k (frexp, m in [0.5, 1)) its grid spacing is 2^(k - 8) for
+    normal values (|x| >= 2^-126, k >= -125), and the fixed subnormal
+    spacing 2^-133 below that.  rint(x / spacing) rounds to that grid with
+    ties to even.  Finite inputs below the bf16 overflow threshold.
     """
     x = np.asarray(x32, dtype=np.float64)
     return f64_to_bf16_bits(x)
@@ -144,10 +146,12 @@ def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
 
 def f64_to_bf16_bits(x64: np.ndarray) -> np.ndarray:
     x = np.asarray(x64, dtype=np.float64)
-    m, k = np.frexp(x)
-    r = np.ldexp(np.rint(np.ldexp(m, 8)), k - 8)      # exact: <= 9 significant bits
-    bits = r.astype(np.float32).view(np.uint32)       # exact: r has <= 8 significant bits
-    return (bits >> 16).astype(np.uint16)
+    _, k = np.frexp(x)
+    q = np.maximum(k, -125) - 8                        # log2 of the grid spacing at x
+    r = np.ldexp(np.rint(np.ldexp(x, -q)), q)          # exact: <= 9 significant bits
+    bits = r.astype(np.float32).view(np.uint32)        # exact: r lies on the bf16 grid
+    sign = np.signbit(x).astype(np.uint32) << 31       # keeps -0 (and values that round to -0)
+    return (((bits & 0x7FFFFFFF) | sign) >> 16).astype(np.uint16)
 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:

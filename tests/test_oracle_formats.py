@@ -205,3 +205,14 @@ def test_bf16_rounding_matches_torch():
     x = x[np.isfinite(x) & (np.abs(x) > 1.2e-38) & (np.abs(x) < 3e38)]
     ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(mx.f32_to_bf16_bits(x), ref)
+
+
+def test_bf16_rounding_of_subnormals_and_zeros_matches_torch():
+    """Every fp32 subnormal pattern of both signs (the bf16 grid there is the
+    fixed spacing 2^-133), the signed zeros, and the smallest normals."""
+    mags = np.arange(0, 1 << 23, dtype=np.uint32)
+    normals = np.arange(0x00800000, 0x00800000 + (1 << 20), dtype=np.uint32)
+    bits = np.concatenate([mags, mags | 0x80000000, normals, normals | 0x80000000])
+    x = bits.view(np.float32)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mx.f32_to_bf16_bits(x), ref)
