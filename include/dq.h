@@ -91,14 +91,17 @@ dq_status dq_lowrank_factors(const void* w_host, dq_dtype dt, int64_t Ci, int64_
  * rank order, then MX-FP4-encodes each output channel of R along Ci.
  *   w_host   [Co][Ci] W^T (dtype dt);  l1_host [Ci][rank], l2_host [rank][Co]
  *            bf16 bits (may be NULL when rank == 0)
- * Requires Ci % 32 == 0, Ci >= 32, Co >= 1, 0 <= rank <= min(Ci, Co).
+ * Requires Ci % 32 == 0, 32 <= Ci <= 2^24, 1 <= Co <= 2^24 and
+ * 0 <= rank <= min(Ci, Co, 128) (the activation pass keeps U's rank tiles
+ * on chip; DQ_ERR_INVALID_ARG above 128).  l1_host and l2_host must hold
+ * Ci*rank and rank*Co values: the library cannot check their sizes.
  * The handle owns every device buffer it allocates; free it with
  * dq_weights_destroy.  Synchronous (returns when the weight is ready). */
 dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
                                      const uint16_t* l1_host, const uint16_t* l2_host, int32_t device,
                                      dq_weights** out);
 
-/* dq_lowrank_factors followed by dq_prepare_weights_lowrank. */
+/* dq_lowrank_factors followed by dq_prepare_weights_lowrank (so rank <= 128). */
 dq_status dq_prepare_weights(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
                              uint64_t seed, int32_t device, dq_weights** out);
 
@@ -157,14 +160,20 @@ dq_status dq_qact_info(const dq_qact* q, int64_t* N, int64_t* K, int64_t* device
  * token, delta = fl32(x - core); cores -> MX-FP8, deltas -> MX-FP4 (smallest
  * power-of-two scale with max|v| <= q_max 2^e, round to nearest even); and
  * U = bf16(bf16(X) L1) with fp32 accumulation.
- *   x_dev  [N][Ci] of dtype dt, N = T*H*W of the workspace's geometry.
+ *   x_dev  [N][Ci] of dtype dt, N = T*H*W of the workspace's geometry (the
+ *          geometry is the one given to dq_qact_create, held by `q`),
+ *          contiguous and 16-byte aligned (DQ_ERR_INVALID_ARG otherwise).
+ *          Its size cannot be checked here: a shorter buffer is read out of
+ *          bounds.
  * Asynchronous on `stream`. */
 dq_status dq_quantize_act(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, void* stream);
 
 /* The GEMMs (关键设计 4, the three-term equation): for every token n of cube
  * k, y[n] = U[n] L2 + Q8(core_k) Q4(R) + Q4(delta_n) Q4(R), fp32 accumulation,
- * written to y_dev [N][Co] fp32 (every element written).  Uses the state left
- * in `q` by the last dq_quantize_act.  Asynchronous on `stream`. */
+ * written to y_dev [N][Co] fp32 (every element written; contiguous, 4-byte
+ * aligned, else DQ_ERR_INVALID_ARG; a shorter buffer is written out of
+ * bounds, which the library cannot detect).  Uses the state left in `q` by
+ * the last dq_quantize_act.  Asynchronous on `stream`. */
 dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
 
 /* The two halves of dq_linear_forward, in its order, for callers that time

@@ -1,9 +1,14 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Bars: delta/core/R codes and scale codes bit-exact; U within one bf16 ulp;
-the fp32 output within 2e-3 relative Frobenius error (and every row within
-2e-3 relative, to catch a misplaced row).  Small layers are compared in
-full; the full-size layers on sampled whole cubes (partial cubes included).
+Bars: delta/core/R codes and scale codes bit-exact; U within one bf16 ulp
+plus the fp32 summation bound; the fp32 output within 2e-3 relative
+Frobenius error, every element inside the accumulation bound derived from
+the instruction precisions (_abs_bound), and every row within ROW_TOL
+relative (a misplaced or wrong row is off by O(1)).  Single rows can exceed
+2e-3 relative where their terms cancel: the FP8 x FP4 MFMA keeps about 13
+bits, and the worst row measured is 3.5e-3 (720p FFN down, 1x4x4 cubes).
+Small layers are compared in full; the full-size layers' codes and scales on
+every cube, their outputs on sampled whole cubes (partial cubes included).
 Factors L1, L2 come from the oracle's LAPACK SVD (small layers) or from a
 seeded generator (full-size layers): parity is about computing the layer
 for given factors; the library's own SVD is checked by its properties.
@@ -22,6 +27,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 TOL = 2e-3
+ROW_TOL = 1e-2
 
 
 def _say(msg):
@@ -101,6 +107,7 @@ def _check_y(y, yo, bound=None):
     den = np.linalg.norm(yo.astype(np.float64), axis=1) + 1e-30
     row = float((num / den).max())
     assert err <= TOL, f"rel Frobenius error {err}"
+    assert row <= ROW_TOL, f"worst row relative error {row}"
     if bound is not None:
         diff = np.abs(y.astype(np.float64) - yo.astype(np.float64))
         lim = bound + 2.0 ** -23 * np.abs(yo.astype(np.float64))
@@ -319,9 +326,10 @@ def test_forward_halves_match_forward(dqm):
     assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
 
 def test_library_svd_path(dqm):
-    """dq_prepare_weights: the host SVD factors meet Eckart-Young, and R / Q4(R)
-    follow from them (R = fl32(W - L1 L2) within one rounding; codes decode to
-    within the MX-FP4 step of R)."""
+    """dq_prepare_weights: the host SVD factors meet Eckart-Young, and R and
+    Q4(R) are those the oracle forms from the library's own factors, bit for
+    bit (R = fl32(W - L1 L2) with the product summed in fp64 in rank order,
+    then MX-FP4 along Ci)."""
     _say("case library svd")
     Ci, Co, r = 256, 384, 32
     wt = synth.make_weight(Ci, Co, seed=31, dtype="bf16", outlier_rows=3)
@@ -331,12 +339,11 @@ def test_library_svd_path(dqm):
     s = np.linalg.svd(wf.astype(np.float64), compute_uv=False)
     ey = lowrank.eckart_young_ratio(wf, e["l1"], e["l2"], s)
     assert ey["err"] <= (1 + 1e-3) * ey["best"] + ey["bf16_slack"], ey
-    p = (mx.bf16_bits_to_f64(e["l1"]) @ mx.bf16_bits_to_f64(e["l2"])).T
-    exact = wf.astype(np.float64) - p
-    assert np.all(np.abs(e["r"] - exact) <= 2.0 ** -24 * np.abs(exact))
-    deq = mx.mx_dequantize(mx.unpack_fp4(e["rcodes"]), e["rscales"], "fp4")
-    step = np.ldexp(1.0, e["rscales"].astype(np.int64) - 127)          # 2^e: half the widest FP4 gap
-    assert np.all(np.abs(deq - e["r"]).reshape(Co, Ci // 32, 32) <= step[..., None])
+    ro = lowrank.residual(wf, e["l1"], e["l2"])
+    assert np.array_equal(e["r"].view(np.uint32), ro.view(np.uint32)), "R"
+    rc, rs = lowrank.quantize_residual(ro)
+    assert np.array_equal(e["rcodes"], rc), "Q4(R) codes"
+    assert np.array_equal(e["rscales"], rs), "Q4(R) scale codes"
 
 
 # -------------------------------------------------------- full size, sampled ----
@@ -368,7 +375,39 @@ def _oracle_weight(cfg):
     return _WEIGHT_CACHE[cfg.name]
 
 
-def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=512, versus_direct=False):
+def _workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _compare_every_cube(got, xf, g, chunk=2048):
+    """Core codes and scale codes of every cube and delta codes and scale
+    codes of every token, against the oracle's steps (cube cores, deltas
+    against them, MX encoding: what layer.quantize_activation does), taken in
+    chunks of cubes and tokens on a thread pool (numpy releases the GIL in
+    the bulk of this work).  Bit-exact."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    core = cubes.cube_core(xf, g)
+
+    def cores(k0):
+        c, sc = mx.mx_quantize(core[k0:k0 + chunk], "fp8")
+        ok = np.array_equal(got["core_codes"][k0:k0 + chunk], c) and np.array_equal(got["core_scales"][k0:k0 + chunk], sc)
+        return None if ok else f"core codes or scales differ in cubes [{k0}, {k0 + chunk})"
+
+    def deltas(n0):
+        toks = np.arange(n0, min(g.N, n0 + chunk))
+        c, sc = mx.mx_quantize(cubes.cube_delta(xf, core, g, toks), "fp4")
+        ok = np.array_equal(got["delta_codes"][toks], mx.pack_fp4(c)) and np.array_equal(got["delta_scales"][toks], sc)
+        return None if ok else f"delta codes or scales differ in tokens [{n0}, {n0 + chunk})"
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        bad = [m for m in ex.map(cores, range(0, g.K, chunk)) if m]
+        bad += [m for m in ex.map(deltas, range(0, g.N, chunk)) if m]
+    assert not bad, bad[:4]
+
+
+def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=512, versus_direct=False,
+                    every_cube=True):
     T, H, W = cfg.T, cfg.H, cfg.W
     g = cubes.Geometry(T, H, W, *cube)
     _say(f"case {cfg.name} cube {cube} seed {xseed}: generating")
@@ -382,6 +421,10 @@ def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=5
     torch.cuda.synchronize()
     assert not torch.isnan(y).any().item(), "unwritten outputs"
     got = dqm.dq_qact_export(qa)
+    xf = synth.to_f32_numpy(x)
+    if every_cube:
+        _say(f"case {cfg.name} cube {cube}: codes of every cube against the oracle")
+        _compare_every_cube(got, xf, g)
     ids = _sample_cubes(g, n_cubes, xseed)
     tbl, cnt = cubes.cube_tokens(g, ids)
     toks = np.sort(tbl[tbl >= 0])
@@ -391,7 +434,6 @@ def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=5
         keep = np.concatenate([toks[part][:max_rows // 2],
                                rng.choice(toks[~part], size=max_rows - min(part.sum(), max_rows // 2), replace=False)])
         toks = np.sort(keep)
-    xf = synth.to_f32_numpy(x)
     _say(f"case {cfg.name} cube {cube}: oracle on {len(ids)} cubes, {len(toks)} tokens")
     q = layer.quantize_activation(xf, g, l1, cube_ids=ids, tokens=toks)
     assert np.array_equal(got["core_codes"][ids], q["core_codes"]), "core codes"

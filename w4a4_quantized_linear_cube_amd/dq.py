@@ -112,8 +112,58 @@ def _dtype_of(t) -> int:
 def _host_weight(w):
     """W^T [Co][Ci] as a contiguous CPU torch tensor; returns (tensor, dtype code)."""
     import torch
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise DQError(1, "weight", "the weight must be a 2-D torch tensor [Co][Ci]")
     w = w.detach().to("cpu").contiguous()
     return w, _dtype_of(w)
+
+
+def _invalid(func: str, msg: str):
+    raise DQError(1, func, msg)
+
+
+def _device_tensor(func: str, name: str, t, shape, dtypes, device: int, align: int):
+    """Checks a caller-owned device buffer before its pointer crosses the C ABI,
+    which cannot see sizes: a torch tensor of one of `dtypes`, exactly `shape`,
+    contiguous, on CUDA device `device`, its data `align`-byte aligned."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        _invalid(func, f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        _invalid(func, f"{name} has dtype {t.dtype}; expected one of {[str(d) for d in dtypes]}")
+    if tuple(t.shape) != tuple(shape):
+        _invalid(func, f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    if not t.is_contiguous():
+        _invalid(func, f"{name} must be contiguous")
+    if t.device.type != "cuda" or t.device.index != device:
+        _invalid(func, f"{name} is on {t.device}; expected cuda:{device}")
+    if t.data_ptr() % align:
+        _invalid(func, f"{name} must be {align}-byte aligned")
+
+
+def _check_x(func: str, w: "Weights", q: "QAct", x):
+    import torch
+    _device_tensor(func, "x", x, (q.N, w.Ci), (torch.bfloat16, torch.float32), w.device, 16)
+
+
+def _check_y(func: str, w: "Weights", q: "QAct", y):
+    import torch
+    _device_tensor(func, "y", y, (q.N, w.Co), (torch.float32,), w.device, 4)
+
+
+def _check_pair(func: str, w: "Weights", q: "QAct"):
+    if q.weights is not w and (q.weights.Ci, q.weights.Co, q.weights.rank) != (w.Ci, w.Co, w.rank):
+        _invalid(func, "the workspace was created for a different weight")
+
+
+def _factor(func: str, name: str, a, shape):
+    """A bf16 factor given as uint16 (or int16) bits of exactly `shape`."""
+    a = np.asarray(a)
+    if a.dtype not in (np.uint16, np.int16):
+        _invalid(func, f"{name} must hold bf16 bits as uint16 (got {a.dtype})")
+    if a.shape != tuple(shape):
+        _invalid(func, f"{name} has shape {a.shape}; expected {tuple(shape)}")
+    return np.ascontiguousarray(a.view(np.uint16))
 
 
 class Weights:
@@ -161,11 +211,16 @@ def dq_lowrank_factors(w, rank: int, seed: int):
 
 
 def dq_prepare_weights_lowrank(w, l1: Optional[np.ndarray], l2: Optional[np.ndarray], device: int = 0) -> Weights:
+    f = "dq_prepare_weights_lowrank"
     wt, dt = _host_weight(w)
     Co, Ci = wt.shape
-    rank = 0 if l1 is None else l1.shape[1]
-    l1c = None if l1 is None else np.ascontiguousarray(l1, dtype=np.uint16)
-    l2c = None if l2 is None else np.ascontiguousarray(l2, dtype=np.uint16)
+    if (l1 is None) != (l2 is None):
+        _invalid(f, "give both factors or neither")
+    rank = 0 if l1 is None else np.asarray(l1).shape[-1]
+    if l1 is not None and np.asarray(l1).ndim != 2:
+        _invalid(f, "l1 must be 2-D [Ci][rank]")
+    l1c = None if l1 is None else _factor(f, "l1", l1, (Ci, rank))
+    l2c = None if l2 is None else _factor(f, "l2", l2, (rank, Co))
     h = ctypes.c_void_p()
     _check(load().dq_prepare_weights_lowrank(_ptr(wt), dt, Ci, Co, rank, _ptr(l1c), _ptr(l2c), device,
                                              ctypes.byref(h)), "dq_prepare_weights_lowrank")
@@ -203,22 +258,32 @@ def dq_qact_create(w: Weights, geom: Sequence[int], core_group: int = 32, core_b
 
 
 def dq_quantize_act(w: Weights, x, q: QAct, stream=None):
+    _check_pair("dq_quantize_act", w, q)
+    _check_x("dq_quantize_act", w, q, x)
     _check(load().dq_quantize_act(w.handle, _ptr(x), _dtype_of(x), q.handle, _stream(stream)), "dq_quantize_act")
 
 
 def dq_linear_forward(w: Weights, q: QAct, y, stream=None):
+    _check_pair("dq_linear_forward", w, q)
+    _check_y("dq_linear_forward", w, q, y)
     _check(load().dq_linear_forward(w.handle, q.handle, _ptr(y), _stream(stream)), "dq_linear_forward")
 
 
 def dq_core_term(w: Weights, q: QAct, stream=None):
+    _check_pair("dq_core_term", w, q)
     _check(load().dq_core_term(w.handle, q.handle, _stream(stream)), "dq_core_term")
 
 
 def dq_delta_term(w: Weights, q: QAct, y, stream=None):
+    _check_pair("dq_delta_term", w, q)
+    _check_y("dq_delta_term", w, q, y)
     _check(load().dq_delta_term(w.handle, q.handle, _ptr(y), _stream(stream)), "dq_delta_term")
 
 
 def dq_linear(w: Weights, x, q: QAct, y, stream=None):
+    _check_pair("dq_linear", w, q)
+    _check_x("dq_linear", w, q, x)
+    _check_y("dq_linear", w, q, y)
     _check(load().dq_linear(w.handle, _ptr(x), _dtype_of(x), q.handle, _ptr(y), _stream(stream)), "dq_linear")
 
 
