@@ -10,11 +10,15 @@ value  = effective TOPS of the whole step, 2 N Ci Co / t_step (the dense
 roofline = the dominant kernel, the delta GEMM (dq_delta_term: one launch of
          the FP4 x FP4 scaled-MFMA GEMM over the slots, with the low-rank
          branch, the core-term broadcast and the token-order stores in its
-         epilogue): algorithmic FP4 flops per launch, 2 N_slot Ci Co, / its
-         average duration from HIP events on the launch stream, against the
-         dense FP4 peak; traffic from the committed rocprofv3 counter summary
-         of the same kernel source, else null.
-cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+         epilogue): algorithmic FP4 flops per launch, 2 N Ci Co (one row per
+         token: the pad slots of clipped cubes are executed but not counted;
+         their share is reported as pad_slot_waste), / its average duration
+         from HIP events on the launch stream, against the dense FP4 peak;
+         traffic from the committed rocprofv3 counter summary of the same
+         kernel source, else null.  With one-token cubes the delta term is
+         one FP8 x FP4 GEMM over the cubes and is rated against the FP8 peak.
+cpu_baseline = the CPU oracle on a bounded sample of the same workload, its
+         time extrapolated to the whole layer by the token count.
 
 --sweep instead prints one JSON line per cube shape of the config's list
 (e.g. --config ffn_down_720p --sweep: 1x1x1, 1x2x2, 2x2x2, 1x4x4 and one
@@ -112,19 +116,22 @@ def work(cfg, cube, core_bits=8):
     segs = [(T0, t_)] + ([(cfg.T - T0, cfg.T - T0)] if T0 < cfg.T else [])
     K = sum(-(-Ts // ts) * Hc * Wc for Ts, ts in segs)
     Nslot = sum(-(-Ts // ts) * Hc * Wc * ts * h_ * w_ for Ts, ts in segs)
-    # X once (twice in a segment of cubes of more than 64 tokens)
-    xreads = sum(Ts * cfg.H * cfg.W * (2 if ts * h_ * w_ > 64 else 1) for Ts, ts in segs)
+    # cubes of more than 64 tokens read X a second time (the partial-sum
+    # pass): traffic beyond the algorithmic bytes, reported on its own
+    xreread = sum(Ts * cfg.H * cfg.W for Ts, ts in segs if ts * h_ * w_ > 64) * Ci * xbytes
     return {
-        "K": K, "S": S, "Nslot": Nslot,
+        "K": K, "S": S, "Nslot": Nslot, "N_tok": N,
         "dense": 2.0 * N * Ci * Co,
-        "fp4": 2.0 * Nslot * Ci * Co,        # delta term, one row per slot (pad slots of clipped cubes included)
+        "fp4": 2.0 * N * Ci * Co,            # delta term, one row per token (algorithmic)
+        "fp4_slots": 2.0 * Nslot * Ci * Co,  # executed: one row per slot, pad slots of clipped cubes included
         "fp8": 2.0 * K * Ci * Co,            # core term, one row per cube (FP8, or FP4 cores)
         "bf16": 2.0 * N * r * (Ci + Co),     # low-rank branch
-        # X, delta codes and scales (not stored for one-token cubes: all
+        # X once, delta codes and scales (not stored for one-token cubes: all
         # zero), core codes and scales (bf16 cores: their bf16 rows and the
         # FP8 codes, which the pass writes as well), U
-        "quant_bytes": xreads * Ci * xbytes + (0 if S == 1 else N * Ci * (0.5 + 1 / 32))
+        "quant_bytes": N * Ci * xbytes + (0 if S == 1 else N * Ci * (0.5 + 1 / 32))
                        + K * Ci * ((2 + 1) if core_bits == 16 else core_bits / 8) + K * Ci / 32 + 2 * N * r,
+        "x_reread_bytes": xreread,
     }
 
 
@@ -156,8 +163,23 @@ def shape_record(cfg, cube, ms, q_ms, c_ms, d_ms, core_bits=8):
         "core_term": {"ms": round(c_ms, 4)} if one else
                      {"ms": round(c_ms, 4), ck: round(wk["fp8"] / (c_ms * 1e-3) / 1e12, 1)},
         "delta_term": {"ms": round(d_ms, 4), ck: round(wk["fp8"] / (d_ms * 1e-3) / 1e12, 1)} if one else
-                      {"ms": round(d_ms, 4), "fp4_tflops": round(wk["fp4"] / (d_ms * 1e-3) / 1e12, 1)},
+                      {"ms": round(d_ms, 4), "fp4_tflops": round(wk["fp4"] / (d_ms * 1e-3) / 1e12, 1),
+                       "pad_slot_waste": round(wk["fp4_slots"] / wk["fp4"] - 1, 4)},
+        "core_overhead": core_overhead(wk, c_ms, d_ms, core_bits),
     }
+
+
+def core_overhead(wk, c_ms, d_ms, core_bits=8):
+    """The core term's cost next to the delta term's, the analogue of the
+    pages' overhead figure for the core tokens' W4A8 GEMM (+3.2 % at cube size
+    64, DeltaQuant page, 关键设计 4 and 亮点与洞察).  Measured: core-term time
+    over delta-term time.  Rate model: the core GEMM has 1/S of the delta
+    GEMM's rows and, for FP8 cores, runs at half the FP4 rate, so 2/S."""
+    if wk["S"] == 1:
+        return None
+    rate = {8: 2.0, 4: 1.0, 16: 4.0}[core_bits]
+    return {"measured_pct": round(100 * c_ms / d_ms, 2), "rate_model_pct": round(100 * rate * wk["K"] / wk["N_tok"], 2),
+            "pages_pct_at_cube_64": 3.2}
 
 
 # Timestep-aware cube sizes (DeltaQuant notes, 损失函数/训练策略): 16-token
@@ -290,7 +312,18 @@ def main():
     del csrc, cdst
 
     value = dense_flops / (ms_step * 1e-3) / 1e12
-    achieved = f_fp4 / (d_ms * 1e-3)
+    # the dominant kernel: the delta GEMM (FP4 x FP4) on 2 N Ci Co; with
+    # one-token cubes it is the FP8 x FP4 GEMM over the cubes (FP4 x FP4 for
+    # FP4 cores), on 2 K Ci Co
+    if S == 1:
+        rl_flops, rl_peak = f_fp8, {8: PEAK_FP8, 4: PEAK_FP4, 16: PEAK_FP8}[args.core_bits]
+        rl_kernel = ("GEMM over the one-token cubes (dq_delta_term: FP8 x FP4 scaled MFMA, Q8(x) Q4(R); "
+                     "low-rank branch and token-order stores in the epilogue)")
+    else:
+        rl_flops, rl_peak = f_fp4, PEAK_FP4
+        rl_kernel = ("delta GEMM (dq_delta_term: FP4 x FP4 scaled MFMA over the slots; low-rank branch, "
+                     "core-term broadcast and token-order stores in the epilogue)")
+    achieved = rl_flops / (d_ms * 1e-3)
     traffic = committed_traffic(args.config, cube)
 
     cpu = None
@@ -308,7 +341,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"mxfp4 (deltas, R) + {'bf16' if args.core_bits == 16 else 'mxfp%d' % args.core_bits} (cores) + bf16 (low rank), fp32 accumulate",
+        "dtype": "mxfp4" if args.core_bits == 4 else ("mxfp4+bf16" if args.core_bits == 16 else "mxfp4+mxfp8"),
+        "precision": ("deltas and R in MX-FP4 (FP4 x FP4 scaled MFMA: each 64-term block exact, rounded once into "
+                      "fp32); cores in " + {8: "MX-FP8 (FP8 x FP4 scaled MFMA keeps about 13 bits per block)",
+                                            4: "MX-FP4", 16: "bf16 (bf16 MFMA, fp32 accumulation)"}[args.core_bits]
+                      + "; low-rank branch in bf16 with fp32 accumulation; fp32 output"),
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: X {N}x{Ci} ({T}x{H}x{W} tokens) {cfg.dtype} -> Y {N}x{Co} fp32, "
@@ -325,27 +362,30 @@ def main():
         "quantize": {
             "ms": round(q_ms, 4),
             "algorithmic_bytes": int(quant_bytes),
+            "x_reread_bytes": int(wk["x_reread_bytes"]),
             "GBps": round(quant_bytes / (q_ms * 1e-3) / 1e9, 1),
             "pct_hbm": round(100 * quant_bytes / (q_ms * 1e-3) / PEAK_HBM, 2),
             "copy_GBps": round(copy_gbps, 1),
             "pct_copy": round(100 * quant_bytes / (q_ms * 1e-3) / 1e9 / copy_gbps, 2),
         },
+        "core_overhead": core_overhead(wk, c_ms, d_ms, args.core_bits),
         "core_term": {
             "ms": round(c_ms, 4),
             f"{ctype}_tflops": round(f_fp8 / (c_ms * 1e-3) / 1e12, 2),
             f"pct_{ctype}_peak": round(100 * f_fp8 / (c_ms * 1e-3) / {8: PEAK_FP8, 4: PEAK_FP4, 16: PEAK_BF16}[args.core_bits], 2),
         },
         "roofline": {
-            "kernel": "delta GEMM (dq_delta_term: FP4 x FP4 scaled MFMA over the slots; low-rank branch, "
-                      "core-term broadcast and token-order stores in the epilogue)",
+            "kernel": rl_kernel,
             "bound": "mfma",
             "achieved": round(achieved / 1e12, 2),
-            "peak": round(PEAK_FP4 / 1e12, 2),
+            "peak": round(rl_peak / 1e12, 2),
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP4, 4),
+            "frac": round(achieved / rl_peak, 4),
             "traffic": traffic,
             "ms": round(d_ms, 4),
-            "work": {"fp4_flops": f_fp4, "fp8_flops": f_fp8, "bf16_flops": f_bf16},
+            "work": {"fp4_flops": f_fp4, "fp4_flops_executed": wk["fp4_slots"], "fp8_flops": f_fp8,
+                     "bf16_flops": f_bf16},
+            "pad_slot_waste": round(wk["fp4_slots"] / f_fp4 - 1, 4),
         },
         "cpu_baseline": cpu,
     }
@@ -412,8 +452,10 @@ def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
         "unit": "TOPS",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{len(ids)} whole cubes ({n} tokens) of the same layer: activation pass + forward, "
-                  f"{dt:.2f} s wall",
+        "sample": f"{len(ids)} whole cubes ({n} of {cfg.N} tokens) of the same layer: activation pass + forward, "
+                  f"{dt:.2f} s wall; the whole layer extrapolated by the token count",
+        "extrapolated": True,
+        "full_layer_s": round(dt * cfg.N / n, 1),
     }
 
 
