@@ -205,6 +205,23 @@ dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact
 dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscales_host, uint8_t* ccodes_host,
                          uint8_t* cscales_host, uint16_t* u_host, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): dq_linear
+ * for the geometry `geom` with MX-FP8 cores in groups of 32, without a
+ * dq_qact.  The activation state (codes, scales, U, per-cube core term, slot
+ * table) lives in a fixed per-device array of 128 MiB that the library holds
+ * on every GPU it runs on until the process ends; the call allocates nothing
+ * and calls no allocating routine.  Same arguments and layouts as
+ * dq_quantize_act and dq_linear_forward (x_dev [N][Ci] 16-byte aligned,
+ * y_dev [N][Co] fp32 4-byte aligned, every element written), with the same
+ * results as dq_linear bit for bit.  Errors: those of dq_qact_create and
+ * dq_linear, and DQ_ERR_SHAPE (with the bytes needed) when the layer does
+ * not fit the array.  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (two streams, or two threads) race and give wrong
+ * results; serialize them.  Asynchronous on `stream`. */
+dq_status dq_linear_noalloc(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_geom geom, float* y_dev,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

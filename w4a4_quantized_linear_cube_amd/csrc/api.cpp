@@ -24,24 +24,19 @@ void lowrank_svd(const float* wt, int64_t Ci, int64_t Co, int rank, uint64_t see
 
 namespace {
 thread_local std::string g_last_error;
+}  // namespace
 
 dq_status fail(dq_status s, const std::string& msg) {
     g_last_error = msg;
     return s;
 }
 
-// Makes the handle's device current for the scope and restores the caller's.
-struct DeviceGuard {
-    int prev = -1;
-    bool ok = false;
-    explicit DeviceGuard(int dev) {
-        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-        ok = hipSetDevice(dev) == hipSuccess;
-    }
-    ~DeviceGuard() {
-        if (prev >= 0) (void)hipSetDevice(prev);
-    }
-};
+dq_status hip_fail(hipError_t e, const char* what) {
+    if (e == hipErrorOutOfMemory) return fail(DQ_ERR_OUT_OF_MEMORY, std::string(what) + ": out of device memory");
+    return fail(DQ_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+namespace {
 
 dq_status check_device(int device) {
     int n = 0;
@@ -52,11 +47,6 @@ dq_status check_device(int device) {
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(DQ_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", gfx950 required");
     return DQ_OK;
-}
-
-dq_status hip_fail(hipError_t e, const char* what) {
-    if (e == hipErrorOutOfMemory) return fail(DQ_ERR_OUT_OF_MEMORY, std::string(what) + ": out of device memory");
-    return fail(DQ_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
 
 // Zero-filled device allocation.
@@ -320,12 +310,13 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
     return dq_qact_create_ex(w, geom, 32, 8, out);
 }
 
-dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, int32_t core_bits,
-                            dq_qact** out) {
-    g_last_error.clear();
-    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
-    *out = nullptr;
-    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+}  // extern "C"
+
+namespace dq {
+// Checks a geometry and the core options against a weight and fills the
+// workspace's sizes and frame segments (no allocation, no device work).
+dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, int core_bits, dq_qact* q,
+                    int64_t* max_partials_out) {
     if (core_group != 32 && core_group != 64) return fail(DQ_ERR_INVALID_ARG, "core_group must be 32 or 64");
     if (core_bits != 8 && core_bits != 4 && core_bits != 16) return fail(DQ_ERR_INVALID_ARG, "core_bits must be 8, 4 or 16");
     if (w->Ci % core_group != 0) return fail(DQ_ERR_SHAPE, "core_group must divide Ci");
@@ -341,12 +332,6 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
     if (N > (int64_t(1) << 31) || !mul_ok(K, S, lim)) return fail(DQ_ERR_SHAPE, "token grid too large");
     int64_t Nslot = K * S;
     if (Nslot > (int64_t(1) << 31) - MPAD) return fail(DQ_ERR_SHAPE, "slot count too large");
-    DeviceGuard dg(w->device);
-    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
-
-    auto* q = new (std::nothrow) dq_qact();
-    if (!q) return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
-    std::unique_ptr<dq_qact, void (*)(dq_qact*)> guard(q, free_qact);
     q->device = w->device;
     q->Ci = w->Ci;
     q->Co = w->Co;
@@ -385,6 +370,27 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
     q->K_pad = krow;
     if (!mul_ok(q->Nslot_pad, q->Kp, lim) || !mul_ok(q->K_pad, q->Cop, lim) || !mul_ok(max_partials, q->Kp, lim))
         return fail(DQ_ERR_SHAPE, "workspace too large");
+    *max_partials_out = max_partials;
+    return DQ_OK;
+}
+}  // namespace dq
+
+extern "C" {
+
+dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, int32_t core_bits,
+                            dq_qact** out) {
+    g_last_error.clear();
+    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    auto* q = new (std::nothrow) dq_qact();
+    if (!q) return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    std::unique_ptr<dq_qact, void (*)(dq_qact*)> guard(q, free_qact);
+    int64_t max_partials = 0;
+    dq_status st = plan_qact(w, geom, core_group, core_bits, q, &max_partials);
+    if (st != DQ_OK) return st;
+    DeviceGuard dg(w->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
     hipError_t e;
     if ((e = dalloc(&q->dq, (size_t)(q->Nslot_pad * q->Kp / 2), &q->bytes)) != hipSuccess ||
         (e = dalloc(&q->ds, (size_t)(q->Nslot_pad * q->Kp / 32), &q->bytes)) != hipSuccess ||

@@ -21,6 +21,10 @@ constexpr int MPAD = 256;
 constexpr int NPAD = 256;
 constexpr int RPAD = 32;      // low-rank width padded for 32x32 bf16 MFMA tiles
 constexpr int CORE_BLOCK = 64;  // tokens per fp32 partial sum of a cube's core
+// Size of the per-device array that dq_linear_noalloc carves its activation
+// workspace from (128 MiB: the Wan 1.3B projection, 32 760 tokens of
+// 1536 channels in 4-token cubes, needs about 92 MB).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(128) << 20;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -135,6 +139,29 @@ struct dq_qact {
 namespace dq {
 
 void set_error(const std::string& msg);
+// Record `msg` as the thread's last error and return `s`; the HIP flavour
+// maps hipErrorOutOfMemory to DQ_ERR_OUT_OF_MEMORY, the rest to DQ_ERR_DEVICE.
+dq_status fail(dq_status s, const std::string& msg);
+dq_status hip_fail(hipError_t e, const char* what);
+// Checks a geometry and the core options against a weight and fills the
+// workspace's sizes and frame segments (no allocation, no device work);
+// *max_partials is the row count of the block-partial buffer (0 if no
+// segment has cubes of more than 64 tokens).
+dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, int core_bits, dq_qact* q,
+                    int64_t* max_partials);
+
+// Makes a handle's device current for the scope and restores the caller's.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
 
 // ---- launchers (quant.hip) ----
 hipError_t launch_residual(const void* w_dev, int w_bf16, const uint16_t* l1_dev, const uint16_t* l2_dev,

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from types import SimpleNamespace
 from typing import Optional, Sequence, Tuple
 
 import numpy as np
@@ -24,7 +25,7 @@ STATUS = {0: "DQ_OK", 1: "DQ_ERR_INVALID_ARG", 2: "DQ_ERR_SHAPE", 3: "DQ_ERR_UNS
 EXPORTS = ("dq_last_error", "dq_status_str", "dq_lowrank_factors", "dq_prepare_weights_lowrank",
            "dq_prepare_weights", "dq_weights_destroy", "dq_weights_info", "dq_weights_export",
            "dq_qact_create", "dq_qact_create_ex", "dq_qact_destroy", "dq_qact_info", "dq_quantize_act", "dq_linear_forward",
-           "dq_core_term", "dq_delta_term", "dq_linear", "dq_qact_export")
+           "dq_core_term", "dq_delta_term", "dq_linear", "dq_qact_export", "dq_linear_noalloc")
 
 
 class DQError(RuntimeError):
@@ -71,6 +72,7 @@ def load():
         "dq_delta_term": ([P, P, P, P], ctypes.c_int),
         "dq_linear": ([P, P, ctypes.c_int, P, P, P], ctypes.c_int),
         "dq_qact_export": ([P, P, P, P, P, P, P], ctypes.c_int),
+        "dq_linear_noalloc": ([P, P, ctypes.c_int, Geom, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -300,3 +302,14 @@ def dq_qact_export(q: QAct, stream=None) -> dict:
                                  _stream(stream)),
            "dq_qact_export")
     return out
+
+
+def dq_linear_noalloc(w: Weights, x, geom: Sequence[int], y, stream=None):
+    """dq_linear without a workspace handle: the activation state lives in
+    the library's fixed per-device array (calls on one GPU must not overlap)."""
+    f = "dq_linear_noalloc"
+    T, H, W = geom[:3]
+    ws = SimpleNamespace(N=T * H * W)
+    _check_x(f, w, ws, x)
+    _check_y(f, w, ws, y)
+    _check(load().dq_linear_noalloc(w.handle, _ptr(x), _dtype_of(x), Geom(*geom), _ptr(y), _stream(stream)), f)
