@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mx import bf16_bits_to_f64, f64_to_bf16_bits, mx_quantize, pack_fp4
+from .mx import bf16_bits_to_f64, f64_to_bf16_bits, mx_quantize, pack_fp4, pack_fp6
 
 
 def svd_factors(wt32: np.ndarray, rank: int):
@@ -42,11 +42,13 @@ def residual(wt32: np.ndarray, l1_bits: np.ndarray, l2_bits: np.ndarray) -> np.n
     return (wt - acc).astype(np.float32)
 
 
-def quantize_residual(rt32: np.ndarray):
-    """Q4(R): MX-FP4 along Ci for every output channel.
-    Returns (packed codes uint8 [Co][Ci/2], scale codes uint8 [Co][Ci/32])."""
-    codes, scales = mx_quantize(rt32, "fp4")
-    return pack_fp4(codes), scales
+def quantize_residual(rt32: np.ndarray, fmt: str = "fp4"):
+    """Q4(R): MX-FP4 along Ci for every output channel (or Q6(R), fmt
+    "fp6_e2m3" / "fp6_e3m2", for the 6-bit layers).
+    Returns (packed codes uint8 [Co][Ci/2] for FP4, [Co][3 Ci/4] for FP6,
+    scale codes uint8 [Co][Ci/32])."""
+    codes, scales = mx_quantize(rt32, fmt)
+    return (pack_fp4(codes) if fmt == "fp4" else pack_fp6(codes)), scales
 
 
 def eckart_young_ratio(wt32: np.ndarray, l1_bits: np.ndarray, l2_bits: np.ndarray, sigma: np.ndarray) -> dict:

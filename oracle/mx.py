@@ -15,6 +15,8 @@ import numpy as np
 
 FP4_QMAX = 6.0      # 关键设计 4: q_max = 6 for 4-bit floats
 FP8_QMAX = 448.0    # reading R6: largest finite OCP E4M3 value
+FP6_E2M3_QMAX = 7.5   # 6-bit floats (the 6-bit K/V projections): largest finite
+FP6_E3M2_QMAX = 28.0  #   values of the OCP MX FP6 formats E2M3 and E3M2
 GROUP = 32          # reading R5: MX block of 32 consecutive channels
 E_MIN, E_MAX = -127, 127
 
@@ -37,12 +39,27 @@ def fp8_decode_magnitude(code: int) -> float:
     return (1.0 + M / 8.0) * 2.0 ** (E - 7)
 
 
+def fp6_decode_magnitude(code: int, ebits: int) -> float:
+    """OCP MX FP6: E2M3 (ebits 2, bias 1) or E3M2 (ebits 3, bias 3); no
+    infinities or NaN; E = 0 is subnormal."""
+    mbits = 5 - ebits
+    bias = (1 << (ebits - 1)) - 1
+    E, M = (code >> mbits) & ((1 << ebits) - 1), code & ((1 << mbits) - 1)
+    if E == 0:
+        return (M / 2.0 ** mbits) * 2.0 ** (1 - bias)
+    return (1.0 + M / 2.0 ** mbits) * 2.0 ** (E - bias)
+
+
 # magnitudes indexed by the code with its sign bit cleared, ascending
 FP4_MAGS = np.array([fp4_decode_magnitude(c) for c in range(8)], dtype=np.float64)
 FP8_MAGS = np.array([fp8_decode_magnitude(c) for c in range(127)], dtype=np.float64)
+FP6_E2M3_MAGS = np.array([fp6_decode_magnitude(c, 2) for c in range(32)], dtype=np.float64)
+FP6_E3M2_MAGS = np.array([fp6_decode_magnitude(c, 3) for c in range(32)], dtype=np.float64)
 _FORMATS = {
     "fp4": (FP4_MAGS, FP4_QMAX, 3),
     "fp8": (FP8_MAGS, FP8_QMAX, 7),
+    "fp6_e2m3": (FP6_E2M3_MAGS, FP6_E2M3_QMAX, 5),
+    "fp6_e3m2": (FP6_E3M2_MAGS, FP6_E3M2_QMAX, 5),
 }
 
 
@@ -128,6 +145,27 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
     out[..., 0::2] = p & 15
     out[..., 1::2] = p >> 4
     return out
+
+
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """Six bits per code, packed little-endian in order: code i of a row at
+    bits [6 i, 6 i + 6) of the row's byte string (four codes per three
+    bytes, 24 bytes per 32-code MX block)."""
+    c = np.asarray(codes, dtype=np.uint32)
+    if c.shape[-1] % 4:
+        raise ValueError("code count must be a multiple of 4")
+    q = c.reshape(c.shape[:-1] + (c.shape[-1] // 4, 4))
+    word = q[..., 0] | (q[..., 1] << 6) | (q[..., 2] << 12) | (q[..., 3] << 18)
+    b = np.stack([word & 255, (word >> 8) & 255, (word >> 16) & 255], axis=-1)
+    return b.reshape(c.shape[:-1] + (c.shape[-1] // 4 * 3,)).astype(np.uint8)
+
+
+def unpack_fp6(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint32)
+    t = p.reshape(p.shape[:-1] + (p.shape[-1] // 3, 3))
+    word = t[..., 0] | (t[..., 1] << 8) | (t[..., 2] << 16)
+    q = np.stack([(word >> (6 * i)) & 63 for i in range(4)], axis=-1)
+    return q.reshape(p.shape[:-1] + (p.shape[-1] // 3 * 4,)).astype(np.uint8)
 
 
 # ---------------------------------------------------------------- bf16 ----
