@@ -65,6 +65,8 @@ def parse():
                     help="channels per FP8 exponent of the cores (64: the pages' group size)")
     ap.add_argument("--core-bits", type=int, default=8, choices=(8, 4, 16),
                     help="MX-FP8 cores (the pages' choice), MX-FP4 or bf16 cores (the 4- and 16-bit points of their ablation)")
+    ap.add_argument("--fp6", default="fp6_e2m3", choices=("fp6_e2m3", "fp6_e3m2"),
+                    help="6-bit format of a text-token layer (--config kv_text_14b)")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
@@ -231,6 +233,67 @@ def schedule(args, cfg, dq, torch):
     }), flush=True)
 
 
+PEAK_FP6 = 10.1e15      # MI355X dense FP6 (the FP4 rate)
+
+
+def bench_text(args, cfg, dq, torch):
+    """The 6-bit layer on text tokens (the cross-attention K/V projections):
+    one JSON line.  A step is dq_quantize_act6 (Q6(X), U) followed by
+    dq_linear6_forward (the FP6 x FP6 GEMM with the low-rank branch), on the
+    same stream; both timed with HIP events."""
+    import numpy as np
+    synth = synth_mod()
+    fmt = args.fp6
+    x = synth.make_text_activation(cfg.prompts, cfg.ctx, cfg.valid, cfg.Ci, cfg.x_seed, cfg.dtype,
+                                   cfg.n_outliers).to("cuda:0")
+    wt = synth.make_weight(cfg.Ci, cfg.Co, cfg.w_seed, cfg.dtype)
+    l1, l2 = dq.dq_lowrank_factors(wt, cfg.rank, cfg.w_seed)
+    weights = dq.dq_prepare_weights_w6(wt, l1, l2, fmt)
+    act = dq.dq_act6_create(weights, cfg.N)
+    y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        dq.dq_linear6(weights, x, act, y, stream)
+    torch.cuda.synchronize()
+    start, end = ev(), ev()
+    marks = []
+    start.record(stream)
+    for _ in range(args.steps):
+        a, b, c = ev(), ev(), ev()
+        a.record(stream)
+        dq.dq_quantize_act6(weights, x, act, stream)
+        b.record(stream)
+        dq.dq_linear6_forward(weights, act, y, stream)
+        c.record(stream)
+        marks.append((a, b, c))
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    q_ms = float(np.mean([a.elapsed_time(b) for a, b, c in marks]))
+    f_ms = float(np.mean([b.elapsed_time(c) for a, b, c in marks]))
+    N, Ci, Co, r = cfg.N, cfg.Ci, cfg.Co, cfg.rank
+    flops = 2.0 * N * Ci * Co
+    xbytes = 2 if cfg.dtype == "bf16" else 4
+    qbytes = N * Ci * xbytes + N * Ci * (0.75 + 1 / 32) + 2 * N * r
+    out = {
+        "metric": "effective TOPS of the 6-bit text-token layer (W6A6 + low rank)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": fmt,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: X {N}x{Ci} ({cfg.prompts} contexts of {cfg.ctx} text tokens) {cfg.dtype} "
+                               f"-> Y {N}x{Co} fp32, {fmt}, rank {r}", "tokens": N, "Ci": Ci, "Co": Co, "rank": r},
+        "quantize": {"ms": round(q_ms, 4), "algorithmic_bytes": int(qbytes),
+                     "GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": "FP6 x FP6 GEMM (dq_linear6_forward: scaled MFMA, low-rank branch in the epilogue)",
+                     "bound": "mfma", "achieved": round(flops / (f_ms * 1e-3) / 1e12, 2),
+                     "peak": round(PEAK_FP6 / 1e12, 2), "unit": "TFLOP/s",
+                     "frac": round(flops / (f_ms * 1e-3) / PEAK_FP6, 4), "ms": round(f_ms, 4),
+                     "output_bytes": int(4 * N * Co), "weight_bytes": int(Co * Ci * (0.75 + 1 / 32))},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def synth_mod():
     from w4a4_quantized_linear_cube_amd import synth
     return synth
@@ -262,6 +325,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     dq.load()
+    if args.config in synth.TEXT_CONFIGS:
+        bench_text(args, synth.TEXT_CONFIGS[args.config], dq, torch)
+        return
     cfg = synth.CONFIGS[args.config]
     if args.sweep:
         sweep(args, cfg, dq, torch)

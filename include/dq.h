@@ -205,6 +205,47 @@ dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact
 dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscales_host, uint8_t* ccodes_host,
                          uint8_t* cscales_host, uint16_t* u_host, void* stream);
 
+/* ---- 6-bit layers on text tokens ------------------------------------------
+ * The pages quantize every linear layer to 4 bits except the cross-attention
+ * K and V projections, which act only on the text tokens and are kept at 6
+ * bits (DeltaQuant notes, 损失函数/训练策略).  Text tokens have no (T, H, W)
+ * grid, so these layers have no cubes: for token n,
+ *     y_n = U_n L2 + Q6(x_n) Q6(R),   W = L1 L2 + R,  U = bf16(bf16(X) L1)
+ * with Q6 an MX 6-bit float (one E8M0 scale per 32 channels, the quantizer of
+ * 关键设计 4 with q_max the format's largest value, round to nearest even)
+ * and fp32 accumulation (E2M3 x E2M3 exactly per 64-term block; E3M2 x E3M2
+ * keeps fewer bits, like FP8 x FP4).  6-bit codes are exported packed in
+ * order, code i of a row at bits [6 i, 6 i + 6) of its byte string (24 bytes
+ * per 32 channels). */
+typedef enum { DQ_FP6_E2M3 = 2, DQ_FP6_E3M2 = 3 } dq_fp6_format;
+typedef struct dq_act6 dq_act6;         /* workspace of a 6-bit layer for N text tokens */
+
+/* dq_prepare_weights_lowrank with R quantized to MX-FP6 (`fp6_format`), for
+ * the 6-bit entry points below only (the 4-bit ones reject it).
+ * dq_weights_export then writes rcodes as [Co][3 Ci/4] packed 6-bit codes.
+ * Same requirements and errors, and DQ_ERR_INVALID_ARG for another format. */
+dq_status dq_prepare_weights_w6(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                                const uint16_t* l1_host, const uint16_t* l2_host, int32_t fp6_format, int32_t device,
+                                dq_weights** out);
+
+/* Workspace for N text tokens (1 <= N <= 2^31 - 256) of a 6-bit weight: the
+ * codes and scales of Q6(X), U.  Owns its device buffers. */
+dq_status dq_act6_create(const dq_weights* w, int64_t N, dq_act6** out);
+void dq_act6_destroy(dq_act6* a);
+
+/* Q6(X) per token and U = bf16(bf16(X) L1) (fp32 accumulation).
+ *   x_dev [N][Ci] of dtype dt, contiguous, 16-byte aligned.
+ * Asynchronous on `stream`. */
+dq_status dq_quantize_act6(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_act6* a, void* stream);
+/* y_dev [N][Co] fp32 (every element written, 4-byte aligned) = U L2 +
+ * Q6(X) Q6(R) from the state of the last dq_quantize_act6.  Asynchronous. */
+dq_status dq_linear6_forward(const dq_weights* w, dq_act6* a, float* y_dev, void* stream);
+/* dq_quantize_act6 followed by dq_linear6_forward. */
+dq_status dq_linear6(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_act6* a, float* y_dev, void* stream);
+/* Host copies (any pointer may be NULL): codes [N][3 Ci/4], scale codes
+ * [N][Ci/32], U [N][rank] bf16 bits.  Synchronises `stream` first. */
+dq_status dq_act6_export(const dq_act6* a, uint8_t* codes_host, uint8_t* scales_host, uint16_t* u_host, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): dq_linear
  * for the geometry `geom` with MX-FP8 cores in groups of 32, without a

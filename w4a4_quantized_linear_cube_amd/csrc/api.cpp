@@ -122,6 +122,10 @@ void unstep_fp4(const std::vector<uint8_t>& buf, long long row, int64_t Ci, int6
 void unstep_fp8(const std::vector<uint8_t>& buf, long long row, int64_t Ci, int64_t Kp, uint8_t* out) {
     for (long long c = 0; c < Ci / 16; ++c) std::memcpy(out + 16 * c, &buf[off_fp8(row, c >> 3, (int)(c & 7), Kp / 128)], 16);
 }
+void unstep_fp6(const std::vector<uint8_t>& buf, long long row, int64_t Ci, int64_t Kp, uint8_t* out) {
+    for (long long G = 0; G < Ci / 32; ++G)
+        for (int i = 0; i < 3; ++i) std::memcpy(out + 24 * G + 8 * i, &buf[off_fp6(row, G, i, Kp / 128)], 8);
+}
 void unstep_scales(const std::vector<uint8_t>& buf, long long row, int64_t Ci, int64_t Kp, uint8_t* out) {
     for (long long G = 0; G < Ci / 32; ++G) out[G] = buf[off_scale(row, G, Kp / 128)];
 }
@@ -175,9 +179,13 @@ dq_status dq_lowrank_factors(const void* w_host, dq_dtype dt, int64_t Ci, int64_
     return DQ_OK;
 }
 
-dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
-                                     const uint16_t* l1_host, const uint16_t* l2_host, int32_t device,
-                                     dq_weights** out) {
+}  // extern "C"
+
+// Weight preparation for a given code format of R (FMT_FP4, or the 6-bit
+// FMT_FP6 / FMT_BF6).
+static dq_status prepare_weights(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                                 const uint16_t* l1_host, const uint16_t* l2_host, int32_t device, int wfmt,
+                                 dq_weights** out) {
     g_last_error.clear();
     if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
@@ -204,6 +212,8 @@ dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci
     w->rp = (int)round_up(rank, RPAD);
     w->Kp = round_up(Ci, KPAD);
     w->Cop = round_up(Co, NPAD);
+    w->wfmt = wfmt;
+    const bool six = wfmt != 4;
     const size_t esz = dt == DQ_BF16 ? 2 : 4;
 
     void* wdev = nullptr;
@@ -230,10 +240,12 @@ dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci
             (e = hipMemcpy(l2d, l2_host, (size_t)(rank * Co) * 2, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(e, "copy factors"); }
     }
     if ((e = dalloc(&w->r, (size_t)(Ci * Co), &w->bytes)) != hipSuccess ||
-        (e = dalloc(&w->rq, (size_t)(w->Cop * w->Kp / 2), &w->bytes)) != hipSuccess ||
+        (e = dalloc(&w->rq, (size_t)(w->Cop * w->Kp / 2 * (six ? 3 : 2) / 2), &w->bytes)) != hipSuccess ||
         (e = dalloc(&w->rs, (size_t)(w->Cop * w->Kp / 32), &w->bytes)) != hipSuccess) { cleanup(); return hip_fail(e, "hipMalloc weight"); }
     if ((e = launch_residual(wdev, dt == DQ_BF16, l1d, l2d, Ci, Co, rank, w->r, nullptr)) != hipSuccess) { cleanup(); return hip_fail(e, "residual kernel"); }
-    if ((e = launch_encode_fp4_rows(w->r, Co, Ci, Ci, w->Kp, w->rq, w->rs, nullptr)) != hipSuccess) { cleanup(); return hip_fail(e, "encode kernel"); }
+    e = six ? launch_encode_fp6(w->r, 0, Co, Ci, Ci, w->Kp, w->rq, w->rs, wfmt == 3, nullptr)
+            : launch_encode_fp4_rows(w->r, Co, Ci, Ci, w->Kp, w->rq, w->rs, nullptr);
+    if (e != hipSuccess) { cleanup(); return hip_fail(e, "encode kernel"); }
     if (w->rp > 0) {
         std::vector<uint16_t> l1t((size_t)(w->rp * w->Kp), 0), l2t((size_t)(w->Cop * w->rp), 0);
         for (int64_t c = 0; c < Ci; ++c)
@@ -249,6 +261,25 @@ dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci
     cleanup();
     *out = guard.release();
     return DQ_OK;
+}
+
+extern "C" {
+
+dq_status dq_prepare_weights_lowrank(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                                     const uint16_t* l1_host, const uint16_t* l2_host, int32_t device,
+                                     dq_weights** out) {
+    return prepare_weights(w_host, dt, Ci, Co, rank, l1_host, l2_host, device, 4, out);
+}
+
+dq_status dq_prepare_weights_w6(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank,
+                                const uint16_t* l1_host, const uint16_t* l2_host, int32_t fp6_format, int32_t device,
+                                dq_weights** out) {
+    if (out) *out = nullptr;
+    if (fp6_format != DQ_FP6_E2M3 && fp6_format != DQ_FP6_E3M2) {
+        g_last_error.clear();
+        return fail(DQ_ERR_INVALID_ARG, "fp6_format must be DQ_FP6_E2M3 or DQ_FP6_E3M2");
+    }
+    return prepare_weights(w_host, dt, Ci, Co, rank, l1_host, l2_host, device, (int)fp6_format, out);
 }
 
 dq_status dq_prepare_weights(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, int32_t rank, uint64_t seed,
@@ -292,7 +323,10 @@ dq_status dq_weights_export(const dq_weights* w, uint16_t* l1_host, uint16_t* l2
         return hip_fail(e, "copy R");
     try {
         std::vector<uint8_t> buf;
-        if (rcodes_host) {
+        if (rcodes_host && w->wfmt != 4) {
+            if ((e = fetch_all(w->rq, (size_t)(w->Cop * w->Kp / 4 * 3), buf)) != hipSuccess) return hip_fail(e, "copy R codes");
+            for (int64_t j = 0; j < w->Co; ++j) unstep_fp6(buf, j, w->Ci, w->Kp, rcodes_host + j * (w->Ci / 4 * 3));
+        } else if (rcodes_host) {
             if ((e = fetch_all(w->rq, (size_t)(w->Cop * w->Kp / 2), buf)) != hipSuccess) return hip_fail(e, "copy R codes");
             for (int64_t j = 0; j < w->Co; ++j) unstep_fp4(buf, j, w->Ci, w->Kp, rcodes_host + j * (w->Ci / 2));
         }
@@ -317,6 +351,7 @@ namespace dq {
 // workspace's sizes and frame segments (no allocation, no device work).
 dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, int core_bits, dq_qact* q,
                     int64_t* max_partials_out) {
+    if (w->wfmt != 4) return fail(DQ_ERR_INVALID_ARG, "a 6-bit weight takes the 6-bit entry points");
     if (core_group != 32 && core_group != 64) return fail(DQ_ERR_INVALID_ARG, "core_group must be 32 or 64");
     if (core_bits != 8 && core_bits != 4 && core_bits != 16) return fail(DQ_ERR_INVALID_ARG, "core_bits must be 8, 4 or 16");
     if (w->Ci % core_group != 0) return fail(DQ_ERR_SHAPE, "core_group must divide Ci");
@@ -441,6 +476,7 @@ dq_status dq_qact_info(const dq_qact* q, int64_t* N, int64_t* K, int64_t* device
 static dq_status check_pair(const dq_weights* w, const dq_qact* q) {
     if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
     if (!q) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    if (w->wfmt != 4) return fail(DQ_ERR_INVALID_ARG, "a 6-bit weight takes the 6-bit entry points");
     if (q->Ci != w->Ci || q->Co != w->Co || q->rp != w->rp || q->device != w->device)
         return fail(DQ_ERR_INVALID_ARG, "workspace was created for a different weight");
     return DQ_OK;
@@ -571,6 +607,135 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
             if ((e = fetch_all(q->u, (size_t)(q->Nslot_pad * q->rp * 2), buf)) != hipSuccess) return hip_fail(e, "copy U");
             const uint16_t* ub = (const uint16_t*)buf.data();
             each_slot([&](long long s, long long t) { std::memcpy(u_host + t * q->rank, ub + s * q->rp, (size_t)q->rank * 2); });
+        }
+    } catch (const std::bad_alloc&) {
+        return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    return DQ_OK;
+}
+
+
+// ---------------------------------------------------------------- 6-bit layers ----
+static void free_act6(dq_act6* a) {
+    if (!a) return;
+    DeviceGuard dg(a->device);
+    (void)hipFree(a->xq);
+    (void)hipFree(a->xs);
+    (void)hipFree(a->u);
+    (void)hipFree(a->upart);
+    (void)hipFree(a->stok);
+    (void)hipFree(a->sink);
+    delete a;
+}
+
+dq_status dq_act6_create(const dq_weights* w, int64_t N, dq_act6** out) {
+    g_last_error.clear();
+    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    if (w->wfmt == 4) return fail(DQ_ERR_INVALID_ARG, "a 4-bit weight takes dq_qact_create");
+    if (N < 1 || N > (int64_t(1) << 31) - MPAD) return fail(DQ_ERR_SHAPE, "N must be in [1, 2^31 - 256]");
+    if (!mul_ok(round_up(N, MPAD), w->Kp, int64_t(1) << 40) || !mul_ok(N, w->Co, int64_t(1) << 40))
+        return fail(DQ_ERR_SHAPE, "workspace too large");
+    DeviceGuard dg(w->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    auto* a = new (std::nothrow) dq_act6();
+    if (!a) return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    std::unique_ptr<dq_act6, void (*)(dq_act6*)> guard(a, free_act6);
+    a->device = w->device;
+    a->N = N;
+    a->N_pad = round_up(N, MPAD);
+    a->Ci = w->Ci;
+    a->Co = w->Co;
+    a->Kp = w->Kp;
+    a->Cop = w->Cop;
+    a->rp = w->rp;
+    a->rank = w->rank;
+    a->wfmt = w->wfmt;
+    hipError_t e;
+    if ((e = dalloc(&a->xq, (size_t)(a->N_pad * a->Kp / 4 * 3), &a->bytes)) != hipSuccess ||
+        (e = dalloc(&a->xs, (size_t)(a->N_pad * a->Kp / 32), &a->bytes)) != hipSuccess ||
+        (e = dalloc(&a->u, (size_t)(a->N_pad * a->rp), &a->bytes)) != hipSuccess ||
+        (e = dalloc(&a->upart, (size_t)(text_lowrank_splits((int)a->Ci) * a->N_pad * a->rp), &a->bytes)) != hipSuccess ||
+        (e = dalloc(&a->stok, (size_t)a->N_pad, &a->bytes)) != hipSuccess ||
+        (e = dalloc(&a->sink, (size_t)512, &a->bytes)) != hipSuccess)
+        return hip_fail(e, "hipMalloc workspace");
+    // rows are tokens: the identity map (one-token "cubes" of a 1 x 1 x N grid), -1 past N
+    const Geom g{1, 1, (int)N, 1, 1, 1, 1, 1, (int)N, 1, (long long)N, (long long)N, (long long)N};
+    if ((e = launch_slot_tokens(g, 0, a->stok, a->N_pad, nullptr)) != hipSuccess) return hip_fail(e, "row table");
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "workspace init");
+    *out = guard.release();
+    return DQ_OK;
+}
+
+void dq_act6_destroy(dq_act6* a) { free_act6(a); }
+
+static dq_status check_pair6(const dq_weights* w, const dq_act6* a) {
+    if (!w) return fail(DQ_ERR_INVALID_ARG, "weights handle is NULL");
+    if (!a) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    if (w->wfmt == 4) return fail(DQ_ERR_INVALID_ARG, "a 4-bit weight takes the 4-bit entry points");
+    if (a->Ci != w->Ci || a->Co != w->Co || a->rp != w->rp || a->device != w->device || a->wfmt != w->wfmt)
+        return fail(DQ_ERR_INVALID_ARG, "workspace was created for a different weight");
+    return DQ_OK;
+}
+
+dq_status dq_quantize_act6(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_act6* a, void* stream) {
+    g_last_error.clear();
+    dq_status st = check_pair6(w, a);
+    if (st != DQ_OK) return st;
+    if (!x_dev) return fail(DQ_ERR_INVALID_ARG, "x_dev is NULL");
+    if (((uintptr_t)x_dev) % 16 != 0) return fail(DQ_ERR_INVALID_ARG, "x_dev must be 16-byte aligned");
+    if (dt != DQ_F32 && dt != DQ_BF16) return fail(DQ_ERR_INVALID_ARG, "unknown dtype");
+    DeviceGuard dg(a->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_encode_fp6(x_dev, dt == DQ_BF16, a->N, a->Ci, a->Ci, a->Kp, a->xq, a->xs, a->wfmt == 3, s);
+    if (e != hipSuccess) return hip_fail(e, "6-bit activation launch");
+    e = launch_text_lowrank(x_dev, dt == DQ_BF16, a->N, a->N_pad, (int)a->Ci, (int)a->Kp, w->l1t, a->rp, a->upart, a->u, s);
+    if (e != hipSuccess) return hip_fail(e, "low-rank launch");
+    return DQ_OK;
+}
+
+dq_status dq_linear6_forward(const dq_weights* w, dq_act6* a, float* y_dev, void* stream) {
+    g_last_error.clear();
+    dq_status st = check_pair6(w, a);
+    if (st != DQ_OK) return st;
+    if (!y_dev) return fail(DQ_ERR_INVALID_ARG, "y_dev is NULL");
+    if (((uintptr_t)y_dev) % 4 != 0) return fail(DQ_ERR_INVALID_ARG, "y_dev must be 4-byte aligned");
+    DeviceGuard dg(a->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = launch_forward6(w, a, y_dev, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "6-bit forward launch");
+    return DQ_OK;
+}
+
+dq_status dq_linear6(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_act6* a, float* y_dev, void* stream) {
+    dq_status st = dq_quantize_act6(w, x_dev, dt, a, stream);
+    if (st != DQ_OK) return st;
+    return dq_linear6_forward(w, a, y_dev, stream);
+}
+
+dq_status dq_act6_export(const dq_act6* a, uint8_t* codes_host, uint8_t* scales_host, uint16_t* u_host, void* stream) {
+    g_last_error.clear();
+    if (!a) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    DeviceGuard dg(a->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    try {
+        std::vector<uint8_t> buf;
+        if (codes_host) {
+            if ((e = fetch_all(a->xq, (size_t)(a->N_pad * a->Kp / 4 * 3), buf)) != hipSuccess) return hip_fail(e, "copy codes");
+            for (int64_t n = 0; n < a->N; ++n) unstep_fp6(buf, n, a->Ci, a->Kp, codes_host + n * (a->Ci / 4 * 3));
+        }
+        if (scales_host) {
+            if ((e = fetch_all(a->xs, (size_t)(a->N_pad * a->Kp / 32), buf)) != hipSuccess) return hip_fail(e, "copy scales");
+            for (int64_t n = 0; n < a->N; ++n) unstep_scales(buf, n, a->Ci, a->Kp, scales_host + n * (a->Ci / 32));
+        }
+        if (u_host && a->rank > 0) {
+            if ((e = fetch_all(a->u, (size_t)(a->N_pad * a->rp * 2), buf)) != hipSuccess) return hip_fail(e, "copy U");
+            const uint16_t* ub = (const uint16_t*)buf.data();
+            for (int64_t n = 0; n < a->N; ++n) std::memcpy(u_host + n * a->rank, ub + n * a->rp, (size_t)a->rank * 2);
         }
     } catch (const std::bad_alloc&) {
         return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");

@@ -17,6 +17,8 @@ typedef short v2s __attribute__((ext_vector_type(2)));
 
 // Formats of the scaled MFMA (cbsz / blgp field values).
 constexpr int FMT_FP8 = 0;
+constexpr int FMT_FP6 = 2;   // FP6 E2M3
+constexpr int FMT_BF6 = 3;   // FP6 E3M2
 constexpr int FMT_FP4 = 4;
 
 // Scale exponent of an MX group (关键设计 4, quantizer definition, with the
@@ -34,6 +36,13 @@ __device__ __forceinline__ int mx_exp_fp8(float amax) {
     uint32_t b = __float_as_uint(amax);
     int ef = (int)(b >> 23);
     int e = ef - 135 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+    return ef == 0 ? -127 : max(e, -127);
+}
+// 6-bit formats: q_max = 7.5 = 1.875 2^2 (E2M3) or 28 = 1.75 2^4 (E3M2).
+__device__ __forceinline__ int mx_exp_fp6(float amax, bool e3m2) {
+    uint32_t b = __float_as_uint(amax);
+    int ef = (int)(b >> 23);
+    int e = e3m2 ? ef - 131 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0) : ef - 129 + ((b & 0x7fffffu) > 0x700000u ? 1 : 0);
     return ef == 0 ? -127 : max(e, -127);
 }
 // 2^e as a float operand of the scaled converts (2^-127 is the subnormal 0x00400000).
@@ -72,6 +81,25 @@ __device__ __forceinline__ void encode_fp8x32(const float* v, float scale, uint4
     }
     lo = make_uint4(d[0], d[1], d[2], d[3]);
     hi = make_uint4(d[4], d[5], d[6], d[7]);
+}
+
+// 32 fp32 values -> 32 FP6 codes (E2M3, or E3M2), v / 2^e rounded to nearest
+// even by the hardware converter, packed six bits each in order (value i at
+// bits [6 i, 6 i + 6) of d[0..5]).  The converter interleaves its two
+// 16-value sources (output value 2 j from the first, 2 j + 1 from the
+// second), so the even-indexed values go first and the odd ones second.
+__device__ __forceinline__ void encode_fp6x32(const float* v, float scale, bool e3m2, uint32_t* d) {
+    v16f ev, od;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        ev[j] = v[2 * j];
+        od[j] = v[2 * j + 1];
+    }
+    typedef unsigned v6u __attribute__((ext_vector_type(6)));
+    const v6u w = e3m2 ? __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, scale)
+                       : __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, scale);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) d[i] = w[i];
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -60,6 +60,21 @@ __host__ __device__ inline uint32_t toff_fp8(int r, int ks, int c) {
 __host__ __device__ inline uint32_t toff_scale(int r, int G) {
     return (uint32_t)(G >> 2) * 1024 + (uint32_t)((((r >> 7) * 2 + (G & 1)) * 32 + (r & 31)) * 8 + ((r >> 5) & 3) * 2 + ((G & 3) >> 1));
 }
+// FP6 codes (the 6-bit layers): 96 bytes per row step, four 32-channel
+// groups of 24 bytes (channel i of a group at bits [6 i, 6 i + 6),
+// little-endian), i.e. twelve 8-byte words, group G holding words
+// 3 (G % 4) .. 3 (G % 4) + 2.  The words are rotated by the row's octet:
+// word w sits at position (w + rot6(r)) % 12, so the 32 lanes of a GEMM
+// fragment read (rows r0 .. r0 + 31, one word each) hit 64 distinct banks.
+__host__ __device__ inline int rot6(int r) { return (r >> 3) & 3; }
+// byte offset of word i (0 .. 2) of group G of tile row r
+__host__ __device__ inline uint32_t toff_fp6(int r, int G, int i) {
+    return ((uint32_t)(G >> 2) * 256 + (uint32_t)r) * 96 + (uint32_t)(((3 * (G & 3) + i + rot6(r)) % 12) * 8);
+}
+// the same for any row of a matrix of nks K steps
+__host__ __device__ inline size_t off_fp6(long long row, long long G, int i, long long nks) {
+    return (size_t)(row >> 8) * (size_t)nks * 24576 + toff_fp6((int)(row & 255), (int)G, i);
+}
 // the same for any row of a matrix of nks K steps
 __host__ __device__ inline size_t off_fp4(long long row, long long G, long long nks) {
     return (size_t)(row >> 8) * (size_t)nks * 16384 + toff_fp4((int)(row & 255), (int)G);
@@ -84,7 +99,8 @@ struct dq_weights {
     int device = 0;
     int64_t Ci = 0, Co = 0, Kp = 0, Cop = 0;
     int rank = 0, rp = 0;
-    uint8_t* rq = nullptr;     // Cop x Kp/2    Q4(R) codes, step-major (device)
+    int wfmt = 4;              // R's codes: MX-FP4 (4), or MX-FP6 E2M3 (2) / E3M2 (3) for the 6-bit layers
+    uint8_t* rq = nullptr;     // Cop x Kp/2    Q4(R) codes (Cop x 3 Kp/4 for Q6(R)), step-major (device)
     uint8_t* rs = nullptr;     // Cop x Kp/32   Q4(R) scale codes, step-major (device)
     float* r = nullptr;        // [Co][Ci]      fp32 residual R^T (device, for export)
     uint16_t* l1t = nullptr;   // [rp][Kp]      L1^T bf16 (device)
@@ -136,6 +152,20 @@ struct dq_qact {
     size_t bytes = 0;
 };
 
+// Workspace of a 6-bit layer: N text tokens (no cubes).
+struct dq_act6 {
+    int device = 0;
+    int64_t N = 0, N_pad = 0, Ci = 0, Co = 0, Kp = 0, Cop = 0;
+    int rp = 0, rank = 0, wfmt = 2;
+    uint8_t* xq = nullptr;     // N_pad x 3 Kp/4   Q6(X) codes, step-major
+    uint8_t* xs = nullptr;     // N_pad x Kp/32    scale codes, step-major
+    uint16_t* u = nullptr;     // [N_pad][rp]      U = bf16(bf16(X) L1)
+    float* upart = nullptr;    // [splits][N_pad][rp] partial sums of U
+    int* stok = nullptr;       // [N_pad]          row -> token (identity, -1 past N)
+    float* sink = nullptr;     // [512]            target of the GEMM's discarded stores
+    size_t bytes = 0;
+};
+
 namespace dq {
 
 void set_error(const std::string& msg);
@@ -173,8 +203,19 @@ hipError_t launch_slot_tokens(const Geom& g, int64_t tok0, int* stok, int64_t n,
 hipError_t launch_decode_fp4_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t Kp, uint16_t* out,
                                   hipStream_t st);
 
+// 6-bit layers: MX-FP6 encode of rows (src fp32, or bf16 when src_bf16) into
+// the step-major FP6 layout; U of text tokens (part: text_lowrank_splits(Ci)
+// x Npad x rp fp32).
+hipError_t launch_encode_fp6(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int64_t Kp,
+                             uint8_t* codes, uint8_t* scales, int e3m2, hipStream_t st);
+hipError_t launch_text_lowrank(const void* x, int x_bf16, int64_t N, int64_t Npad, int Ci, int Kp, const uint16_t* l1t,
+                               int rp, float* part, uint16_t* u, hipStream_t st);
+int text_lowrank_splits(int Ci);
+
 // ---- launchers (gemm.hip) ----
 constexpr int FWD_CORE = 1, FWD_DELTA = 2;   // parts of the forward pass
 hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, hipStream_t st);
+// y = U L2 + Q6(X) Q6(R) for a 6-bit layer
+hipError_t launch_forward6(const dq_weights* w, dq_act6* a, float* y, hipStream_t st);
 
 }  // namespace dq

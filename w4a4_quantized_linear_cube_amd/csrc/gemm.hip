@@ -163,16 +163,22 @@ __device__ __forceinline__ TileWalk tile_walk(int b, int G, int mt, int nt, int 
 // ahead of the MFMAs' tile from a tile's first step on, or several tiles
 // ahead); that form recomputes the copy sources every step, the other one
 // only once per tile.
-template <int BFMT, int EPI, bool SMALLK>
+// AFMT: Q4(R) (FMT_FP4) or, for the 6-bit layers, Q6(R) (FMT_FP6 E2M3 or
+// FMT_BF6 E3M2, with BFMT the same 6-bit format).
+template <int AFMT, int BFMT, int EPI, bool SMALLK>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
-    constexpr int BROW = BFMT == FMT_FP4 ? 64 : 128;         // B bytes per row per K step
-    constexpr int A_STEP = 256 * 64;                          // A bytes per tile step
+    constexpr bool A6 = AFMT == FMT_FP6 || AFMT == FMT_BF6;
+    constexpr bool B6 = BFMT == FMT_FP6 || BFMT == FMT_BF6;
+    static_assert(A6 == B6, "6-bit operands come in pairs");
+    constexpr int AROW = A6 ? 96 : 64;                        // A bytes per row per K step
+    constexpr int BROW = BFMT == FMT_FP4 ? 64 : (B6 ? 96 : 128);   // B bytes per row per K step
+    constexpr int A_STEP = 256 * AROW;                        // A bytes per tile step
     constexpr int B_STEP = 256 * BROW;
     constexpr int B_OFF = A_STEP;
     constexpr int SA_OFF = B_OFF + B_STEP;
     constexpr int SB_OFF = SA_OFF + 1024;
     constexpr int STAGE = SB_OFF + 1024;
-    constexpr int NS = BFMT == FMT_FP4 ? 4 : 3;               // LDS stages in the ring
+    constexpr int NS = BFMT == FMT_FP4 ? 4 : 3;               // LDS stages in the ring (50 KB stages: 3)
     constexpr int APC = A_STEP / 1024 / 4;                    // 1 KB copies per wave: A
     constexpr int BPC = B_STEP / 1024 / 4;                    //                       B
     constexpr int DMAS = APC + BPC + 2;                       // copies per wave per stage
@@ -287,25 +293,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     const int brow0 = wc * 128 + l32;            // + 32 ni
     const int asw = swz4(arow0);                 // the swizzles depend on row % 16 only
     const int bsw = BFMT == FMT_FP4 ? swz4(brow0) : swz8(brow0);
+    const int r6 = rot6(l32);                    // FP6 word rotation (rows arow0 + 32 mi, brow0 + 32 ni: rot6(l32))
     // Scale codes: one 8-byte read per operand gives the lane's codes for the
     // whole step (four 32-row blocks x two halves); code (block r, half kk) is
     // byte 2 (r % 2) + kk of dword r / 2, selected by the MFMA's op_sel.
     const int sa_off = SA_OFF + ((wr * 2 + g) * 32 + l32) * 8;
     const int sb_off = SB_OFF + ((wc * 2 + g) * 32 + l32) * 8;
     struct Half {
-        uint4 a[4];
+        uint4 a[A6 ? 1 : 4];                   // FP4 A fragments
+        uint2 a6[A6 ? 4 : 1][3];               // FP6 A fragments (three 8-byte words each)
         uint4 b[BFMT == FMT_FP4 ? 4 : 1];      // FP4 B fragments
-        v8i b8[BFMT == FMT_FP4 ? 1 : 4];       // FP8 B fragments (two 16-byte chunks each)
+        v8i b8[BFMT == FMT_FP8 ? 4 : 1];       // FP8 B fragments (two 16-byte chunks each)
+        uint2 b6[B6 ? 4 : 1][3];               // FP6 B fragments
         uint2 sa, sb;
+    };
+    // the three words of FP6 group Gl (0 .. 3 within the step) of a row whose
+    // step starts at rowp
+    auto rd6 = [&](const uint8_t* rowp, int Gl, uint2* w) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) w[i] = *(const uint2*)(rowp + ((3 * Gl + i + r6) % 12) * 8);
     };
     // LDS read number i (0 .. 9) of half kk's fragments, in the order of
     // their first use by the MFMA sequence below: a0 b0 sa sb b1 b2 b3 a1 a2 a3.
     auto rd = [&](int buf, int kk, Half& F, int i) {
         const uint8_t* st = smem + buf * STAGE;
-        auto rda = [&](int mi) { F.a[mi] = *(const uint4*)(st + (arow0 + 32 * mi) * 64 + (((2 * kk + g) ^ asw) << 4)); };
+        auto rda = [&](int mi) {
+            if constexpr (A6) rd6(st + (arow0 + 32 * mi) * AROW, 2 * kk + g, F.a6[mi]);
+            else F.a[mi] = *(const uint4*)(st + (arow0 + 32 * mi) * 64 + (((2 * kk + g) ^ asw) << 4));
+        };
         auto rdb = [&](int ni) {
             const uint8_t* rowp = st + B_OFF + (brow0 + 32 * ni) * BROW;
-            if constexpr (BFMT == FMT_FP4) {
+            if constexpr (B6) {
+                rd6(rowp, 2 * kk + g, F.b6[ni]);
+            } else if constexpr (BFMT == FMT_FP4) {
                 F.b[ni] = *(const uint4*)(rowp + (((2 * kk + g) ^ bsw) << 4));
             } else {
                 const v4i lo = *(const v4i*)(rowp + (((4 * kk + g) ^ bsw) << 4));
@@ -330,10 +350,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // MFMA number i (0 .. 15) of half kk: row block mi = i / 4, column block ni = i % 4
     auto mma = [&](const Half& F, int kk, int i) {
         const int mi = i >> 2, ni = i & 3;
-        const uint4 v = F.a[mi];
-        const v8i af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        v8i bf;
-        if constexpr (BFMT == FMT_FP4) {
+        v8i af, bf;
+        if constexpr (A6) {
+            const uint2* w = F.a6[mi];
+            af = (v8i){(int)w[0].x, (int)w[0].y, (int)w[1].x, (int)w[1].y, (int)w[2].x, (int)w[2].y, 0, 0};
+        } else {
+            const uint4 v = F.a[mi];
+            af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        }
+        if constexpr (B6) {
+            const uint2* w = F.b6[ni];
+            bf = (v8i){(int)w[0].x, (int)w[0].y, (int)w[1].x, (int)w[1].y, (int)w[2].x, (int)w[2].y, 0, 0};
+        } else if constexpr (BFMT == FMT_FP4) {
             const uint4 u = F.b[ni];
             bf = (v8i){(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
         } else {
@@ -341,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         }
         const int sa = (mi >> 1) ? (int)F.sa.y : (int)F.sa.x, sb = (ni >> 1) ? (int)F.sb.y : (int)F.sb.x;
         // op_sel operands must be constants: spell out the byte choices
-#define DQ_MFMA(OA, OB) acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[mi][ni], FMT_FP4, BFMT, OA, sa, OB, sb)
+#define DQ_MFMA(OA, OB) acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[mi][ni], AFMT, BFMT, OA, sa, OB, sb)
         const int oa = 2 * (mi & 1) + kk, ob = 2 * (ni & 1) + kk;
         switch (oa * 4 + ob) {
             case 0: DQ_MFMA(0, 0); break;   case 1: DQ_MFMA(0, 1); break;   case 2: DQ_MFMA(0, 2); break;   case 3: DQ_MFMA(0, 3); break;
@@ -697,12 +725,12 @@ static int persistent_grid(int total) {
     return min(grid, (total + 7) / 8 * 8);
 }
 
-template <int BFMT, int EPI>
+template <int BFMT, int EPI, int AFMT = FMT_FP4>
 static hipError_t launch(const GemmArgs& a, hipStream_t st) {
     constexpr int NS = BFMT == FMT_FP4 ? 4 : 3;      // the kernel's LDS stages
     const int grid = persistent_grid(a.mtiles * a.ntiles);
-    if (a.nks < NS) k_gemm<BFMT, EPI, true><<<grid, 256, 0, st>>>(a);
-    else k_gemm<BFMT, EPI, false><<<grid, 256, 0, st>>>(a);
+    if (a.nks < NS) k_gemm<AFMT, BFMT, EPI, true><<<grid, 256, 0, st>>>(a);
+    else k_gemm<AFMT, BFMT, EPI, false><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -767,6 +795,39 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
         return launch<FMT_FP4, EPI_TOKENS>(d, st);
     }
     return hipSuccess;
+}
+
+// The 6-bit layers: one FP6 x FP6 GEMM over the text tokens with the
+// low-rank branch in the epilogue (no per-cube term).  Tokens are their own
+// rows (the table is the identity), grouped in fours only for the quad layout
+// of the fast epilogue.
+hipError_t launch_forward6(const dq_weights* w, dq_act6* a, float* y, hipStream_t st) {
+    GemmArgs d{};
+    d.a = w->rq;
+    d.as = w->rs;
+    d.nks = (int)(w->Kp / 128);
+    d.mtiles = (int)(w->Cop / 256);
+    d.b = a->xq;
+    d.bs = a->xs;
+    d.ntiles = (int)(a->N_pad / 256);
+    d.y = y;
+    d.Co = (int)w->Co;
+    d.vec4 = (w->Co % 4 == 0) && ((uintptr_t)y % 16 == 0);
+    d.stok = a->stok;
+    d.S = 4;
+    d.S2 = 4;
+    d.split = (int)a->N_pad;
+    d.ksplit = 0;
+    d.kmax = 0;
+    d.bias = nullptr;
+    d.u = a->u;
+    d.l2t = w->l2t;
+    d.rp = w->rp;
+    d.sink = a->sink;
+    const bool fast = d.rp == 32 && d.vec4 && a->N * w->Co < (1ll << 31) && d.Co % 256 == 0;
+    if (w->wfmt == FMT_BF6)
+        return fast ? launch<FMT_BF6, EPI_TOKENS_Q, FMT_BF6>(d, st) : launch<FMT_BF6, EPI_TOKENS, FMT_BF6>(d, st);
+    return fast ? launch<FMT_FP6, EPI_TOKENS_Q, FMT_FP6>(d, st) : launch<FMT_FP6, EPI_TOKENS, FMT_FP6>(d, st);
 }
 
 }  // namespace dq

@@ -1412,6 +1412,133 @@ __global__ __launch_bounds__(256) void k_encode_fp4_rows(const float* src, long 
     scales[off_scale(rrow, grp, Kp / 128)] = (uint8_t)(e + 127);
 }
 
+// ---- the 6-bit layers (text tokens: no cubes) ----
+// MX-FP6 encode of rows (Q6(R) at weight preparation, Q6(X) per call) into
+// the GEMM's step-major FP6 layout: one (row, 32-group) per thread; rows of
+// `src` are `ld_src` elements apart.
+template <typename ST>
+__global__ __launch_bounds__(256) void k_encode_fp6(const ST* src, long long rows, long long cols, long long ld_src,
+                                                   long long Kp, uint8_t* codes, uint8_t* scales, int e3m2) {
+    const long long ng = cols / 32;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * ng) return;
+    const long long rrow = idx / ng, grp = idx - rrow * ng;
+    const ST* p = src + rrow * ld_src + grp * 32;
+    float v[32];
+    if constexpr (std::is_same<ST, float>::value) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 f = ((const float4*)p)[i];
+            v[4 * i] = f.x;
+            v[4 * i + 1] = f.y;
+            v[4 * i + 2] = f.z;
+            v[4 * i + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 b = ((const uint4*)p)[i];
+            const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+                v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const int e = mx_exp_fp6(amax, e3m2 != 0);
+    uint32_t d[6];
+    encode_fp6x32(v, pow2f(e), e3m2 != 0, d);
+    const long long nks = Kp / 128;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) *(uint2*)(codes + off_fp6(rrow, grp, i, nks)) = make_uint2(d[2 * i], d[2 * i + 1]);
+    scales[off_scale(rrow, grp, nks)] = (uint8_t)(e + 127);
+}
+
+// U = bf16(bf16(X) L1) for text tokens, in two passes: partial sums over
+// channel splits of USPLIT channels (one wave per (32 tokens, split):
+// 32x32x16 bf16 MFMAs, D[rank][token], fp32 accumulation), then their sum in
+// split order and the bf16 rounding.
+constexpr int USPLIT = 256;
+template <typename XT>
+__global__ __launch_bounds__(64) void k_u_partial(const XT* x, long long N, int Ci, int Kp, const uint16_t* l1t,
+                                                  int rp, float* part, long long Npad) {
+    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+    const long long n = (long long)blockIdx.x * 32 + l32;
+    const bool live = n < N;
+    const int c0 = blockIdx.y * USPLIT, c1 = min(Ci, c0 + USPLIT);
+    const int nct = rp / 32;
+    v16f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = (v16f){};
+    for (int c = c0; c < c1; c += 16) {
+        uint4 xr = make_uint4(0u, 0u, 0u, 0u);           // bf16 of channels c + 8 g .. c + 8 g + 7 of token n
+        if (live) {
+            if constexpr (std::is_same<XT, float>::value) {
+                const float4 f0 = *(const float4*)(x + n * Ci + c + 8 * g), f1 = *(const float4*)(x + n * Ci + c + 8 * g + 4);
+                xr = make_uint4(bf16x2(f0.x, f0.y), bf16x2(f0.z, f0.w), bf16x2(f1.x, f1.y), bf16x2(f1.z, f1.w));
+            } else {
+                xr = *(const uint4*)(x + n * Ci + c + 8 * g);
+            }
+        }
+        const v8bf xb = __builtin_bit_cast(v8bf, xr);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t < nct) {
+                const v8bf a = __builtin_bit_cast(v8bf, *(const uint4*)(l1t + (long long)(t * 32 + l32) * Kp + c + 8 * g));
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb, acc[t], 0, 0, 0);
+            }
+    }
+    if (!live) return;
+    float* dst = part + ((long long)blockIdx.y * Npad + n) * rp;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        if (t < nct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)   // ranks t 32 + 8 i + 4 g .. + 3
+                *(float4*)(dst + t * 32 + 8 * i + 4 * g) =
+                    make_float4(acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]);
+}
+
+__global__ __launch_bounds__(256) void k_u_combine(const float* part, int nsplit, long long N, long long Npad, int rp,
+                                                   uint16_t* u) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= N * rp) return;
+    float s = part[idx];
+    for (int k = 1; k < nsplit; ++k) s = s + part[(long long)k * Npad * rp + idx];
+    u[idx] = bf16_rne(s);
+}
+
+hipError_t launch_encode_fp6(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int64_t Kp,
+                             uint8_t* codes, uint8_t* scales, int e3m2, hipStream_t st) {
+    const long long n = rows * (cols / 32);
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (src_bf16)
+        k_encode_fp6<uint16_t><<<blocks, 256, 0, st>>>((const uint16_t*)src, rows, cols, ld_src, Kp, codes, scales, e3m2);
+    else
+        k_encode_fp6<float><<<blocks, 256, 0, st>>>((const float*)src, rows, cols, ld_src, Kp, codes, scales, e3m2);
+    return hipGetLastError();
+}
+
+hipError_t launch_text_lowrank(const void* x, int x_bf16, int64_t N, int64_t Npad, int Ci, int Kp, const uint16_t* l1t,
+                               int rp, float* part, uint16_t* u, hipStream_t st) {
+    if (rp == 0 || N == 0) return hipSuccess;
+    const int nsplit = (Ci + USPLIT - 1) / USPLIT;
+    dim3 grid((unsigned)((N + 31) / 32), (unsigned)nsplit);
+    if (x_bf16) k_u_partial<uint16_t><<<grid, 64, 0, st>>>((const uint16_t*)x, N, Ci, Kp, l1t, rp, part, Npad);
+    else k_u_partial<float><<<grid, 64, 0, st>>>((const float*)x, N, Ci, Kp, l1t, rp, part, Npad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_u_combine<<<(unsigned)((N * rp + 255) / 256), 256, 0, st>>>(part, nsplit, N, Npad, rp, u);
+    return hipGetLastError();
+}
+
+int text_lowrank_splits(int Ci) { return (Ci + USPLIT - 1) / USPLIT; }
+
 // Q4(R) decoded to bf16 (exact: an FP4 value times a power of two), row-major
 // [rows][Kp], for the bf16-core ablation's library GEMM.  One (row, 32-group)
 // per thread.

@@ -25,7 +25,11 @@ STATUS = {0: "DQ_OK", 1: "DQ_ERR_INVALID_ARG", 2: "DQ_ERR_SHAPE", 3: "DQ_ERR_UNS
 EXPORTS = ("dq_last_error", "dq_status_str", "dq_lowrank_factors", "dq_prepare_weights_lowrank",
            "dq_prepare_weights", "dq_weights_destroy", "dq_weights_info", "dq_weights_export",
            "dq_qact_create", "dq_qact_create_ex", "dq_qact_destroy", "dq_qact_info", "dq_quantize_act", "dq_linear_forward",
-           "dq_core_term", "dq_delta_term", "dq_linear", "dq_qact_export", "dq_linear_noalloc")
+           "dq_core_term", "dq_delta_term", "dq_linear", "dq_qact_export", "dq_linear_noalloc",
+           "dq_prepare_weights_w6", "dq_act6_create", "dq_act6_destroy", "dq_quantize_act6", "dq_linear6_forward",
+           "dq_linear6", "dq_act6_export")
+DQ_FP6_E2M3, DQ_FP6_E3M2 = 2, 3
+FP6_FORMATS = {"fp6_e2m3": DQ_FP6_E2M3, "fp6_e3m2": DQ_FP6_E3M2}
 
 
 class DQError(RuntimeError):
@@ -73,6 +77,13 @@ def load():
         "dq_linear": ([P, P, ctypes.c_int, P, P, P], ctypes.c_int),
         "dq_qact_export": ([P, P, P, P, P, P, P], ctypes.c_int),
         "dq_linear_noalloc": ([P, P, ctypes.c_int, Geom, P, P], ctypes.c_int),
+        "dq_prepare_weights_w6": ([P, ctypes.c_int, I64, I64, I32, P, P, I32, I32, PP], ctypes.c_int),
+        "dq_act6_create": ([P, I64, PP], ctypes.c_int),
+        "dq_act6_destroy": ([P], None),
+        "dq_quantize_act6": ([P, P, ctypes.c_int, P, P], ctypes.c_int),
+        "dq_linear6_forward": ([P, P, P, P], ctypes.c_int),
+        "dq_linear6": ([P, P, ctypes.c_int, P, P, P], ctypes.c_int),
+        "dq_act6_export": ([P, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -184,6 +195,20 @@ class Weights:
             self.handle = None
 
 
+class Act6:
+    """Owns a dq_act6 handle (keeps its weights alive)."""
+
+    def __init__(self, handle: ctypes.c_void_p, weights: "Weights", N: int):
+        self.handle = handle
+        self.weights = weights
+        self.N = N
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.dq_act6_destroy(self.handle)
+            self.handle = None
+
+
 class QAct:
     """Owns a dq_qact handle (keeps its weights alive)."""
 
@@ -239,8 +264,9 @@ def dq_prepare_weights(w, rank: int, seed: int = 0, device: int = 0) -> Weights:
 
 def dq_weights_export(w: Weights) -> dict:
     Ci, Co, r = w.Ci, w.Co, w.rank
+    cbytes = Ci // 4 * 3 if getattr(w, "fp6_format", None) else Ci // 2
     out = dict(l1=np.zeros((Ci, r), np.uint16), l2=np.zeros((r, Co), np.uint16), r=np.zeros((Co, Ci), np.float32),
-               rcodes=np.zeros((Co, Ci // 2), np.uint8), rscales=np.zeros((Co, Ci // 32), np.uint8))
+               rcodes=np.zeros((Co, cbytes), np.uint8), rscales=np.zeros((Co, Ci // 32), np.uint8))
     _check(load().dq_weights_export(w.handle, _ptr(out["l1"]), _ptr(out["l2"]), _ptr(out["r"]), _ptr(out["rcodes"]),
                                     _ptr(out["rscales"])), "dq_weights_export")
     return out
@@ -313,3 +339,62 @@ def dq_linear_noalloc(w: Weights, x, geom: Sequence[int], y, stream=None):
     _check_x(f, w, ws, x)
     _check_y(f, w, ws, y)
     _check(load().dq_linear_noalloc(w.handle, _ptr(x), _dtype_of(x), Geom(*geom), _ptr(y), _stream(stream)), f)
+
+
+# ---------------------------------------------------------------- 6-bit layers ----
+def dq_prepare_weights_w6(w, l1: Optional[np.ndarray], l2: Optional[np.ndarray], fmt: str = "fp6_e2m3",
+                          device: int = 0) -> Weights:
+    """A 6-bit weight (Q6(R) in MX-FP6 `fmt`: "fp6_e2m3" or "fp6_e3m2")."""
+    f = "dq_prepare_weights_w6"
+    if fmt not in FP6_FORMATS:
+        _invalid(f, f"fmt must be one of {sorted(FP6_FORMATS)}")
+    wt, dt = _host_weight(w)
+    Co, Ci = wt.shape
+    if (l1 is None) != (l2 is None):
+        _invalid(f, "give both factors or neither")
+    rank = 0 if l1 is None else np.asarray(l1).shape[-1]
+    if l1 is not None and np.asarray(l1).ndim != 2:
+        _invalid(f, "l1 must be 2-D [Ci][rank]")
+    l1c = None if l1 is None else _factor(f, "l1", l1, (Ci, rank))
+    l2c = None if l2 is None else _factor(f, "l2", l2, (rank, Co))
+    h = ctypes.c_void_p()
+    _check(load().dq_prepare_weights_w6(_ptr(wt), dt, Ci, Co, rank, _ptr(l1c), _ptr(l2c), FP6_FORMATS[fmt], device,
+                                        ctypes.byref(h)), f)
+    wts = Weights(h)
+    wts.fp6_format = fmt
+    return wts
+
+
+def dq_act6_create(w: Weights, N: int) -> Act6:
+    h = ctypes.c_void_p()
+    _check(load().dq_act6_create(w.handle, N, ctypes.byref(h)), "dq_act6_create")
+    return Act6(h, w, N)
+
+
+def dq_quantize_act6(w: Weights, x, a: Act6, stream=None):
+    _check_pair("dq_quantize_act6", w, a)
+    _check_x("dq_quantize_act6", w, a, x)
+    _check(load().dq_quantize_act6(w.handle, _ptr(x), _dtype_of(x), a.handle, _stream(stream)), "dq_quantize_act6")
+
+
+def dq_linear6_forward(w: Weights, a: Act6, y, stream=None):
+    _check_pair("dq_linear6_forward", w, a)
+    _check_y("dq_linear6_forward", w, a, y)
+    _check(load().dq_linear6_forward(w.handle, a.handle, _ptr(y), _stream(stream)), "dq_linear6_forward")
+
+
+def dq_linear6(w: Weights, x, a: Act6, y, stream=None):
+    _check_pair("dq_linear6", w, a)
+    _check_x("dq_linear6", w, a, x)
+    _check_y("dq_linear6", w, a, y)
+    _check(load().dq_linear6(w.handle, _ptr(x), _dtype_of(x), a.handle, _ptr(y), _stream(stream)), "dq_linear6")
+
+
+def dq_act6_export(a: Act6, stream=None) -> dict:
+    w = a.weights
+    N, Ci, r = a.N, w.Ci, w.rank
+    out = dict(codes=np.zeros((N, Ci // 4 * 3), np.uint8), scales=np.zeros((N, Ci // 32), np.uint8),
+               U=np.zeros((N, r), np.uint16))
+    _check(load().dq_act6_export(a.handle, _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["U"]), _stream(stream)),
+           "dq_act6_export")
+    return out

@@ -32,8 +32,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["LayerConfig", "CONFIGS", "make_activation", "make_weight", "dyadic_activation",
-           "to_f32_numpy"]
+__all__ = ["LayerConfig", "CONFIGS", "TextConfig", "TEXT_CONFIGS", "make_activation", "make_weight",
+           "make_text_activation", "dyadic_activation", "to_f32_numpy"]
 
 
 @dataclass(frozen=True)
@@ -75,6 +75,55 @@ CONFIGS = {
                                  ((1, 1, 1), (1, 2, 2), (2, 2, 2), (1, 4, 4), (21, 45, 80)), 32,
                                  16, 20.0, 100.0, (5000,), 5500),
 }
+
+
+@dataclass(frozen=True)
+class TextConfig:
+    """A 6-bit layer on text tokens: `prompts` contexts of `ctx` token slots
+    each (N = prompts x ctx rows), Ci -> Co."""
+    name: str
+    prompts: int
+    ctx: int
+    valid: Tuple[int, ...]          # prompt tokens at the start of each context (the rest is zero padding)
+    Ci: int
+    Co: int
+    dtype: str
+    rank: int
+    n_outliers: int
+    x_seed: int
+    w_seed: int
+
+    @property
+    def N(self) -> int:
+        return self.prompts * self.ctx
+
+
+# The cross-attention K and V projections of a 14B-class video DiT: two
+# 512-slot text contexts (a conditional prompt of 180 tokens and an empty
+# negative prompt, the pair that classifier-free guidance evaluates),
+# channels 5120 -> K and V stacked (2 x 5120).
+TEXT_CONFIGS = {
+    "kv_text_14b": TextConfig("kv_text_14b", 2, 512, (180, 1), 5120, 10240, "bf16", 32, 8, 6000, 6500),
+}
+
+
+def make_text_activation(prompts: int, ctx: int, valid: Sequence[int], Ci: int, seed: int, dtype: str = "bf16",
+                         n_outliers: int = 8, outlier_lo: float = 20.0, outlier_hi: float = 100.0) -> torch.Tensor:
+    """Text-token activation [prompts * ctx, Ci]: in context p, tokens
+    0 .. valid[p] - 1 are N(0, 1) embeddings with per-channel log-normal
+    scales (sigma 0.5) and `n_outliers` channels scaled by U(lo, hi); the
+    remaining slots are zero padding.  Rounded once to `dtype`."""
+    g = torch.Generator().manual_seed(int(seed))
+    scale = torch.exp(0.5 * torch.randn(Ci, generator=g))
+    out = torch.zeros(prompts * ctx, Ci, dtype=torch.float32)
+    perm = torch.randperm(Ci, generator=g)[:n_outliers]
+    fac = outlier_lo + (outlier_hi - outlier_lo) * torch.rand(n_outliers, generator=g)
+    for p in range(prompts):
+        v = min(int(valid[p % len(valid)]), ctx)
+        tok = torch.randn(v, Ci, generator=g) * scale
+        tok[:, perm] *= fac
+        out[p * ctx:p * ctx + v] = tok
+    return out.to(_torch_dtype(dtype))
 
 
 def _torch_dtype(dtype: str) -> torch.dtype:
