@@ -136,15 +136,14 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out);
  *     cores, the 4-bit point of the pages' core-precision ablation (消融实验);
  *     the core GEMM then runs FP4 x FP4; 16: bf16 cores (round to nearest
  *     even, no scales; core_group is then unused), the ablation's 16-bit
- *     point: the core term is a library GEMM (rocBLAS, fp32 accumulation) of
+ *     point: the core term is a bf16 x bf16 MFMA GEMM (fp32 accumulation) of
  *     the bf16 cores against Q4(R) decoded to bf16 (exact), which the
  *     workspace holds (Co x Ci x 2 bytes more).
  * Deltas keep MX-FP4 with groups of 32.  dq_qact_export reports core codes one
  * per byte for 8 and 4 bits; for 16 bits it writes the bf16 bits (2 bytes per
  * value, so ccodes needs K x Ci x 2 bytes) and leaves cscales untouched.
  * Errors: DQ_ERR_INVALID_ARG for another core_group or core_bits, DQ_ERR_SHAPE
- * when core_group does not divide Ci, DQ_ERR_DEVICE if the library GEMM's
- * handle cannot be created, and those of dq_qact_create. */
+ * when core_group does not divide Ci, and those of dq_qact_create. */
 dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_group, int32_t core_bits,
                             dq_qact** out);
 void dq_qact_destroy(dq_qact* q);

@@ -53,9 +53,7 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB + ".tmp"
-    # (rocBLAS: the library GEMM of the bf16-core ablation)
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp, "-lpthread",
-           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp, "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -13,8 +13,6 @@
 #include <string>
 #include <vector>
 
-#include <rocblas/rocblas.h>
-
 #include "dq.h"
 #include "dq_internal.h"
 
@@ -93,7 +91,6 @@ void free_qact(dq_qact* q) {
     (void)hipFree(q->part);
     (void)hipFree(q->cbf);
     (void)hipFree(q->rbf);
-    if (q->blas) (void)rocblas_destroy_handle((rocblas_handle)q->blas);
     delete q;
 }
 
@@ -448,15 +445,12 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
             (e = dalloc(&q->part, (size_t)(max_partials * q->Kp), &q->bytes)) != hipSuccess)
             return hip_fail(e, "hipMalloc workspace");
     }
-    if (core_bits == 16) {                          // bf16 cores: Q4(R) as bf16 and a library GEMM
+    if (core_bits == 16) {                          // bf16 cores: Q4(R) as bf16 for the bf16 GEMM
         if ((e = dalloc(&q->cbf, (size_t)(q->K_pad * q->Kp), &q->bytes)) != hipSuccess ||
             (e = dalloc(&q->rbf, (size_t)(q->Cop * q->Kp), &q->bytes)) != hipSuccess)
             return hip_fail(e, "hipMalloc workspace");
         if ((e = launch_decode_fp4_bf16(w->rq, w->rs, q->Cop, q->Kp, q->rbf, nullptr)) != hipSuccess)
             return hip_fail(e, "decode Q4(R)");
-        rocblas_handle h = nullptr;
-        if (rocblas_create_handle(&h) != rocblas_status_success) return fail(DQ_ERR_DEVICE, "rocblas_create_handle failed");
-        q->blas = h;
     }
     if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "workspace init");
     *out = guard.release();
@@ -504,21 +498,6 @@ static dq_status forward_parts(const dq_weights* w, dq_qact* q, float* y_dev, in
     if (((uintptr_t)y_dev) % 4 != 0) return fail(DQ_ERR_INVALID_ARG, "y_dev must be 4-byte aligned");
     DeviceGuard dg(q->device);
     if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
-    if (q->core_bits == 16 && (parts & dq::FWD_CORE)) {
-        // bf16 cores: per-cube term [K_pad][Cop] = cores [K_pad][Kp] x (Q4(R) as bf16 [Cop][Kp])^T, fp32
-        // accumulation and output (column-major: term^T = R_bf16 (transposed view) x cores^T)
-        rocblas_handle h = (rocblas_handle)q->blas;
-        const float one = 1.0f, zero = 0.0f;
-        if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success ||
-            rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)q->Cop,
-                            (rocblas_int)q->K_pad, (rocblas_int)q->Kp, &one, q->rbf, rocblas_datatype_bf16_r,
-                            (rocblas_int)q->Kp, q->cbf, rocblas_datatype_bf16_r, (rocblas_int)q->Kp, &zero, q->bias,
-                            rocblas_datatype_f32_r, (rocblas_int)q->Cop, q->bias, rocblas_datatype_f32_r,
-                            (rocblas_int)q->Cop, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) !=
-                rocblas_status_success)
-            return fail(DQ_ERR_DEVICE, "bf16 core GEMM failed");
-        parts &= ~dq::FWD_CORE;
-    }
     hipError_t e = launch_forward(w, q, y_dev, parts, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return DQ_OK;
@@ -586,7 +565,8 @@ dq_status dq_qact_export(const dq_qact* q, uint8_t* dcodes_host, uint8_t* dscale
         if (ccodes_host && q->core_bits == 16) {            // bf16 bits, two bytes per value
             if ((e = fetch_all(q->cbf, (size_t)(q->K_pad * Kp * 2), buf)) != hipSuccess) return hip_fail(e, "copy cores");
             for (long long k = 0; k < g.K; ++k)
-                std::memcpy(ccodes_host + k * Ci * 2, &buf[(size_t)(cube_row(k) * Kp * 2)], (size_t)(Ci * 2));
+                for (int64_t c = 0; c < Ci; c += 8)
+                    std::memcpy(ccodes_host + (k * Ci + c) * 2, &buf[off_bf16(cube_row(k), c, Kp / 32)], 16);
         } else if (ccodes_host) {
             if ((e = fetch_all(q->cq, (size_t)(q->K_pad * Kp), buf)) != hipSuccess) return hip_fail(e, "copy core codes");
             if (q->core_bits == 4) {                      // packed nibbles -> one code per byte

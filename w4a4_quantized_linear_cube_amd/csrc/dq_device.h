@@ -20,6 +20,7 @@ constexpr int FMT_FP8 = 0;
 constexpr int FMT_FP6 = 2;   // FP6 E2M3
 constexpr int FMT_BF6 = 3;   // FP6 E3M2
 constexpr int FMT_FP4 = 4;
+constexpr int FMT_BF16 = 16;  // plain bf16 operands (the bf16-core ablation), not a scaled-MFMA format
 
 // Scale exponent of an MX group (关键设计 4, quantizer definition, with the
 // scale restricted to a power of two): the smallest e with

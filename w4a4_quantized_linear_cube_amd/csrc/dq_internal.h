@@ -86,6 +86,18 @@ __host__ __device__ inline size_t off_scale(long long row, long long G, long lon
     return (size_t)(row >> 8) * (size_t)nks * 1024 + toff_scale((int)(row & 255), (int)G);
 }
 
+// bf16 operands of the bf16 GEMM (the 16-bit cores and Q4(R) decoded to
+// bf16): 32 channels (64 bytes) per row step, laid out like the FP4 codes
+// (16-byte chunk c, channels 8 c .. 8 c + 7 of the step, at chunk c ^ swz4(r)),
+// so a 32x32x16 bf16 MFMA fragment is one chunk, read like an FP4 one.
+// Byte offset of channel ch of row `row` in a matrix of nks32 = Kp / 32 steps.
+__host__ __device__ inline size_t off_bf16(long long row, long long ch, long long nks32) {
+    const int r = (int)(row & 255);
+    const int c = (int)((ch >> 3) & 3);
+    return (size_t)(row >> 8) * (size_t)nks32 * 16384 + ((size_t)(ch >> 5) * 256 + (size_t)r) * 64 +
+           (size_t)((c ^ swz4(r)) << 4) + (size_t)(ch & 7) * 2;
+}
+
 // Token grid and cube shape, with derived counts, as kernels see them.
 struct Geom {
     int T, H, W, t, h, w;
@@ -132,9 +144,8 @@ struct dq_qact {
     dq::Geom g{};              // the full token grid and cube shape
     int core_group = 32;       // channels per exponent of the cores (32 or 64)
     int core_bits = 8;         // cores as MX-FP8 (8), MX-FP4 (4, the FP4 layout in cq) or bf16 (16, in cbf)
-    uint16_t* cbf = nullptr;   // [K_pad][Kp]        bf16 cores (core_bits 16)
-    uint16_t* rbf = nullptr;   // [Cop][Kp]          Q4(R) decoded to bf16 (core_bits 16)
-    void* blas = nullptr;      // rocBLAS handle of the bf16 core GEMM (core_bits 16)
+    uint16_t* cbf = nullptr;   // K_pad x Kp         bf16 cores, step-major (off_bf16) (core_bits 16)
+    uint16_t* rbf = nullptr;   // Cop x Kp           Q4(R) decoded to bf16, step-major (off_bf16) (core_bits 16)
     int nseg = 1;
     dq_segment seg[2]{};
     int64_t Nslot_pad = 0, K_pad = 0;

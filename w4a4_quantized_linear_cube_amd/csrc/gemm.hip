@@ -164,24 +164,28 @@ __device__ __forceinline__ TileWalk tile_walk(int b, int G, int mt, int nt, int 
 // ahead); that form recomputes the copy sources every step, the other one
 // only once per tile.
 // AFMT: Q4(R) (FMT_FP4) or, for the 6-bit layers, Q6(R) (FMT_FP6 E2M3 or
-// FMT_BF6 E3M2, with BFMT the same 6-bit format).
+// FMT_BF6 E3M2, with BFMT the same 6-bit format), or Q4(R) decoded to bf16
+// with bf16 cores (FMT_BF16 for both: 32x32x16 bf16 MFMAs, no scales, K
+// steps of 32 channels in the FP4 layout's 64-byte rows).
 template <int AFMT, int BFMT, int EPI, bool SMALLK>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     constexpr bool A6 = AFMT == FMT_FP6 || AFMT == FMT_BF6;
     constexpr bool B6 = BFMT == FMT_FP6 || BFMT == FMT_BF6;
+    constexpr bool BF = AFMT == FMT_BF16;
     static_assert(A6 == B6, "6-bit operands come in pairs");
+    static_assert(BF == (BFMT == FMT_BF16), "bf16 operands come in pairs");
     constexpr int AROW = A6 ? 96 : 64;                        // A bytes per row per K step
-    constexpr int BROW = BFMT == FMT_FP4 ? 64 : (B6 ? 96 : 128);   // B bytes per row per K step
+    constexpr int BROW = (BFMT == FMT_FP4 || BF) ? 64 : (B6 ? 96 : 128);   // B bytes per row per K step
     constexpr int A_STEP = 256 * AROW;                        // A bytes per tile step
     constexpr int B_STEP = 256 * BROW;
     constexpr int B_OFF = A_STEP;
     constexpr int SA_OFF = B_OFF + B_STEP;
     constexpr int SB_OFF = SA_OFF + 1024;
     constexpr int STAGE = SB_OFF + 1024;
-    constexpr int NS = BFMT == FMT_FP4 ? 4 : 3;               // LDS stages in the ring (50 KB stages: 3)
+    constexpr int NS = (BFMT == FMT_FP4 || BF) ? 4 : 3;       // LDS stages in the ring (50 KB stages: 3)
     constexpr int APC = A_STEP / 1024 / 4;                    // 1 KB copies per wave: A
     constexpr int BPC = B_STEP / 1024 / 4;                    //                       B
-    constexpr int DMAS = APC + BPC + 2;                       // copies per wave per stage
+    constexpr int DMAS = APC + BPC + (BF ? 0 : 2);            // copies per wave per stage (+ scale codes)
     static_assert((NS - 2) * DMAS < 63, "vmcnt range");
     // With four stages a stage's copies go out in two halves: H1 of them in
     // phase 2 of one step, the rest in phase 1 of the next, so the copy
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     const int arow0 = wr * 128 + l32;            // + 32 mi
     const int brow0 = wc * 128 + l32;            // + 32 ni
     const int asw = swz4(arow0);                 // the swizzles depend on row % 16 only
-    const int bsw = BFMT == FMT_FP4 ? swz4(brow0) : swz8(brow0);
+    const int bsw = (BFMT == FMT_FP4 || BF) ? swz4(brow0) : swz8(brow0);   // bf16 rows use the FP4 layout
     const int r6 = rot6(l32);                    // FP6 word rotation (rows arow0 + 32 mi, brow0 + 32 ni: rot6(l32))
     // Scale codes: one 8-byte read per operand gives the lane's codes for the
     // whole step (four 32-row blocks x two halves); code (block r, half kk) is
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     struct Half {
         uint4 a[A6 ? 1 : 4];                   // FP4 A fragments
         uint2 a6[A6 ? 4 : 1][3];               // FP6 A fragments (three 8-byte words each)
-        uint4 b[BFMT == FMT_FP4 ? 4 : 1];      // FP4 B fragments
+        uint4 b[(BFMT == FMT_FP4 || BF) ? 4 : 1];   // FP4 (or bf16) B fragments
         v8i b8[BFMT == FMT_FP8 ? 4 : 1];       // FP8 B fragments (two 16-byte chunks each)
         uint2 b6[B6 ? 4 : 1][3];               // FP6 B fragments
         uint2 sa, sb;
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             const uint8_t* rowp = st + B_OFF + (brow0 + 32 * ni) * BROW;
             if constexpr (B6) {
                 rd6(rowp, 2 * kk + g, F.b6[ni]);
-            } else if constexpr (BFMT == FMT_FP4) {
+            } else if constexpr (BFMT == FMT_FP4 || BF) {
                 F.b[ni] = *(const uint4*)(rowp + (((2 * kk + g) ^ bsw) << 4));
             } else {
                 const v4i lo = *(const v4i*)(rowp + (((4 * kk + g) ^ bsw) << 4));
@@ -336,8 +340,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         switch (i) {
             case 0: rda(0); break;
             case 1: rdb(0); break;
-            case 2: F.sa = *(const uint2*)(st + sa_off); break;
-            case 3: F.sb = *(const uint2*)(st + sb_off); break;
+            case 2: if constexpr (!BF) F.sa = *(const uint2*)(st + sa_off); break;
+            case 3: if constexpr (!BF) F.sb = *(const uint2*)(st + sb_off); break;
             case 4: rdb(1); break;
             case 5: rdb(2); break;
             case 6: rdb(3); break;
@@ -350,6 +354,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // MFMA number i (0 .. 15) of half kk: row block mi = i / 4, column block ni = i % 4
     auto mma = [&](const Half& F, int kk, int i) {
         const int mi = i >> 2, ni = i & 3;
+        if constexpr (BF) {
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, F.a[mi]),
+                                                                  __builtin_bit_cast(v8bf, F.b[ni]), acc[mi][ni], 0, 0, 0);
+            return;
+        }
         v8i af, bf;
         if constexpr (A6) {
             const uint2* w = F.a6[mi];
@@ -727,7 +736,7 @@ static int persistent_grid(int total) {
 
 template <int BFMT, int EPI, int AFMT = FMT_FP4>
 static hipError_t launch(const GemmArgs& a, hipStream_t st) {
-    constexpr int NS = BFMT == FMT_FP4 ? 4 : 3;      // the kernel's LDS stages
+    constexpr int NS = (BFMT == FMT_FP4 || BFMT == FMT_BF16) ? 4 : 3;      // the kernel's LDS stages
     const int grid = persistent_grid(a.mtiles * a.ntiles);
     if (a.nks < NS) k_gemm<AFMT, BFMT, EPI, true><<<grid, 256, 0, st>>>(a);
     else k_gemm<AFMT, BFMT, EPI, false><<<grid, 256, 0, st>>>(a);
@@ -775,7 +784,21 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
         if (d.rp == 32 && d.vec4 && off32 && d.Co % 256 == 0) return launch<FMT_FP8, EPI_TOKENS_Q>(d, st);
         return launch<FMT_FP8, EPI_TOKENS>(d, st);
     }
-    if (parts & FWD_CORE) {
+    if ((parts & FWD_CORE) && q->core_bits == 16) {
+        // bf16 cores: bias[k] = bf16(core_k) Q4(R), with Q4(R) decoded to bf16
+        // (exact), 32x32x16 bf16 MFMAs with fp32 accumulation
+        GemmArgs c = d;
+        c.a = (const uint8_t*)q->rbf;
+        c.as = nullptr;
+        c.b = (const uint8_t*)q->cbf;
+        c.bs = nullptr;
+        c.nks = (int)(w->Kp / 32);
+        c.ntiles = (int)(q->K_pad / 256);
+        c.c = q->bias;
+        c.ldc = w->Cop;
+        hipError_t e = launch<FMT_BF16, EPI_STORE, FMT_BF16>(c, st);
+        if (e != hipSuccess) return e;
+    } else if (parts & FWD_CORE) {
         // per-cube core term bias[k] = Q8(core_k) Q4(R) (Q4(core_k) for 4-bit cores)
         GemmArgs c = d;
         c.b = q->cq;

@@ -55,11 +55,16 @@ struct QuantArgs {
     const int* stok;          // [Nslot_pad] token of each slot, -1 for pad slots
     int core_g64;             // cores: one exponent per 64 channels (the maximum of two 32-channel groups)
     int core_fp4;             // cores as MX-FP4 (the FP4 layout in cq) instead of MX-FP8
-    uint16_t* cbf;            // bf16 cores [K][Kp] row-major (16-bit cores), else null
+    uint16_t* cbf;            // bf16 cores, step-major (off_bf16) (16-bit cores), else null
 };
 
 // bf16 bits of n consecutive core values (n = 2, 4, 8), packed for one store
 __device__ __forceinline__ uint32_t bf16x2(float a, float b) { return (uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16); }
+// address of channel ch of cube row k of the bf16 cores (1, 2, 4 or 8
+// channels aligned to their count are contiguous)
+__device__ __forceinline__ uint16_t* cbf_at(uint16_t* cbf, long long k, long long ch, int Kp) {
+    return (uint16_t*)((uint8_t*)cbf + off_bf16(k, ch, Kp / 32));
+}
 
 // LDS chunk layout: 16-byte piece c of row r at r QROWB + ((c ^ (r & 15)) << 4);
 // the XOR makes the quantizer's row reads and the MFMA's column reads free of
@@ -602,7 +607,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const float cmax = core_pair_max<32>(amax, a.core_g64);
                     const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const int gch = c0 + ch;                       // channel within the row
-                    if (a.cbf) a.cbf[k * a.Kp + gch] = bf16_rne(s0);
+                    if (a.cbf) *cbf_at(a.cbf, k, gch, a.Kp) = bf16_rne(s0);
                     if (a.core_fp4) {
                         // a channel pair's two nibbles meet in its even lane
                         const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0xB1, 0xF, 0xF, false));
@@ -681,7 +686,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const float cmax = core_pair_max<16>(amax, a.core_g64);
                     const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const int gch = c0 + ch;                       // channel within the row
-                    if (a.cbf) *(uint32_t*)(a.cbf + k * a.Kp + gch) = bf16x2(s0, s1);
+                    if (a.cbf) *(uint32_t*)cbf_at(a.cbf, k, gch, a.Kp) = bf16x2(s0, s1);
                     if (a.core_fp4) {
                         *(uint8_t*)(a.cq + off_fp4(k, gch >> 5, nks) + ((gch & 31) >> 1)) =
                             (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s0, s1, pow2f(ex), 0);
@@ -843,7 +848,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 const int ex = a.core_fp4 ? mx_exp_fp4(amax) : mx_exp_fp8(amax);
                 const float sc = pow2f(ex);
                 if (a.cbf)
-                    *(uint4*)(a.cbf + k * a.Kp + G * 32 + 8 * qq) = make_uint4(bf16x2(core[0], core[1]), bf16x2(core[2], core[3]),
+                    *(uint4*)cbf_at(a.cbf, k, G * 32 + 8 * qq, a.Kp) = make_uint4(bf16x2(core[0], core[1]), bf16x2(core[2], core[3]),
                                                                             bf16x2(core[4], core[5]), bf16x2(core[6], core[7]));
                 if (a.core_fp4) {
                     uint32_t w = 0u;
@@ -1011,7 +1016,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const int gch = c0 + ch;               // channel within the row
                     if (ch < CC) {
                         if (gch < a.Ci) {
-                            if (a.cbf) *(uint32_t*)(a.cbf + k * a.Kp + gch) = bf16x2(s0, s1);
+                            if (a.cbf) *(uint32_t*)cbf_at(a.cbf, k, gch, a.Kp) = bf16x2(s0, s1);
                             if (a.core_fp4) *(uint8_t*)(a.cq + off_fp4(k, gch >> 5, nks) + ((gch & 31) >> 1)) = (uint8_t)cd;
                             else *(uint16_t*)(a.cq + off_fp8(k, gch >> 7, (gch & 127) >> 4, nks) + (gch & 15)) = cd;
                             if ((ch & 31) == 0) a.cs[off_scale(k, gch >> 5, nks)] = (uint8_t)(ex + 127);
@@ -1114,7 +1119,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const int ex = a.core_fp4 ? mx_exp_fp4(cmax) : mx_exp_fp8(cmax);
                     const float sc = pow2f(ex);
                     if (a.cbf)
-                        *(uint2*)(a.cbf + (B.k_first + cr) * a.Kp + G * 32 + 4 * e) = make_uint2(bf16x2(core[0], core[1]), bf16x2(core[2], core[3]));
+                        *(uint2*)cbf_at(a.cbf, B.k_first + cr, G * 32 + 4 * e, a.Kp) = make_uint2(bf16x2(core[0], core[1]), bf16x2(core[2], core[3]));
                     if (a.core_fp4) {
                         uint32_t w = 0u;
                         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, core[0], core[1], sc, 0);
@@ -1175,7 +1180,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 amax = core_pair_max<4>(quad_max(amax), a.core_g64);
                 const int kt = (int)(B.k_first & 255) + cr;
                 if (a.cbf)
-                    *(uint4*)(a.cbf + (B.k_first + cr) * a.Kp + G * 32 + 8 * qq) = make_uint4(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]),
+                    *(uint4*)cbf_at(a.cbf, B.k_first + cr, G * 32 + 8 * qq, a.Kp) = make_uint4(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]),
                                                                                          bf16x2(v[4], v[5]), bf16x2(v[6], v[7]));
                 if (a.core_fp4) {
                     const int ex = mx_exp_fp4(amax);
@@ -1306,7 +1311,7 @@ struct CombineArgs {
     uint8_t* cs;     // K_pad x Kp/32, step-major
     int core_g64;    // one exponent per 64 channels
     int core_fp4;    // MX-FP4 cores (FP4 layout in cq)
-    uint16_t* cbf;   // bf16 cores [K][Kp] (16-bit cores), else null
+    uint16_t* cbf;   // bf16 cores, step-major (off_bf16) (16-bit cores), else null
 };
 
 // core = fl32(sum of the block partials in block order / count), then FP8 codes.
@@ -1360,7 +1365,7 @@ __global__ __launch_bounds__(256) void k_core_combine(CombineArgs a) {
         if (a.cbf)
 #pragma unroll
             for (int i = 0; i < 32; i += 8)
-                *(uint4*)(a.cbf + k * a.Kp + cg + i) = make_uint4(bf16x2(v[i], v[i + 1]), bf16x2(v[i + 2], v[i + 3]),
+                *(uint4*)cbf_at(a.cbf, k, cg + i, a.Kp) = make_uint4(bf16x2(v[i], v[i + 1]), bf16x2(v[i + 2], v[i + 3]),
                                                                   bf16x2(v[i + 4], v[i + 5]), bf16x2(v[i + 6], v[i + 7]));
         int e;
         if (a.core_fp4) {
@@ -1539,9 +1544,9 @@ hipError_t launch_text_lowrank(const void* x, int x_bf16, int64_t N, int64_t Npa
 
 int text_lowrank_splits(int Ci) { return (Ci + USPLIT - 1) / USPLIT; }
 
-// Q4(R) decoded to bf16 (exact: an FP4 value times a power of two), row-major
-// [rows][Kp], for the bf16-core ablation's library GEMM.  One (row, 32-group)
-// per thread.
+// Q4(R) decoded to bf16 (exact: an FP4 value times a power of two), in the
+// bf16 GEMM's step-major layout (off_bf16), for the bf16-core ablation.  One
+// (row, 32-group) per thread.
 __global__ __launch_bounds__(256) void k_decode_fp4_bf16(const uint8_t* codes, const uint8_t* scales, long long rows,
                                                         long long Kp, uint16_t* out) {
     const long long ng = Kp / 32, idx = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -1559,9 +1564,9 @@ __global__ __launch_bounds__(256) void k_decode_fp4_bf16(const uint8_t* codes, c
         const float hi = ((byte & 128u) ? -1.0f : 1.0f) * mag[(byte >> 4) & 7u] * sc;
         o[i] = bf16x2(lo, hi);
     }
-    uint4* dst = (uint4*)(out + r * Kp + G * 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    for (int i = 0; i < 4; ++i)
+        *(uint4*)((uint8_t*)out + off_bf16(r, G * 32 + 8 * i, Kp / 32)) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
 }
 
 hipError_t launch_decode_fp4_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t Kp, uint16_t* out,

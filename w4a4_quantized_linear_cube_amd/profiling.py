@@ -28,8 +28,10 @@ import sys
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-DELTA_KERNEL = re.compile(r"k_gemm<4, [12], ")     # the delta GEMM (FP4 B operand, token epilogue)
-CORE_KERNEL = re.compile(r"k_gemm<[04], 0, ")     # the core GEMM (FP8 or FP4 cores, plain-store epilogue)
+# k_gemm<A format, B format, epilogue, ...>
+DELTA_KERNEL = re.compile(r"k_gemm<4, 4, [12], ")          # the delta GEMM (FP4 x FP4, token epilogue)
+CORE_KERNEL = re.compile(r"k_gemm<(4, [04]|16, 16), 0, ")   # the core GEMM (FP8, FP4 or bf16 cores, plain stores)
+W6_KERNEL = re.compile(r"k_gemm<[23], [23], [12], ")        # the 6-bit layers' FP6 x FP6 GEMM
 QUANT_KERNEL = re.compile(r"k_quantize<")
 SIMDS = 1024                                     # 256 CUs x 4 SIMDs
 XCDS = 8                                         # GRBM_GUI_ACTIVE comes summed over the XCDs
