@@ -1,0 +1,160 @@
+// Host-only exercise of the library's C++ (argument checks, the workspace
+// layout planning, the randomized SVD) built with AddressSanitizer and
+// UndefinedBehaviorSanitizer, without a GPU: the device launchers are stubs
+// that never run, and every device-touching path returns an error status
+// before reaching them.  Exit status 0 when every expectation holds.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <vector>
+
+#include "dq.h"
+#include "dq_internal.h"
+
+namespace dq {
+static hipError_t stub() { return hipErrorNoDevice; }
+hipError_t launch_residual(const void*, int, const uint16_t*, const uint16_t*, int64_t, int64_t, int, float*, hipStream_t) { return stub(); }
+hipError_t launch_encode_fp4_rows(const float*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t) { return stub(); }
+hipError_t launch_quantize(const dq_weights*, const void*, int, dq_qact*, hipStream_t) { return stub(); }
+hipError_t launch_slot_tokens(const Geom&, int64_t, int*, int64_t, hipStream_t) { return stub(); }
+hipError_t launch_decode_fp4_bf16(const uint8_t*, const uint8_t*, int64_t, int64_t, uint16_t*, hipStream_t) { return stub(); }
+hipError_t launch_forward(const dq_weights*, dq_qact*, float*, int, hipStream_t) { return stub(); }
+hipError_t launch_forward6(const dq_weights*, dq_act6*, float*, hipStream_t) { return stub(); }
+hipError_t launch_encode_fp6(const void*, int, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, hipStream_t) { return stub(); }
+hipError_t launch_text_lowrank(const void*, int, int64_t, int64_t, int, int, const uint16_t*, int, float*, uint16_t*, hipStream_t) { return stub(); }
+int text_lowrank_splits(int Ci) { return (Ci + 255) / 256; }
+}  // namespace dq
+
+static int failures = 0;
+#define EXPECT(cond)                                                              \
+    do {                                                                          \
+        if (!(cond)) {                                                            \
+            std::printf("FAILED line %d: %s (%s)\n", __LINE__, #cond, dq_last_error()); \
+            ++failures;                                                           \
+        }                                                                         \
+    } while (0)
+
+static float bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+int main() {
+    std::mt19937 rng(7);
+    std::normal_distribution<float> nd(0.0f, 1.0f);
+    // ---- the host SVD on several shapes, fp32 and bf16 weights
+    const int shapes[][3] = {{64, 48, 8}, {96, 200, 32}, {256, 128, 128}, {32, 1, 1}, {160, 33, 16}};
+    for (auto& sh : shapes) {
+        const int Ci = sh[0], Co = sh[1], r = sh[2];
+        std::vector<float> w((size_t)Ci * Co);
+        for (auto& v : w) v = nd(rng) / std::sqrt((float)Ci);
+        std::vector<uint16_t> wb(w.size());
+        for (size_t i = 0; i < w.size(); ++i) {
+            uint32_t u;
+            std::memcpy(&u, &w[i], 4);
+            wb[i] = (uint16_t)(u >> 16);
+        }
+        std::vector<uint16_t> l1((size_t)Ci * r), l2((size_t)r * Co);
+        EXPECT(dq_lowrank_factors(w.data(), DQ_F32, Ci, Co, r, 3, l1.data(), l2.data()) == DQ_OK);
+        for (uint16_t b : l1) EXPECT(std::isfinite(bf16_to_f32(b)));
+        EXPECT(dq_lowrank_factors(wb.data(), DQ_BF16, Ci, Co, r, 4, l1.data(), l2.data()) == DQ_OK);
+        for (uint16_t b : l2) EXPECT(std::isfinite(bf16_to_f32(b)));
+    }
+    // ---- argument rejections (no device is reached)
+    std::vector<float> w(96 * 64, 0.5f);
+    std::vector<uint16_t> l1(96 * 8), l2(8 * 64);
+    dq_weights* hw = nullptr;
+    dq_act6* ha = nullptr;
+    EXPECT(dq_lowrank_factors(nullptr, DQ_F32, 96, 64, 8, 0, l1.data(), l2.data()) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_lowrank_factors(w.data(), DQ_F32, 96, 64, 65, 0, l1.data(), l2.data()) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_lowrank_factors(w.data(), DQ_F32, 0, 64, 0, 0, nullptr, nullptr) == DQ_ERR_SHAPE);
+    EXPECT(dq_lowrank_factors(w.data(), (dq_dtype)9, 96, 64, 8, 0, l1.data(), l2.data()) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_lowrank_factors(w.data(), DQ_F32, 96, 64, 0, 0, nullptr, nullptr) == DQ_OK);
+    EXPECT(dq_prepare_weights_lowrank(w.data(), DQ_F32, 48, 64, 8, l1.data(), l2.data(), 0, &hw) == DQ_ERR_SHAPE);
+    EXPECT(dq_prepare_weights_lowrank(w.data(), DQ_F32, 96, 64, 129, l1.data(), l2.data(), 0, &hw) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_prepare_weights_lowrank(w.data(), DQ_F32, 96, 64, 8, nullptr, l2.data(), 0, &hw) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_prepare_weights_lowrank(w.data(), DQ_F32, 96, 64, 8, l1.data(), l2.data(), 0, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_prepare_weights_w6(w.data(), DQ_F32, 96, 64, 8, l1.data(), l2.data(), 5, 0, &hw) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_prepare_weights(w.data(), DQ_F32, 96, 64, 65, 0, 0, &hw) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_prepare_weights(w.data(), DQ_F32, int64_t(1) << 62, 64, 8, 0, 0, &hw) == DQ_ERR_SHAPE);
+    EXPECT(dq_lowrank_factors(w.data(), DQ_F32, int64_t(1) << 62, int64_t(1) << 62, 8, 0, l1.data(), l2.data()) == DQ_ERR_SHAPE);
+    EXPECT(dq_act6_create(nullptr, -1, &ha) == DQ_ERR_INVALID_ARG);
+    {   // without a GPU the device check fails cleanly
+        dq_status st = dq_prepare_weights_lowrank(w.data(), DQ_F32, 96, 64, 8, l1.data(), l2.data(), 0, &hw);
+        EXPECT(st == DQ_ERR_DEVICE || st == DQ_ERR_UNSUPPORTED || st == DQ_ERR_INVALID_ARG);
+        EXPECT(hw == nullptr);
+    }
+    dq_qact* hq = nullptr;
+    dq_geom g0{2, 4, 4, 1, 2, 2};
+    EXPECT(dq_qact_create(nullptr, g0, &hq) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_qact_create_ex(nullptr, g0, 32, 8, &hq) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_act6_create(nullptr, 16, &ha) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_quantize_act(nullptr, w.data(), DQ_F32, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_linear_forward(nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_core_term(nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_delta_term(nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_linear(nullptr, nullptr, DQ_F32, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_quantize_act6(nullptr, nullptr, DQ_F32, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_linear6_forward(nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_linear6(nullptr, nullptr, DQ_F32, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_qact_export(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_act6_export(nullptr, nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_weights_info(nullptr, nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_weights_export(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    EXPECT(dq_qact_info(nullptr, nullptr, nullptr, nullptr) == DQ_ERR_INVALID_ARG);
+    for (int s = 0; s < 7; ++s) EXPECT(dq_status_str((dq_status)s)[0] != 0);
+    dq_weights_destroy(nullptr);
+    dq_qact_destroy(nullptr);
+    dq_act6_destroy(nullptr);
+    // ---- workspace layout planning over many geometries, with a weight that
+    // exists only on the host (sizes only)
+    dq_weights fw;
+    fw.Ci = 160;
+    fw.Co = 200;
+    fw.Kp = 256;
+    fw.Cop = 256;
+    fw.rank = 16;
+    fw.rp = 32;
+    long long planned = 0;
+    for (int T = 1; T <= 9; ++T)
+        for (int H = 1; H <= 7; H += 2)
+            for (int W = 1; W <= 11; W += 3)
+                for (int t = 1; t <= T; ++t)
+                    for (int h = 1; h <= H; ++h)
+                        for (int ww = 1; ww <= W; ++ww) {
+                            dq_qact q{};
+                            int64_t mp = 0;
+                            dq_geom g{T, H, W, t, h, ww};
+                            if (dq::plan_qact(&fw, g, 32, 8, &q, &mp) != DQ_OK) { ++failures; continue; }
+                            // the segments tile the grid: tokens and cubes add up, rows are 256-aligned
+                            int64_t tok = 0, cubes = 0;
+                            for (int i = 0; i < q.nseg; ++i) {
+                                EXPECT(q.seg[i].row0 % 256 == 0 && q.seg[i].krow0 % 256 == 0);
+                                EXPECT(q.seg[i].tok0 == tok && q.seg[i].k0 == cubes);
+                                tok += q.seg[i].g.N;
+                                cubes += q.seg[i].g.K;
+                            }
+                            EXPECT(tok == (int64_t)T * H * W && cubes == q.g.K);
+                            EXPECT(q.Nslot_pad % 256 == 0 && q.K_pad % 256 == 0);
+                            ++planned;
+                        }
+    {   // invalid and huge geometries are refused
+        dq_qact q{};
+        int64_t mp = 0;
+        EXPECT(dq::plan_qact(&fw, dq_geom{2, 2, 2, 3, 1, 1}, 32, 8, &q, &mp) == DQ_ERR_SHAPE);
+        EXPECT(dq::plan_qact(&fw, dq_geom{0, 2, 2, 1, 1, 1}, 32, 8, &q, &mp) == DQ_ERR_SHAPE);
+        EXPECT(dq::plan_qact(&fw, dq_geom{2, 2, 2, 1, 1, 1}, 48, 8, &q, &mp) == DQ_ERR_INVALID_ARG);
+        EXPECT(dq::plan_qact(&fw, dq_geom{2, 2, 2, 1, 1, 1}, 32, 6, &q, &mp) == DQ_ERR_INVALID_ARG);
+        EXPECT(dq::plan_qact(&fw, dq_geom{2, 2, 2, 1, 1, 1}, 64, 8, &q, &mp) == DQ_ERR_SHAPE);   // 64 does not divide 160
+        EXPECT(dq::plan_qact(&fw, dq_geom{1 << 20, 1 << 20, 1 << 20, 1, 1, 1}, 32, 8, &q, &mp) == DQ_ERR_SHAPE);
+        EXPECT(dq::plan_qact(&fw, dq_geom{2147483647, 2147483647, 2147483647, 2, 2, 2}, 32, 8, &q, &mp) == DQ_ERR_SHAPE);
+        fw.wfmt = 2;
+        EXPECT(dq::plan_qact(&fw, dq_geom{2, 2, 2, 1, 1, 1}, 32, 8, &q, &mp) == DQ_ERR_INVALID_ARG);
+    }
+    std::printf("host sanitize driver: %lld geometries planned, %d failures\n", planned, failures);
+    return failures ? 1 : 0;
+}

@@ -284,6 +284,7 @@ dq_status dq_prepare_weights(const void* w_host, dq_dtype dt, int64_t Ci, int64_
     if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (Ci < 1 || Co < 1) return fail(DQ_ERR_SHAPE, "Ci and Co must be >= 1");
+    if (Ci > (1 << 24) || Co > (1 << 24)) return fail(DQ_ERR_SHAPE, "Ci and Co must be <= 2^24");
     if (rank < 0 || rank > std::min(Ci, Co)) return fail(DQ_ERR_INVALID_ARG, "rank must be in [0, min(Ci, Co)]");
     std::vector<uint16_t> l1, l2;
     try {
@@ -357,8 +358,11 @@ dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, in
     if (G.t < 1 || G.t > G.T || G.h < 1 || G.h > G.H || G.w < 1 || G.w > G.W)
         return fail(DQ_ERR_SHAPE, "cube extents must satisfy 1 <= t <= T, 1 <= h <= H, 1 <= w <= W");
     const int64_t lim = int64_t(1) << 40;
+    // (products checked before they are formed: T, H, W reach 2^31 - 1)
+    if (!mul_ok(G.T, G.H, lim) || !mul_ok((int64_t)G.T * G.H, G.W, lim)) return fail(DQ_ERR_SHAPE, "token grid too large");
     int64_t N = (int64_t)G.T * G.H * G.W;
-    int Tc = (G.T + G.t - 1) / G.t, Hc = (G.H + G.h - 1) / G.h, Wc = (G.W + G.w - 1) / G.w;
+    int Tc = (int)(((int64_t)G.T + G.t - 1) / G.t), Hc = (int)(((int64_t)G.H + G.h - 1) / G.h),
+        Wc = (int)(((int64_t)G.W + G.w - 1) / G.w);
     int64_t K = (int64_t)Tc * Hc * Wc;
     int64_t S = (int64_t)G.t * G.h * G.w;
     if (N > (int64_t(1) << 31) || !mul_ok(K, S, lim)) return fail(DQ_ERR_SHAPE, "token grid too large");
