@@ -65,6 +65,9 @@ def parse():
                     help="channels per FP8 exponent of the cores (64: the pages' group size)")
     ap.add_argument("--core-bits", type=int, default=8, choices=(8, 4, 16),
                     help="MX-FP8 cores (the pages' choice), MX-FP4 or bf16 cores (the 4- and 16-bit points of their ablation)")
+    ap.add_argument("--orbit", action="store_true",
+                    help="the rotated-basis W4A4 layer (RPBH + Lloyd-Max codebook) on the config's shape")
+    ap.add_argument("--orbit-bits", type=int, default=4, choices=(2, 3, 4))
     ap.add_argument("--fp6", default="fp6_e2m3", choices=("fp6_e2m3", "fp6_e3m2"),
                     help="6-bit format of a text-token layer (--config kv_text_14b)")
     ap.add_argument("--copy-only-mib", type=int, default=0,
@@ -294,6 +297,59 @@ def bench_text(args, cfg, dq, torch):
     print(json.dumps(out), flush=True)
 
 
+def bench_orbit(args, cfg, dq, torch):
+    """The rotated-basis W4A4 layer (OrbitQuant notes: RPBH rotation,
+    Lloyd-Max codebook) on a video layer's shape: one JSON line.  A step is
+    dq_orbit_quantize_act (rotation, RMS, codes, decoded levels) followed by
+    dq_orbit_forward (the bf16 GEMM over the decoded levels, scaled by the
+    row scales), both timed with HIP events on the launch stream."""
+    import numpy as np
+    synth = synth_mod()
+    x = synth.make_activation(cfg.T, cfg.H, cfg.W, cfg.Ci, seed=cfg.x_seeds[0], dtype=cfg.dtype,
+                              n_outliers=cfg.n_outliers, device="cuda")
+    wt = synth.config_weight(cfg)
+    perm = np.random.default_rng(cfg.w_seed).permutation(cfg.Ci).astype(np.int32)
+    o = dq.dq_orbit_prepare(wt, perm, args.orbit_bits, args.orbit_bits)
+    act = dq.dq_orbit_act_create(o, cfg.N)
+    y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        dq.dq_orbit_linear(o, x, act, y, stream)
+    torch.cuda.synchronize()
+    start, end = ev(), ev()
+    marks = []
+    start.record(stream)
+    for _ in range(args.steps):
+        a, b, c = ev(), ev(), ev()
+        a.record(stream)
+        dq.dq_orbit_quantize_act(o, x, act, stream)
+        b.record(stream)
+        dq.dq_orbit_forward(o, act, y, stream)
+        c.record(stream)
+        marks.append((a, b, c))
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    q_ms = float(np.mean([a.elapsed_time(b) for a, b, c in marks]))
+    f_ms = float(np.mean([b.elapsed_time(c) for a, b, c in marks]))
+    N, Ci, Co = cfg.N, cfg.Ci, cfg.Co
+    flops = 2.0 * N * Ci * Co
+    qbytes = N * Ci * (2 if cfg.dtype == "bf16" else 4) + N * Ci * (0.5 + 2) + 4 * N
+    print(json.dumps({
+        "metric": "effective TOPS of the rotated-basis W4A4 layer (RPBH + Lloyd-Max codebook)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16 (decoded levels)",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: X {N}x{Ci} {cfg.dtype} -> Y {N}x{Co} fp32, W{args.orbit_bits}A{args.orbit_bits} "
+                               f"Lloyd-Max, blocks of 256", "tokens": N, "Ci": Ci, "Co": Co},
+        "rotation": {"ms": round(q_ms, 4), "algorithmic_bytes": int(qbytes), "GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": "bf16 GEMM over the decoded levels (dq_orbit_forward)", "bound": "mfma",
+                     "achieved": round(flops / (f_ms * 1e-3) / 1e12, 2), "peak": round(PEAK_BF16 / 1e12, 2),
+                     "unit": "TFLOP/s", "frac": round(flops / (f_ms * 1e-3) / PEAK_BF16, 4), "ms": round(f_ms, 4)},
+    }), flush=True)
+
+
 def synth_mod():
     from w4a4_quantized_linear_cube_amd import synth
     return synth
@@ -329,6 +385,9 @@ def main():
         bench_text(args, synth.TEXT_CONFIGS[args.config], dq, torch)
         return
     cfg = synth.CONFIGS[args.config]
+    if args.orbit:
+        bench_orbit(args, cfg, dq, torch)
+        return
     if args.sweep:
         sweep(args, cfg, dq, torch)
         return

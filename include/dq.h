@@ -245,6 +245,47 @@ dq_status dq_linear6(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_act
  * [N][Ci/32], U [N][rank] bf16 bits.  Synchronises `stream` first. */
 dq_status dq_act6_export(const dq_act6* a, uint8_t* codes_host, uint8_t* scales_host, uint16_t* u_host, void* stream);
 
+/* ---- rotated-basis W4A4 layers (OrbitQuant notes: 方法, 离线的权重量化, 在线的激活量化)
+ * Rows (tokens, and output channels of the weight) are rotated by a random
+ * permuted block Hadamard transform, x' = blockdiag(H_256 / 16) x[perm],
+ * divided by their RMS s = sqrt(sum x'^2 / Ci) (fp32; squares summed per
+ * 256-channel block in channel order, then over the blocks), and each
+ * coordinate is coded as its nearest level of the Lloyd-Max quantizer of
+ * N(0, 1) with 2^bits levels, each level rounded to bf16 (exact ties to the
+ * even index).  Weights are coded offline with the same permutation, so the
+ * rotation cancels: y[n][j] = (sum_c lvl(x'_nc) lvl(w'_jc)) s_x[n] s_w[j],
+ * the sum by bf16 MFMAs over the decoded levels with fp32 accumulation. */
+typedef struct dq_orbit dq_orbit;           /* rotated, coded weight on one device */
+typedef struct dq_orbit_act dq_orbit_act;   /* workspace for N tokens */
+
+/* w_host [Co][Ci] (W^T, dtype dt); perm_host [Ci] a permutation of
+ * 0 .. Ci - 1 (the caller draws it; DQ_ERR_INVALID_ARG otherwise);
+ * wbits, abits in {2, 3, 4} (codebooks of 4, 8 or 16 levels).  Requires
+ * Ci a multiple of 256 with Ci <= 15360 (one row in LDS), 1 <= Co <= 2^24.
+ * Synchronous; the handle owns its device buffers. */
+dq_status dq_orbit_prepare(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, const int32_t* perm_host,
+                           int32_t wbits, int32_t abits, int32_t device, dq_orbit** out);
+void dq_orbit_destroy(dq_orbit* o);
+/* Host copies (any pointer may be NULL): the bf16 levels of the weight and
+ * activation codebooks (2^wbits and 2^abits entries, ascending), the weight's
+ * level indices [Co][Ci/2] (two per byte, even channel in the low nibble) and
+ * row scales [Co]. */
+dq_status dq_orbit_export(const dq_orbit* o, uint16_t* wlev_host, uint16_t* alev_host, uint8_t* wcodes_host,
+                          float* wscale_host);
+/* Workspace for N tokens (1 <= N <= 2^31 - 256). */
+dq_status dq_orbit_act_create(const dq_orbit* o, int64_t N, dq_orbit_act** out);
+void dq_orbit_act_destroy(dq_orbit_act* a);
+/* Rotate, normalize and code x_dev [N][Ci] (dtype dt, 16-byte aligned).
+ * Asynchronous on `stream`. */
+dq_status dq_orbit_quantize_act(const dq_orbit* o, const void* x_dev, dq_dtype dt, dq_orbit_act* a, void* stream);
+/* y_dev [N][Co] fp32 (every element written) from the last
+ * dq_orbit_quantize_act.  Asynchronous on `stream`. */
+dq_status dq_orbit_forward(const dq_orbit* o, dq_orbit_act* a, float* y_dev, void* stream);
+dq_status dq_orbit_linear(const dq_orbit* o, const void* x_dev, dq_dtype dt, dq_orbit_act* a, float* y_dev, void* stream);
+/* Host copies: level indices [N][Ci/2] and row scales [N].  Synchronises
+ * `stream` first. */
+dq_status dq_orbit_act_export(const dq_orbit_act* a, uint8_t* codes_host, float* scale_host, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): dq_linear
  * for the geometry `geom` with MX-FP8 cores in groups of 32, without a

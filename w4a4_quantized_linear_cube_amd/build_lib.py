@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdq.so")
-SOURCES = ["api.cpp", "svd.cpp", "quant.hip", "gemm.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "svd.cpp", "quant.hip", "gemm.hip", "noalloc.hip", "orbit.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -228,5 +228,9 @@ constexpr int FWD_CORE = 1, FWD_DELTA = 2;   // parts of the forward pass
 hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, hipStream_t st);
 // y = U L2 + Q6(X) Q6(R) for a 6-bit layer
 hipError_t launch_forward6(const dq_weights* w, dq_act6* a, float* y, hipStream_t st);
+// y[n][j] = (sum_c wdec[j][c] xdec[n][c]) s_x[n] s_w[j] over bf16 operands in the off_bf16 layout
+hipError_t launch_orbit_gemm(const uint16_t* wdec, const uint16_t* xdec, int64_t Kp, int64_t Cop, int64_t Npad, int64_t Co,
+                             const int* rows, const float* xscale, const float* wscale, float* y, float* sink,
+                             hipStream_t st);
 
 }  // namespace dq

@@ -63,6 +63,8 @@ struct GemmArgs {
     const uint16_t* l2t;   // [Cop][rp]
     int rp;
     float* sink;        // 2 KB the token epilogue stores lanes without an output to (never read)
+    const float* xscale;   // general token epilogue: y = (acc x xscale[slot]) x wscale[channel] when set
+    const float* wscale;   //   (the rotated-basis layers' per-row scales), [Nslot_pad] and [Cop]
 };
 
 constexpr int EPI_STORE = 0;      // plain fp32 stores c[b row][a row]
@@ -600,9 +602,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const v16f& a = acc[mi][ni];
-                    const float4 o = make_float4(a[4 * j] + bv[mi][j].x, a[4 * j + 1] + bv[mi][j].y,
-                                                 a[4 * j + 2] + bv[mi][j].z, a[4 * j + 3] + bv[mi][j].w);
+                    float4 o = make_float4(a[4 * j] + bv[mi][j].x, a[4 * j + 1] + bv[mi][j].y,
+                                           a[4 * j + 2] + bv[mi][j].z, a[4 * j + 3] + bv[mi][j].w);
                     const int ch = ch0 + 32 * mi + 8 * j;
+                    if (p.xscale) {                         // (acc s_x) s_w, each product rounded
+                        const float sx = p.xscale[slot];
+                        const float4 sw = *(const float4*)(p.wscale + ch);
+                        o = make_float4((o.x * sx) * sw.x, (o.y * sx) * sw.y, (o.z * sx) * sw.z, (o.w * sx) * sw.w);
+                    }
                     if (p.vec4 && ch + 4 <= p.Co) {
                         __builtin_nontemporal_store(__builtin_bit_cast(v4f, o), (v4f*)(yrow + ch));
                     } else {
@@ -851,6 +858,32 @@ hipError_t launch_forward6(const dq_weights* w, dq_act6* a, float* y, hipStream_
     if (w->wfmt == FMT_BF6)
         return fast ? launch<FMT_BF6, EPI_TOKENS_Q, FMT_BF6>(d, st) : launch<FMT_BF6, EPI_TOKENS, FMT_BF6>(d, st);
     return fast ? launch<FMT_FP6, EPI_TOKENS_Q, FMT_FP6>(d, st) : launch<FMT_FP6, EPI_TOKENS, FMT_FP6>(d, st);
+}
+
+// The rotated-basis (OrbitQuant-style) layers: the decoded Lloyd-Max levels
+// as bf16 operands, y = (acc s_x[token]) s_w[channel] in the token epilogue.
+hipError_t launch_orbit_gemm(const uint16_t* wdec, const uint16_t* xdec, int64_t Kp, int64_t Cop, int64_t Npad, int64_t Co,
+                             const int* rows, const float* xscale, const float* wscale, float* y, float* sink,
+                             hipStream_t st) {
+    GemmArgs d{};
+    d.a = (const uint8_t*)wdec;
+    d.b = (const uint8_t*)xdec;
+    d.nks = (int)(Kp / 32);
+    d.mtiles = (int)(Cop / 256);
+    d.ntiles = (int)(Npad / 256);
+    d.y = y;
+    d.Co = (int)Co;
+    d.vec4 = (Co % 4 == 0) && ((uintptr_t)y % 16 == 0);
+    d.stok = rows;
+    d.S = 1;
+    d.S2 = 1;
+    d.split = (int)Npad;
+    d.kmax = 0;
+    d.rp = 0;
+    d.sink = sink;
+    d.xscale = xscale;
+    d.wscale = wscale;
+    return launch<FMT_BF16, EPI_TOKENS, FMT_BF16>(d, st);
 }
 
 }  // namespace dq

@@ -1,0 +1,425 @@
+// Rotated-basis W4A4 layers in the manner of the OrbitQuant notes (方法:
+// 核心思路, 离线的权重量化, 在线的激活量化): a random permuted block Hadamard
+// rotation (RPBH) maps every row onto a normalized basis in which its
+// coordinates are close to N(0, 1); each coordinate is coded as its nearest
+// level of one fixed Lloyd-Max codebook of N(0, 1).  Weights are rotated and
+// coded offline, row by row; activations per call, token by token; the
+// rotation cancels in the product, y = x W^T.
+//
+// Conventions of this implementation (the notes fix none of them):
+//   * rotation: x' = blockdiag(H_256 / 16) x[perm], the permutation given by
+//     the caller; the Walsh-Hadamard transform as the radix-2 butterfly
+//     network in fp32 (stages h = 1, 2, .., 128), then the exact 1/16;
+//   * normalization: s = sqrt(sum x'^2 / Ci) in fp32 (squares summed per
+//     256-channel block in channel order, then over blocks in order); the
+//     coordinates coded are fl32(x' / s) (0 when s = 0);
+//   * codebook: the Lloyd-Max quantizer of N(0, 1) with 2^bits levels, each
+//     level rounded to bf16 (the operand type of the matrix cores, since a
+//     Lloyd-Max level set is no float format); nearest level, exact ties to
+//     the even index;
+//   * y[n][j] = fl32(fl32(acc s_x[n]) s_w[j]), acc the bf16 MFMA contraction
+//     of the decoded levels (fp32 accumulation).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dq.h"
+#include "dq_device.h"
+#include "dq_internal.h"
+
+struct dq_orbit {
+    int device = 0;
+    int64_t Ci = 0, Co = 0, Kp = 0, Cop = 0;
+    int wbits = 4, abits = 4;
+    uint16_t wlev[16] = {}, alev[16] = {};   // bf16 codebooks (ascending)
+    int* perm = nullptr;       // [Ci] device
+    uint16_t* wdec = nullptr;  // Cop x Kp bf16 decoded weight levels, off_bf16 layout
+    uint8_t* wcodes = nullptr; // [Cop][Kp/2] level indices, two per byte
+    float* wscale = nullptr;   // [Cop] row scales (0 past Co)
+    size_t bytes = 0;
+};
+
+struct dq_orbit_act {
+    int device = 0;
+    int64_t N = 0, N_pad = 0, Ci = 0, Kp = 0;
+    uint16_t* xdec = nullptr;  // N_pad x Kp bf16 decoded activation levels, off_bf16 layout
+    uint8_t* xcodes = nullptr; // [N_pad][Kp/2]
+    float* xscale = nullptr;   // [N_pad]
+    int* rows = nullptr;       // [N_pad] identity, -1 past N
+    float* sink = nullptr;     // [512]
+    size_t bytes = 0;
+};
+
+namespace dq {
+namespace {
+
+constexpr int OBLOCK = 256;       // Hadamard block
+constexpr int MAX_CI = 15360;     // one row of fp32 in LDS (60 KB, under the 64 KB of dynamic LDS)
+
+// Lloyd-Max quantizer of N(0, 1) with L levels, ascending: the fixed point of
+// boundaries at the midpoints of neighbouring levels and levels at the
+// conditional means of their cells, E[X | a < X <= b] =
+// (pdf(a) - pdf(b)) / (cdf(b) - cdf(a)), iterated from evenly spaced points.
+void lloyd_max(int L, double* y) {
+    const double rt2pi = std::sqrt(2.0 * M_PI);
+    auto pdf = [&](double t) { return std::isinf(t) ? 0.0 : std::exp(-0.5 * t * t) / rt2pi; };
+    auto cdf = [&](double t) { return std::isinf(t) ? (t > 0 ? 1.0 : 0.0) : 0.5 * std::erfc(-t / std::sqrt(2.0)); };
+    for (int i = 0; i < L; ++i) y[i] = -2.5 + 5.0 * (i + 0.5) / L;
+    std::vector<double> t(L + 1);
+    for (int it = 0; it < 100000; ++it) {
+        t[0] = -INFINITY;
+        t[L] = INFINITY;
+        for (int i = 1; i < L; ++i) t[i] = 0.5 * (y[i - 1] + y[i]);
+        double moved = 0.0;
+        for (int i = 0; i < L; ++i) {
+            const double v = (pdf(t[i]) - pdf(t[i + 1])) / (cdf(t[i + 1]) - cdf(t[i]));
+            moved = std::max(moved, std::fabs(v - y[i]));
+            y[i] = v;
+        }
+        if (moved <= 1e-15) break;
+    }
+}
+
+// double -> bf16 bits, round to nearest even (one rounding to 8 significant bits)
+uint16_t bf16_of(double v) {
+    int k;
+    const double m = std::frexp(v, &k);
+    const double r = std::ldexp(std::rint(std::ldexp(m, 8)), k - 8);
+    const float f = (float)r;
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+void codebook(int bits, uint16_t* lev) {
+    double y[16];
+    lloyd_max(1 << bits, y);
+    for (int i = 0; i < (1 << bits); ++i) lev[i] = bf16_of(y[i]);
+}
+
+float bf16_value(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+struct RowsArgs {
+    const void* x;
+    int x_bf16;
+    int Ci, Kp, nlev;
+    const int* perm;
+    float mids[16];          // midpoints of neighbouring levels (exact in fp32)
+    uint16_t lev[16];        // bf16 levels
+    uint8_t* codes;          // [rows_pad][Kp/2]
+    float* scale;            // [rows_pad]
+    uint16_t* dec;           // off_bf16 layout
+};
+
+// One workgroup per row: gather by the permutation into LDS, butterflies,
+// the row's RMS, then codes and decoded levels (8 channels per thread and
+// pass: one 4-byte code store and one 16-byte level store).
+__global__ __launch_bounds__(256) void k_orbit_rows(RowsArgs a) {
+    extern __shared__ float s[];
+    __shared__ float part[MAX_CI / OBLOCK];
+    __shared__ float srow;
+    const long long r = blockIdx.x;
+    const int t = threadIdx.x, Ci = a.Ci;
+    if (a.x_bf16) {
+        const uint16_t* x = (const uint16_t*)a.x + r * Ci;
+        for (int c = t; c < Ci; c += 256) s[c] = bf16_to_f32(x[a.perm[c]]);
+    } else {
+        const float* x = (const float*)a.x + r * Ci;
+        for (int c = t; c < Ci; c += 256) s[c] = x[a.perm[c]];
+    }
+    __syncthreads();
+    for (int h = 1; h < OBLOCK; h <<= 1) {
+        for (int q = t; q < Ci / 2; q += 256) {
+            const int i = (q >> 7) * OBLOCK + (q & 127) / h * 2 * h + (q & 127) % h;
+            const float u = s[i], v = s[i + h];
+            s[i] = u + v;
+            s[i + h] = u - v;
+        }
+        __syncthreads();
+    }
+    for (int c = t; c < Ci; c += 256) s[c] = s[c] * 0.0625f;
+    __syncthreads();
+    const int nb = Ci / OBLOCK;
+    if (t < nb) {
+        float p = s[OBLOCK * t] * s[OBLOCK * t];
+        for (int i = 1; i < OBLOCK; ++i) {
+            const float v = s[OBLOCK * t + i];
+            p = p + v * v;
+        }
+        part[t] = p;
+    }
+    __syncthreads();
+    if (t == 0) {
+        float tot = part[0];
+        for (int j = 1; j < nb; ++j) tot = tot + part[j];
+        srow = sqrtf(__fdiv_rn(tot, (float)Ci));          // correctly rounded (llvm.sqrt.f32), unlike __fsqrt_rn here
+        a.scale[r] = srow;
+    }
+    __syncthreads();
+    const float sr = srow;
+    for (int c0 = 8 * t; c0 < Ci; c0 += 2048) {
+        uint32_t nib = 0;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = sr > 0.0f ? __fdiv_rn(s[c0 + e], sr) : 0.0f;
+            int idx = 0;
+            for (int m = 0; m < a.nlev - 1; ++m) idx += v > a.mids[m] ? 1 : 0;   // midpoints strictly below v
+            if (idx < a.nlev - 1 && v == a.mids[idx] && (idx & 1)) ++idx;        // exact tie: the even index
+            nib |= (uint32_t)idx << (4 * e);
+            if (e & 1) w[e >> 1] |= (uint32_t)a.lev[idx] << 16;
+            else w[e >> 1] = a.lev[idx];
+        }
+        *(uint32_t*)(a.codes + r * (a.Kp / 2) + c0 / 2) = nib;
+        *(uint4*)((uint8_t*)a.dec + off_bf16(r, c0, a.Kp / 32)) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+hipError_t launch_rows(const void* x, int x_bf16, int64_t rows, int Ci, int Kp, const int* perm, const uint16_t* lev,
+                       int nlev, uint8_t* codes, float* scale, uint16_t* dec, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    RowsArgs a{};
+    a.x = x;
+    a.x_bf16 = x_bf16;
+    a.Ci = Ci;
+    a.Kp = Kp;
+    a.nlev = nlev;
+    a.perm = perm;
+    for (int i = 0; i < nlev; ++i) a.lev[i] = lev[i];
+    for (int i = 0; i + 1 < nlev; ++i) a.mids[i] = 0.5f * (bf16_value(lev[i]) + bf16_value(lev[i + 1]));
+    a.codes = codes;
+    a.scale = scale;
+    a.dec = dec;
+    k_orbit_rows<<<(unsigned)rows, 256, (size_t)Ci * 4, st>>>(a);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t zalloc(T** p, size_t count, size_t* total) {
+    *p = nullptr;
+    if (count == 0) return hipSuccess;
+    hipError_t e = hipMalloc((void**)p, count * sizeof(T));
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return e;
+    }
+    *total += count * sizeof(T);
+    return hipMemset(*p, 0, count * sizeof(T));
+}
+
+void free_orbit(dq_orbit* o) {
+    if (!o) return;
+    DeviceGuard dg(o->device);
+    (void)hipFree(o->perm);
+    (void)hipFree(o->wdec);
+    (void)hipFree(o->wcodes);
+    (void)hipFree(o->wscale);
+    delete o;
+}
+
+void free_orbit_act(dq_orbit_act* a) {
+    if (!a) return;
+    DeviceGuard dg(a->device);
+    (void)hipFree(a->xdec);
+    (void)hipFree(a->xcodes);
+    (void)hipFree(a->xscale);
+    (void)hipFree(a->rows);
+    (void)hipFree(a->sink);
+    delete a;
+}
+
+}  // namespace
+}  // namespace dq
+
+using namespace dq;
+
+extern "C" {
+
+dq_status dq_orbit_prepare(const void* w_host, dq_dtype dt, int64_t Ci, int64_t Co, const int32_t* perm_host,
+                           int32_t wbits, int32_t abits, int32_t device, dq_orbit** out) {
+    set_error("");
+    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w_host || !perm_host) return fail(DQ_ERR_INVALID_ARG, "w_host or perm_host is NULL");
+    if (dt != DQ_F32 && dt != DQ_BF16) return fail(DQ_ERR_INVALID_ARG, "unknown dtype");
+    if (Ci < OBLOCK || Ci % OBLOCK != 0 || Ci > MAX_CI) return fail(DQ_ERR_SHAPE, "Ci must be a multiple of 256, at most 15360");
+    if (Co < 1 || Co > (1 << 24)) return fail(DQ_ERR_SHAPE, "Co must be in [1, 2^24]");
+    if (wbits < 2 || wbits > 4 || abits < 2 || abits > 4) return fail(DQ_ERR_INVALID_ARG, "wbits and abits must be 2, 3 or 4");
+    {   // a permutation of 0 .. Ci - 1 (the kernels index rows with it)
+        std::vector<char> seen((size_t)Ci, 0);
+        for (int64_t c = 0; c < Ci; ++c) {
+            const int32_t v = perm_host[c];
+            if (v < 0 || v >= Ci || seen[(size_t)v]) return fail(DQ_ERR_INVALID_ARG, "perm is not a permutation of 0 .. Ci - 1");
+            seen[(size_t)v] = 1;
+        }
+    }
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return fail(DQ_ERR_DEVICE, "no HIP device available");
+    if (device < 0 || device >= n) return fail(DQ_ERR_INVALID_ARG, "device index out of range");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return fail(DQ_ERR_DEVICE, "hipGetDeviceProperties failed");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return fail(DQ_ERR_UNSUPPORTED, "gfx950 required");
+    DeviceGuard dg(device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    auto* o = new (std::nothrow) dq_orbit();
+    if (!o) return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    std::unique_ptr<dq_orbit, void (*)(dq_orbit*)> guard(o, free_orbit);
+    o->device = device;
+    o->Ci = Ci;
+    o->Co = Co;
+    o->Kp = round_up(Ci, KPAD);
+    o->Cop = round_up(Co, NPAD);
+    o->wbits = wbits;
+    o->abits = abits;
+    codebook(wbits, o->wlev);
+    codebook(abits, o->alev);
+    const size_t esz = dt == DQ_BF16 ? 2 : 4;
+    void* wd = nullptr;
+    hipError_t e;
+    if ((e = zalloc(&o->perm, (size_t)Ci, &o->bytes)) != hipSuccess ||
+        (e = zalloc(&o->wdec, (size_t)(o->Cop * o->Kp), &o->bytes)) != hipSuccess ||
+        (e = zalloc(&o->wcodes, (size_t)(o->Cop * o->Kp / 2), &o->bytes)) != hipSuccess ||
+        (e = zalloc(&o->wscale, (size_t)o->Cop, &o->bytes)) != hipSuccess)
+        return hip_fail(e, "hipMalloc weight");
+    if ((e = hipMemcpy(o->perm, perm_host, (size_t)Ci * 4, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "copy perm");
+    if ((e = hipMalloc(&wd, (size_t)(Ci * Co) * esz)) != hipSuccess) return hip_fail(e, "hipMalloc W");
+    if ((e = hipMemcpy(wd, w_host, (size_t)(Ci * Co) * esz, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = launch_rows(wd, dt == DQ_BF16, Co, (int)Ci, (int)o->Kp, o->perm, o->wlev, 1 << wbits, o->wcodes, o->wscale,
+                         o->wdec, nullptr)) != hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess) {
+        (void)hipFree(wd);
+        return hip_fail(e, "weight rotation");
+    }
+    (void)hipFree(wd);
+    *out = guard.release();
+    return DQ_OK;
+}
+
+void dq_orbit_destroy(dq_orbit* o) { free_orbit(o); }
+
+dq_status dq_orbit_export(const dq_orbit* o, uint16_t* wlev_host, uint16_t* alev_host, uint8_t* wcodes_host,
+                          float* wscale_host) {
+    set_error("");
+    if (!o) return fail(DQ_ERR_INVALID_ARG, "weight handle is NULL");
+    if (wlev_host) std::memcpy(wlev_host, o->wlev, (size_t)(2 << o->wbits));
+    if (alev_host) std::memcpy(alev_host, o->alev, (size_t)(2 << o->abits));
+    DeviceGuard dg(o->device);
+    hipError_t e;
+    if (wcodes_host) {
+        std::vector<uint8_t> buf((size_t)(o->Cop * o->Kp / 2));
+        if ((e = hipMemcpy(buf.data(), o->wcodes, buf.size(), hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "copy codes");
+        for (int64_t j = 0; j < o->Co; ++j) std::memcpy(wcodes_host + j * (o->Ci / 2), &buf[(size_t)(j * (o->Kp / 2))], (size_t)(o->Ci / 2));
+    }
+    if (wscale_host && (e = hipMemcpy(wscale_host, o->wscale, (size_t)o->Co * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_fail(e, "copy scales");
+    return DQ_OK;
+}
+
+dq_status dq_orbit_act_create(const dq_orbit* o, int64_t N, dq_orbit_act** out) {
+    set_error("");
+    if (!out) return fail(DQ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!o) return fail(DQ_ERR_INVALID_ARG, "weight handle is NULL");
+    if (N < 1 || N > (int64_t(1) << 31) - MPAD) return fail(DQ_ERR_SHAPE, "N must be in [1, 2^31 - 256]");
+    if (N * o->Co >= (int64_t(1) << 40)) return fail(DQ_ERR_SHAPE, "workspace too large");
+    DeviceGuard dg(o->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    auto* a = new (std::nothrow) dq_orbit_act();
+    if (!a) return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    std::unique_ptr<dq_orbit_act, void (*)(dq_orbit_act*)> guard(a, free_orbit_act);
+    a->device = o->device;
+    a->N = N;
+    a->N_pad = round_up(N, MPAD);
+    a->Ci = o->Ci;
+    a->Kp = o->Kp;
+    hipError_t e;
+    if ((e = zalloc(&a->xdec, (size_t)(a->N_pad * a->Kp), &a->bytes)) != hipSuccess ||
+        (e = zalloc(&a->xcodes, (size_t)(a->N_pad * a->Kp / 2), &a->bytes)) != hipSuccess ||
+        (e = zalloc(&a->xscale, (size_t)a->N_pad, &a->bytes)) != hipSuccess ||
+        (e = zalloc(&a->rows, (size_t)a->N_pad, &a->bytes)) != hipSuccess ||
+        (e = zalloc(&a->sink, (size_t)512, &a->bytes)) != hipSuccess)
+        return hip_fail(e, "hipMalloc workspace");
+    const Geom g{1, 1, (int)N, 1, 1, 1, 1, 1, (int)N, 1, (long long)N, (long long)N, (long long)N};
+    if ((e = launch_slot_tokens(g, 0, a->rows, a->N_pad, nullptr)) != hipSuccess) return hip_fail(e, "row table");
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "workspace init");
+    *out = guard.release();
+    return DQ_OK;
+}
+
+void dq_orbit_act_destroy(dq_orbit_act* a) { free_orbit_act(a); }
+
+static dq_status orbit_pair(const dq_orbit* o, const dq_orbit_act* a) {
+    if (!o) return fail(DQ_ERR_INVALID_ARG, "weight handle is NULL");
+    if (!a) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    if (a->Ci != o->Ci || a->device != o->device) return fail(DQ_ERR_INVALID_ARG, "workspace was created for a different weight");
+    return DQ_OK;
+}
+
+dq_status dq_orbit_quantize_act(const dq_orbit* o, const void* x_dev, dq_dtype dt, dq_orbit_act* a, void* stream) {
+    set_error("");
+    dq_status st = orbit_pair(o, a);
+    if (st != DQ_OK) return st;
+    if (!x_dev) return fail(DQ_ERR_INVALID_ARG, "x_dev is NULL");
+    if (((uintptr_t)x_dev) % 16 != 0) return fail(DQ_ERR_INVALID_ARG, "x_dev must be 16-byte aligned");
+    if (dt != DQ_F32 && dt != DQ_BF16) return fail(DQ_ERR_INVALID_ARG, "unknown dtype");
+    DeviceGuard dg(a->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = launch_rows(x_dev, dt == DQ_BF16, a->N, (int)a->Ci, (int)a->Kp, o->perm, o->alev, 1 << o->abits,
+                               a->xcodes, a->xscale, a->xdec, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "rotation launch");
+    return DQ_OK;
+}
+
+dq_status dq_orbit_forward(const dq_orbit* o, dq_orbit_act* a, float* y_dev, void* stream) {
+    set_error("");
+    dq_status st = orbit_pair(o, a);
+    if (st != DQ_OK) return st;
+    if (!y_dev) return fail(DQ_ERR_INVALID_ARG, "y_dev is NULL");
+    if (((uintptr_t)y_dev) % 4 != 0) return fail(DQ_ERR_INVALID_ARG, "y_dev must be 4-byte aligned");
+    DeviceGuard dg(a->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = launch_orbit_gemm(o->wdec, a->xdec, o->Kp, o->Cop, a->N_pad, o->Co, a->rows, a->xscale, o->wscale, y_dev,
+                                     a->sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+    return DQ_OK;
+}
+
+dq_status dq_orbit_linear(const dq_orbit* o, const void* x_dev, dq_dtype dt, dq_orbit_act* a, float* y_dev, void* stream) {
+    dq_status st = dq_orbit_quantize_act(o, x_dev, dt, a, stream);
+    if (st != DQ_OK) return st;
+    return dq_orbit_forward(o, a, y_dev, stream);
+}
+
+dq_status dq_orbit_act_export(const dq_orbit_act* a, uint8_t* codes_host, float* scale_host, void* stream) {
+    set_error("");
+    if (!a) return fail(DQ_ERR_INVALID_ARG, "workspace handle is NULL");
+    DeviceGuard dg(a->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    try {
+        if (codes_host) {
+            std::vector<uint8_t> buf((size_t)(a->N_pad * a->Kp / 2));
+            if ((e = hipMemcpy(buf.data(), a->xcodes, buf.size(), hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "copy codes");
+            for (int64_t n = 0; n < a->N; ++n) std::memcpy(codes_host + n * (a->Ci / 2), &buf[(size_t)(n * (a->Kp / 2))], (size_t)(a->Ci / 2));
+        }
+        if (scale_host && (e = hipMemcpy(scale_host, a->xscale, (size_t)a->N * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+            return hip_fail(e, "copy scales");
+    } catch (const std::bad_alloc&) {
+        return fail(DQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    return DQ_OK;
+}
+
+}  // extern "C"

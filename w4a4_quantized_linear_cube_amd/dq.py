@@ -27,7 +27,9 @@ EXPORTS = ("dq_last_error", "dq_status_str", "dq_lowrank_factors", "dq_prepare_w
            "dq_qact_create", "dq_qact_create_ex", "dq_qact_destroy", "dq_qact_info", "dq_quantize_act", "dq_linear_forward",
            "dq_core_term", "dq_delta_term", "dq_linear", "dq_qact_export", "dq_linear_noalloc",
            "dq_prepare_weights_w6", "dq_act6_create", "dq_act6_destroy", "dq_quantize_act6", "dq_linear6_forward",
-           "dq_linear6", "dq_act6_export")
+           "dq_linear6", "dq_act6_export", "dq_orbit_prepare", "dq_orbit_destroy", "dq_orbit_export",
+           "dq_orbit_act_create", "dq_orbit_act_destroy", "dq_orbit_quantize_act", "dq_orbit_forward", "dq_orbit_linear",
+           "dq_orbit_act_export")
 DQ_FP6_E2M3, DQ_FP6_E3M2 = 2, 3
 FP6_FORMATS = {"fp6_e2m3": DQ_FP6_E2M3, "fp6_e3m2": DQ_FP6_E3M2}
 
@@ -84,6 +86,15 @@ def load():
         "dq_linear6_forward": ([P, P, P, P], ctypes.c_int),
         "dq_linear6": ([P, P, ctypes.c_int, P, P, P], ctypes.c_int),
         "dq_act6_export": ([P, P, P, P, P], ctypes.c_int),
+        "dq_orbit_prepare": ([P, ctypes.c_int, I64, I64, P, I32, I32, I32, PP], ctypes.c_int),
+        "dq_orbit_destroy": ([P], None),
+        "dq_orbit_export": ([P, P, P, P, P], ctypes.c_int),
+        "dq_orbit_act_create": ([P, I64, PP], ctypes.c_int),
+        "dq_orbit_act_destroy": ([P], None),
+        "dq_orbit_quantize_act": ([P, P, ctypes.c_int, P, P], ctypes.c_int),
+        "dq_orbit_forward": ([P, P, P, P], ctypes.c_int),
+        "dq_orbit_linear": ([P, P, ctypes.c_int, P, P, P], ctypes.c_int),
+        "dq_orbit_act_export": ([P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -397,4 +408,84 @@ def dq_act6_export(a: Act6, stream=None) -> dict:
                U=np.zeros((N, r), np.uint16))
     _check(load().dq_act6_export(a.handle, _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["U"]), _stream(stream)),
            "dq_act6_export")
+    return out
+
+
+# -------------------------------------------------------- rotated-basis layers ----
+class Orbit:
+    """Owns a dq_orbit handle (a rotated, Lloyd-Max-coded weight)."""
+
+    def __init__(self, handle, Ci, Co, wbits, abits, device):
+        self.handle, self.Ci, self.Co, self.wbits, self.abits, self.device = handle, Ci, Co, wbits, abits, device
+        self.rank = 0
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.dq_orbit_destroy(self.handle)
+            self.handle = None
+
+
+class OrbitAct:
+    """Owns a dq_orbit_act handle (keeps its weight alive)."""
+
+    def __init__(self, handle, weights: Orbit, N: int):
+        self.handle, self.weights, self.N = handle, weights, N
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.dq_orbit_act_destroy(self.handle)
+            self.handle = None
+
+
+def dq_orbit_prepare(w, perm, wbits: int = 4, abits: int = 4, device: int = 0) -> Orbit:
+    f = "dq_orbit_prepare"
+    wt, dt = _host_weight(w)
+    Co, Ci = wt.shape
+    p = np.ascontiguousarray(np.asarray(perm), dtype=np.int32)
+    if p.shape != (Ci,):
+        _invalid(f, f"perm has shape {p.shape}; expected ({Ci},)")
+    h = ctypes.c_void_p()
+    _check(load().dq_orbit_prepare(_ptr(wt), dt, Ci, Co, _ptr(p), wbits, abits, device, ctypes.byref(h)), f)
+    return Orbit(h, Ci, Co, wbits, abits, device)
+
+
+def dq_orbit_export(o: Orbit) -> dict:
+    out = dict(wlev=np.zeros(1 << o.wbits, np.uint16), alev=np.zeros(1 << o.abits, np.uint16),
+               wcodes=np.zeros((o.Co, o.Ci // 2), np.uint8), wscale=np.zeros(o.Co, np.float32))
+    _check(load().dq_orbit_export(o.handle, _ptr(out["wlev"]), _ptr(out["alev"]), _ptr(out["wcodes"]),
+                                  _ptr(out["wscale"])), "dq_orbit_export")
+    return out
+
+
+def dq_orbit_act_create(o: Orbit, N: int) -> OrbitAct:
+    h = ctypes.c_void_p()
+    _check(load().dq_orbit_act_create(o.handle, N, ctypes.byref(h)), "dq_orbit_act_create")
+    return OrbitAct(h, o, N)
+
+
+def dq_orbit_quantize_act(o: Orbit, x, a: OrbitAct, stream=None):
+    _check_pair("dq_orbit_quantize_act", o, a)
+    _check_x("dq_orbit_quantize_act", o, a, x)
+    _check(load().dq_orbit_quantize_act(o.handle, _ptr(x), _dtype_of(x), a.handle, _stream(stream)),
+           "dq_orbit_quantize_act")
+
+
+def dq_orbit_forward(o: Orbit, a: OrbitAct, y, stream=None):
+    _check_pair("dq_orbit_forward", o, a)
+    _check_y("dq_orbit_forward", o, a, y)
+    _check(load().dq_orbit_forward(o.handle, a.handle, _ptr(y), _stream(stream)), "dq_orbit_forward")
+
+
+def dq_orbit_linear(o: Orbit, x, a: OrbitAct, y, stream=None):
+    _check_pair("dq_orbit_linear", o, a)
+    _check_x("dq_orbit_linear", o, a, x)
+    _check_y("dq_orbit_linear", o, a, y)
+    _check(load().dq_orbit_linear(o.handle, _ptr(x), _dtype_of(x), a.handle, _ptr(y), _stream(stream)),
+           "dq_orbit_linear")
+
+
+def dq_orbit_act_export(a: OrbitAct, stream=None) -> dict:
+    out = dict(codes=np.zeros((a.N, a.weights.Ci // 2), np.uint8), scale=np.zeros(a.N, np.float32))
+    _check(load().dq_orbit_act_export(a.handle, _ptr(out["codes"]), _ptr(out["scale"]), _stream(stream)),
+           "dq_orbit_act_export")
     return out
