@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--orbit-bits", type=int, default=4, choices=(2, 3, 4))
     ap.add_argument("--fp6", default="fp6_e2m3", choices=("fp6_e2m3", "fp6_e3m2"),
                     help="6-bit format of a text-token layer (--config kv_text_14b)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only measure plain streams of the activation pass's read/write mix and a device copy")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run 3 plain device-to-device copies of this size and exit (counter calibration)")
     return ap.parse_args()
@@ -365,6 +367,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.stream_probe:
+        stream_probe(args, torch)
+        return
     if args.copy_only_mib:
         nbytes = args.copy_only_mib << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
@@ -515,6 +520,43 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def stream_probe(args, torch):
+    """The attainable HBM rate for the activation pass's traffic mix: a
+    plain elementwise kernel that reads the whole of a layer's X and writes
+    half of its bytes (the pass reads X once and writes its codes, scales
+    and U, about 0.4 of X's bytes), next to a plain device copy.  One JSON
+    line."""
+    from w4a4_quantized_linear_cube_amd import synth
+    cfg = synth.CONFIGS[args.config]
+    x = synth.make_activation(cfg.T, cfg.H, cfg.W, cfg.Ci, seed=cfg.x_seeds[0], dtype=cfg.dtype,
+                              n_outliers=cfg.n_outliers, device="cuda")
+    xi = x.view(torch.int32)                       # 2-byte or 4-byte elements alike
+    half = xi.shape[1] // 2
+    a, b = xi[:, :half], xi[:, half:2 * half]
+    out = torch.empty(xi.shape[0], half, dtype=torch.int32, device=x.device)
+    dst = torch.empty_like(x)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, nbytes, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s0, s1 = ev(), ev()
+        s0.record()
+        for _ in range(reps):
+            fn()
+        s1.record()
+        torch.cuda.synchronize()
+        return nbytes * reps / (s0.elapsed_time(s1) * 1e-3) / 1e9
+
+    xb = x.numel() * x.element_size()
+    mix = rate(lambda: torch.bitwise_xor(a, b, out=out), xb + out.numel() * 4)
+    copy = rate(lambda: dst.copy_(x), 2 * xb)
+    print(json.dumps({"probe": "stream", "config": cfg.name, "read_bytes": xb, "write_bytes": out.numel() * 4,
+                      "mix_GBps": round(mix, 1), "copy_GBps": round(copy, 1),
+                      "mix_pct_hbm": round(100 * mix / (PEAK_HBM / 1e9), 2)}), flush=True)
 
 
 def committed_traffic(config, cube):

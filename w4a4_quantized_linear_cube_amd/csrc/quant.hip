@@ -600,7 +600,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                         }
                     }
                     for (; r < re; ++r) s0 += __uint_as_float(raw1(r) | (((pres >> r) & 1) ? 0u : 0x80000000u));
-                    if ((cnt & (cnt - 1)) == 0) s0 *= 1.0f / (float)cnt;   // exact power-of-two scaling
+                    if ((cnt & (cnt - 1)) == 0) s0 *= inv_pow2(cnt);   // exact power-of-two scaling
                     else s0 = __fdiv_rn(s0, (float)cnt);
                     float amax = row16_max(fabsf(s0));
                     amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, amax), 0x401F)));   // lane ^ 16
@@ -675,7 +675,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                         s1 += v.y;
                     }
                     if ((cnt & (cnt - 1)) == 0) {                  // exact power-of-two scaling
-                        const float rc = 1.0f / (float)cnt;
+                        const float rc = inv_pow2(cnt);
                         s0 *= rc;
                         s1 *= rc;
                     } else {
@@ -834,7 +834,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 }
                 const int cnt = md.w;
                 if ((cnt & (cnt - 1)) == 0) {                  // exact power-of-two scaling
-                    const float rc = 1.0f / (float)cnt;
+                    const float rc = inv_pow2(cnt);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) core[e] *= rc;
                 } else {
@@ -996,7 +996,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     s1 += v.y;
                 }
                 if ((cnt & (cnt - 1)) == 0) {              // exact power-of-two scaling
-                    const float rc = 1.0f / (float)cnt;
+                    const float rc = inv_pow2(cnt);
                     s0 *= rc;
                     s1 *= rc;
                 } else {
@@ -1103,7 +1103,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 }
                 const int cnt = meta_s[qgrp][mb][cr].w;
                 if ((cnt & (cnt - 1)) == 0) {                  // exact power-of-two scaling
-                    const float rc = 1.0f / (float)cnt;
+                    const float rc = inv_pow2(cnt);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) core[q] *= rc;
                 } else {

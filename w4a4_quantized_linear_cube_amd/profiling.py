@@ -12,6 +12,10 @@
         SQ_INSTS_VALU_MFMA_MOPS_{F6F4,F8,BF16}, SQ_VALU_MFMA_BUSY_CYCLES and
         GRBM_GUI_ACTIVE per dispatch of each kernel -> MFMA flops executed and
         MFMA utilisation (busy cycles per SIMD / active cycles per XCD)
+    python -m w4a4_quantized_linear_cube_amd.profiling issue RUN OUT.md --elements E --cmd "..." [--probe F]
+        SQ_WAVES, SQ_INSTS_{VALU,SALU,LDS} and GRBM_GUI_ACTIVE per dispatch
+        -> instructions per wave, VALU issue share, VALU lane-instructions
+        per activation element (E = N x Ci); F: a --stream-probe line
 
 The counter JSON records the SHA-256 of gemm.hip; bench.py reports its
 traffic only while the kernel source is unchanged.
@@ -161,6 +165,40 @@ def summarize_mfma(run: str, out: str, cmd: str) -> None:
     print("\n".join(lines))
 
 
+def summarize_issue(run: str, out: str, cmd: str, elements: int, probe: str = "") -> None:
+    """Instruction issue per kernel: SQ_INSTS_{VALU,SALU,LDS} per dispatch
+    and per wave, and the share of the average SIMD's cycles its VALU is
+    issuing (a wave64 VALU instruction holds a 16-lane SIMD for 4 cycles)."""
+    lines = ["# Instruction issue: " + os.path.splitext(os.path.basename(out))[0], "",
+             "Command (from the repository root on the GPU box):", "", "```", cmd, "```", "",
+             "Per dispatch, averaged over the dispatches of each kernel.  VALU issue share = SQ_INSTS_VALU x 4 cycles "
+             "/ %d SIMDs / active cycles (GRBM_GUI_ACTIVE / %d XCDs); SQ_INSTS_VALU counts wave instructions, "
+             "MFMAs included.  Lane-instructions per element = SQ_INSTS_VALU x 64 / %d activation elements "
+             "(the activation pass only)." % (SIMDS, XCDS, elements), "",
+             "| kernel | dispatches | duration (us) | clock (GHz) | waves | VALU / dispatch | VALU / wave | "
+             "SALU / wave | LDS / wave | VALU issue share | VALU lane-instr / element |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, pat in (("activation pass (k_quantize)", QUANT_KERNEL), ("core GEMM (k_gemm, plain store)", CORE_KERNEL),
+                      ("delta GEMM (k_gemm, token epilogue)", DELTA_KERNEL)):
+        act = _counter_per_dispatch(run, "GRBM_GUI_ACTIVE", pat, reduce="max")
+        if not act:
+            continue
+        waves = _mean(_counter_per_dispatch(run, "SQ_WAVES", pat))
+        valu = _mean(_counter_per_dispatch(run, "SQ_INSTS_VALU", pat))
+        salu = _mean(_counter_per_dispatch(run, "SQ_INSTS_SALU", pat))
+        lds = _mean(_counter_per_dispatch(run, "SQ_INSTS_LDS", pat))
+        a = _mean(act) / XCDS
+        dur = _mean(_durations_ns(run, pat))
+        per_el = f"{valu * 64 / elements:.1f}" if pat is QUANT_KERNEL else "-"
+        lines.append(f"| {name} | {len(act)} | {dur / 1e3:.1f} | {a / dur:.2f} | {waves:.0f} | {valu:.4g} | "
+                     f"{valu / waves:.0f} | {salu / waves:.0f} | {lds / waves:.0f} | "
+                     f"{100 * valu * 4 / SIMDS / a:.1f} % | {per_el} |")
+    if probe:
+        lines += ["", "Plain streams on the same box (`python3 bench.py --stream-probe`):", "", "```", probe.strip(), "```"]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "trace":
         summarize_trace(argv[1], argv[2], " ".join(argv[3:]))
@@ -185,6 +223,17 @@ def main(argv):
         ap.add_argument("--cmd", required=True)
         a = ap.parse_args(argv[1:])
         summarize_mfma(a.run, a.out, a.cmd)
+        return
+    if len(argv) >= 3 and argv[0] == "issue":
+        import argparse
+        ap = argparse.ArgumentParser()
+        ap.add_argument("run")
+        ap.add_argument("out")
+        ap.add_argument("--cmd", required=True)
+        ap.add_argument("--elements", type=int, required=True)
+        ap.add_argument("--probe", default="", help="file holding a bench.py --stream-probe line")
+        a = ap.parse_args(argv[1:])
+        summarize_issue(a.run, a.out, a.cmd, a.elements, open(a.probe).read() if a.probe else "")
         return
     raise SystemExit(__doc__)
 
