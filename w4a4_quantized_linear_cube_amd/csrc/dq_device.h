@@ -25,30 +25,27 @@ constexpr int FMT_BF16 = 16;  // plain bf16 operands (the bf16-core ablation), n
 // Scale exponent of an MX group (关键设计 4, quantizer definition, with the
 // scale restricted to a power of two): the smallest e with
 // amax <= q_max * 2^e.  With amax = m 2^E (1 <= m < 2) and
-// q_max = 1.5 * 2^2 (FP4) or 1.75 * 2^8 (FP8), that is E - 2 + [m > 1.5] or
-// E - 8 + [m > 1.75]; zero and subnormal maxima give the floor -127.
-__device__ __forceinline__ int mx_exp_fp4(float amax) {
-    uint32_t b = __float_as_uint(amax);
-    int ef = (int)(b >> 23);
-    int e = ef - 129 + ((b & 0x7fffffu) > 0x400000u ? 1 : 0);
-    return ef == 0 ? -127 : max(e, -127);
+// q_max = c 2^Q, that is E - Q + [m > c]; zero and subnormal maxima give the
+// floor -127.  Adding 2^23 - 1 - (c - 1) 2^23 to amax's bits carries into the
+// exponent field exactly when the fraction exceeds c - 1, so the biased
+// exponent field of the sum is E + 127 + [m > c], and e + 127 is that minus
+// Q, saturated at 0 (the floor; also every subnormal and zero maximum).
+//   FP4 E2M1 q_max = 1.5 2^2, FP8 E4M3 1.75 2^8, FP6 E2M3 1.875 2^2,
+//   FP6 E3M2 1.75 2^4.
+__device__ __forceinline__ int mx_exp_carry(float amax, uint32_t add, uint32_t q) {
+    const uint32_t ef = (__float_as_uint(amax) + add) >> 23;
+    return (int)__builtin_elementwise_sub_sat(ef, q) - 127;
 }
-__device__ __forceinline__ int mx_exp_fp8(float amax) {
-    uint32_t b = __float_as_uint(amax);
-    int ef = (int)(b >> 23);
-    int e = ef - 135 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
-    return ef == 0 ? -127 : max(e, -127);
-}
-// 6-bit formats: q_max = 7.5 = 1.875 2^2 (E2M3) or 28 = 1.75 2^4 (E3M2).
+__device__ __forceinline__ int mx_exp_fp4(float amax) { return mx_exp_carry(amax, 0x3fffffu, 2u); }
+__device__ __forceinline__ int mx_exp_fp8(float amax) { return mx_exp_carry(amax, 0x1fffffu, 8u); }
 __device__ __forceinline__ int mx_exp_fp6(float amax, bool e3m2) {
-    uint32_t b = __float_as_uint(amax);
-    int ef = (int)(b >> 23);
-    int e = e3m2 ? ef - 131 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0) : ef - 129 + ((b & 0x7fffffu) > 0x700000u ? 1 : 0);
-    return ef == 0 ? -127 : max(e, -127);
+    return e3m2 ? mx_exp_carry(amax, 0x1fffffu, 4u) : mx_exp_carry(amax, 0x0fffffu, 2u);
 }
-// 2^e as a float operand of the scaled converts (2^-127 is the subnormal 0x00400000).
+// 2^e (-127 <= e <= 127) as a float operand of the scaled converts: the
+// bits (e + 127) << 23, or for e = -127 the subnormal 0x00400000; every
+// normal power's bits exceed 0x00400000, so that is the unsigned maximum.
 __device__ __forceinline__ float pow2f(int e) {
-    return e > -127 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+    return __uint_as_float(max((uint32_t)(e + 127) << 23, 0x00400000u));
 }
 
 // 32 fp32 values -> 32 FP4 E2M1 codes (16 bytes, element 2i in the low

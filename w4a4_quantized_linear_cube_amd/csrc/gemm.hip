@@ -276,13 +276,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             inc = wrap ? ninc : inc;
         }
     };
+    // K order of the plain-store GEMM (nk >= NS): a workgroup's odd tiles
+    // run their K steps backwards.  The workgroups of an XCD start a tile
+    // together and keep their channel tiles from one tile to the next, so the
+    // operand steps a tile starts with are those its predecessor ended with,
+    // still in L2.  (The token-epilogue GEMM measured faster in one order.)
+    constexpr bool SERP = !SMALLK && EPI == EPI_STORE;
+    auto kdir = [&](int t) { return SERP ? 1 - 2 * (t & 1) : 1; };
     auto prepare_next = [&](int it) {                  // tile it + 1 (or the clamp), for the cursor's wrap
         if constexpr (!SMALLK) {
             if (it + 1 < ntiles) {
-                nsrc = src_of(it + 1, 0);
-                ninc = 1;
+                ninc = kdir(it + 1);
+                nsrc = src_of(it + 1, ninc > 0 ? 0 : nk - 1);
             } else {
-                nsrc = src_of(ntiles - 1, nk - 1);
+                nsrc = src_of(ntiles - 1, kdir(ntiles - 1) > 0 ? nk - 1 : 0);
                 ninc = 0;
             }
         }
@@ -499,6 +506,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             // the copies of the next tile's first stages land before the next
             // tile reads them (its first steps wait loosely)
             wait_vm<0>();
+            // token of each row the lane stores after the transposition (row
+            // 8 i + lane / 8 of the blocks of ni: lane rr's slot), all 16
+            // permutes in flight together
+            int trow[4][4];
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) trow[ni][i] = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) * 4, tok[ni]);
             // low-rank branch: acc += (U L2)^T, 32x32x16 bf16 MFMAs over the 32 ranks
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -542,9 +557,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                     if (mi == 0) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int t = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) * 4, tok[ni]);   // token of row rr (lane rr)
-                            float* yrow = p.y + (uint32_t)(t * p.Co + chq);
-                            rowp[i] = t >= 0 ? yrow : p.sink + 4 * lane;
+                            // bit select (no branch): the token's y row, or the sink
+                            const int t = trow[ni][i];
+                            const uint64_t yrow = (uint64_t)(p.y + (uint32_t)(t * p.Co + chq));
+                            const uint64_t sink = (uint64_t)(p.sink + 4 * lane);
+                            const uint64_t m = (uint64_t)(int64_t)(t >> 31);   // all ones for a slot without a token
+                            rowp[i] = (float*)((yrow & ~m) | (sink & m));
                         }
                     }
 #pragma unroll

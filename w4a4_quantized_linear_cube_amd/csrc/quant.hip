@@ -205,28 +205,38 @@ struct QCfg {
     static constexpr int THREADS = (3 + 4 * SP) * 64;
 };
 
+// Cross-lane maxima of group maxima.  These are maxima of absolute values
+// (non-negative floats; no NaN arises), ordered like their bit patterns as
+// unsigned integers, so the exchanges take integer maxima: no NaN
+// canonicalisation, and the DPP moves fold into the max instructions.
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t b) {
+    // (every lane reads a lane of its own row: bound_ctrl never applies, and
+    // setting it lets the move fold into the max)
+    return max(b, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, CTRL, 0xF, 0xF, true));
+}
+
 // maximum over the four lanes of a quad (DPP quad_perm exchanges)
 __device__ __forceinline__ float quad_max(float v) {
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-    return v;
+    uint32_t b = __float_as_uint(v);
+    b = umax_dpp<0xB1>(b);
+    b = umax_dpp<0x4E>(b);
+    return __uint_as_float(b);
 }
 
 // maximum over a row of 16 lanes (quad exchanges, then the half-row and row
 // mirrors: lane i meets lane 7 - i, then lane 15 - i)
 __device__ __forceinline__ float row16_max(float v) {
-    v = quad_max(v);
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
-    return v;
+    uint32_t b = __float_as_uint(quad_max(v));
+    b = umax_dpp<0x141>(b);
+    b = umax_dpp<0x140>(b);
+    return __uint_as_float(b);
 }
 
 // maximum over an aligned group of 8 lanes (quad exchanges, then the
 // half-row mirror: lane i meets lane 7 - i)
 __device__ __forceinline__ float oct_max(float v) {
-    v = quad_max(v);
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-    return v;
+    return __uint_as_float(umax_dpp<0x141>(__float_as_uint(quad_max(v))));
 }
 
 // The maximum of a 64-channel core group from those of its two 32-channel
@@ -236,12 +246,13 @@ __device__ __forceinline__ float oct_max(float v) {
 template <int D>
 __device__ __forceinline__ float core_pair_max(float m, int g64) {
     if (!g64) return m;
-    int o;
-    if constexpr (D == 4) o = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x141, 0xF, 0xF, false);
-    else if constexpr (D == 8) o = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x140, 0xF, 0xF, false);
-    else if constexpr (D == 16) o = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x401F);
-    else o = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32) << 2), __builtin_bit_cast(int, m));
-    return fmaxf(m, __builtin_bit_cast(float, o));
+    const uint32_t b = __float_as_uint(m);
+    uint32_t o;
+    if constexpr (D == 4) o = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x141, 0xF, 0xF, true);
+    else if constexpr (D == 8) o = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x140, 0xF, 0xF, true);
+    else if constexpr (D == 16) o = (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, 0x401F);
+    else o = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32) << 2), (int)b);
+    return __uint_as_float(max(b, o));
 }
 
 // channels ch, ch + 1 (ch even, chunk-relative) of row r as raw bits, and
@@ -933,8 +944,17 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][6], xr[j][7], sc, 3);
                     code[j] = w;
                 }
-#pragma unroll
-                for (int j = 0; j < QKEEP; ++j) *(uint32_t*)(dq_t + toff_fp4(rt0 + j, (int)G) + 4 * qq) = code[j];
+                // rt0 is a multiple of 4 (cubes of 4, 8, .. 64 slots from a
+                // tile row that is a multiple of S), so rows rt0 + j take
+                // toff_fp4's swizzle of rt0 with j / 2 flipped into it: rows
+                // j and j + 1 (j even) sit 64 bytes apart from one address
+                static_assert(QKEEP == 4, "two row pairs");
+                uint8_t* const d01 = dq_t + toff_fp4(rt0, (int)G) + 4 * qq;
+                uint8_t* const d23 = dq_t + toff_fp4(rt0 + 2, (int)G) + 4 * qq;
+                *(uint32_t*)d01 = code[0];
+                *(uint32_t*)(d01 + 64) = code[1];
+                *(uint32_t*)d23 = code[2];
+                *(uint32_t*)(d23 + 64) = code[3];
                 const int exq = qq == 0 ? ex[0] : qq == 1 ? ex[1] : qq == 2 ? ex[2] : ex[3];
                 ds_t[toff_scale(rt0 + qq, (int)G)] = (uint8_t)(exq + 127);
             } else if (g.S > 1) {                           // one-token cubes: every delta is 0, not stored
