@@ -13,9 +13,11 @@
         GRBM_GUI_ACTIVE per dispatch of each kernel -> MFMA flops executed and
         MFMA utilisation (busy cycles per SIMD / active cycles per XCD)
     python -m w4a4_quantized_linear_cube_amd.profiling issue RUN OUT.md --elements E --cmd "..." [--probe F]
+            [--lds RUN2 --lds-cmd "..."]
         SQ_WAVES, SQ_INSTS_{VALU,SALU,LDS} and GRBM_GUI_ACTIVE per dispatch
         -> instructions per wave, VALU issue share, VALU lane-instructions
-        per activation element (E = N x Ci); F: a --stream-probe line
+        per activation element (E = N x Ci); F: a --stream-probe line;
+        RUN2: SQ_LDS_BANK_CONFLICT per LDS instruction and per active cycle
 
 The counter JSON records the SHA-256 of gemm.hip; bench.py reports its
 traffic only while the kernel source is unchanged.
@@ -38,12 +40,13 @@ CORE_KERNEL = re.compile(r"k_gemm<(4, [04]|16, 16), 0, ")   # the core GEMM (FP8
 W6_KERNEL = re.compile(r"k_gemm<[23], [23], [12], ")        # the 6-bit layers' FP6 x FP6 GEMM
 QUANT_KERNEL = re.compile(r"k_quantize<")
 SIMDS = 1024                                     # 256 CUs x 4 SIMDs
+CUS = 256
 XCDS = 8                                         # GRBM_GUI_ACTIVE comes summed over the XCDs
 COPY_KERNEL = re.compile(r"copyBuffer")
 
 
 def _short(name: str) -> str:
-    return re.sub(r"\(.*", "", name)
+    return re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))
 
 
 def summarize_trace(d: str, out: str, cmd: str) -> None:
@@ -165,7 +168,7 @@ def summarize_mfma(run: str, out: str, cmd: str) -> None:
     print("\n".join(lines))
 
 
-def summarize_issue(run: str, out: str, cmd: str, elements: int, probe: str = "") -> None:
+def summarize_issue(run: str, out: str, cmd: str, elements: int, probe: str = "", lds_run: str = "", lds_cmd: str = "") -> None:
     """Instruction issue per kernel: SQ_INSTS_{VALU,SALU,LDS} per dispatch
     and per wave, and the share of the average SIMD's cycles its VALU is
     issuing (a wave64 VALU instruction holds a 16-lane SIMD for 4 cycles)."""
@@ -193,6 +196,21 @@ def summarize_issue(run: str, out: str, cmd: str, elements: int, probe: str = ""
         lines.append(f"| {name} | {len(act)} | {dur / 1e3:.1f} | {a / dur:.2f} | {waves:.0f} | {valu:.4g} | "
                      f"{valu / waves:.0f} | {salu / waves:.0f} | {lds / waves:.0f} | "
                      f"{100 * valu * 4 / SIMDS / a:.1f} % | {per_el} |")
+    if lds_run:
+        lines += ["", "LDS bank conflicts (a second counter run):", "", "```", lds_cmd, "```", "",
+                  "SQ_LDS_BANK_CONFLICT and SQ_INSTS_LDS come summed over every CU; conflict share = the conflict cycles "
+                  "per CU (/ %d) over the active cycles." % CUS, "",
+                  "| kernel | LDS instructions | bank-conflict cycles | per LDS instruction | conflict share |",
+                  "|---|---|---|---|---|"]
+        for name, pat in (("activation pass (k_quantize)", QUANT_KERNEL), ("core GEMM (k_gemm, plain store)", CORE_KERNEL),
+                          ("delta GEMM (k_gemm, token epilogue)", DELTA_KERNEL)):
+            act = _counter_per_dispatch(lds_run, "GRBM_GUI_ACTIVE", pat, reduce="max")
+            if not act:
+                continue
+            n = _mean(_counter_per_dispatch(lds_run, "SQ_INSTS_LDS", pat))
+            c = _mean(_counter_per_dispatch(lds_run, "SQ_LDS_BANK_CONFLICT", pat))
+            a = _mean(act) / XCDS
+            lines.append(f"| {name} | {n:.4g} | {c:.4g} | {c / n:.2f} | {100 * c / CUS / a:.1f} % |")
     if probe:
         lines += ["", "Plain streams on the same box (`python3 bench.py --stream-probe`):", "", "```", probe.strip(), "```"]
     open(out, "w").write("\n".join(lines) + "\n")
@@ -232,8 +250,13 @@ def main(argv):
         ap.add_argument("--cmd", required=True)
         ap.add_argument("--elements", type=int, required=True)
         ap.add_argument("--probe", default="", help="file holding a bench.py --stream-probe line")
+        ap.add_argument("--lds", default="", help="a run with SQ_LDS_BANK_CONFLICT, SQ_INSTS_LDS, GRBM_GUI_ACTIVE")
+        ap.add_argument("--lds-cmd", default="")
         a = ap.parse_args(argv[1:])
-        summarize_issue(a.run, a.out, a.cmd, a.elements, open(a.probe).read() if a.probe else "")
+        probe = ""
+        if a.probe:   # the JSON line only
+            probe = "\n".join(l for l in open(a.probe).read().splitlines() if l.startswith("{"))
+        summarize_issue(a.run, a.out, a.cmd, a.elements, probe, a.lds, a.lds_cmd)
         return
     raise SystemExit(__doc__)
 
