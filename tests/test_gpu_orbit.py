@@ -78,6 +78,8 @@ CASES = [
     (513, 768, 256, 2, 4, "bf16"),     # W2A4, a second row tile
     (64, 1024, 96, 3, 3, "f32"),
     (1, 256, 48, 4, 2, "f32"),
+    (40, 15360, 64, 4, 4, "f32"),      # the largest Ci: the rotation pass holds 120 KB of LDS
+    (33, 15360, 40, 3, 4, "bf16"),
 ]
 
 

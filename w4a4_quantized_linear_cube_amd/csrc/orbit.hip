@@ -60,7 +60,7 @@ namespace dq {
 namespace {
 
 constexpr int OBLOCK = 256;       // Hadamard block
-constexpr int MAX_CI = 15360;     // one row of fp32 in LDS (60 KB, under the 64 KB of dynamic LDS)
+constexpr int MAX_CI = 15360;     // the rotation pass holds a row twice in LDS (at most 120 KB of the 160 KB)
 
 // Lloyd-Max quantizer of N(0, 1) with L levels, ascending: the fixed point of
 // boundaries at the midpoints of neighbouring levels and levels at the
@@ -112,74 +112,142 @@ float bf16_value(uint16_t b) {
 
 struct RowsArgs {
     const void* x;
-    int x_bf16;
-    int Ci, Kp, nlev;
+    int Ci, Kp;
     const int* perm;
-    float mids[16];          // midpoints of neighbouring levels (exact in fp32)
+    float mids[16];          // midpoints of neighbouring levels (exact in fp32), +inf past the last
     uint16_t lev[16];        // bf16 levels
     uint8_t* codes;          // [rows_pad][Kp/2]
     float* scale;            // [rows_pad]
     uint16_t* dec;           // off_bf16 layout
 };
 
-// One workgroup per row: gather by the permutation into LDS, butterflies,
-// the row's RMS, then codes and decoded levels (8 channels per thread and
-// pass: one 4-byte code store and one 16-byte level store).
+// Four radix-2 butterfly stages over 16 values (index bits 0-3, h = 1, 2, 4,
+// 8 in that order): (v[i], v[i + h]) -> (v[i] + v[i + h], v[i] - v[i + h]).
+__device__ __forceinline__ void butterfly16(float* v) {
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if ((i & h) == 0) {
+                const float u = v[i], w = v[i + h];
+                v[i] = u + w;
+                v[i + h] = u - w;
+            }
+}
+
+// One workgroup (4 waves) per row.
+//  1. The row is copied into LDS (16 bytes per lane).
+//  2. Rotation, per 256-channel block b: element i = 16 a + g.  Pair (b, g)
+//     (16 lanes of one wave per block) gathers channels 16 g .. 16 g + 15 by
+//     the permutation and runs the stages on index bits 0-3 (h = 1 .. 8) in
+//     registers; the same 16 lanes then take the columns (element 16 a + g,
+//     a = 0 .. 15: bits 4-7, h = 16 .. 128) through LDS.  The block never
+//     leaves its wave, whose LDS operations complete in order: no barrier.
+//     The stages run in the order h = 1, 2, .., 128, then the exact 1/16.
+//  3. The squares are summed per block in channel order (one lane per
+//     block), then over the blocks in order; s = sqrt(sum / Ci), IEEE
+//     division and correctly rounded square root.
+//  4. Codes: v = fl32(x' / s) (IEEE division; 0 when s = 0), the count of
+//     midpoints strictly below v by a branch-free binary search over the
+//     16-entry table (+inf past the last midpoint), an exact tie to the even
+//     index; 8 channels per thread and pass (one 4-byte code store, one
+//     16-byte store of the decoded bf16 levels).
+template <bool BF16X>
 __global__ __launch_bounds__(256) void k_orbit_rows(RowsArgs a) {
-    extern __shared__ float s[];
+    constexpr int ESZ = BF16X ? 2 : 4;
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+    __shared__ float tbl[16];
+    __shared__ uint16_t lvl[16];
     __shared__ float part[MAX_CI / OBLOCK];
     __shared__ float srow;
+    const int Ci = a.Ci, nb = Ci / OBLOCK;
+    float* const rot = (float*)dyn;                    // [Ci] fp32
+    uint8_t* const raw = dyn + 4 * (size_t)Ci;         // [Ci] input elements
     const long long r = blockIdx.x;
-    const int t = threadIdx.x, Ci = a.Ci;
-    if (a.x_bf16) {
-        const uint16_t* x = (const uint16_t*)a.x + r * Ci;
-        for (int c = t; c < Ci; c += 256) s[c] = bf16_to_f32(x[a.perm[c]]);
-    } else {
-        const float* x = (const float*)a.x + r * Ci;
-        for (int c = t; c < Ci; c += 256) s[c] = x[a.perm[c]];
+    const int t = threadIdx.x;
+    if (t < 16) {
+        tbl[t] = a.mids[t];
+        lvl[t] = a.lev[t];
     }
+    const uint8_t* xr = (const uint8_t*)a.x + r * (long long)Ci * ESZ;
+    for (int o = 16 * t; o < Ci * ESZ; o += 4096) *(uint4*)(raw + o) = *(const uint4*)(xr + o);
     __syncthreads();
-    for (int h = 1; h < OBLOCK; h <<= 1) {
-        for (int q = t; q < Ci / 2; q += 256) {
-            const int i = (q >> 7) * OBLOCK + (q & 127) / h * 2 * h + (q & 127) % h;
-            const float u = s[i], v = s[i + h];
-            s[i] = u + v;
-            s[i + h] = u - v;
+
+    for (int p = t; p < nb * 16; p += 256) {           // a block's 16 pairs: 16 lanes of one wave
+        const int b = p >> 4, g = p & 15;
+        float v[16];
+        const int4* pp = (const int4*)(a.perm + 256 * b + 16 * g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int4 c = pp[q];
+            const int cs[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (BF16X) v[4 * q + e] = __uint_as_float((uint32_t)((const uint16_t*)raw)[cs[e]] << 16);
+                else v[4 * q + e] = ((const float*)raw)[cs[e]];
+            }
         }
-        __syncthreads();
+        butterfly16(v);
+        float4* rg = (float4*)(rot + 256 * b + 16 * g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rg[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float* col = rot + 256 * b + g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = col[16 * i];
+        butterfly16(v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) col[16 * i] = v[i] * 0.0625f;
     }
-    for (int c = t; c < Ci; c += 256) s[c] = s[c] * 0.0625f;
     __syncthreads();
-    const int nb = Ci / OBLOCK;
-    if (t < nb) {
-        float p = s[OBLOCK * t] * s[OBLOCK * t];
-        for (int i = 1; i < OBLOCK; ++i) {
-            const float v = s[OBLOCK * t + i];
-            p = p + v * v;
+
+    if (t < nb) {                                      // wave 0 (nb <= 60)
+        const float4* rb = (const float4*)(rot + 256 * t);
+        float4 q = rb[0];
+        float s2 = q.x * q.x;
+        s2 = s2 + q.y * q.y;
+        s2 = s2 + q.z * q.z;
+        s2 = s2 + q.w * q.w;
+        for (int i = 1; i < 64; ++i) {
+            q = rb[i];
+            s2 = s2 + q.x * q.x;
+            s2 = s2 + q.y * q.y;
+            s2 = s2 + q.z * q.z;
+            s2 = s2 + q.w * q.w;
         }
-        part[t] = p;
+        part[t] = s2;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (t == 0) {
         float tot = part[0];
         for (int j = 1; j < nb; ++j) tot = tot + part[j];
-        srow = sqrtf(__fdiv_rn(tot, (float)Ci));          // correctly rounded (llvm.sqrt.f32), unlike __fsqrt_rn here
-        a.scale[r] = srow;
+        const float sr = sqrtf(__fdiv_rn(tot, (float)Ci));   // correctly rounded (llvm.sqrt.f32), unlike __fsqrt_rn here
+        srow = sr;
+        a.scale[r] = sr;
     }
     __syncthreads();
     const float sr = srow;
     for (int c0 = 8 * t; c0 < Ci; c0 += 2048) {
+        const float4 x0 = *(const float4*)(rot + c0), x1 = *(const float4*)(rot + c0 + 4);
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         uint32_t nib = 0;
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float v = sr > 0.0f ? __fdiv_rn(s[c0 + e], sr) : 0.0f;
-            int idx = 0;
-            for (int m = 0; m < a.nlev - 1; ++m) idx += v > a.mids[m] ? 1 : 0;   // midpoints strictly below v
-            if (idx < a.nlev - 1 && v == a.mids[idx] && (idx & 1)) ++idx;        // exact tie: the even index
+            const float v = sr > 0.0f ? __fdiv_rn(xs[e], sr) : 0.0f;
+            int idx = v > tbl[7] ? 8 : 0;
+            idx += v > tbl[idx + 3] ? 4 : 0;
+            idx += v > tbl[idx + 1] ? 2 : 0;
+            idx += v > tbl[idx] ? 1 : 0;
+            idx += (v == tbl[idx] && (idx & 1)) ? 1 : 0;          // exact tie: the even index
             nib |= (uint32_t)idx << (4 * e);
-            if (e & 1) w[e >> 1] |= (uint32_t)a.lev[idx] << 16;
-            else w[e >> 1] = a.lev[idx];
+            const uint32_t l = lvl[idx];
+            if (e & 1) w[e >> 1] |= l << 16;
+            else w[e >> 1] = l;
         }
         *(uint32_t*)(a.codes + r * (a.Kp / 2) + c0 / 2) = nib;
         *(uint4*)((uint8_t*)a.dec + off_bf16(r, c0, a.Kp / 32)) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -191,17 +259,23 @@ hipError_t launch_rows(const void* x, int x_bf16, int64_t rows, int Ci, int Kp, 
     if (rows == 0) return hipSuccess;
     RowsArgs a{};
     a.x = x;
-    a.x_bf16 = x_bf16;
     a.Ci = Ci;
     a.Kp = Kp;
-    a.nlev = nlev;
     a.perm = perm;
+    for (int i = 0; i < 16; ++i) a.mids[i] = INFINITY;
     for (int i = 0; i < nlev; ++i) a.lev[i] = lev[i];
     for (int i = 0; i + 1 < nlev; ++i) a.mids[i] = 0.5f * (bf16_value(lev[i]) + bf16_value(lev[i + 1]));
     a.codes = codes;
     a.scale = scale;
     a.dec = dec;
-    k_orbit_rows<<<(unsigned)rows, 256, (size_t)Ci * 4, st>>>(a);
+    const size_t lds = (size_t)Ci * (4 + (x_bf16 ? 2 : 4));   // rotated row + the row as given (at most 120 KB)
+    const void* fn = x_bf16 ? (const void*)k_orbit_rows<true> : (const void*)k_orbit_rows<false>;
+    if (lds > 65536) {                                         // beyond the default dynamic LDS limit
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    if (x_bf16) k_orbit_rows<true><<<(unsigned)rows, 256, lds, st>>>(a);
+    else k_orbit_rows<false><<<(unsigned)rows, 256, lds, st>>>(a);
     return hipGetLastError();
 }
 
