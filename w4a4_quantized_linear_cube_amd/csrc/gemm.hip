@@ -124,21 +124,25 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Persistent schedule.  Workgroup b runs on XCD b & 7 (dispatch is
-// round-robin over the 8 XCDs) and takes the tiles of its XCD's share: XCD x
-// owns tile indices [x per, (x + 1) per), and its workgroups walk them with
-// stride G / 8, so the workgroups resident on one XCD at one time hold
-// consecutive indices.  Index v -> (channel tile, slot tile) in groups of gm
-// channel tiles x all slot tiles, column-major inside a group, so those
-// resident workgroups cover a compact block of 4 channel tiles x 8 slot
-// tiles and share their operand steps in the XCD's L2.  Long K loops (64 or
-// more steps) take groups of 8 (a 8 x 4 block: fewer re-reads of the slot
-// panels, whose steps are then the larger share of each tile's bytes; 2 %
-// faster on a 108-step layer, 0.6-1.5 % slower on 40-step ones).
+// round-robin over the 8 XCDs).  The tiles, in the order below, are taken
+// in windows of G (one per iteration of every workgroup): XCD x takes the
+// x-th G / 8 tiles of each window, its workgroups one each.  Index v ->
+// (channel tile, slot tile) in groups of gm channel tiles x all slot tiles,
+// column-major inside a group, so an XCD's resident workgroups cover a
+// compact block of 4 channel tiles x 8 slot tiles and share their operand
+// steps in the XCD's L2, and the eight XCDs work on neighbouring slot tiles
+// of the same channel tiles: the weight panels they share come from the
+// Infinity Cache once one XCD has fetched them from HBM.  (Giving each XCD a
+// contiguous eighth of the tiles instead fetched 1.4x the bytes from HBM.)
+// Long K loops (64 or more steps) take groups of 8 (a 8 x 4 block: fewer
+// re-reads of the slot panels, whose steps are then the larger share of each
+// tile's bytes; 2 % faster on a 108-step layer, 0.6-1.5 % slower on 40-step
+// ones).
 struct TileWalk {
-    int x, y0, ystride, ylim, per, mt, nt, gm;
-    __device__ int count() const { return y0 < ylim ? (ylim - y0 + ystride - 1) / ystride : 0; }
+    int base, G, total, mt, nt, gm;
+    __device__ int count() const { return base < total ? (total - base + G - 1) / G : 0; }
     __device__ void coords(int it, int* tm, int* tn) const {
-        const int v = x * per + y0 + it * ystride;
+        const int v = it * G + base;
         const int grp = v / (gm * nt);
         const int first = grp * gm;
         const int g = min(gm, mt - first);
@@ -150,12 +154,9 @@ struct TileWalk {
 __device__ __forceinline__ TileWalk tile_walk(int b, int G, int mt, int nt, int nks) {
     TileWalk w;
     w.gm = nks >= 64 ? 8 : 4;
-    const int total = mt * nt;
-    w.per = (total + 7) / 8;
-    w.x = b & 7;
-    w.y0 = b >> 3;
-    w.ystride = G >> 3;
-    w.ylim = min(w.per, total - w.x * w.per);
+    w.total = mt * nt;
+    w.G = G;
+    w.base = (b & 7) * (G >> 3) + (b >> 3);     // XCD b & 7, its (b >> 3)-th workgroup
     w.mt = mt;
     w.nt = nt;
     return w;
