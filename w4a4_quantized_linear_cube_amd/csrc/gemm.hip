@@ -70,6 +70,7 @@ struct GemmArgs {
 constexpr int EPI_STORE = 0;      // plain fp32 stores c[b row][a row]
 constexpr int EPI_TOKENS = 1;     // low-rank branch + core term, rows scattered to token order
 constexpr int EPI_TOKENS_Q = 2;   // the same for cubes of a multiple of 4 slots, rank 32, Co a multiple of 256
+constexpr int EPI_ROWS_Q = 3;     // y[row] = (acc x xscale[row]) x wscale[channel]: rows in order, Co a multiple of 256
 
 // Direct global -> LDS copies (global_load_lds, saddr form): lane i copies
 // 16 (or 4) bytes from base + voff_i to LDS address m0 + 16 i (or 4 i), with
@@ -575,6 +576,66 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             }
             return;
         }
+        if constexpr (EPI == EPI_ROWS_Q) {
+            // Rows scaled by their row scale, then by the channel scales, each
+            // product rounded: the loads go out before the one full wait; the
+            // output passes through the transposition buffers as in the token
+            // epilogue, and is scaled after it (the lane then holds 4
+            // consecutive channels of one row).
+            int tok[4];
+            float sx[4][4];
+            float4 sw[4];
+            const int chq = m0 + wr * 128 + 4 * (lane & 7);   // this lane's channels after the transposition (+ 32 mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                tok[ni] = ld_off<int>(p.stok, (uint32_t)(n0 + wc * 128 + 32 * ni + l32) * 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sx[ni][i] = ld_off<float>(p.xscale, (uint32_t)(n0 + wc * 128 + 32 * ni + 8 * i + (lane >> 3)) * 4);
+            }
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) sw[mi] = ld_off<float4>(p.wscale, (uint32_t)(chq + 32 * mi) * 4);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();                                // every wave is done with the last step's stage
+            wait_vm<0>();
+            int trow[4][4];
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) trow[ni][i] = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) * 4, tok[ni]);
+            float* rowp[4];
+#pragma unroll
+            for (int b = 0; b < 17; ++b) {
+                if (b < 16) {                               // block b: mi = b % 4, ni = b / 4
+                    const v16f& a = acc[b & 3][b >> 2];
+                    float4 o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = make_float4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
+                    tput(b & 1, o);
+                }
+                if (b > 0) {
+                    const int pb = b - 1, mi = pb & 3, ni = pb >> 2;
+                    if (mi == 0) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int t = trow[ni][i];
+                            const uint64_t yrow = (uint64_t)(p.y + (uint32_t)(t * p.Co + chq));
+                            const uint64_t sink = (uint64_t)(p.sink + 4 * lane);
+                            const uint64_t m = (uint64_t)(int64_t)(t >> 31);   // all ones for a row past the end
+                            rowp[i] = (float*)((yrow & ~m) | (sink & m));
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float4 v = tget(pb & 1, i);
+                        const float r = sx[ni][i];
+                        const float4 o = make_float4((v.x * r) * sw[mi].x, (v.y * r) * sw[mi].y, (v.z * r) * sw[mi].z,
+                                                     (v.w * r) * sw[mi].w);
+                        __builtin_nontemporal_store(__builtin_bit_cast(v4f, o), (v4f*)(rowp[i] + 32 * mi));
+                    }
+                }
+            }
+            return;
+        }
         // low-rank branch: acc += (U L2)^T with 32x32x16 bf16 MFMAs over the padded rank
         for (int kq = 0; kq < p.rp; kq += 16) {
             v8bf la[4], ub[4];
@@ -737,7 +798,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             }
         }
         for (; ks < nk; ++ks, ++gs) kstep(ks);
-        if (EPI != EPI_TOKENS_Q) wait_vm<0>();   // that epilogue waits after issuing its loads
+        if (EPI != EPI_TOKENS_Q && EPI != EPI_ROWS_Q) wait_vm<0>();   // those epilogues wait after issuing their loads
         int tm, tn;
         walk.coords(it, &tm, &tn);
         tstage = (unsigned)(gs - 1) % NS;
@@ -902,6 +963,7 @@ hipError_t launch_orbit_gemm(const uint16_t* wdec, const uint16_t* xdec, int64_t
     d.sink = sink;
     d.xscale = xscale;
     d.wscale = wscale;
+    if (d.vec4 && Co % 256 == 0 && Npad * Co < (1ll << 31)) return launch<FMT_BF16, EPI_ROWS_Q, FMT_BF16>(d, st);
     return launch<FMT_BF16, EPI_TOKENS, FMT_BF16>(d, st);
 }
 
