@@ -196,6 +196,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // stream (and the wait to issue it) is spread over the whole step.
     constexpr bool SPLIT = NS >= 4;
     constexpr int H1 = SPLIT ? DMAS / 2 : DMAS;
+    // DEFER (the token epilogue with a three-stage ring): the copies of a
+    // tile's last steps do not run into the next tile.  The cursor holds on
+    // the tile's last step (those copies repeat it, into stages nothing reads
+    // before they are written again), and the epilogue issues the next tile's
+    // first NS - 1 stages once its own loads are in: its full wait then covers
+    // no slow copies, and its stores hide the new copies' latency.  The wait
+    // counts are those of the uniform stream (every step still issues DMAS
+    // copies).  (720p FFN down, one-token cubes, FP8 x FP4: 3.75 -> 3.71 ms;
+    // with the four-stage FP4 ring, whose copies lead by three steps, the FFN
+    // up delta GEMM measured 0.7 % slower, so it keeps the continuous stream.)
+    constexpr bool DEFER = !SMALLK && EPI == EPI_TOKENS_Q && NS == 3;
+    // after the deferred stage 0: the other deferred copies and the epilogue's 64 stores
+    static_assert(!DEFER || (NS - 3) * DMAS + (SPLIT ? H1 : DMAS) + 64 >= 63, "stage 0 covered by vmcnt(63)");
     // Split copies sit after every third MFMA of a phase (phase 1 from MFMA
     // 0, phase 2 from MFMA 2), which measured faster than issuing them after
     // consecutive MFMAs; unsplit, copy j follows MFMA j.
@@ -269,6 +282,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
             kf = stay ? kf : (wrap ? 0 : kf + 1);
             tf = (wrap && !stay) ? tf + 1 : tf;
             src = src_of(tf, kf);
+        } else if constexpr (DEFER) {
+            const int d = wrap ? 0 : inc;                  // hold on the tile's last step
+            kf = wrap ? kf : kf + 1;
+            src.a += d * A_STEP;
+            src.b += d * B_STEP;
+            src.as += d * 1024;
+            src.bs += d * 1024;
         } else {
             kf = wrap ? 0 : kf + 1;
             src.a = wrap ? nsrc.a : src.a + inc * A_STEP;
@@ -410,6 +430,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     // epilogue's first barrier and no copy fills before the next tile's first
     // barrier.
     int tstage = 0;                                       // stage of the tile's last K step
+    // The next tile's first NS - 1 stages (DEFER), as in the prologue, into
+    // the stages after the tile's last one (global steps gs ..); the last of
+    // them only its first half when split, the cursor then staying on it.
+    auto issue_next = [&]() {
+        src = nsrc;
+        inc = ninc;
+        kf = 0;
+        const int g0 = tstage + 1;
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s) {
+            const bool half = SPLIT && s == NS - 2;
+#pragma unroll
+            for (int j = 0; j < DMAS; ++j)
+                if (!half || j < H1) dma(src, (g0 + s) % NS, j);
+            if (!half) advance();
+        }
+    };
 
     // ---- core-term rows of the token epilogue.  A cube spans a multiple of
     // 4 slots and tiles and frame segments start at multiples of 256 rows, so the four lanes of a quad
@@ -525,6 +562,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                     for (int ni = 0; ni < 4; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[h][mi], ub[h][ni], acc[mi][ni], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (DEFER) issue_next();
             // y[token] = acc + core term of the token's cube, through the
             // transposition buffers.  The broadcasts run in every lane (a pad
             // slot's lane still serves its quad); a row is stored if its slot
@@ -803,12 +841,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         walk.coords(it, &tm, &tn);
         tstage = (unsigned)(gs - 1) % NS;
         epilogue(tm, tn);
+        if constexpr (DEFER) {                             // the next tile's stage 0, every wave's copies
+            wait_vm<63>();
+            __syncthreads();
+        }
         // The last step already read half 0 of the next tile's first stage
         // (landed: its barrier covered it); reading it again here keeps those
         // registers free during the epilogue.
 #pragma unroll
         for (int i = 0; i < NRD; ++i) rd((unsigned)gs % NS, 0, F0, i);
     }
+    if constexpr (DEFER) wait_vm<0>();                   // the last tile's surplus copies land before the LDS is released
 }
 
 // One persistent workgroup per CU (a multiple of 8, one share per XCD),
