@@ -790,6 +790,92 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             }
         }
     } else {
+    // The common one-pass case (see fast4 below): per-thread task constants.
+    const bool fast4 = CM == 0 && sizeof(XT) == 2 && g.S == 4 && !a.core_fp4 && !a.cbf;
+    const int f4_qq = qtid & 3, f4_gc = (qtid >> 2) & 3, f4_cr = qtid >> 4;
+    uint32_t f4_lds[QKEEP];
+#pragma unroll
+    for (int j = 0; j < QKEEP; ++j) f4_lds[j] = (uint32_t)qoff(4 * f4_cr + j, 4 * f4_gc + f4_qq);
+    long long f4_block = -1;
+    uint32_t f4_d01 = 0, f4_d23 = 0, f4_ds = 0, f4_cq = 0, f4_cs = 0;
+    // One (cube, group, quarter) task of a 4-slot cube: the same arithmetic
+    // as the general task below in its FULL form (fp32 sum of the rows in
+    // slot order, pad rows as -0.0; the core divided, FP8-coded; the deltas
+    // FP4-coded), with the offsets above.  K step kc of the outputs.
+    auto task4 = [&](const uint8_t* buf, int kc, uint8_t* dq_t, uint8_t* ds_t, uint8_t* cq_t, uint8_t* cs_t) {
+      if constexpr (sizeof(XT) == 2) {
+        const int4 md = meta_s[qgrp][mb][f4_cr];
+        const int pm = md.z, cnt = md.w;
+        float core[8], xr[QKEEP][8];
+        uint4 raw[QKEEP];
+#pragma unroll
+        for (int j = 0; j < QKEEP; ++j) raw[j] = *(const uint4*)(buf + f4_lds[j]);
+#pragma unroll
+        for (int j = 0; j < QKEEP; ++j) {
+            QRaw<XT> q;
+            q.w[0] = raw[j];
+            qconv8<XT>(q, ((pm >> j) & 1) ? 0u : 0x80000000u, xr[j]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) core[e] = ((xr[0][e] + xr[1][e]) + xr[2][e]) + xr[3][e];
+        if ((cnt & (cnt - 1)) == 0) {                      // exact power-of-two scaling
+            const float rc = inv_pow2(cnt);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) core[e] *= rc;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) core[e] = __fdiv_rn(core[e], (float)cnt);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(core[e]));
+        amax = core_pair_max<4>(quad_max(amax), a.core_g64);
+        const int cex = mx_exp_fp8(amax);
+        const float csc = pow2f(cex);
+        uint32_t d[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v2s z = {0, 0};
+            v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, core[4 * h], core[4 * h + 1], csc, false);
+            v2s hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, core[4 * h + 2], core[4 * h + 3], csc, true);
+            d[h] = __builtin_bit_cast(uint32_t, hi);
+        }
+        *(uint2*)(cq_t + (size_t)kc * 32768 + f4_cq) = make_uint2(d[0], d[1]);
+        if (f4_qq == 0) cs_t[(size_t)kc * 1024 + f4_cs] = (uint8_t)(cex + 127);
+        float am[QKEEP];
+        uint32_t code[QKEEP];
+        int ex[QKEEP];
+#pragma unroll
+        for (int j = 0; j < QKEEP; ++j) {
+            am[j] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                xr[j][e] = xr[j][e] - core[e];
+                am[j] = fmaxf(am[j], fabsf(xr[j][e]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < QKEEP; ++j) am[j] = quad_max(am[j]);
+#pragma unroll
+        for (int j = 0; j < QKEEP; ++j) {
+            ex[j] = mx_exp_fp4(am[j]);
+            const float sc = pow2f(ex[j]);
+            uint32_t w = 0u;
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][0], xr[j][1], sc, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][2], xr[j][3], sc, 1);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][4], xr[j][5], sc, 2);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][6], xr[j][7], sc, 3);
+            code[j] = w;
+        }
+        uint8_t* const dk = dq_t + (size_t)kc * 16384;
+        *(uint32_t*)(dk + f4_d01) = code[0];
+        *(uint32_t*)(dk + f4_d01 + 64) = code[1];
+        *(uint32_t*)(dk + f4_d23) = code[2];
+        *(uint32_t*)(dk + f4_d23 + 64) = code[3];
+        const int exq = f4_qq == 0 ? ex[0] : f4_qq == 1 ? ex[1] : f4_qq == 2 ? ex[2] : ex[3];
+        ds_t[(size_t)kc * 1024 + f4_ds] = (uint8_t)(exq + 127);
+      }
+    };
     for (long long u = 0; u < nsteps; ++u) {
         barrier();
         const long long s = SP * u + qgrp;
@@ -1228,9 +1314,27 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 }
             }
         } else {
+            if (fast4) {
+                // cubes of 4 slots, bf16 rows, FP8 cores without a bf16 copy:
+                // thread t's (cube, group, quarter) is the same in every chunk
+                // of every block, so its LDS and output offsets are fixed, up
+                // to per-block parts (taken when the block changes) and the
+                // chunk's K step (uniform)
+                if (i != f4_block) {
+                    f4_block = i;
+                    const int rt0 = (int)(B.slot0 & 255) + 4 * f4_cr, kt = (int)(B.k_first & 255) + f4_cr;
+                    f4_d01 = toff_fp4(rt0, f4_gc) + 4 * f4_qq;
+                    f4_d23 = toff_fp4(rt0 + 2, f4_gc) + 4 * f4_qq;
+                    f4_ds = toff_scale(rt0 + f4_qq, f4_gc);
+                    f4_cq = toff_fp8(kt, 0, 2 * f4_gc + (f4_qq >> 1)) + 8 * (f4_qq & 1);
+                    f4_cs = toff_scale(kt, f4_gc);
+                }
+                if (qtid < ntask && c0 + 32 * f4_gc < a.Ci) task4(buf, c, dq_t, ds_t, cq_t, cs_t);
+            } else {
             for (int t = qtid; t < ntask; t += 256) {
                 if (full) task(t, std::true_type{});
                 else task(t, std::false_type{});
+            }
             }
         }
         // the group's next chunk; a new block's metadata goes to the other
