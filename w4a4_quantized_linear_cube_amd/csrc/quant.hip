@@ -797,7 +797,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
 #pragma unroll
     for (int j = 0; j < QKEEP; ++j) f4_lds[j] = (uint32_t)qoff(4 * f4_cr + j, 4 * f4_gc + f4_qq);
     long long f4_block = -1;
-    uint32_t f4_d01 = 0, f4_d23 = 0, f4_ds = 0, f4_cq = 0, f4_cs = 0;
+    uint32_t f4_drow = 0, f4_ds = 0, f4_cq = 0, f4_cs = 0;
     // One (cube, group, quarter) task of a 4-slot cube: the same arithmetic
     // as the general task below in its FULL form (fp32 sum of the rows in
     // slot order, pad rows as -0.0; the core divided, FP8-coded; the deltas
@@ -867,11 +867,28 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][6], xr[j][7], sc, 3);
             code[j] = w;
         }
-        uint8_t* const dk = dq_t + (size_t)kc * 16384;
-        *(uint32_t*)(dk + f4_d01) = code[0];
-        *(uint32_t*)(dk + f4_d01 + 64) = code[1];
-        *(uint32_t*)(dk + f4_d23) = code[2];
-        *(uint32_t*)(dk + f4_d23 + 64) = code[3];
+        // Lane qq holds 4 bytes (its 8 channels) of each row's 16-byte group
+        // code; a 4 x 4 transpose inside the quad (lane exchanges at distance
+        // 1, then 2) gives lane qq row qq's whole code, stored with one
+        // 16-byte store (the quads of a row's four groups then write its
+        // 64 bytes in full).  Exchange at distance d: a lane keeps slot j when
+        // bit d of j equals its own and takes the partner's slot j ^ d
+        // otherwise.
+        auto xchg = [&](uint32_t* v, auto dd, auto cc) {
+            constexpr int d = decltype(dd)::value, ctrl = decltype(cc)::value;
+            const bool hi = (f4_qq & d) != 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j & d) continue;                           // slot pair (j, j + d)
+                const uint32_t send = hi ? v[j] : v[j + d];
+                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, ctrl, 0xF, 0xF, true);
+                v[j] = hi ? recv : v[j];
+                v[j + d] = hi ? v[j + d] : recv;
+            }
+        };
+        xchg(code, std::integral_constant<int, 1>{}, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+        xchg(code, std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+        *(uint4*)(dq_t + (size_t)kc * 16384 + f4_drow) = make_uint4(code[0], code[1], code[2], code[3]);
         const int exq = f4_qq == 0 ? ex[0] : f4_qq == 1 ? ex[1] : f4_qq == 2 ? ex[2] : ex[3];
         ds_t[(size_t)kc * 1024 + f4_ds] = (uint8_t)(exq + 127);
       }
@@ -1323,8 +1340,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 if (i != f4_block) {
                     f4_block = i;
                     const int rt0 = (int)(B.slot0 & 255) + 4 * f4_cr, kt = (int)(B.k_first & 255) + f4_cr;
-                    f4_d01 = toff_fp4(rt0, f4_gc) + 4 * f4_qq;
-                    f4_d23 = toff_fp4(rt0 + 2, f4_gc) + 4 * f4_qq;
+                    f4_drow = toff_fp4(rt0 + f4_qq, f4_gc);
                     f4_ds = toff_scale(rt0 + f4_qq, f4_gc);
                     f4_cq = toff_fp8(kt, 0, 2 * f4_gc + (f4_qq >> 1)) + 8 * (f4_qq & 1);
                     f4_cs = toff_scale(kt, f4_gc);
