@@ -226,7 +226,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     const int ntiles = walk.count();
     if (ntiles == 0) return;
     const int nk = p.nks;
-    const int nsteps = ntiles * nk;
 
     // ---- copies.  Global step s (over all of this workgroup's tiles) is
     // K step s % nk of tile s / nk; the issue cursor walks them in order.
