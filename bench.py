@@ -456,9 +456,9 @@ def main():
     achieved = rl_flops / (d_ms * 1e-3)
     traffic = committed_traffic(args.config, cube)
 
-    cpu = None
+    cpu = sanity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, cube, x, weights, dq, args.cpu_tokens)
+        cpu, sanity = cpu_baseline(cfg, cube, x, y, weights, dq, args.cpu_tokens)
 
     out = {
         "metric": "effective TOPS of fused delta-W4A4 linear + % of MI355X FP4 MFMA peak",
@@ -518,6 +518,7 @@ def main():
             "pad_slot_waste": round(wk["fp4_slots"] / f_fp4 - 1, 4),
         },
         "cpu_baseline": cpu,
+        "sanity_error": sanity,
     }
     print(json.dumps(out), flush=True)
 
@@ -578,7 +579,7 @@ def committed_traffic(config, cube):
     return rec.get("traffic_bytes")
 
 
-def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
+def cpu_baseline(cfg, cube, x, y, weights, dq, n_tokens):
     """The oracle, as it stands, on a bounded sample: whole cubes covering
     about n_tokens tokens, quantized and pushed through the layer on the host
     (weights prepared beforehand and not timed, as on the GPU)."""
@@ -614,7 +615,7 @@ def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
     yo = layer.forward(q, g, rc, rs, l2)
     dt = time.perf_counter() - t0
     n = len(q["tokens"])
-    return {
+    base = {
         "value": round(2.0 * n * cfg.Ci * cfg.Co / dt / 1e12, 6),
         "unit": "TOPS",
         "cores": int(threads),
@@ -624,6 +625,19 @@ def cpu_baseline(cfg, cube, x, weights, dq, n_tokens):
         "extrapolated": True,
         "full_layer_s": round(dt * cfg.N / n, 1),
     }
+    # Sanity check (untimed): the layer output's error against the exact
+    # X W (fp64) on 256 of the sampled tokens, for delta W4A4 (the GPU's y of
+    # the timed steps) and for direct W4A4 of X (the oracle: the same R,
+    # rank, low-rank branch and MX rule, X quantized per token, no cubes).
+    sel = np.sort(rng.choice(n, size=min(256, n), replace=False))
+    tk = np.asarray(q["tokens"])[sel]
+    ex = layer.exact_output(xf[tk], wf)
+    yg = y.index_select(0, torch.from_numpy(tk).to(y.device)).cpu().numpy()
+    yd = layer.direct_output(xf[tk], q["U"][sel], l2, rc, rs)
+    sanity = {"tokens": int(len(tk)), "rel_err_delta_w4a4": round(layer.rel_fro(yg, ex), 5),
+              "rel_err_direct_w4a4": round(layer.rel_fro(yd, ex), 5),
+              "against": "exact X W in fp64; delta: the GPU output, direct: the oracle with X quantized per token"}
+    return base, sanity
 
 
 if __name__ == "__main__":
