@@ -128,8 +128,8 @@ def test_core_fp4(dqm, case):
 
 
 # bf16 cores (the 16-bit point of the pages' core-precision ablation: the
-# cores rounded to bf16, the core term a library bf16 GEMM against Q4(R)),
-# through every form of the activation pass
+# cores rounded to bf16, the core term a bf16 MFMA GEMM against Q4(R) decoded
+# to bf16), through every form of the activation pass
 @pytest.mark.parametrize("case", CORE64, ids=[f"{c[0]}x{c[1]}x{c[2]}_c{'x'.join(map(str, c[3]))}_ci{c[4]}_{c[7]}"
                                               for c in CORE64])
 def test_core_bf16(dqm, case):
@@ -139,6 +139,30 @@ def test_core_bf16(dqm, case):
                n_out=min(4, Ci // 16), core_bits=16)
     err, row = _full_compare(dqm, L)
     _say(f"bf16 cores {case}: rel err {err:.2e} worst row {row:.2e}")
+
+
+# The core GEMM's last, partly filled round split along K: layers of a few
+# tiles with long K loops run every tile as K-chunk units whose partials a
+# second kernel sums.  Chunks of unequal length (17 FP8 steps in 5 chunks:
+# 3, 3, 4, 3, 4), FP4 cores (40 steps), bf16 cores (68 steps of 32 channels,
+# the walk's 8-tile groups), channels not a multiple of 128.
+KSPLIT = [
+    # T, H, W, cube, Ci, Co, rank, dtype, core bits
+    (3, 16, 16, (1, 2, 2), 2176, 512, 32, "bf16", 8),
+    (2, 16, 16, (2, 2, 2), 5120, 320, 32, "bf16", 4),
+    (3, 16, 16, (1, 2, 2), 2176, 512, 16, "f32", 16),
+    (3, 12, 14, (1, 2, 2), 2080, 256, 16, "bf16", 8),
+]
+
+
+@pytest.mark.parametrize("case", KSPLIT, ids=[f"{c[0]}x{c[1]}x{c[2]}_ci{c[4]}_co{c[5]}_core{c[8]}" for c in KSPLIT])
+def test_core_term_k_split(dqm, case):
+    T, H, W, cube, Ci, Co, rank, dtype, bits = case
+    _say(f"case core K split {case}")
+    L = _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed=T * 100 + Ci + 5, wseed=Co + 15,
+               n_out=4, core_bits=bits)
+    err, row = _full_compare(dqm, L)
+    _say(f"core K split {case}: rel err {err:.2e} worst row {row:.2e}")
 
 
 def test_core_group_errors(dqm):

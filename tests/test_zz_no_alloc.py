@@ -7,8 +7,8 @@ differently shaped layer, so the fixed scratch array holds the previous
 call's bytes when the next one starts: a state that is not cleared or
 rewritten would show as a difference.  The second layer has Ci = 192 (channel
 padding up to 256, which the entry point must clear) and cubes of more than
-64 tokens (block partials), the third one-token cubes; then the first layer
-again.
+64 tokens (block partials), the third one-token cubes, the fourth a core GEMM
+split along K (K-chunk partials in the array); then the first layer again.
 """
 import ctypes
 
@@ -26,6 +26,7 @@ LAYERS = [
     (4, 12, 14, (1, 2, 2), 512, 768, 32, "bf16"),
     (3, 9, 10, (3, 9, 10), 192, 320, 16, "f32"),
     (2, 5, 6, (1, 1, 1), 128, 256, 32, "bf16"),
+    (3, 16, 16, (1, 2, 2), 2176, 512, 32, "bf16"),
     (4, 12, 14, (1, 2, 2), 512, 768, 32, "bf16"),
 ]
 

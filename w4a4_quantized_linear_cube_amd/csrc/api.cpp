@@ -89,6 +89,7 @@ void free_qact(dq_qact* q) {
     (void)hipFree(q->bias);
     (void)hipFree(q->coref);
     (void)hipFree(q->part);
+    (void)hipFree(q->kpart);
     (void)hipFree(q->cbf);
     (void)hipFree(q->rbf);
     delete q;
@@ -347,6 +348,37 @@ dq_status dq_qact_create(const dq_weights* w, dq_geom geom, dq_qact** out) {
 namespace dq {
 // Checks a geometry and the core options against a weight and fills the
 // workspace's sizes and frame segments (no allocation, no device work).
+KSplit plan_ksplit(int mt, int nt, int nks, int ns, int cus, double step_us) {
+    KSplit k;
+    const int G = std::max(8, cus / 8 * 8);                         // the persistent grid of a full round
+    const int T = mt * nt, full = T / G * G, rm = T - full;
+    if (rm == 0) return k;
+    // time saved against one more round of whole tiles: the chunks' share of
+    // the tile, less the partials' HBM round trip (0.13 us per 256 KB unit,
+    // written and read back), about 10 us for the two extra launches, and
+    // the part of the last round that hides in the spread of the full
+    // rounds' finishing times (the workgroups of a persistent launch end
+    // about 4 % of its length apart, and each starts its last-round tile as
+    // it finishes).  Same-box core-term times, FP8 x FP4: 720p FFN down,
+    // 2x2x2 cubes (3 rounds + 32 tiles, 108 steps) 0.642 -> 0.557 ms and the
+    // global cube (20 tiles) 0.149 -> 0.043 ms; 720p FFN up, 1x2x2 cubes
+    // (16 rounds + 8 tiles of 40 steps) 1.094 -> 1.112 ms, so that one, with
+    // a drift term of 41 us against a 38 us saving, keeps one launch.
+    const double tile = nks * step_us, drift = 0.04 * (full / G) * tile;
+    double best = 0;
+    for (int q = 2; q * rm <= G && nks / q >= ns; ++q) {
+        const double gain = tile * (1.0 - 1.0 / q) - 0.13 * rm * q - 10.0 - drift;
+        if (gain > best) {
+            best = gain;
+            k.p = q;
+        }
+    }
+    if (best < std::max(5.0, 0.15 * tile)) return KSplit{};         // (within the model's error: keep one launch)
+    k.main_tiles = full;
+    k.rm = rm;
+    return k;
+}
+
 dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, int core_bits, dq_qact* q,
                     int64_t* max_partials_out) {
     if (w->wfmt != 4) return fail(DQ_ERR_INVALID_ARG, "a 6-bit weight takes the 6-bit entry points");
@@ -406,6 +438,18 @@ dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, in
     q->K_pad = krow;
     if (!mul_ok(q->Nslot_pad, q->Kp, lim) || !mul_ok(q->K_pad, q->Cop, lim) || !mul_ok(max_partials, q->Kp, lim))
         return fail(DQ_ERR_SHAPE, "workspace too large");
+    // the core GEMM's K split (one-token cubes with FP8 or FP4 cores run no
+    // core GEMM).  Per-step times of a tile with every CU busy: FP8 x FP4
+    // steps of 128 channels 1.6 us, FP4 x FP4 1.0 us, bf16 steps of 32
+    // channels 0.8 us (720p FFN up-projection).
+    q->ks = KSplit{};
+    if (!(S == 1 && core_bits != 16)) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, w->device) != hipSuccess) cus = 256;
+        const int nks = (int)(core_bits == 16 ? q->Kp / 32 : q->Kp / 128);
+        q->ks = plan_ksplit((int)(q->Cop / 256), (int)(q->K_pad / 256), nks, core_bits == 8 ? 3 : 4, cus,
+                            core_bits == 8 ? 1.6 : (core_bits == 4 ? 1.0 : 0.8));
+    }
     *max_partials_out = max_partials;
     return DQ_OK;
 }
@@ -449,6 +493,8 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
             (e = dalloc(&q->part, (size_t)(max_partials * q->Kp), &q->bytes)) != hipSuccess)
             return hip_fail(e, "hipMalloc workspace");
     }
+    if (q->ks.rm > 0 && (e = dalloc(&q->kpart, q->ks.part_bytes() / 4, &q->bytes)) != hipSuccess)
+        return hip_fail(e, "hipMalloc workspace");
     if (core_bits == 16) {                          // bf16 cores: Q4(R) as bf16 for the bf16 GEMM
         if ((e = dalloc(&q->cbf, (size_t)(q->K_pad * q->Kp), &q->bytes)) != hipSuccess ||
             (e = dalloc(&q->rbf, (size_t)(q->Cop * q->Kp), &q->bytes)) != hipSuccess)

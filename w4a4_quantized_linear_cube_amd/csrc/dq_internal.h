@@ -105,6 +105,23 @@ struct Geom {
     long long N, K, Nslot;
 };
 
+// K split of a plain-store GEMM's last, partly filled round.  The persistent
+// GEMM runs its tiles in rounds of one tile per workgroup; when the tile
+// count is not a multiple of the grid, the last round leaves most CUs idle
+// for a whole tile.  Instead, one launch runs the full rounds (walk tiles
+// 0 .. main_tiles - 1), a second runs the rm remaining tiles (walk tiles
+// main_tiles ..) as rm x p units, unit u taking K chunk u / rm of tile
+// u % rm into its own 256 x 256 fp32 partial, and a third sums each tile's
+// p partials in chunk order into the output.  rm == 0: one launch.
+struct KSplit {
+    int main_tiles = 0, rm = 0, p = 1;
+    size_t part_bytes() const { return (size_t)rm * (size_t)p * 65536 * 4; }
+};
+// The split of an mt x nt tile GEMM with nks K steps of about step_us each
+// (per tile, with every CU busy) on `cus` CUs, ring depth ns: the chunk count
+// that saves the most time (each chunk at least ns steps), or none.
+KSplit plan_ksplit(int mt, int nt, int nks, int ns, int cus, double step_us);
+
 }  // namespace dq
 
 struct dq_weights {
@@ -160,6 +177,8 @@ struct dq_qact {
     float* sink = nullptr;     // [512]              target of the GEMM's discarded 16-byte stores
     float* coref = nullptr;    // [K_pad][Kp]        fp32 cores (segments of core_mode 1), cube rows
     float* part = nullptr;     // [K*nblk][Kp]       fp32 block partials (core_mode 1; the segments take turns)
+    dq::KSplit ks{};           // K split of the core GEMM's last round (set by plan_qact)
+    float* kpart = nullptr;    // [ks.rm * ks.p][256][256] fp32 K-chunk partials of that round (ks.rm > 0)
     size_t bytes = 0;
 };
 
@@ -185,7 +204,8 @@ void set_error(const std::string& msg);
 dq_status fail(dq_status s, const std::string& msg);
 dq_status hip_fail(hipError_t e, const char* what);
 // Checks a geometry and the core options against a weight and fills the
-// workspace's sizes and frame segments (no allocation, no device work);
+// workspace's sizes, frame segments and the core GEMM's K split (no
+// allocation, no device work);
 // *max_partials is the row count of the block-partial buffer (0 if no
 // segment has cubes of more than 64 tokens).
 dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, int core_bits, dq_qact* q,

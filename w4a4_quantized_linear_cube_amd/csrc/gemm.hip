@@ -34,6 +34,7 @@
 // indices are remapped so the workgroups resident on one XCD at a time cover
 // a compact block of 4 channel tiles x 8 slot tiles and share their operand
 // steps in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "dq_device.h"
@@ -65,6 +66,12 @@ struct GemmArgs {
     float* sink;        // 2 KB the token epilogue stores lanes without an output to (never read)
     const float* xscale;   // general token epilogue: y = (acc x xscale[slot]) x wscale[channel] when set
     const float* wscale;   //   (the rotated-basis layers' per-row scales), [Nslot_pad] and [Cop]
+    // K split of the plain-store GEMM's last round (KSplit).  ttotal > 0:
+    // run only walk tiles 0 .. ttotal - 1.  su_rm > 0: workgroup u runs K
+    // steps [c nks / su_p, (c + 1) nks / su_p), c = u / su_rm, of walk tile
+    // su_v0 + u % su_rm and stores the 256 x 256 partial at c + u 65536.
+    int ttotal;
+    int su_v0, su_rm, su_p;
 };
 
 constexpr int EPI_STORE = 0;      // plain fp32 stores c[b row][a row]
@@ -223,10 +230,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     const int wr = wave >> 1, wc = wave & 1;
     const int g = lane >> 5, l32 = lane & 31;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const TileWalk walk = tile_walk(blockIdx.x, gridDim.x, p.mtiles, p.ntiles, p.nks);
+    TileWalk walk = tile_walk(blockIdx.x, gridDim.x, p.mtiles, p.ntiles, p.nks);
+    int k0 = 0, nk = p.nks;                      // the K steps this workgroup runs of each tile
+    if constexpr (EPI == EPI_STORE) {
+        if (p.ttotal > 0) walk.total = p.ttotal;
+        if (p.su_rm > 0) {                       // one split-K unit
+            const int u = blockIdx.x, c = u / p.su_rm;
+            walk.base = p.su_v0 + u % p.su_rm;
+            walk.total = walk.base + 1;
+            k0 = c * p.nks / p.su_p;
+            nk = (c + 1) * p.nks / p.su_p - k0;
+        }
+    }
     const int ntiles = walk.count();
     if (ntiles == 0) return;
-    const int nk = p.nks;
 
     // ---- copies.  Global step s (over all of this workgroup's tiles) is
     // K step s % nk of tile s / nk; the issue cursor walks them in order.
@@ -247,10 +264,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         int tm, tn;
         walk.coords(t, &tm, &tn);
         Src r;
-        r.a = (const uint8_t*)uniform_ptr(p.a + ((size_t)tm * p.nks + k) * A_STEP);
-        r.b = (const uint8_t*)uniform_ptr(p.b + ((size_t)tn * p.nks + k) * B_STEP);
-        r.as = (const uint8_t*)uniform_ptr(p.as + ((size_t)tm * p.nks + k) * 1024);
-        r.bs = (const uint8_t*)uniform_ptr(p.bs + ((size_t)tn * p.nks + k) * 1024);
+        r.a = (const uint8_t*)uniform_ptr(p.a + ((size_t)tm * p.nks + k0 + k) * A_STEP);
+        r.b = (const uint8_t*)uniform_ptr(p.b + ((size_t)tn * p.nks + k0 + k) * B_STEP);
+        r.as = (const uint8_t*)uniform_ptr(p.as + ((size_t)tm * p.nks + k0 + k) * 1024);
+        r.bs = (const uint8_t*)uniform_ptr(p.bs + ((size_t)tn * p.nks + k0 + k) * 1024);
         return r;
     };
     // copy number j (0 .. DMAS - 1) of a step into LDS buffer buf
@@ -494,6 +511,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
         const int m0 = tm * 256, n0 = tn * 256;
         const int ch0 = m0 + wr * 128 + 4 * g;             // + 32 mi + 8 j
         if constexpr (EPI == EPI_STORE) {
+            // the tile's rows of c, or the unit's own partial (split-K units)
+            float* const cb = p.su_rm > 0 ? p.c + (size_t)blockIdx.x * 65536 : p.c + (long long)n0 * p.ldc + m0;
+            const long long ldc = p.su_rm > 0 ? 256 : p.ldc;
             __syncthreads();                                // every wave is done with the last step's stage
 #pragma unroll
             for (int b = 0; b < 17; ++b) {
@@ -511,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
                         const int rr = 8 * i + (lane >> 3);
                         const float4 v = tget(pb & 1, i);
                         __builtin_nontemporal_store(__builtin_bit_cast(v4f, v),   // read once, by the delta GEMM
-                                                    (v4f*)(p.c + (long long)(n0 + wc * 128 + 32 * ni + rr) * p.ldc + m0 + wr * 128 + 32 * mi + 4 * (lane & 7)));
+                                                    (v4f*)(cb + (long long)(wc * 128 + 32 * ni + rr) * ldc + wr * 128 + 32 * mi + 4 * (lane & 7)));
                     }
                 }
             }
@@ -867,9 +887,60 @@ static int persistent_grid(int total) {
 template <int BFMT, int EPI, int AFMT = FMT_FP4>
 static hipError_t launch(const GemmArgs& a, hipStream_t st) {
     constexpr int NS = (BFMT == FMT_FP4 || BFMT == FMT_BF16) ? 4 : 3;      // the kernel's LDS stages
-    const int grid = persistent_grid(a.mtiles * a.ntiles);
+    const int grid = persistent_grid(a.ttotal > 0 ? a.ttotal : a.mtiles * a.ntiles);
     if (a.nks < NS) k_gemm<AFMT, BFMT, EPI, true><<<grid, 256, 0, st>>>(a);
     else k_gemm<AFMT, BFMT, EPI, false><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+// Sum of the split-K partials: c[tile rows][tile channels] = sum over chunks
+// j = 0 .. p - 1, in that order, of partial j rm + r, for the rm tail tiles
+// r (walk tiles v0 + r).  64 workgroups per tile, one float4 per thread.
+__global__ __launch_bounds__(256) void k_ksum(const float* part, float* c, long long ldc, int mt, int nt, int nks,
+                                              int v0, int rm, int p) {
+    const int r = blockIdx.x >> 6;
+    const int e = ((blockIdx.x & 63) << 8) + threadIdx.x;           // float4 of the tile: row e / 64, channels 4 (e % 64) ..
+    const v4f* src = (const v4f*)part + (size_t)r * 16384 + e;
+    v4f acc = __builtin_nontemporal_load(src);
+    for (int j = 1; j < p; ++j) {
+        const v4f v = __builtin_nontemporal_load(src + (size_t)j * rm * 16384);
+        acc[0] += v[0];
+        acc[1] += v[1];
+        acc[2] += v[2];
+        acc[3] += v[3];
+    }
+    TileWalk w = tile_walk(0, 8, mt, nt, nks);
+    w.base = v0 + r;
+    int tm, tn;
+    w.coords(0, &tm, &tn);
+    __builtin_nontemporal_store(acc, (v4f*)(c + (long long)(tn * 256 + (e >> 6)) * ldc + tm * 256 + 4 * (e & 63)));
+}
+
+// The plain-store GEMM, with the K split `ks` when it has one (partials in
+// `part`, ks.part_bytes()).
+template <int BFMT, int AFMT = FMT_FP4>
+static hipError_t launch_store(const GemmArgs& a, const KSplit& ks, float* part, hipStream_t st) {
+    constexpr int NS = (BFMT == FMT_FP4 || BFMT == FMT_BF16) ? 4 : 3;
+    if (ks.rm == 0) return launch<BFMT, EPI_STORE, AFMT>(a, st);
+    // the plan must fit this GEMM: whole chunks of at least NS steps, one unit per workgroup slot
+    if (!part || ks.p < 2 || a.nks / ks.p < NS || ks.main_tiles + ks.rm != a.mtiles * a.ntiles ||
+        (long long)ks.rm * ks.p > 65535)
+        return hipErrorInvalidValue;
+    if (ks.main_tiles > 0) {
+        GemmArgs m = a;
+        m.ttotal = ks.main_tiles;
+        hipError_t e = launch<BFMT, EPI_STORE, AFMT>(m, st);
+        if (e != hipSuccess) return e;
+    }
+    GemmArgs t = a;
+    t.c = part;
+    t.su_v0 = ks.main_tiles;
+    t.su_rm = ks.rm;
+    t.su_p = ks.p;
+    k_gemm<AFMT, BFMT, EPI_STORE, false><<<ks.rm * ks.p, 256, 0, st>>>(t);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_ksum<<<ks.rm * 64, 256, 0, st>>>(part, a.c, a.ldc, a.mtiles, a.ntiles, a.nks, ks.main_tiles, ks.rm, ks.p);
     return hipGetLastError();
 }
 
@@ -926,7 +997,7 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
         c.ntiles = (int)(q->K_pad / 256);
         c.c = q->bias;
         c.ldc = w->Cop;
-        hipError_t e = launch<FMT_BF16, EPI_STORE, FMT_BF16>(c, st);
+        hipError_t e = launch_store<FMT_BF16, FMT_BF16>(c, q->ks, q->kpart, st);
         if (e != hipSuccess) return e;
     } else if (parts & FWD_CORE) {
         // per-cube core term bias[k] = Q8(core_k) Q4(R) (Q4(core_k) for 4-bit cores)
@@ -936,7 +1007,8 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
         c.ntiles = (int)(q->K_pad / 256);
         c.c = q->bias;
         c.ldc = w->Cop;
-        hipError_t e = q->core_bits == 4 ? launch<FMT_FP4, EPI_STORE>(c, st) : launch<FMT_FP8, EPI_STORE>(c, st);
+        hipError_t e = q->core_bits == 4 ? launch_store<FMT_FP4>(c, q->ks, q->kpart, st)
+                                         : launch_store<FMT_FP8>(c, q->ks, q->kpart, st);
         if (e != hipSuccess) return e;
     }
     if (parts & FWD_DELTA) {
