@@ -58,9 +58,14 @@ def summarize_trace(d: str, out: str, cmd: str) -> None:
     # Per-dispatch durations (DIR/*_kernel_trace.csv) give the median, which
     # the first dispatches (clock still ramping) do not move.
     durs = defaultdict(list)
+    shapes = defaultdict(list)                   # (library kernel, grid) -> durations
     for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            durs[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            durs[r["Kernel_Name"]].append(ns)
+            if "dq::" in r["Kernel_Name"]:
+                grid = r.get("Grid_Size_X") or r.get("Grid_Size") or "?"
+                shapes[(r["Kernel_Name"], grid)].append(ns)
 
     def median_us(name):
         v = sorted(durs.get(name, []))
@@ -74,6 +79,15 @@ def summarize_trace(d: str, out: str, cmd: str) -> None:
         lines.append(f"| `{_short(r['Name'])[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{median_us(r['Name'])} | {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.2f} |")
+    # every launch shape of the library's kernels (a kernel launched with
+    # several grids, such as a GEMM split into a main launch and K-chunk
+    # units, gets a row per grid)
+    lines += ["", "Library kernels by launch grid (work-items in x):", "",
+              "| kernel | grid | calls | average (us) | median (us) | total (ms) |", "|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        lines.append(f"| `{_short(name)[:70]}` | {grid} | {len(v)} | {sum(v) / len(v) / 1e3:.1f} | "
+                     f"{v[len(v) // 2] / 1e3:.1f} | {sum(v) / 1e6:.2f} |")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
