@@ -354,20 +354,25 @@ KSplit plan_ksplit(int mt, int nt, int nks, int ns, int cus, double step_us) {
     const int T = mt * nt, full = T / G * G, rm = T - full;
     if (rm == 0) return k;
     // time saved against one more round of whole tiles: the chunks' share of
-    // the tile, less the partials' HBM round trip (0.13 us per 256 KB unit,
+    // the tile, less the partials' round trip (0.07 us per 256 KB unit,
     // written and read back), about 10 us for the two extra launches, and
     // the part of the last round that hides in the spread of the full
     // rounds' finishing times (the workgroups of a persistent launch end
     // about 4 % of its length apart, and each starts its last-round tile as
-    // it finishes).  Same-box core-term times, FP8 x FP4: 720p FFN down,
-    // 2x2x2 cubes (3 rounds + 32 tiles, 108 steps) 0.642 -> 0.557 ms and the
-    // global cube (20 tiles) 0.149 -> 0.043 ms; 720p FFN up, 1x2x2 cubes
-    // (16 rounds + 8 tiles of 40 steps) 1.094 -> 1.112 ms, so that one, with
-    // a drift term of 41 us against a 38 us saving, keeps one launch.
+    // it finishes).  Same-box core-term times, split against one launch:
+    //   FP8 x FP4, 720p FFN down, 2x2x2 cubes (3 rounds + 32 tiles of 108
+    //     steps): 0.642 -> 0.55 ms; global cube (20 tiles): 0.149 -> 0.043;
+    //   FP8 x FP4, 14B attention projection (1 round + 64 tiles of 40 steps):
+    //     0.140 -> 0.124; 720p FFN up, 4x2x8 cubes (1 round + 68): 0.147 -> 0.128;
+    //   bf16, the same two layers (160 steps of 32 channels): 0.259 -> 0.199
+    //     and 0.268 -> 0.212;
+    //   FP8 x FP4, 720p FFN up, 1x2x2 cubes (16 rounds + 8 tiles of 40 steps):
+    //     1.094 -> 1.112, so that one (drift 41 us against a 38 us saving)
+    //     keeps one launch.
     const double tile = nks * step_us, drift = 0.04 * (full / G) * tile;
     double best = 0;
     for (int q = 2; q * rm <= G && nks / q >= ns; ++q) {
-        const double gain = tile * (1.0 - 1.0 / q) - 0.13 * rm * q - 10.0 - drift;
+        const double gain = tile * (1.0 - 1.0 / q) - 0.07 * rm * q - 10.0 - drift;
         if (gain > best) {
             best = gain;
             k.p = q;
