@@ -588,29 +588,51 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     // -0.0 and drop out exactly); sixteen rows' loads in flight
                     const uint8_t* const pc = buf + (ch % EPC) * (int)sizeof(XT);
                     const int pch = ch / EPC;
+                    // the raw bits of row r's element (the bf16 widening
+                    // happens after the reads: a widening inside the read
+                    // would be a use, and the compiler would wait for each
+                    // read before issuing the next)
                     auto raw1 = [&](int r) -> uint32_t {
-                        if constexpr (sizeof(XT) == 2) return (uint32_t)*(const uint16_t*)(pc + qoff(r, pch)) << 16;
+                        if constexpr (sizeof(XT) == 2) return (uint32_t)*(const uint16_t*)(pc + qoff(r, pch));
                         else return *(const uint32_t*)(pc + qoff(r, pch));
+                    };
+                    auto val1 = [&](uint32_t v, uint32_t sgn) -> float {
+                        if constexpr (sizeof(XT) == 2) return __uint_as_float((v << 16) | sgn);
+                        else return __uint_as_float(v | sgn);
                     };
                     float s0 = -0.0f;
                     int r = rb;
                     // (a cube with all its tokens needs no pad-row masks)
                     const uint32_t full = cnt == g.S ? 0xffffffffu : 0u;
-                    for (; r + 16 <= re; r += 16) {
-                        uint32_t raw[16];
+                    // Batches of sixteen rows: the batch's values are widened
+                    // (and masked) first, then the next batch's reads go out,
+                    // then the sixteen adds of the chain issue back to back
+                    // while those reads are in flight.
+                    uint32_t raw[16];
+                    if (r + 16 <= re) {
 #pragma unroll
                         for (int j = 0; j < 16; ++j) raw[j] = raw1(r + j);
-                        __builtin_amdgcn_sched_barrier(0);     // all sixteen reads issued before the first use
+                    }
+                    for (; r + 16 <= re; r += 16) {
+                        float v[16];
                         if (full) {
 #pragma unroll
-                            for (int j = 0; j < 16; ++j) s0 += __uint_as_float(raw[j]);
+                            for (int j = 0; j < 16; ++j) v[j] = val1(raw[j], 0u);
                         } else {
                             const uint32_t absent = ~(uint32_t)(pres >> r);   // bit j: row r + j has no token
 #pragma unroll
-                            for (int j = 0; j < 16; ++j) s0 += __uint_as_float(raw[j] | ((absent << (31 - j)) & 0x80000000u));
+                            for (int j = 0; j < 16; ++j) v[j] = val1(raw[j], (absent << (31 - j)) & 0x80000000u);
                         }
+                        if (r + 32 <= re) {
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) raw[j] = raw1(r + 16 + j);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) s0 += v[j];
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    for (; r < re; ++r) s0 += __uint_as_float(raw1(r) | (((pres >> r) & 1) ? 0u : 0x80000000u));
+                    for (; r < re; ++r) s0 += val1(raw1(r), ((pres >> r) & 1) ? 0u : 0x80000000u);
                     if ((cnt & (cnt - 1)) == 0) s0 *= inv_pow2(cnt);   // exact power-of-two scaling
                     else s0 = __fdiv_rn(s0, (float)cnt);
                     float amax = row16_max(fabsf(s0));
