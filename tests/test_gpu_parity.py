@@ -165,6 +165,43 @@ def test_core_term_k_split(dqm, case):
     _say(f"core K split {case}: rel err {err:.2e} worst row {row:.2e}")
 
 
+# The activation pass's channel split: segments whose blocks fill at most
+# half of the CUs run each block as 2-8 parts of its channel chunks, and U is
+# the bf16 of the parts' fp32 sums in part order.  Every form of the pass:
+# one pass (bf16 four-token cubes and the general fp32 form), two phases
+# (one 64-token cube per block, two 24-token cubes), a wave per cube
+# (16 tokens), eighths (8 tokens), cubes of more than 64 tokens, one-token
+# cubes, two frame segments, no low-rank branch, rank 96 (one quantizer
+# group), FP4 cores with 64-channel groups, bf16 cores.
+CSPLIT = [
+    # T, H, W, cube, Ci, Co, rank, dtype, core bits, core group
+    (3, 10, 12, (1, 2, 2), 1024, 256, 32, "bf16", 8, 32),
+    (3, 10, 12, (1, 2, 2), 512, 256, 32, "f32", 8, 32),
+    (4, 8, 16, (4, 2, 8), 2048, 256, 32, "bf16", 8, 32),
+    (2, 6, 8, (2, 3, 4), 1024, 128, 16, "bf16", 8, 32),
+    (4, 8, 8, (4, 1, 4), 1024, 256, 32, "bf16", 8, 32),
+    (4, 6, 8, (2, 2, 2), 1024, 256, 32, "f32", 8, 32),
+    (3, 9, 10, (3, 9, 10), 1024, 128, 16, "bf16", 8, 32),
+    (2, 5, 6, (1, 1, 1), 1024, 128, 32, "bf16", 8, 32),
+    (5, 6, 8, (2, 2, 2), 1024, 256, 32, "bf16", 8, 32),
+    (3, 10, 12, (1, 2, 2), 1024, 256, 0, "bf16", 8, 32),
+    (3, 10, 12, (1, 2, 2), 1024, 256, 96, "bf16", 8, 32),
+    (4, 8, 16, (4, 2, 8), 2048, 256, 32, "bf16", 4, 64),
+    (3, 10, 12, (1, 2, 2), 1024, 256, 32, "bf16", 16, 32),
+]
+
+
+@pytest.mark.parametrize("case", CSPLIT, ids=[f"{c[0]}x{c[1]}x{c[2]}_c{'x'.join(map(str, c[3]))}_ci{c[4]}_r{c[6]}_{c[7]}"
+                                              f"_core{c[8]}g{c[9]}" for c in CSPLIT])
+def test_activation_channel_split(dqm, case):
+    T, H, W, cube, Ci, Co, rank, dtype, bits, grp = case
+    _say(f"case activation channel split {case}")
+    L = _layer(dqm, T, H, W, cube, Ci, Co, rank, dtype, xseed=T * 100 + Ci + 7, wseed=Co + 17,
+               n_out=4, core_bits=bits, core_group=grp)
+    err, row = _full_compare(dqm, L)
+    _say(f"activation channel split {case}: rel err {err:.2e} worst row {row:.2e}")
+
+
 def test_core_group_errors(dqm):
     wt = synth.make_weight(96, 64, seed=3, dtype="f32")
     weights = dqm.dq_prepare_weights_lowrank(wt, None, None)

@@ -90,6 +90,7 @@ void free_qact(dq_qact* q) {
     (void)hipFree(q->coref);
     (void)hipFree(q->part);
     (void)hipFree(q->kpart);
+    (void)hipFree(q->upart);
     (void)hipFree(q->cbf);
     (void)hipFree(q->rbf);
     delete q;
@@ -443,14 +444,23 @@ dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, in
     q->K_pad = krow;
     if (!mul_ok(q->Nslot_pad, q->Kp, lim) || !mul_ok(q->K_pad, q->Cop, lim) || !mul_ok(max_partials, q->Kp, lim))
         return fail(DQ_ERR_SHAPE, "workspace too large");
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, w->device) != hipSuccess) cus = 256;
+    // the activation pass's channel split: the U partials of the largest
+    // segment it may split (blocks of 64 slots, or of whole cubes up to 64
+    // tokens)
+    q->upart_rows = 0;
+    for (int i = 0; i < q->nseg; ++i) {
+        const dq_segment& sg = q->seg[i];
+        const int64_t nblocks = sg.core_mode == 0 ? (sg.g.K + 64 / sg.g.S - 1) / (64 / sg.g.S) : (sg.g.Nslot + 63) / 64;
+        if (nblocks * 2 <= cus) q->upart_rows = std::max<int64_t>(q->upart_rows, sg.g.Nslot);
+    }
     // the core GEMM's K split (one-token cubes with FP8 or FP4 cores run no
     // core GEMM).  Per-step times of a tile with every CU busy: FP8 x FP4
     // steps of 128 channels 1.6 us, FP4 x FP4 1.0 us, bf16 steps of 32
     // channels 0.8 us (720p FFN up-projection).
     q->ks = KSplit{};
     if (!(S == 1 && core_bits != 16)) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, w->device) != hipSuccess) cus = 256;
         const int nks = (int)(core_bits == 16 ? q->Kp / 32 : q->Kp / 128);
         q->ks = plan_ksplit((int)(q->Cop / 256), (int)(q->K_pad / 256), nks, core_bits == 8 ? 3 : 4, cus,
                             core_bits == 8 ? 1.6 : (core_bits == 4 ? 1.0 : 0.8));
@@ -499,6 +509,9 @@ dq_status dq_qact_create_ex(const dq_weights* w, dq_geom geom, int32_t core_grou
             return hip_fail(e, "hipMalloc workspace");
     }
     if (q->ks.rm > 0 && (e = dalloc(&q->kpart, q->ks.part_bytes() / 4, &q->bytes)) != hipSuccess)
+        return hip_fail(e, "hipMalloc workspace");
+    if (q->upart_rows > 0 && q->rp > 0 &&
+        (e = dalloc(&q->upart, (size_t)(QMAXPARTS * q->upart_rows * q->rp), &q->bytes)) != hipSuccess)
         return hip_fail(e, "hipMalloc workspace");
     if (core_bits == 16) {                          // bf16 cores: Q4(R) as bf16 for the bf16 GEMM
         if ((e = dalloc(&q->cbf, (size_t)(q->K_pad * q->Kp), &q->bytes)) != hipSuccess ||

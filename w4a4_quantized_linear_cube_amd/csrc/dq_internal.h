@@ -117,6 +117,21 @@ struct KSplit {
     int main_tiles = 0, rm = 0, p = 1;
     size_t part_bytes() const { return (size_t)rm * (size_t)p * 65536 * 4; }
 };
+// Channel split of an activation-pass segment with few blocks (a frame
+// segment of a clipped last frame group: a few dozen blocks of up to 108
+// chunks each would keep most CUs idle): the largest part count up to
+// QMAXPARTS that divides its nchunks chunks, leaves at least 4 chunks per
+// part and keeps nblocks x parts within the CUs; 1 (no split) when the
+// blocks fill more than half of the CUs.
+constexpr int QMAXPARTS = 8;
+inline int quant_kparts(long long nblocks, int nchunks, int cus) {
+    if (nblocks * 2 > cus) return 1;
+    int best = 1;
+    for (int p = 2; p <= QMAXPARTS; ++p)
+        if (nchunks % p == 0 && nchunks / p >= 4 && nblocks * p <= cus) best = p;
+    return best;
+}
+
 // The split of an mt x nt tile GEMM with nks K steps of about step_us each
 // (per tile, with every CU busy) on `cus` CUs, ring depth ns: the chunk count
 // that saves the most time (each chunk at least ns steps), or none.
@@ -177,6 +192,8 @@ struct dq_qact {
     float* sink = nullptr;     // [512]              target of the GEMM's discarded 16-byte stores
     float* coref = nullptr;    // [K_pad][Kp]        fp32 cores (segments of core_mode 1), cube rows
     float* part = nullptr;     // [K*nblk][Kp]       fp32 block partials (core_mode 1; the segments take turns)
+    int64_t upart_rows = 0;    // largest slot count of a segment the activation pass may split by channels
+    float* upart = nullptr;    // [QMAXPARTS][upart_rows][rp] fp32 U partials of such a segment (upart_rows > 0, rp > 0)
     dq::KSplit ks{};           // K split of the core GEMM's last round (set by plan_qact)
     float* kpart = nullptr;    // [ks.rm * ks.p][256][256] fp32 K-chunk partials of that round (ks.rm > 0)
     size_t bytes = 0;

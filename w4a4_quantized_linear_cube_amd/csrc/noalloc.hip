@@ -80,7 +80,8 @@ extern "C" dq_status dq_linear_noalloc(const dq_weights* w, const void* x_dev, d
     // layout: zero page, sink, codes and scales (cleared below when Ci is
     // not a multiple of 128), U, per-cube term, slot table, fp32 cores and
     // block partials (cubes of more than 64 tokens), the core GEMM's K-chunk
-    // partials (the same split as dq_qact_create's, so the same results)
+    // partials and the activation pass's U partials (the same splits as
+    // dq_qact_create's, so the same results)
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     const size_t o_zero = take(512), o_sink = take(2048);
@@ -93,6 +94,8 @@ extern "C" dq_status dq_linear_noalloc(const dq_weights* w, const void* x_dev, d
     const size_t o_coref = max_partials ? take((size_t)(q.K_pad * q.Kp * 4)) : 0;
     const size_t o_part = max_partials ? take((size_t)(max_partials * q.Kp * 4)) : 0;
     const size_t o_kpart = q.ks.rm ? take(q.ks.part_bytes()) : 0;
+    const bool upart = q.upart_rows > 0 && q.rp > 0;
+    const size_t o_upart = upart ? take((size_t)(QMAXPARTS * q.upart_rows * q.rp * 4)) : 0;
     if (off > NOALLOC_SCRATCH_BYTES)
         return fail(DQ_ERR_SHAPE, "this layer needs " + std::to_string(off) + " bytes of scratch; the static scratch of "
                                   "dq_linear_noalloc holds " + std::to_string(NOALLOC_SCRATCH_BYTES));
@@ -113,6 +116,7 @@ extern "C" dq_status dq_linear_noalloc(const dq_weights* w, const void* x_dev, d
     q.coref = max_partials ? (float*)(base + o_coref) : nullptr;
     q.part = max_partials ? (float*)(base + o_part) : nullptr;
     q.kpart = q.ks.rm ? (float*)(base + o_kpart) : nullptr;
+    q.upart = upart ? (float*)(base + o_upart) : nullptr;
     hipError_t e;
     // The activation pass writes every code and scale of channels below Ci;
     // the padding channels up to Kp must hold zero codes and scale codes

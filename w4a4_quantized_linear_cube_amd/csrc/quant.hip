@@ -56,6 +56,14 @@ struct QuantArgs {
     int core_g64;             // cores: one exponent per 64 channels (the maximum of two 32-channel groups)
     int core_fp4;             // cores as MX-FP4 (the FP4 layout in cq) instead of MX-FP8
     uint16_t* cbf;            // bf16 cores, step-major (off_bf16) (16-bit cores), else null
+    // Channel split of a segment with few blocks: block b's chunks are taken
+    // by kparts workgroup blocks (nblocks counts those), part j taking the
+    // j-th run of chunks; each part's U sum goes to upart[j][slot][rank]
+    // (fp32, urows rows per part) for a later sum in part order.  kparts 1:
+    // one part, U stored here as bf16.
+    int kparts;
+    long long urows;
+    float* upart;
 };
 
 // bf16 bits of n consecutive core values (n = 2, 4, 8), packed for one store
@@ -72,13 +80,17 @@ __device__ __forceinline__ uint16_t* cbf_at(uint16_t* cbf, long long k, long lon
 __device__ __forceinline__ int qoff(int r, int c) { return r * QROWB + ((c ^ (r & 15)) << 4); }
 
 // Block b: its first slot, first cube, rows and cubes.  Cubes of at most 64
-// tokens: whole cubes (64 / S of them); larger cubes: 64 slots.
+// tokens: whole cubes (64 / S of them); larger cubes: 64 slots.  With a
+// channel split, workgroup block v is part v % kparts of block v / kparts.
 struct QBlock {
     long long slot0, k_first;
     int nrows, ncores;
+    int part;
 };
-__device__ __forceinline__ QBlock qblock(const QuantArgs& a, long long b) {
+__device__ __forceinline__ QBlock qblock(const QuantArgs& a, long long v) {
     QBlock q;
+    const long long b = v / a.kparts;
+    q.part = (int)(v - b * a.kparts);
     if (a.core_mode == 0) {
         const int cpb = QROWS / a.g.S;
         q.k_first = b * cpb;
@@ -333,7 +345,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     const Geom& g = a.g;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int nchunks = (a.Ci + CC - 1) / CC;
+    const int nchunks = (a.Ci + CC - 1) / CC / a.kparts;   // chunks per (part of a) block
     const long long nmine = a.nblocks > (long long)blockIdx.x ? (a.nblocks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
     if (nmine == 0) return;
     const long long total = nmine * nchunks;
@@ -373,7 +385,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     // the same number of copies.
     const int cw = __builtin_amdgcn_readfirstlane(wave - 1);
     long long i_f = 0, s_f = 0;
-    int c_f = 0;
+    int c_f = 0, clo_f = 0;          // chunk within the part; the part's first chunk
     int tokr[QDMA];
     // tokens of a block's rows: scalar loads (they count on lgkmcnt, so the
     // copy counter keeps tracking the copies alone), then each lane picks its row
@@ -382,6 +394,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     auto load_toks = [&](long long i) {
         int t[QDMA][4];
         const QBlock Bn = qblock(a, blockIdx.x + min(i, nmine - 1) * gridDim.x);
+        clo_f = Bn.part * nchunks;
 #pragma unroll
         for (int j = 0; j < QDMA; ++j)
 #pragma unroll
@@ -396,7 +409,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
     auto issue = [&]() {
         const uint32_t stage = lds0 + (uint32_t)(s_f % QNBUF) * STAGE;
         const uint32_t base = stage + cw * (QCHUNK / 2);
-        const int c0 = c_f * CC;
+        const int c0 = (clo_f + c_f) * CC;
 #pragma unroll
         for (int j = 0; j < QDMA; ++j) {
             const int r = 32 * cw + 4 * j + (lane >> 4);
@@ -516,7 +529,11 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int row = rt * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                            if (row < B.nrows) a.u[(B.slot0 + row) * a.rp + ct * 32 + (lane & 31)] = bf16_rne(uacc[rt][ct][e]);
+                            if (row >= B.nrows) continue;
+                            if (a.kparts == 1)
+                                a.u[(B.slot0 + row) * a.rp + ct * 32 + (lane & 31)] = bf16_rne(uacc[rt][ct][e]);
+                            else
+                                a.upart[((long long)B.part * a.urows + B.slot0 + row) * a.rp + ct * 32 + (lane & 31)] = uacc[rt][ct][e];
                         }
                         uacc[rt][ct] = (v16f){};
                     }
@@ -550,7 +567,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const int qq = t & 3, pr = t >> 2;
                     const int r = pr / NGC, gc = pr - r * NGC;
                     const long long k = min((B.slot0 + r) / g.S, g.K - 1);
-                    const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + (c * CC + gc * 32) + 8 * qq);
+                    const float4* cp = (const float4*)(a.coref + k * (long long)a.Kp + ((B.part * nchunks + c) * CC + gc * 32) + 8 * qq);
                     kn[n][0] = cp[0];
                     kn[n][1] = cp[1];
                 }
@@ -561,7 +578,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             barrier();
             const long long s = SP * u + qgrp;
             const bool have = s < total;
-            const int c0 = c * CC;
+            const int c0 = (B.part * nchunks + c) * CC;
             const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
             float(*const cs_)[CC] = core_s[qgrp];
             // ---- phase 1 (CM 2): the cores, one (cube, channel pair) per
@@ -919,7 +936,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
         barrier();
         const long long s = SP * u + qgrp;
         if (s >= total) continue;
-        const int c0 = c * CC;
+        const int c0 = (B.part * nchunks + c) * CC;
         const uint8_t* buf = xbuf + (int)(s % QNBUF) * STAGE;
         // ---- quantizer: one (cube, group, quarter) per thread
         const long long nks = a.Kp / 128;
@@ -1367,7 +1384,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     f4_cq = toff_fp8(kt, 0, 2 * f4_gc + (f4_qq >> 1)) + 8 * (f4_qq & 1);
                     f4_cs = toff_scale(kt, f4_gc);
                 }
-                if (qtid < ntask && c0 + 32 * f4_gc < a.Ci) task4(buf, c, dq_t, ds_t, cq_t, cs_t);
+                if (qtid < ntask && c0 + 32 * f4_gc < a.Ci) task4(buf, B.part * nchunks + c, dq_t, ds_t, cq_t, cs_t);
             } else {
             for (int t = qtid; t < ntask; t += 256) {
                 if (full) task(t, std::true_type{});
@@ -1815,10 +1832,19 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
     a.cbf = q->cbf ? q->cbf + sg.krow0 * q->Kp : nullptr;
     if (a.core_fp4) a.cq = cq4;
     const long long cpb = QROWS / g.S;
-    a.nblocks = sg.core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;
+    const long long nblocks = sg.core_mode == 0 ? (g.K + cpb - 1) / cpb : (g.Nslot + QROWS - 1) / QROWS;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
+    // few blocks: split their channel chunks over several workgroups (the U
+    // partials then summed in part order below)
+    const int cc = x_bf16 ? 128 : 64;                  // channels per chunk
+    int kparts = quant_kparts(nblocks, (int)((q->Ci + cc - 1) / cc), cus);
+    if (q->rp > 0 && !(q->upart && g.Nslot <= q->upart_rows)) kparts = 1;
+    a.kparts = kparts;
+    a.urows = g.Nslot;
+    a.upart = q->upart;
+    a.nblocks = nblocks * kparts;
     const unsigned blocks = (unsigned)std::min<long long>(a.nblocks, cus);   // persistent: one workgroup per CU
     const int nct = q->rp / 32;
     // one-pass quantizer for blocks of 7 or more cubes (a thread per (cube,
@@ -1853,6 +1879,10 @@ static hipError_t launch_quantize_segment(const dq_weights* w, const void* x, in
     };
     if (x_bf16) by_rank(uint16_t{});
     else by_rank(float{});
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || kparts == 1 || q->rp == 0) return e;
+    // U = bf16 of the parts' fp32 sums, added in part order
+    k_u_combine<<<(unsigned)((g.Nslot * q->rp + 255) / 256), 256, 0, st>>>(q->upart, kparts, g.Nslot, g.Nslot, q->rp, a.u);
     return hipGetLastError();
 }
 
