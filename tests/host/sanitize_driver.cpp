@@ -155,6 +155,56 @@ int main() {
         fw.wfmt = 2;
         EXPECT(dq::plan_qact(&fw, dq_geom{2, 2, 2, 1, 1, 1}, 32, 8, &q, &mp) == DQ_ERR_INVALID_ARG);
     }
+    // ---- the core GEMM's last-round K split: structure over many shapes, and
+    // the decisions on the 720p and 14B layers' core GEMMs (FP8 x FP4, 256 CUs)
+    for (int mt = 1; mt <= 60; mt += 7)
+        for (int nt = 1; nt <= 90; nt += 11)
+            for (int nks : {1, 3, 8, 40, 108, 160})
+                for (int ns : {3, 4}) {
+                    const dq::KSplit k = dq::plan_ksplit(mt, nt, nks, ns, 256, 1.6);
+                    if (k.rm == 0) continue;
+                    EXPECT(k.main_tiles + k.rm == mt * nt && k.main_tiles % 256 == 0 && k.rm < 256);
+                    EXPECT(k.p >= 2 && k.rm * k.p <= 256 && nks / k.p >= ns);
+                }
+    {
+        const dq::KSplit up = dq::plan_ksplit(54, 76, 40, 3, 256, 1.6);        // FFN up, 1x2x2: one launch
+        EXPECT(up.rm == 0);
+        const dq::KSplit d222 = dq::plan_ksplit(20, 40, 108, 3, 256, 1.6);     // FFN down, 2x2x2
+        EXPECT(d222.main_tiles == 768 && d222.rm == 32 && d222.p == 8);
+        const dq::KSplit glob = dq::plan_ksplit(20, 1, 108, 3, 256, 1.6);      // FFN down, global cube
+        EXPECT(glob.main_tiles == 0 && glob.rm == 20 && glob.p == 11);
+        const dq::KSplit attn = dq::plan_ksplit(20, 16, 40, 3, 256, 1.6);      // 14B attention, 2x2x2
+        EXPECT(attn.main_tiles == 256 && attn.rm == 64 && attn.p == 4);
+        const dq::KSplit u428 = dq::plan_ksplit(54, 6, 40, 3, 256, 1.6);       // FFN up, 4x2x8
+        EXPECT(u428.main_tiles == 256 && u428.rm == 68 && u428.p == 3);
+        EXPECT(dq::plan_ksplit(6, 32, 12, 3, 256, 1.6).rm == 0);             // Wan 1.3B: one round of 192 tiles, short K
+    }
+    // ---- the activation pass's channel split: the part count divides the
+    // chunks, leaves at least 4 per part and fits the CUs; the decisions on
+    // the 21-frame layers' last-frame segments and their main segments
+    for (long long nb = 1; nb <= 300; nb += 13)
+        for (int nch = 1; nch <= 120; nch += 7) {
+            const int p = dq::quant_kparts(nb, nch, 256);
+            EXPECT(p >= 1 && p <= dq::QMAXPARTS && nch % p == 0);
+            EXPECT(p == 1 || (nch / p >= 4 && nb * p <= 256 && nb * 2 <= 256));
+        }
+    EXPECT(dq::quant_kparts(57, 40, 256) == 4);      // 4x2x8 / 4x1x4, last frame (5120 bf16 channels)
+    EXPECT(dq::quant_kparts(58, 108, 256) == 4);     // FFN down 2x2x2, last frame (13824 channels)
+    EXPECT(dq::quant_kparts(1125, 40, 256) == 1);    // 4x2x8, the other 20 frames
+    EXPECT(dq::quant_kparts(2, 17, 256) == 1);       // 17 chunks: no divisor
+    {   // a clipped last frame group: its small segment gets U partials
+        dq_weights fu;
+        fu.Ci = 5120;
+        fu.Co = 512;
+        fu.Kp = 5120;
+        fu.Cop = 512;
+        fu.rank = 32;
+        fu.rp = 32;
+        dq_qact q{};
+        int64_t mp = 0;
+        EXPECT(dq::plan_qact(&fu, dq_geom{21, 45, 80, 4, 2, 8}, 32, 8, &q, &mp) == DQ_OK);
+        EXPECT(q.nseg == 2 && q.upart_rows == q.seg[1].g.Nslot && q.seg[1].g.Nslot == 23 * 10 * 16);
+    }
     std::printf("host sanitize driver: %lld geometries planned, %d failures\n", planned, failures);
     return failures ? 1 : 0;
 }
