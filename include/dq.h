@@ -290,7 +290,8 @@ dq_status dq_orbit_act_export(const dq_orbit_act* a, uint8_t* codes_host, float*
  * capture, tight serving loops, harnesses that forbid hipMalloc): dq_linear
  * for the geometry `geom` with MX-FP8 cores in groups of 32, without a
  * dq_qact.  The activation state (codes, scales, U, per-cube core term, slot
- * table) lives in a fixed per-device array of 128 MiB that the library holds
+ * table, and the fp32 partial sums of launches split over more workgroups)
+ * lives in a fixed per-device array of 128 MiB that the library holds
  * on every GPU it runs on until the process ends; the call allocates nothing
  * and calls no allocating routine.  Same arguments and layouts as
  * dq_quantize_act and dq_linear_forward (x_dev [N][Ci] 16-byte aligned,
