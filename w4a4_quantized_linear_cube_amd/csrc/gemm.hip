@@ -9,13 +9,15 @@
 // slot) adds U L2, adds its cube's core term in the epilogue and scatters rows
 // to token order.  Both are V_MFMA_SCALE_F32_32X32X64_F8F6F4 contractions
 // over Ci with the E8M0 block scales applied inside the instruction, fp32
-// accumulation.
+// accumulation.  The core GEMM's last, partly filled round may run split
+// along K: K-chunk units write fp32 partials that k_ksum adds in order.
 //
 // Operand roles: the MFMA's A operand is Q4(R) (its rows are output
 // channels) and its B operand is the activation (rows are slots or cubes), so
 // the accumulator tile is the transposed output: each lane holds, for one
-// token, runs of four consecutive output channels, which the epilogue writes
-// as 16-byte stores straight into the token's output row.
+// token, runs of four consecutive output channels.  The epilogues pass them
+// through LDS and store 128-byte row segments (the general token epilogue
+// stores the 16-byte runs directly).
 //
 // Work decomposition: a 256-thread workgroup computes a 256-channel x
 // 256-slot tile; its four waves each own 128 x 128 (4 x 4 MFMA tiles of
