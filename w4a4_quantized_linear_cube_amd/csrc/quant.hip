@@ -285,14 +285,15 @@ __device__ __forceinline__ float2 qconv2(uint2 d, uint32_t sgn) {
 }
 
 // Persistent activation pass.  Workgroup w takes the 64-slot blocks w, w + G,
-// w + 2G, ... and walks each block's channels in chunks of 256 bytes per row;
-// the chunks of all its blocks form one stream.  Waves 1-2 copy chunks
+// w + 2G, ... and walks each block's channels in chunks of 256 bytes per row
+// (with a channel split, those are parts of blocks, each a run of the
+// block's chunks); the chunks of all its blocks form one stream.  Waves 1-2 copy chunks
 // straight into an LDS ring (global_load_lds, one 16-byte piece per lane,
 // absent rows and channels from a zero page) up to seven chunks ahead, across
 // block boundaries, together with the chunk's slice of L1; they issue nothing
 // else, so their copy counters track the ring exactly.  Wave 0 accumulates
 // U = bf16(X) L1 with 32x32x16 bf16 MFMAs from the stage and stores it after
-// a block's last chunk.  Waves 3-6 quantize: one
+// a block's last chunk (a part's fp32 sum, with a channel split).  Waves 3-6 quantize: one
 // (cube, 32-channel group, quarter) per thread, the quad of a group's four
 // quarters sharing its maxima by DPP: the cube's core (fp32 sum in slot
 // order, then the division), its FP8 codes, each row's delta FP4 codes.
