@@ -3,7 +3,8 @@
 One step = the whole hot path on one batch of synthetic activations already
 resident in HBM: the activation pass (cube cores, deltas, MX codes, X L1)
 followed by the forward GEMMs (core term, delta term, low-rank branch,
-broadcast, token-order fp32 output).  Prints one JSON line.
+broadcast, token-order fp32 output), one dq_linear call, timed with HIP
+events around the timed steps only.  Prints one JSON line.
 
 value  = effective TOPS of the whole step, 2 N Ci Co / t_step (the dense
          layer's work; the method's own work differs, see 'work' below).
@@ -13,7 +14,8 @@ roofline = the dominant kernel, the delta GEMM (dq_delta_term: one launch of
          epilogue): algorithmic FP4 flops per launch, 2 N Ci Co (one row per
          token: the pad slots of clipped cubes are executed but not counted;
          their share is reported as pad_slot_waste), / its average duration
-         from HIP events on the launch stream, against the dense FP4 peak;
+         from HIP events on the launch stream (a second run of the steps,
+         with events between the phases), against the dense FP4 peak;
          traffic from the committed rocprofv3 counter summary of the same
          kernel source, else null.  With one-token cubes the delta term is
          one FP8 x FP4 GEMM over the cubes and is rated against the FP8 peak.
