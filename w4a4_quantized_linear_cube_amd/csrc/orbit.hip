@@ -204,18 +204,32 @@ __global__ __launch_bounds__(256) void k_orbit_rows(RowsArgs a) {
     __syncthreads();
 
     if (t < nb) {                                      // wave 0 (nb <= 60)
+        // the block's 256 squares added in channel order (from +0, which
+        // leaves the first square unchanged), 32 at a time, the next 32
+        // channels' reads in flight meanwhile (one read at a time left each
+        // read's latency in the chain)
         const float4* rb = (const float4*)(rot + 256 * t);
-        float4 q = rb[0];
-        float s2 = q.x * q.x;
-        s2 = s2 + q.y * q.y;
-        s2 = s2 + q.z * q.z;
-        s2 = s2 + q.w * q.w;
-        for (int i = 1; i < 64; ++i) {
-            q = rb[i];
-            s2 = s2 + q.x * q.x;
-            s2 = s2 + q.y * q.y;
-            s2 = s2 + q.z * q.z;
-            s2 = s2 + q.w * q.w;
+        float4 q[8], n[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = rb[i];
+        float s2 = 0.0f;
+#pragma unroll
+        for (int b8 = 0; b8 < 8; ++b8) {
+            if (b8 + 1 < 8) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) n[i] = rb[8 * (b8 + 1) + i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                s2 = s2 + q[i].x * q[i].x;
+                s2 = s2 + q[i].y * q[i].y;
+                s2 = s2 + q[i].z * q[i].z;
+                s2 = s2 + q[i].w * q[i].w;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = n[i];
         }
         part[t] = s2;
     }
