@@ -72,3 +72,47 @@ def test_noalloc_rejects_layers_beyond_the_scratch(dqm, lib):
     assert st == 2, st
     msg = lib.dq_last_error().decode()
     assert "bytes of scratch" in msg, msg
+
+
+def test_noalloc_graph_replays(dqm):
+    """dq_linear_noalloc captured into a HIP graph (the callers it is for) and
+    replayed three times, with an eager call on another input and
+    synchronizations between the replays: every replay's output, and every
+    eager output, is bit for bit the first eager call's on the same input.
+    The layer's core GEMM runs split along K (a kernel of partials, then
+    their sum)."""
+    T, H, W, cube, Ci, Co, rank, dtype = (3, 16, 16, (1, 2, 2), 2176, 512, 32, "bf16")
+    _say(f"case no-alloc graph: {T}x{H}x{W} cube {cube} Ci {Ci} Co {Co} rank {rank} {dtype}")
+    x = synth.make_activation(T, H, W, Ci, seed=990, dtype=dtype, n_outliers=4).to(DEV)
+    x2 = synth.make_activation(T, H, W, Ci, seed=991, dtype=dtype, n_outliers=4).to(DEV)
+    wt = synth.make_weight(Ci, Co, seed=992, dtype=dtype)
+    l1, l2 = _random_factors(Ci, Co, rank, 993)
+    weights = dqm.dq_prepare_weights_lowrank(wt, l1, l2)
+    geom = (T, H, W) + tuple(cube)
+    N = T * H * W
+    nan = float("nan")
+    y_ref = torch.full((N, Co), nan, device=DEV)
+    y_ref2 = torch.full((N, Co), nan, device=DEV)
+    dqm.dq_linear_noalloc(weights, x, geom, y_ref)          # first call on the device: outside the capture
+    dqm.dq_linear_noalloc(weights, x2, geom, y_ref2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y_ref).any().item() and not torch.isnan(y_ref2).any().item(), "unwritten outputs"
+    y = torch.full((N, Co), nan, device=DEV)
+    y2 = torch.full((N, Co), nan, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s, capture_error_mode="thread_local"):
+        dqm.dq_linear_noalloc(weights, x, geom, y)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.fill_(nan)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(y), _bits(y_ref)), f"replay {i}: outputs differ from the eager call"
+        y2.fill_(nan)
+        dqm.dq_linear_noalloc(weights, x2, geom, y2)      # eager work between replays, on the same array
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(y2), _bits(y_ref2)), f"eager call after replay {i}: outputs differ"
+    _say("no-alloc graph: three replays bit-identical to the eager call")
