@@ -1194,6 +1194,11 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 uint32_t code[NTW];
                 int exq[NTW];
                 bool live[NTW];
+                // a lane's tasks share their (group, quarter), so their core slice is read once
+                const int qq_l = lane & 3, gc_l = (lane >> 2) % NGC;
+                const float4 k0 = *(const float4*)&cs_[cr][gc_l * 32 + qq_l * 8];
+                const float4 k1 = *(const float4*)&cs_[cr][gc_l * 32 + qq_l * 8 + 4];
+                const float core[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
                 for (int n = 0; n < NTW; ++n) {
                     const int t = lane + 64 * n;
@@ -1204,9 +1209,6 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     live[n] = j < S && G * 32 < a.Ci && ((pres >> rr) & 1);
                     float v[8];
                     qload8<XT>(buf, rr, gc, qq, 0u, v);
-                    const float4 k0 = *(const float4*)&cs_[cr][gc * 32 + qq * 8];
-                    const float4 k1 = *(const float4*)&cs_[cr][gc * 32 + qq * 8 + 4];
-                    const float core[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
                     float dv[8];
                     float amax = 0.0f;
 #pragma unroll
@@ -1224,6 +1226,45 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, dv[6], dv[7], sc, 3);
                     code[n] = w;
                 }
+                if constexpr (NTW == 4) {
+                    // four groups per chunk: a lane's tasks are rows j0, j0 + 4,
+                    // j0 + 8, j0 + 12 (j0 = lane / 16) of its (group, quarter),
+                    // and a quad holds the four quarters of those rows.  A 4 x 4
+                    // transpose inside the quad (lane exchanges at distance 1,
+                    // then 2; a lane keeps slot n when bit d of n equals its own
+                    // and takes the partner's slot n ^ d otherwise) gives lane qq
+                    // row j0 + 4 qq's whole 16-byte group code: one store per
+                    // lane, and the row's scale code from the same lane.
+                    auto xchg = [&](uint32_t* v, auto dd, auto cc) {
+                        constexpr int d = decltype(dd)::value, ctrl = decltype(cc)::value;
+                        const bool hi = (qq_l & d) != 0;
+#pragma unroll
+                        for (int n = 0; n < 4; ++n) {
+                            if (n & d) continue;                       // slot pair (n, n + d)
+                            const uint32_t send = hi ? v[n] : v[n + d];
+                            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, ctrl, 0xF, 0xF, true);
+                            v[n] = hi ? recv : v[n];
+                            v[n + d] = hi ? v[n + d] : recv;
+                        }
+                    };
+                    xchg(code, std::integral_constant<int, 1>{}, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+                    xchg(code, std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+                    // liveness and scale of a row are the same in the four lanes of its quad
+                    const bool lv = qq_l == 0 ? live[0] : qq_l == 1 ? live[1] : qq_l == 2 ? live[2] : live[3];
+                    const int ex = qq_l == 0 ? exq[0] : qq_l == 1 ? exq[1] : qq_l == 2 ? exq[2] : exq[3];
+                    const int j = (lane >> 4) + 4 * qq_l;
+                    if (lv) {
+                        if (tile64) {                              // 32-bit offsets in the block's tile
+                            const int G = (c0 >> 5) + gc_l, rt = (int)(B.slot0 & 255) + rb + j;
+                            *(uint4*)(dq_t + toff_fp4(rt, G)) = make_uint4(code[0], code[1], code[2], code[3]);
+                            ds_t[toff_scale(rt, G)] = (uint8_t)(ex + 127);
+                        } else {
+                            const long long G = (c0 >> 5) + gc_l, sl = B.slot0 + rb + j;
+                            *(uint4*)(a.dq + off_fp4(sl, G, nks)) = make_uint4(code[0], code[1], code[2], code[3]);
+                            a.ds[off_scale(sl, G, nks)] = (uint8_t)(ex + 127);
+                        }
+                    }
+                } else {
 #pragma unroll
                 for (int n = 0; n < NTW; ++n) {
                     if (!live[n]) continue;
@@ -1239,6 +1280,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                         *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
                         if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
                     }
+                }
                 }
             }
         } else if constexpr (CM == 4) {
