@@ -803,6 +803,44 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                 const bool tile64 = B.nrows == 64 && (B.slot0 & 63) == 0;
                 uint8_t* const dq_t = a.dq + (size_t)(B.slot0 >> 8) * (size_t)nks * 16384;
                 uint8_t* const ds_t = a.ds + (size_t)(B.slot0 >> 8) * (size_t)nks * 1024;
+                if constexpr (NT2 == 4) {
+                    // four groups per chunk: a thread's tasks are rows r0, r0 + 16,
+                    // r0 + 32, r0 + 48 (r0 = thread / 16) of its (group, quarter),
+                    // and a quad holds the four quarters of those rows; a 4 x 4
+                    // transpose inside the quad (exchanges at distance 1, then 2)
+                    // gives lane qq row r0 + 16 qq's whole 16-byte group code, one
+                    // store per lane, and that row's scale code
+                    const int qq_l = qtid & 3, gc_l = (qtid >> 2) & 3;
+                    auto xchg = [&](uint32_t* v, auto dd, auto cc) {
+                        constexpr int d = decltype(dd)::value, ctrl = decltype(cc)::value;
+                        const bool hi = (qq_l & d) != 0;
+#pragma unroll
+                        for (int n = 0; n < 4; ++n) {
+                            if (n & d) continue;                       // slot pair (n, n + d)
+                            const uint32_t send = hi ? v[n] : v[n + d];
+                            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, ctrl, 0xF, 0xF, true);
+                            v[n] = hi ? recv : v[n];
+                            v[n + d] = hi ? v[n + d] : recv;
+                        }
+                    };
+                    xchg(code, std::integral_constant<int, 1>{}, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+                    xchg(code, std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+                    // liveness and scale of a row are the same in the four lanes of its quad
+                    const bool lv = qq_l == 0 ? live[0] : qq_l == 1 ? live[1] : qq_l == 2 ? live[2] : live[3];
+                    const int ex = qq_l == 0 ? exq[0] : qq_l == 1 ? exq[1] : qq_l == 2 ? exq[2] : exq[3];
+                    const int r = (qtid >> 4) + 16 * qq_l;
+                    if (lv) {
+                        if (tile64) {
+                            const int G = (c0 >> 5) + gc_l, rt = (int)(B.slot0 & 255) + r;
+                            *(uint4*)(dq_t + toff_fp4(rt, G)) = make_uint4(code[0], code[1], code[2], code[3]);
+                            ds_t[toff_scale(rt, G)] = (uint8_t)(ex + 127);
+                        } else {
+                            const long long G = (c0 >> 5) + gc_l, sl = B.slot0 + r;
+                            *(uint4*)(a.dq + off_fp4(sl, G, nks)) = make_uint4(code[0], code[1], code[2], code[3]);
+                            a.ds[off_scale(sl, G, nks)] = (uint8_t)(ex + 127);
+                        }
+                    }
+                } else {
 #pragma unroll
                 for (int n = 0; n < NT2; ++n) {
                     if (!live[n]) continue;
@@ -818,6 +856,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                         *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
                         if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
                     }
+                }
                 }
                 const long long i_prev = i;
 #pragma unroll
