@@ -1394,6 +1394,7 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
 #pragma unroll
                 for (int j = 0; j < 8; ++j) am[j] = oct_max(am[j]);
                 int exs = 0;
+                uint32_t cd[8];                                // row j's codes of this eighth (2 bytes)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int ex = mx_exp_fp4(am[j]);
@@ -1401,8 +1402,32 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     uint32_t w = 0u;
                     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][0], xr[j][1], sc, 0);
                     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xr[j][2], xr[j][3], sc, 1);
-                    *(uint16_t*)(dq_t + toff_fp4(rt0 + j, (int)G) + 2 * e) = (uint16_t)w;
+                    cd[j] = w & 0xffffu;
                     exs = e == j ? ex : exs;
+                }
+                // Two exchanges inside the quad of eighths (e, e ^ 1, e ^ 2,
+                // e ^ 3): at distance 1 a lane keeps the rows of its parity and
+                // packs its eighth with the partner's (4 bytes), at distance 2
+                // the rows whose bit 1 is its own and packs the two pairs (8
+                // bytes).  Lane e then holds bytes 8 (e / 4) .. + 7 of rows
+                // e % 4 and e % 4 + 4: two 8-byte stores instead of eight
+                // 2-byte ones.
+                const bool o1 = (e & 1) != 0, o2 = (e & 2) != 0;
+                uint32_t d1[4];                                // row 2 m + e % 2, eighths 2 (e / 2), + 1
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t send = o1 ? cd[2 * m] : cd[2 * m + 1];
+                    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);   // lane ^ 1
+                    const uint32_t own = o1 ? cd[2 * m + 1] : cd[2 * m];
+                    d1[m] = o1 ? (recv | (own << 16)) : (own | (recv << 16));
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {                  // row 4 h + e % 4, eighths 4 (e / 4) .. + 3
+                    const uint32_t send = o2 ? d1[2 * h] : d1[2 * h + 1];
+                    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, true);  // lane ^ 2
+                    const uint32_t own = o2 ? d1[2 * h + 1] : d1[2 * h];
+                    *(uint2*)(dq_t + toff_fp4(rt0 + 4 * h + (e & 3), (int)G) + 8 * (e >> 2)) =
+                        o2 ? make_uint2(recv, own) : make_uint2(own, recv);
                 }
                 ds_t[toff_scale(rt0 + e, (int)G)] = (uint8_t)(exs + 127);
             }
