@@ -118,6 +118,28 @@ def time_steps(dq, weights, x, qa, y, stream, steps, warmup):
     return ms_step, q_ms, c_ms, d_ms
 
 
+def time_fused(dq, weights, qa, y, stream, steps):
+    """Mean ms of dq_linear_forward_fused (the one-kernel forward: core and
+    delta partial sums in one K loop) over `steps` calls on the state of one
+    dq_quantize_act, HIP events on the launch stream; None where that form
+    does not apply (it takes 4-token cubes with FP8 cores)."""
+    import torch
+
+    try:
+        dq.dq_linear_forward_fused(weights, qa, y, stream)
+    except dq.DQError:
+        return None
+    for _ in range(5):
+        dq.dq_linear_forward_fused(weights, qa, y, stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        dq.dq_linear_forward_fused(weights, qa, y, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def work(cfg, cube, core_bits=8):
     """Sizes of the method's work for a cube shape: cubes, slots, flops of
     each GEMM, the activation pass's algorithmic bytes."""
@@ -432,6 +454,7 @@ def main():
     # timed steps (activation pass, core term, delta term: dq_linear's work);
     # per-phase events on the launch stream
     ms_step, q_ms, c_ms, d_ms = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
+    fused_ms = time_fused(dq, weights, qa, y, stream, args.steps)
     ctype = "bf16" if args.core_bits == 16 else f"fp{args.core_bits}"      # the core GEMM's input type
     f_ms = c_ms + d_ms
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -508,6 +531,14 @@ def main():
             "pct_copy": round(100 * quant_bytes / (q_ms * 1e-3) / 1e9 / copy_gbps, 2),
         },
         "core_overhead": core_overhead(wk, c_ms, d_ms, args.core_bits),
+        # the one-kernel form of the forward (dq_linear_forward_fused), not
+        # used by the step: the two kernels above measured faster
+        "fused_forward": None if fused_ms is None else {
+            "ms": round(fused_ms, 4),
+            "vs_two_kernels": round(fused_ms / f_ms, 4),
+            "effective_tops": round(dense_flops / (fused_ms * 1e-3) / 1e12, 2),
+            "hbm_saved_bytes": int(2 * 4 * K * Co),
+        },
         "core_term": {
             "ms": round(c_ms, 4),
             f"{ctype}_tflops": round(f_fp8 / (c_ms * 1e-3) / 1e12, 2),

@@ -192,6 +192,22 @@ dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void*
 dq_status dq_core_term(const dq_weights* w, dq_qact* q, void* stream);
 dq_status dq_delta_term(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
 
+/* dq_linear_forward in one kernel, the form of the pages' implementation
+ * (DeltaQuant notes, 损失函数/训练策略: the core partial sums accumulated in
+ * the W4A4 GEMM): each 256-slot x 256-channel tile accumulates the delta term
+ * of its slots and the core term of its 64 cubes in the same K loop, sharing
+ * the Q4(R) operand, and adds them in its epilogue, so the per-cube term is
+ * never written to memory.  Same y as dq_linear_forward (bit-identical where
+ * the core GEMM walks every tile forwards along K; otherwise the core sums
+ * differ only in the order of their fp32 additions).  Only for cubes of 4
+ * tokens (t h w = 4) with FP8 cores in one frame segment, rank 32, Co a
+ * multiple of 256, Ci >= 512 and y_dev 16-byte aligned; other workspaces
+ * return DQ_ERR_INVALID_ARG.  Arguments, ownership and asynchrony as
+ * dq_linear_forward.  On MI355X it measured slower than the two-kernel form
+ * (the fused K loop also carries the cores' operand steps and is bound by
+ * operand delivery), so dq_linear_forward does not use it. */
+dq_status dq_linear_forward_fused(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
+
 /* dq_quantize_act followed by dq_linear_forward on the same stream. */
 dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, float* y_dev, void* stream);
 

@@ -21,6 +21,7 @@ hipError_t launch_quantize(const dq_weights*, const void*, int, dq_qact*, hipStr
 hipError_t launch_slot_tokens(const Geom&, int64_t, int*, int64_t, hipStream_t) { return stub(); }
 hipError_t launch_decode_fp4_bf16(const uint8_t*, const uint8_t*, int64_t, int64_t, uint16_t*, hipStream_t) { return stub(); }
 hipError_t launch_forward(const dq_weights*, dq_qact*, float*, int, hipStream_t) { return stub(); }
+hipError_t launch_forward_fused(const dq_weights*, dq_qact*, float*, hipStream_t) { return stub(); }
 hipError_t launch_forward6(const dq_weights*, dq_act6*, float*, hipStream_t) { return stub(); }
 hipError_t launch_encode_fp6(const void*, int, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, hipStream_t) { return stub(); }
 hipError_t launch_text_lowrank(const void*, int, int64_t, int64_t, int, int, const uint16_t*, int, float*, uint16_t*, hipStream_t) { return stub(); }

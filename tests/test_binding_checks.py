@@ -34,7 +34,7 @@ def test_x_rejections(fn):
     _raises(fn, W, torch.zeros(40, 64, dtype=torch.bfloat16), Q, match="cuda:0")     # CPU tensor
 
 
-@pytest.mark.parametrize("fn", [dq.dq_linear_forward, dq.dq_delta_term])
+@pytest.mark.parametrize("fn", [dq.dq_linear_forward, dq.dq_delta_term, dq.dq_linear_forward_fused])
 def test_y_rejections(fn):
     _raises(fn, W, Q, torch.zeros(40, 96, dtype=torch.bfloat16), match="dtype")
     _raises(fn, W, Q, torch.zeros(40, 95), match="shape")

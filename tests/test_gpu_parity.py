@@ -260,6 +260,53 @@ def test_forward_halves_match_forward(dqm):
     torch.cuda.synchronize()
     assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
 
+
+@pytest.mark.parametrize("shape", [(4, 16, 16, 512, 512), (3, 10, 18, 1024, 768), (2, 9, 30, 640, 256)],
+                         ids=["1024tok_ci512", "540tok_ci1024_ragged", "540tok_ci640_odd_cubes"])
+def test_fused_forward_matches_halves(dqm, shape):
+    """4-token cubes with FP8 cores: dq_linear_forward_fused runs the one-kernel
+    form (core and delta partial sums in one K loop), dq_core_term +
+    dq_delta_term the two-kernel form.  Where the core GEMM runs a single
+    round (every tile walks K forwards, no K split), both accumulate the same
+    MFMA blocks in the same order and add the same terms, so y is
+    bit-identical, pad slots and clipped cubes included; the layer also meets
+    the oracle's bar."""
+    T, H, W, Ci, Co = shape
+    _say(f"case fused forward {shape}")
+    x = synth.make_activation(T, H, W, Ci, seed=25, dtype="bf16", n_outliers=4).to(DEV)
+    wt = synth.make_weight(Ci, Co, seed=26, dtype="bf16")
+    l1, l2 = _random_factors(Ci, Co, 32, 29)
+    weights = dqm.dq_prepare_weights_lowrank(wt, l1, l2)
+    qa = dqm.dq_qact_create(weights, (T, H, W, 1, 2, 2))
+    dqm.dq_quantize_act(weights, x, qa)
+    y1 = torch.full((T * H * W, Co), float("nan"), device=DEV)
+    y2 = torch.full((T * H * W, Co), float("nan"), device=DEV)
+    dqm.dq_linear_forward_fused(weights, qa, y1)
+    dqm.dq_core_term(weights, qa)
+    dqm.dq_delta_term(weights, qa, y2)
+    torch.cuda.synchronize()
+    a, b = y1.cpu().numpy(), y2.cpu().numpy()
+    assert np.isfinite(a).all()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"max diff {np.abs(a - b).max()}"
+    L = dict(x=synth.to_f32_numpy(x.cpu()), wt=synth.to_f32_numpy(wt), l1=l1, l2=l2, weights=weights, qa=qa, y=a,
+             g=cubes.Geometry(T, H, W, 1, 2, 2))
+    err, row = _full_compare(dqm, L)
+    _say(f"fused {shape}: rel err {err:.2e} worst row {row:.2e}")
+
+
+def test_fused_forward_rejects_other_shapes(dqm):
+    """The one-kernel form takes 4-token cubes with FP8 cores only: other
+    workspaces are refused with an error, nothing is launched."""
+    T, H, W, Ci, Co = 2, 8, 8, 512, 256
+    wt = synth.make_weight(Ci, Co, seed=36, dtype="bf16")
+    l1, l2 = _random_factors(Ci, Co, 32, 39)
+    weights = dqm.dq_prepare_weights_lowrank(wt, l1, l2)
+    y = torch.empty(T * H * W, Co, device=DEV)
+    for cube, bits in (((2, 2, 2), 8), ((1, 2, 2), 4), ((1, 2, 2), 16), ((1, 1, 1), 8)):
+        qa = dqm.dq_qact_create(weights, (T, H, W) + cube, core_bits=bits)
+        with pytest.raises(dqm.DQError):
+            dqm.dq_linear_forward_fused(weights, qa, y)
+
 def test_library_svd_path(dqm):
     """dq_prepare_weights: the host SVD factors meet Eckart-Young, and R and
     Q4(R) are those the oracle forms from the library's own factors, bit for

@@ -133,6 +133,18 @@ void unstep_scales(const std::vector<uint8_t>& buf, long long row, int64_t Ci, i
 
 using namespace dq;
 
+namespace dq {
+// The shapes the one-kernel forward takes: cubes of exactly 4 slots with FP8
+// cores in one frame segment (a 256-slot tile's cubes are then the 64 rows
+// 64 tn .. of the core codes, inside one 256-row core tile), rank 32, Co a
+// multiple of 256, y rows 16-byte aligned with 32-bit element offsets, and K
+// loops of 4 or more 128-channel steps.
+bool fused_applies(const dq_weights* w, const dq_qact* q, const float* y) {
+    return q->core_bits == 8 && q->g.S == 4 && q->nseg == 1 && w->Kp / 128 >= 4 && w->rp == 32 && w->Co % 256 == 0 &&
+           (uintptr_t)y % 16 == 0 && q->g.N * w->Co < (1ll << 31) && q->Nslot_pad / 4 <= q->K_pad;
+}
+}  // namespace dq
+
 extern "C" {
 
 const char* dq_last_error(void) { return g_last_error.c_str(); }
@@ -573,6 +585,21 @@ static dq_status forward_parts(const dq_weights* w, dq_qact* q, float* y_dev, in
 
 dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {
     return forward_parts(w, q, y_dev, dq::FWD_CORE | dq::FWD_DELTA, stream);
+}
+
+dq_status dq_linear_forward_fused(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {
+    g_last_error.clear();
+    dq_status st = check_pair(w, q);
+    if (st != DQ_OK) return st;
+    if (!y_dev) return fail(DQ_ERR_INVALID_ARG, "y_dev is NULL");
+    if (!dq::fused_applies(w, q, y_dev))
+        return fail(DQ_ERR_INVALID_ARG, "the fused forward takes cubes of 4 tokens with FP8 cores in one frame segment, "
+                                        "rank 32, Co a multiple of 256, Ci of 512 or more and a 16-byte aligned y_dev");
+    DeviceGuard dg(q->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t e = dq::launch_forward_fused(w, q, y_dev, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "fused forward launch");
+    return DQ_OK;
 }
 
 dq_status dq_core_term(const dq_weights* w, dq_qact* q, void* stream) {

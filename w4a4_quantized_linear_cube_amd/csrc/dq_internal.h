@@ -263,6 +263,11 @@ int text_lowrank_splits(int Ci);
 // ---- launchers (gemm.hip) ----
 constexpr int FWD_CORE = 1, FWD_DELTA = 2;   // parts of the forward pass
 hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, hipStream_t st);
+// The one-kernel forward (core and delta partial sums in one K loop) and the
+// shapes it takes (4-slot cubes, FP8 cores, one frame segment, rank 32,
+// Co % 256 == 0, Ci of 512 or more, y 16-byte aligned).
+bool fused_applies(const dq_weights* w, const dq_qact* q, const float* y);
+hipError_t launch_forward_fused(const dq_weights* w, dq_qact* q, float* y, hipStream_t st);
 // y = U L2 + Q6(X) Q6(R) for a 6-bit layer
 hipError_t launch_forward6(const dq_weights* w, dq_act6* a, float* y, hipStream_t st);
 // y[n][j] = (sum_c wdec[j][c] xdec[n][c]) s_x[n] s_w[j] over bf16 operands in the off_bf16 layout

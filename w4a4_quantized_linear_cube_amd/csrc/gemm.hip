@@ -105,6 +105,16 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff),
                  "s"(base) : "memory", "m0");
 }
+// The same with an immediate byte offset OFF (0 .. 4095) on the source:
+// base + voff_i + OFF -> LDS lds + 16 i.  The instruction's offset field is
+// added to the LDS address as well as to the global one, so m0 takes
+// lds - OFF (lds >= OFF).
+template <int OFF>
+__device__ __forceinline__ void dma16o(const void* base, uint32_t voff, uint32_t lds) {
+    static_assert(OFF >= 0 && OFF < 4096, "offset field");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3" ::"s"(__builtin_amdgcn_readfirstlane(lds - OFF)),
+                 "v"(voff), "s"(base), "n"(OFF) : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // load at a 32-bit byte offset from a base pointer
@@ -876,6 +886,467 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs p) {
     if constexpr (DEFER) wait_vm<0>();                   // the last tile's surplus copies land before the LDS is released
 }
 
+// ---- The fused form: core term and delta term in one K loop --------------
+// For cubes of 4 slots with FP8 cores, one kernel computes, per 256-channel x
+// 256-slot tile, both the delta term over the tile's 256 slots and the core
+// term Q8(core) Q4(R) over its 64 cubes, accumulating the core partial sums
+// beside the delta ones as the pages' kernel does (DeltaQuant notes,
+// 损失函数/训练策略), so the per-cube term never goes to memory.
+//  - Both contractions share the Q4(R) fragments of every K step.  A wave's
+//    core block is its 32 cubes x its 128 channels: 4 FP8 x FP4 MFMAs per half
+//    step beside the 16 FP4 x FP4 ones, 64 fp32 accumulators in VGPRs.
+//  - Slot rows are permuted on their way into LDS: accumulator row
+//    32 ni + l (of a wave's 128-row half) holds slot 4 l + ni, so in every
+//    block ni lane l holds a slot of cube l, the cube whose core term the
+//    lane's own core accumulators hold, and the epilogue adds them with no
+//    exchange between lanes.  The copies move each slot row's 64 bytes to its
+//    new place and re-swizzle its chunks for that row; the delta scale codes
+//    are copied unchanged and each lane reads its four rows' codes apart.
+//  - LDS: 3 stages of 42.5 KB (A, B, their scales, the 64 cube rows' FP8 step
+//    and their scales) and, apart from the ring, the epilogue's transposition
+//    buffers (32 KB).  A stage is released at the barrier of its own step: the
+//    wave waits for its reads of the step's second half before the barrier, so
+//    the copy stream leads the MFMAs by as many steps as with four stages.
+struct FusedArgs {
+    const uint8_t *a, *as;   // Q4(R) codes and scales, step-major (256-channel tiles)
+    const uint8_t *b, *bs;   // delta codes and scales, step-major (256-slot tiles, slot order)
+    const uint8_t *c, *cs;   // core FP8 codes and scales, step-major (256-cube tiles)
+    int nks, mtiles, ntiles;
+    float* y;                // [N][Co] token order, Co a multiple of 256
+    int Co;
+    const int* stok;         // slot -> token (-1 for pad slots)
+    const uint16_t* u;       // [Nslot_pad][32]
+    const uint16_t* l2t;     // [Cop][32]
+    float* sink;
+};
+
+// One FP4 x FP8 scaled MFMA (A = 32 FP4 codes, B = 32 FP8 codes per lane)
+// into an accumulator held in architectural VGPRs.  Written as an asm
+// statement because the compiler gives every MFMA of a kernel an AGPR
+// accumulator: with the delta term's 256 already there, it would shuttle
+// tuples between the two files on every step.  Byte SA of the A scale
+// register and byte SB of the B one select the E8M0 codes (op_sel holds the
+// low bit, op_sel_hi the high one).  The s_nop gives a VALU write of an
+// operand (the B scale is shifted into place just before) the wait states
+// an MFMA read needs after it; the accumulator is written only by this MFMA
+// and read again only after the tile's K loop.
+template <int SA, int SB>
+__device__ __forceinline__ void core_mfma(v16f& acc, uint4 a4, v8i b, int sa, uint32_t sb) {
+    const v4i a = __builtin_bit_cast(v4i, a4);
+    asm volatile("s_nop 4\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] cbsz:4 blgp:0"
+                 : "+v"(acc)
+                 : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(SA & 1), "n"(SB & 1), "n"(SA >> 1), "n"(SB >> 1));
+}
+
+__global__ __launch_bounds__(256, 1) void k_fused(FusedArgs p) {
+    constexpr int A_STEP = 16384, B_STEP = 16384;
+    constexpr int B_OFF = A_STEP, SA_OFF = B_OFF + B_STEP, SB_OFF = SA_OFF + 1024;
+    constexpr int C_OFF = SB_OFF + 1024;       // 64 cube rows x 128 bytes
+    constexpr int SC_OFF = C_OFF + 8192;       // 64 dwords of core scale codes (+ 192 bytes the copies overrun into)
+    constexpr int STAGE = SC_OFF + 512;        // (stages start at multiples of 256 bytes: the swizzles' bank pattern)
+    constexpr int NS = 3;
+    constexpr int T_OFF = NS * STAGE;          // transposition buffers, 8 KB per wave
+    constexpr int DMAS = 13;                   // copies per wave per stage: A 4, B 4, scales 2, cores 2, core scales 1
+    constexpr int H1 = 6;                      // the first half (issued in phase 2), the rest in phase 1 of the next step
+    static_assert(T_OFF + 32768 <= 163840, "LDS");
+    static_assert(DMAS + H1 < 63, "vmcnt range");
+    // copies sit after every third MFMA of a phase (phase 1 from MFMA 0, phase 2 from MFMA 2)
+    auto p1_copy = [](int i) { return i % 3 == 0 && i / 3 < DMAS - H1 ? H1 + i / 3 : -1; };
+    auto p2_copy = [](int i) { return i >= 2 && (i - 2) % 3 == 0 && (i - 2) / 3 < H1 ? (i - 2) / 3 : -1; };
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T_OFF + 32768];
+
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const TileWalk walk = tile_walk(blockIdx.x, gridDim.x, p.mtiles, p.ntiles, p.nks);
+    const int nk = p.nks;
+    const int ntiles = walk.count();
+    if (ntiles == 0) return;
+
+    // ---- per-lane offsets of the copies and of the fragment reads, derived
+    // from the thread index t.  The tile loop recomputes them at every tile's
+    // start from a copy of the index the compiler cannot see through, so none
+    // stays live across an epilogue, whose registers they would take.
+    struct Lanes {
+        uint32_t va, vb, vs, vc, vsc;   // copy offsets: A, B (permuted rows), scales, cores, core scales
+        int aoff[2], boff[2];           // fragment offsets within a stage, half kk (+ 2048 per 32-row block)
+        int sa_off, sb_off, sc_off;
+        int coff[2][2];                 // core fragment, half kk: low and high 16 bytes
+        uint32_t sb_sh, sc_sh;          // where a lane's two scale codes sit in the dwords read
+    };
+    auto lanes_of = [&](int t) {
+        const int lane = t & 63, wave = t >> 6;
+        const int wr = wave >> 1, wc = wave & 1;
+        const int g = lane >> 5, l32 = lane & 31;
+        Lanes L;
+        L.va = (uint32_t)lane * 16 + wv * 4096;
+        // delta rows: LDS row R = 64 wv + 16 jb + lane / 4 of copy jb takes
+        // slot row s(R) = (R & 128) | (R % 32) 4 | (R / 32) % 4, its chunk pc
+        // (of R) holding logical chunk pc ^ swz4(R), found at
+        // (pc ^ swz4(R)) ^ swz4(s) in the slot row.  s = s0 + 64 (jb % 2) +
+        // jb / 2, and neither swizzle depends on jb (they read row bits 1-3),
+        // so copy jb reads at vb + 64 (jb / 2) from the step base + 4096 (jb % 2).
+        {
+            const int R = wv * 64 + (lane >> 2), pc = lane & 3;
+            const int s = (R & 128) | ((R & 31) << 2) | ((R >> 5) & 3);
+            L.vb = (uint32_t)s * 64 + (uint32_t)(((pc ^ swz4(R)) ^ swz4(s)) << 4);
+        }
+        L.vs = (uint32_t)lane * 4 + wv * 256;
+        L.vc = (uint32_t)lane * 16 + wv * 2048;
+        // core scale codes: dword d = 32 g + l (cube row l of the half g
+        // reads) of the LDS block is the dword that holds cube l's codes in
+        // the step's scale block; wave w writes dwords 16 w .. 16 w + 63 (the
+        // last ones repeat dword 63 past the block's 64, into the overrun bytes)
+        L.vsc = (uint32_t)min(16 * wv + lane, 63) * 8;
+        const int arow0 = wr * 128 + l32, brow0 = wc * 128 + l32;
+        const int asw = swz4(arow0), bsw = swz4(brow0), csw = swz8(l32);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            L.aoff[kk] = arow0 * 64 + (((2 * kk + g) ^ asw) << 4);
+            L.boff[kk] = B_OFF + brow0 * 64 + (((2 * kk + g) ^ bsw) << 4);
+            L.coff[kk][0] = C_OFF + (wc * 32 + l32) * 128 + (((4 * kk + g) ^ csw) << 4);
+            L.coff[kk][1] = C_OFF + (wc * 32 + l32) * 128 + (((4 * kk + 2 + g) ^ csw) << 4);
+        }
+        L.sa_off = SA_OFF + ((wr * 2 + g) * 32 + l32) * 8;
+        // delta scale codes of LDS row brow0 + 32 ni (slot wc 128 + 4 l32 +
+        // ni): the 2 bytes (kk 0, 1) at entry (wc, g, (4 l32 + ni) % 32),
+        // bytes 2 (l32 / 8) ..; read as the dword that holds them
+        // ((4 l32 + ni) % 32 = 4 (l32 % 8) + ni: ni in the read's offset
+        // field) and shifted into bytes 0, 1 where an MFMA uses them
+        L.sb_off = SB_OFF + (wc * 2 + g) * 256 + ((l32 >> 4) & 1) * 4 + (l32 & 7) * 32;
+        L.sb_sh = ((l32 >> 3) & 1) * 16;
+        L.sc_off = SC_OFF + (g * 32 + l32) * 4;    // bytes 2 wc + kk of the lane's dword
+        L.sc_sh = 16 * wc;
+        return L;
+    };
+    auto opaque_tid = []() {
+        int t = (int)threadIdx.x;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
+
+    // ---- copies (tile step bases uniform)
+    const uint32_t lds0 = lds_addr(smem);
+    struct Src {
+        const uint8_t *a, *b, *as, *bs, *c, *cs;
+    };
+    auto src_of = [&](int t, int k) {
+        int tm, tn;
+        walk.coords(t, &tm, &tn);
+        const int kt = tn >> 2, q = tn & 3;      // the tile's 64 cubes: rows 64 q .. of core tile kt
+        Src r;
+        r.a = (const uint8_t*)uniform_ptr(p.a + ((size_t)tm * nk + k) * A_STEP);
+        r.b = (const uint8_t*)uniform_ptr(p.b + ((size_t)tn * nk + k) * B_STEP);
+        r.as = (const uint8_t*)uniform_ptr(p.as + ((size_t)tm * nk + k) * 1024);
+        r.bs = (const uint8_t*)uniform_ptr(p.bs + ((size_t)tn * nk + k) * 1024);
+        r.c = (const uint8_t*)uniform_ptr(p.c + ((size_t)kt * nk + k) * 32768 + q * 8192);
+        // rows 64 q + 32 h + l sit in entry (q / 2, half g, l), dword q % 2
+        // (bytes 2 h + kk) of the step's scale block
+        r.cs = (const uint8_t*)uniform_ptr(p.cs + ((size_t)kt * nk + k) * 1024 + (q >> 1) * 512 + 4 * (q & 1));
+        return r;
+    };
+    auto dma = [&](const Lanes& L, const Src& src, int buf, int j) {
+        const uint32_t st = lds0 + buf * STAGE;
+        if (j < 4) {
+            switch (j) {
+                case 0: dma16o<0>(src.a, L.va, st + (wv * 4) * 1024); break;
+                case 1: dma16o<1024>(src.a, L.va, st + (wv * 4 + 1) * 1024); break;
+                case 2: dma16o<2048>(src.a, L.va, st + (wv * 4 + 2) * 1024); break;
+                default: dma16o<3072>(src.a, L.va, st + (wv * 4 + 3) * 1024); break;
+            }
+        } else if (j < 8) {
+            // jb = 0 2 1 3: the copies that share cache lines one after the other
+            switch (j) {
+                case 4: dma16o<0>(src.b, L.vb, st + B_OFF + (wv * 4) * 1024); break;
+                case 5: dma16o<64>(src.b, L.vb, st + B_OFF + (wv * 4 + 2) * 1024); break;
+                case 6: dma16o<0>(uniform_ptr(src.b + 4096), L.vb, st + B_OFF + (wv * 4 + 1) * 1024); break;
+                default: dma16o<64>(uniform_ptr(src.b + 4096), L.vb, st + B_OFF + (wv * 4 + 3) * 1024); break;
+            }
+        } else if (j == 8) {
+            dma4(src.as, L.vs, st + SA_OFF + wv * 256);
+        } else if (j == 9) {
+            dma4(src.bs, L.vs, st + SB_OFF + wv * 256);
+        } else if (j == 10) {
+            dma16o<0>(src.c, L.vc, st + C_OFF + (wv * 2) * 1024);
+        } else if (j == 11) {
+            dma16o<1024>(src.c, L.vc, st + C_OFF + (wv * 2 + 1) * 1024);
+        } else {
+            dma4(src.cs, L.vsc, st + SC_OFF + wv * 64);
+        }
+    };
+    // Cursor (tile tf, step kf): it runs three steps ahead of the MFMAs and
+    // holds on the last tile's last step; inside a tile by pointer
+    // increments, into the next tile at the wrap (sources prepared at the
+    // tile's start in nsrc; ninc = 0 for the last tile).  Branch-free.
+    int kf = 0;
+    Src src = src_of(0, 0), nsrc{};
+    int inc = 1, ninc = 1;
+    auto advance = [&]() {
+        const bool wrap = kf + 1 == nk;
+        kf = wrap ? 0 : kf + 1;
+        src.a = wrap ? nsrc.a : src.a + inc * A_STEP;
+        src.b = wrap ? nsrc.b : src.b + inc * B_STEP;
+        src.as = wrap ? nsrc.as : src.as + inc * 1024;
+        src.bs = wrap ? nsrc.bs : src.bs + inc * 1024;
+        src.c = wrap ? nsrc.c : src.c + inc * 32768;
+        src.cs = wrap ? nsrc.cs : src.cs + inc * 1024;
+        inc = wrap ? ninc : inc;
+    };
+    auto prepare_next = [&](int it) {
+        if (it + 1 < ntiles) {
+            ninc = 1;
+            nsrc = src_of(it + 1, 0);
+        } else {
+            nsrc = src_of(ntiles - 1, nk - 1);
+            ninc = 0;
+        }
+    };
+
+    v16f acc[4][4];      // delta term (+ low-rank branch): channel block mi x slot block ni
+    v16f cacc[4];        // core term: channel block mi x the wave's 32 cubes
+
+    // ---- fragments of one 64-channel half step
+    struct Half {
+        uint4 a[4], b[4];
+        uint2 sa;
+        uint32_t sb[4];      // block ni's two codes (kk 0, 1) in bytes sb_sh / 8 ..
+        v8i c;
+        uint32_t sc;         // the cube's two codes in bytes sc_sh / 8 ..
+    };
+    // LDS read number i (0 .. NRD - 1) of half kk, in the order of first use
+    auto rd = [&](const Lanes& L, int buf, int kk, Half& F, int i) {
+        const uint8_t* st = smem + buf * STAGE;
+        auto rda = [&](int mi) { F.a[mi] = *(const uint4*)(st + L.aoff[kk] + mi * 2048); };
+        auto rdb = [&](int ni) { F.b[ni] = *(const uint4*)(st + L.boff[kk] + ni * 2048); };
+        auto sbh = [&](int ni) { return *(const uint32_t*)(st + L.sb_off + ni * 8); };
+        switch (i) {
+            case 0: rda(0); break;
+            case 1: rdb(0); break;
+            case 2: F.sa = *(const uint2*)(st + L.sa_off); break;
+            case 3:
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) F.sb[ni] = sbh(ni);
+                break;
+            case 4: rdb(1); break;
+            case 5: rdb(2); break;
+            case 6: rdb(3); break;
+            case 7: rda(1); break;
+            case 8: rda(2); break;
+            case 9: rda(3); break;
+            case 10: {
+                const v4i lo = *(const v4i*)(st + L.coff[kk][0]);
+                const v4i hi = *(const v4i*)(st + L.coff[kk][1]);
+                F.c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                break;
+            }
+            default: F.sc = *(const uint32_t*)(st + L.sc_off); break;
+        }
+    };
+    constexpr int NRD = 12;
+    // MFMA number i (0 .. 19) of half kk: 16 delta MFMAs (block mi = i / 4,
+    // ni = i % 4), then the 4 core MFMAs (block mi = i - 16)
+    auto mma = [&](const Lanes& L, const Half& F, int kk, int i) {
+        const int mi = i < 16 ? i >> 2 : i - 16, ni = i & 3;
+        const uint4 v = F.a[mi];
+        const v8i af = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        const int sa = (mi >> 1) ? (int)F.sa.y : (int)F.sa.x;
+        const int oa = 2 * (mi & 1) + kk;
+        if (i >= 16) {
+            switch (oa * 2 + kk) {
+                case 0: core_mfma<0, 0>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+                case 1: core_mfma<0, 1>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+                case 2: core_mfma<1, 0>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+                case 3: core_mfma<1, 1>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+                case 4: core_mfma<2, 0>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+                case 5: core_mfma<2, 1>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+                case 6: core_mfma<3, 0>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+                default: core_mfma<3, 1>(cacc[mi], v, F.c, sa, F.sc >> L.sc_sh); break;
+            }
+            return;
+        }
+        const uint4 u = F.b[ni];
+        const v8i bf = (v8i){(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+        const int sb = (int)(F.sb[ni] >> L.sb_sh);
+#define DQ_MFMA(OA, OB) acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[mi][ni], FMT_FP4, FMT_FP4, OA, sa, OB, sb)
+        switch (oa * 2 + kk) {
+            case 0: DQ_MFMA(0, 0); break;  case 1: DQ_MFMA(0, 1); break;
+            case 2: DQ_MFMA(1, 0); break;  case 3: DQ_MFMA(1, 1); break;
+            case 4: DQ_MFMA(2, 0); break;  case 5: DQ_MFMA(2, 1); break;
+            case 6: DQ_MFMA(3, 0); break;  default: DQ_MFMA(3, 1); break;
+        }
+#undef DQ_MFMA
+    };
+
+    // ---- tile epilogue: acc[mi][ni][4 j + q] is channel m0 + wr 128 + 32 mi
+    // + 8 j + 4 g + q of slot n0 + wc 128 + 4 l32 + ni (cube row l32 of the
+    // wave's half), cacc[mi][4 j + q] the same channel of that cube.
+    auto epilogue = [&](int tm, int tn) {
+        // The epilogue's lane offsets are derived here, from a copy of the
+        // thread index the compiler cannot see through, so they are not
+        // hoisted out of the tile loop and kept live across the K loop
+        // (where the registers are taken).
+        int tid_e = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid_e));
+        const int lane = tid_e & 63, wave = tid_e >> 6;
+        const int wr = wave >> 1, wc = wave & 1;
+        const int g = lane >> 5, l32 = lane & 31;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        // transposition buffers (as in k_gemm's token epilogue), outside the ring
+        auto tbuf = [&](int b) { return smem + T_OFF + wv * 8192 + b * 4096; };
+        auto tput = [&](int b, const float4* o) {
+            uint8_t* t = tbuf(b) + l32 * 128;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *(float4*)(t + (((2 * j + g) ^ ((l32 >> 1) & 7)) << 4)) = o[j];
+        };
+        auto tget = [&](int b, int i) {
+            const int rr = 8 * i + (lane >> 3);
+            return *(const float4*)(tbuf(b) + rr * 128 + (((lane & 7) ^ ((rr >> 1) & 7)) << 4));
+        };
+        const int m0 = tm * 256, n0 = tn * 256;
+        const uint32_t slot0 = (uint32_t)(n0 + wc * 128 + 4 * l32);      // + ni
+        int tok[4];
+        v8bf la[2][4], ub[2][4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) tok[ni] = ld_off<int>(p.stok, (slot0 + ni) * 4);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const uint32_t lo = ((uint32_t)(m0 + wr * 128 + l32 + 32 * mi) * 32 + 8 * g) * 2;
+            la[0][mi] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.l2t, lo));
+            la[1][mi] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.l2t, lo + 32));
+        }
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const uint32_t uo = ((slot0 + ni) * 32 + 8 * g) * 2;
+            ub[0][ni] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.u, uo));
+            ub[1][ni] = __builtin_bit_cast(v8bf, ld_off<uint4>(p.u, uo + 32));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // every copy in flight (the next tile's first stages) and the loads above
+        wait_vm<0>();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[h][mi], ub[h][ni], acc[mi][ni], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const int chq = m0 + wr * 128 + 4 * (lane & 7);
+        float* rowp[4];
+#pragma unroll
+        for (int b = 0; b < 17; ++b) {
+            if (b < 16) {                               // block b: mi = b % 4, ni = b / 4
+                const int mi = b & 3, ni = b >> 2;
+                const v16f& a = acc[mi][ni];
+                const v16f& c = cacc[mi];
+                float4 o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = make_float4(a[4 * j] + c[4 * j], a[4 * j + 1] + c[4 * j + 1], a[4 * j + 2] + c[4 * j + 2],
+                                       a[4 * j + 3] + c[4 * j + 3]);
+                tput(b & 1, o);
+            }
+            if (b > 0) {
+                const int pb = b - 1, mi = pb & 3, ni = pb >> 2;
+                if (mi == 0) {
+                    // the tokens of the rows this lane stores (row 8 i + lane / 8
+                    // of the slot block: lane 8 i + lane / 8's slot), fetched
+                    // when the block's first rows go out
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) * 4, tok[ni]);
+                        const uint64_t yrow = (uint64_t)(p.y + (uint32_t)(t * p.Co + chq));
+                        const uint64_t sink = (uint64_t)(p.sink + 4 * lane);
+                        const uint64_t m = (uint64_t)(int64_t)(t >> 31);   // all ones for a slot without a token
+                        rowp[i] = (float*)((yrow & ~m) | (sink & m));
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 v = tget(pb & 1, i);
+                    __builtin_nontemporal_store(__builtin_bit_cast(v4f, v), (v4f*)(rowp[i] + 32 * mi));
+                }
+            }
+        }
+    };
+
+    // ---- K loop.  Step gs: phase 1 runs the MFMAs of half 0 of stage gs
+    // (F0) while reading half 1 into F1 and issuing the second half of stage
+    // gs + 2's copies; then the wave waits for its F1 reads and for its copies
+    // of stage gs + 1, and the barrier: stage gs + 1 has landed and no wave
+    // reads stage gs any more; phase 2 runs half 1 (F1) while issuing the
+    // first half of stage gs + 3's copies into stage gs's buffer and reading
+    // half 0 of stage gs + 1 into F0.
+    // Prologue: stages 0 and 1, and the first half of stage 2 (the cursor
+    // then stays on step 2).
+    {
+        const Lanes L = lanes_of((int)threadIdx.x);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int j = 0; j < DMAS; ++j) dma(L, src, s, j);
+            advance();
+        }
+#pragma unroll
+        for (int j = 0; j < H1; ++j) dma(L, src, 2, j);
+    }
+    wait_vm<DMAS + H1>();                                  // stage 0 landed
+    __syncthreads();
+    Half F0, F1;
+    // Stage gs + 1 must have landed at the barrier of step gs: the copies
+    // issued after it are stage gs + 2's, DMAS of them.  In a tile's first
+    // step after the first tile, stage gs + 1 was covered by the previous
+    // epilogue's full wait, and a loose count lets that epilogue's stores
+    // stay in flight.
+    int gs = 0;
+    for (int it = 0; it < ntiles; ++it) {
+        const Lanes L = lanes_of(opaque_tid());
+        // half 0 of the tile's first stage (landed: the previous step's
+        // barrier, or the prologue's, covered it)
+#pragma unroll
+        for (int i = 0; i < NRD; ++i) rd(L, (unsigned)gs % NS, 0, F0, i);
+        prepare_next(it);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cacc[i] = (v16f){};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < nk; ++ks, ++gs) {
+            const int cur = (unsigned)gs % NS, nxt = (unsigned)(gs + 1) % NS, fillp = (unsigned)(gs + 2) % NS;
+#pragma unroll
+            for (int i = 0; i < 20; ++i) {
+                mma(L, F0, 0, i);
+                if (i < NRD) rd(L, cur, 1, F1, i);
+                if (p1_copy(i) >= 0) dma(L, src, fillp, p1_copy(i));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            advance();
+            const int loose = __builtin_amdgcn_readfirstlane((it > 0 && ks == 0) ? 1 : 0);
+            asm volatile(
+                "s_waitcnt lgkmcnt(0)\n\t"
+                "s_cmp_eq_u32 %0, 0\n\t"
+                "s_cbranch_scc1 1f\n\t"
+                "s_waitcnt vmcnt(63)\n\t"
+                "s_branch 2f\n"
+                "1:\n\t"
+                "s_waitcnt vmcnt(%1)\n"
+                "2:\n\t"
+                "s_barrier" ::"s"(loose), "n"(DMAS) : "memory", "scc");
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 20; ++i) {
+                mma(L, F1, 1, i);
+                if (p2_copy(i) >= 0) dma(L, src, cur, p2_copy(i));
+                if (i < NRD) rd(L, nxt, 0, F0, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        int tm, tn;
+        walk.coords(it, &tm, &tn);
+        epilogue(tm, tn);
+    }
+}
+
 // One persistent workgroup per CU (a multiple of 8, one share per XCD),
 // never more than the tiles need.
 static int persistent_grid(int total) {
@@ -943,6 +1414,34 @@ static hipError_t launch_store(const GemmArgs& a, const KSplit& ks, float* part,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_ksum<<<ks.rm * 64, 256, 0, st>>>(part, a.c, a.ldc, a.mtiles, a.ntiles, a.nks, ks.main_tiles, ks.rm, ks.p);
+    return hipGetLastError();
+}
+
+// The fused form (fused_applies: cubes of exactly 4 slots with FP8 cores in
+// one frame segment, so a 256-slot tile's cubes are the 64 rows 64 tn .. of
+// the core codes) is the dq_linear_forward_fused entry point;
+// dq_linear_forward keeps the two kernels, which measured faster on MI355X
+// (the fused K loop carries the cores' operand steps too, and it is bound by
+// operand delivery).
+hipError_t launch_forward_fused(const dq_weights* w, dq_qact* q, float* y, hipStream_t st) {
+    if (!fused_applies(w, q, y)) return hipErrorInvalidValue;
+    FusedArgs f{};
+    f.a = w->rq;
+    f.as = w->rs;
+    f.b = q->dq;
+    f.bs = q->ds;
+    f.c = q->cq;
+    f.cs = q->cs;
+    f.nks = (int)(w->Kp / 128);
+    f.mtiles = (int)(w->Cop / 256);
+    f.ntiles = (int)(q->Nslot_pad / 256);
+    f.y = y;
+    f.Co = (int)w->Co;
+    f.stok = q->stok;
+    f.u = q->u;
+    f.l2t = w->l2t;
+    f.sink = q->sink;
+    k_fused<<<persistent_grid(f.mtiles * f.ntiles), 256, 0, st>>>(f);
     return hipGetLastError();
 }
 
