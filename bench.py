@@ -19,6 +19,9 @@ roofline = the dominant kernel, the delta GEMM (dq_delta_term: one launch of
          traffic from the committed rocprofv3 counter summary of the same
          kernel source, else null.  With one-token cubes the delta term is
          one FP8 x FP4 GEMM over the cubes and is rated against the FP8 peak.
+fused_forward = the one-kernel form of the forward (dq_linear_forward_fused:
+         core and delta partial sums in one K loop, no per-cube term in
+         memory), timed beside the two kernels; not part of the step.
 cpu_baseline = the CPU oracle on a bounded sample of the same workload, its
          time extrapolated to the whole layer by the token count.
 
