@@ -39,6 +39,7 @@ DELTA_KERNEL = re.compile(r"k_gemm<4, 4, [12], ")          # the delta GEMM (FP4
 CORE_KERNEL = re.compile(r"k_gemm<(4, [04]|16, 16), 0, ")   # the core GEMM (FP8, FP4 or bf16 cores, plain stores)
 W6_KERNEL = re.compile(r"k_gemm<[23], [23], [12], ")        # the 6-bit layers' FP6 x FP6 GEMM
 QUANT_KERNEL = re.compile(r"k_quantize<")
+FUSED_KERNEL = re.compile(r"k_fused")                      # the one-kernel forward (core and delta in one K loop)
 SIMDS = 1024                                     # 256 CUs x 4 SIMDs
 CUS = 256
 XCDS = 8                                         # GRBM_GUI_ACTIVE comes summed over the XCDs
@@ -144,7 +145,8 @@ def summarize_counters(run_fetch, run_write, copy_fetch, copy_write, copy_bytes,
     }
     # the other two kernels of the step, from the same runs
     others = {}
-    for name, pat in (("activation pass (k_quantize)", QUANT_KERNEL), ("core GEMM (k_gemm, plain-store epilogue)", CORE_KERNEL)):
+    for name, pat in (("activation pass (k_quantize)", QUANT_KERNEL), ("core GEMM (k_gemm, plain-store epilogue)", CORE_KERNEL),
+                      ("one-kernel forward (k_fused: core and delta term in one K loop)", FUSED_KERNEL)):
         f = _mean(_counter_per_dispatch(run_fetch, "FETCH_SIZE", pat))
         w = _mean(_counter_per_dispatch(run_write, "WRITE_SIZE", pat))
         if f is not None and w is not None:
@@ -165,7 +167,7 @@ def summarize_mfma(run: str, out: str, cmd: str) -> None:
              "| kernel | dispatches | duration (us) | clock (GHz) | MFMA TFLOP F6F4 | MFMA TFLOP F8 | MFMA TFLOP BF16 | busy cycles / SIMD | active cycles | MFMA utilisation |",
              "|---|---|---|---|---|---|---|---|---|---|"]
     for name, pat in (("delta GEMM (k_gemm, token epilogue)", DELTA_KERNEL), ("core GEMM (k_gemm, plain store)", CORE_KERNEL),
-                      ("activation pass (k_quantize)", QUANT_KERNEL)):
+                      ("activation pass (k_quantize)", QUANT_KERNEL), ("one-kernel forward (k_fused)", FUSED_KERNEL)):
         m4 = _counter_per_dispatch(run, "SQ_INSTS_VALU_MFMA_MOPS_F6F4", pat)
         m8 = _counter_per_dispatch(run, "SQ_INSTS_VALU_MFMA_MOPS_F8", pat)
         mb = _counter_per_dispatch(run, "SQ_INSTS_VALU_MFMA_MOPS_BF16", pat)
