@@ -220,6 +220,16 @@ def test_wan1p3b_projection_full(dqm):
                cfg.x_seeds[0], cfg.w_seed, svd="oracle", n_out=cfg.n_outliers, w_out=0)
     err, row = _full_compare(dqm, L)
     _say(f"wan1p3b_proj: rel err {err:.2e} worst row {row:.2e}")
+    # the one-kernel forward on the same activation state, against the two
+    # kernels' output (checked in full above) on every element
+    y2 = torch.full((cfg.N, cfg.Co), float("nan"), device=DEV)
+    dqm.dq_linear_forward_fused(L["weights"], L["qa"], y2)
+    torch.cuda.synchronize()
+    a, b = y2.cpu().numpy(), L["y"]
+    assert np.isfinite(a).all(), "unwritten outputs (fused)"
+    d = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    _say(f"wan1p3b_proj: fused forward against the two kernels {d:.2e} (bit-identical: {np.array_equal(a, b)})")
+    assert d <= 1e-6, d
 
 
 def test_two_runs_bit_identical(dqm):
@@ -389,7 +399,7 @@ def _compare_every_cube(got, xf, g, chunk=2048):
 
 
 def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=512, versus_direct=False,
-                    every_cube=True):
+                    every_cube=True, fused=False):
     T, H, W = cfg.T, cfg.H, cfg.W
     g = cubes.Geometry(T, H, W, *cube)
     _say(f"case {cfg.name} cube {cube} seed {xseed}: generating")
@@ -432,6 +442,21 @@ def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=5
     err, row = _check_y(y.cpu().numpy()[q["tokens"]], yo, bound)
     _say(f"{cfg.name} cube {cube} seed {xseed}: codes bit-exact on {len(ids)} cubes; "
          f"Y rel err {err:.2e} worst row {row:.2e} on {len(q['tokens'])} tokens")
+    if fused:
+        # the one-kernel forward on the same activation state: the oracle's bar
+        # on the sampled tokens, and against the two kernels on every output
+        # (the core GEMM's odd tiles sum K backwards, so the two differ only in
+        # the order of the core term's fp32 additions)
+        y2 = torch.full((cfg.N, cfg.Co), float("nan"), device=DEV)
+        dqm.dq_linear_forward_fused(weights, qa, y2)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y2).any().item(), "unwritten outputs (fused)"
+        err2, row2 = _check_y(y2.cpu().numpy()[q["tokens"]], yo, bound)
+        d = (torch.linalg.vector_norm(y2 - y) / torch.linalg.vector_norm(y)).item()
+        same = torch.equal(y2, y)
+        _say(f"{cfg.name} cube {cube}: fused forward Y rel err {err2:.2e} worst row {row2:.2e}; "
+             f"against the two kernels {d:.2e} over all outputs (bit-identical: {same})")
+        assert d <= 1e-6, d
     if versus_direct:
         # output error against the exact X W (fp64) on 128 of the sampled
         # tokens: delta W4A4 (the GPU output) and direct W4A4 of X (oracle:
@@ -456,7 +481,7 @@ def test_attn14b_projection_sampled(dqm):
 
 def test_ffn_up_720p_sampled(dqm):
     cfg = synth.CONFIGS["ffn_up_720p"]
-    _full_size_case(dqm, cfg, cfg.cubes[0], cfg.x_seeds[0], check_weights=True)
+    _full_size_case(dqm, cfg, cfg.cubes[0], cfg.x_seeds[0], check_weights=True, fused=True)
 
 
 @pytest.mark.parametrize("cube,step", [((4, 1, 4), 0), ((4, 2, 8), 1)], ids=["4x1x4", "4x2x8"])
