@@ -271,8 +271,10 @@ def test_forward_halves_match_forward(dqm):
     assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("shape", [(4, 16, 16, 512, 512), (3, 10, 18, 1024, 768), (2, 9, 30, 640, 256)],
-                         ids=["1024tok_ci512", "540tok_ci1024_ragged", "540tok_ci640_odd_cubes"])
+@pytest.mark.parametrize("shape", [(4, 16, 16, 512, 512, "bf16", 32), (3, 10, 18, 1024, 768, "bf16", 32),
+                                   (2, 9, 30, 640, 256, "bf16", 32), (3, 7, 22, 576, 512, "f32", 64)],
+                         ids=["1024tok_ci512", "540tok_ci1024_ragged", "540tok_ci640_odd_cubes",
+                              "462tok_ci576_padded_f32_g64"])
 def test_fused_forward_matches_halves(dqm, shape):
     """4-token cubes with FP8 cores: dq_linear_forward_fused runs the one-kernel
     form (core and delta partial sums in one K loop), dq_core_term +
@@ -281,13 +283,13 @@ def test_fused_forward_matches_halves(dqm, shape):
     MFMA blocks in the same order and add the same terms, so y is
     bit-identical, pad slots and clipped cubes included; the layer also meets
     the oracle's bar."""
-    T, H, W, Ci, Co = shape
+    T, H, W, Ci, Co, dtype, core_group = shape
     _say(f"case fused forward {shape}")
-    x = synth.make_activation(T, H, W, Ci, seed=25, dtype="bf16", n_outliers=4).to(DEV)
-    wt = synth.make_weight(Ci, Co, seed=26, dtype="bf16")
+    x = synth.make_activation(T, H, W, Ci, seed=25, dtype=dtype, n_outliers=4).to(DEV)
+    wt = synth.make_weight(Ci, Co, seed=26, dtype=dtype)
     l1, l2 = _random_factors(Ci, Co, 32, 29)
     weights = dqm.dq_prepare_weights_lowrank(wt, l1, l2)
-    qa = dqm.dq_qact_create(weights, (T, H, W, 1, 2, 2))
+    qa = dqm.dq_qact_create(weights, (T, H, W, 1, 2, 2), core_group=core_group)
     dqm.dq_quantize_act(weights, x, qa)
     y1 = torch.full((T * H * W, Co), float("nan"), device=DEV)
     y2 = torch.full((T * H * W, Co), float("nan"), device=DEV)
@@ -299,7 +301,7 @@ def test_fused_forward_matches_halves(dqm, shape):
     assert np.isfinite(a).all()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"max diff {np.abs(a - b).max()}"
     L = dict(x=synth.to_f32_numpy(x.cpu()), wt=synth.to_f32_numpy(wt), l1=l1, l2=l2, weights=weights, qa=qa, y=a,
-             g=cubes.Geometry(T, H, W, 1, 2, 2))
+             g=cubes.Geometry(T, H, W, 1, 2, 2), core_group=core_group)
     err, row = _full_compare(dqm, L)
     _say(f"fused {shape}: rel err {err:.2e} worst row {row:.2e}")
 
