@@ -21,7 +21,8 @@ roofline = the dominant kernel, the delta GEMM (dq_delta_term: one launch of
          one FP8 x FP4 GEMM over the cubes and is rated against the FP8 peak.
 fused_forward = the one-kernel form of the forward (dq_linear_forward_fused:
          core and delta partial sums in one K loop, no per-cube term in
-         memory), timed beside the two kernels; not part of the step.
+         memory), timed beside the two kernels; dq_linear takes it on small
+         layers (forward.form names the form the step runs).
 cpu_baseline = the CPU oracle on a bounded sample of the same workload, its
          time extrapolated to the whole layer by the token count.
 
@@ -458,8 +459,9 @@ def main():
     # per-phase events on the launch stream
     ms_step, q_ms, c_ms, d_ms = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
     fused_ms = time_fused(dq, weights, qa, y, stream, args.steps)
+    form = dq.dq_forward_form(weights, qa)          # the form dq_linear's forward takes for this layer
     ctype = "bf16" if args.core_bits == 16 else f"fp{args.core_bits}"      # the core GEMM's input type
-    f_ms = c_ms + d_ms
+    f_ms = fused_ms if form == "one kernel" and fused_ms is not None else c_ms + d_ms
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     # device-to-device copy rate (the practical ceiling of the activation pass)
@@ -480,16 +482,25 @@ def main():
     # the dominant kernel: the delta GEMM (FP4 x FP4) on 2 N Ci Co; with
     # one-token cubes it is the FP8 x FP4 GEMM over the cubes (FP4 x FP4 for
     # FP4 cores), on 2 K Ci Co
+    rl_ms = d_ms
     if S == 1:
         rl_flops, rl_peak = f_fp8, {8: PEAK_FP8, 4: PEAK_FP4, 16: PEAK_FP8}[args.core_bits]
         rl_kernel = ("GEMM over the one-token cubes (dq_delta_term: FP8 x FP4 scaled MFMA, Q8(x) Q4(R); "
                      "low-rank branch and token-order stores in the epilogue)")
+    elif form == "one kernel":
+        # the one-kernel forward: both contractions, the FP8 x FP4 flops
+        # counted at the FP4 peak's rate (PEAK_FP4 / PEAK_FP8 each), so frac
+        # is the time both would take at their peaks over the measured time
+        rl_flops, rl_peak, rl_ms = f_fp4 + f_fp8 * PEAK_FP4 / PEAK_FP8, PEAK_FP4, fused_ms
+        rl_kernel = ("one-kernel forward (dq_linear_forward_fused: FP4 x FP4 delta and FP8 x FP4 core MFMAs in one "
+                     "K loop, FP8 flops counted at the FP4 rate; low-rank branch, core term and token-order stores "
+                     "in the epilogue)")
     else:
         rl_flops, rl_peak = f_fp4, PEAK_FP4
         rl_kernel = ("delta GEMM (dq_delta_term: FP4 x FP4 scaled MFMA over the slots; low-rank branch, "
                      "core-term broadcast and token-order stores in the epilogue)")
-    achieved = rl_flops / (d_ms * 1e-3)
-    traffic = committed_traffic(args.config, cube)
+    achieved = rl_flops / (rl_ms * 1e-3)
+    traffic = committed_traffic(args.config, cube) if form == "two kernels" or S == 1 else None
 
     cpu = sanity = None
     if not args.no_cpu_baseline:
@@ -520,6 +531,7 @@ def main():
         },
         "pct_fp4_peak_step": round(100 * dense_flops / (ms_step * 1e-3) / PEAK_FP4, 2),
         "forward": {
+            "form": form,
             "ms": round(f_ms, 4),
             "effective_tops": round(dense_flops / (f_ms * 1e-3) / 1e12, 2),
             "pct_fp4_peak": round(100 * dense_flops / (f_ms * 1e-3) / PEAK_FP4, 2),
@@ -534,11 +546,11 @@ def main():
             "pct_copy": round(100 * quant_bytes / (q_ms * 1e-3) / 1e9 / copy_gbps, 2),
         },
         "core_overhead": core_overhead(wk, c_ms, d_ms, args.core_bits),
-        # the one-kernel form of the forward (dq_linear_forward_fused), not
-        # used by the step: the two kernels above measured faster
+        # the one-kernel form of the forward (dq_linear_forward_fused), which
+        # the step uses on small layers (forward.form)
         "fused_forward": None if fused_ms is None else {
             "ms": round(fused_ms, 4),
-            "vs_two_kernels": round(fused_ms / f_ms, 4),
+            "vs_two_kernels": round(fused_ms / (c_ms + d_ms), 4),
             "effective_tops": round(dense_flops / (fused_ms * 1e-3) / 1e12, 2),
             "hbm_saved_bytes": int(2 * 4 * K * Co),
         },
@@ -555,7 +567,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / rl_peak, 4),
             "traffic": traffic,
-            "ms": round(d_ms, 4),
+            "ms": round(rl_ms, 4),
             "work": {"fp4_flops": f_fp4, "fp4_flops_executed": wk["fp4_slots"], "fp8_flops": f_fp8,
                      "bf16_flops": f_bf16},
             "pad_slot_waste": round(wk["fp4_slots"] / f_fp4 - 1, 4),

@@ -203,10 +203,20 @@ dq_status dq_delta_term(const dq_weights* w, dq_qact* q, float* y_dev, void* str
  * tokens (t h w = 4) with FP8 cores in one frame segment, rank 32, Co a
  * multiple of 256, Ci >= 512 and y_dev 16-byte aligned; other workspaces
  * return DQ_ERR_INVALID_ARG.  Arguments, ownership and asynchrony as
- * dq_linear_forward.  On MI355X it measured slower than the two-kernel form
- * (the fused K loop also carries the cores' operand steps and is bound by
- * operand delivery), so dq_linear_forward does not use it. */
+ * dq_linear_forward.  dq_linear_forward (and so dq_linear and
+ * dq_linear_noalloc) runs this form itself where it applies and the layer has
+ * at most 16 rounds of 256 x 256 output tiles per compute unit: on MI355X it
+ * measured faster on such small layers and slower on larger ones (the fused
+ * K loop also carries the cores' operand steps and is bound by operand
+ * delivery). */
 dq_status dq_linear_forward_fused(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
+
+/* Which form dq_linear_forward takes for this weight and workspace, for a
+ * 16-byte aligned y_dev: *one_kernel = 1 for the one-kernel form above, 0 for
+ * dq_core_term followed by dq_delta_term.  Host only (queries the device's
+ * compute-unit count); DQ_ERR_INVALID_ARG for a NULL or mismatched handle or
+ * a NULL one_kernel. */
+dq_status dq_forward_form(const dq_weights* w, const dq_qact* q, int* one_kernel);
 
 /* dq_quantize_act followed by dq_linear_forward on the same stream. */
 dq_status dq_linear(const dq_weights* w, const void* x_dev, dq_dtype dt, dq_qact* q, float* y_dev, void* stream);

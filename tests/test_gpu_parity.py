@@ -220,16 +220,20 @@ def test_wan1p3b_projection_full(dqm):
                cfg.x_seeds[0], cfg.w_seed, svd="oracle", n_out=cfg.n_outliers, w_out=0)
     err, row = _full_compare(dqm, L)
     _say(f"wan1p3b_proj: rel err {err:.2e} worst row {row:.2e}")
-    # the one-kernel forward on the same activation state, against the two
-    # kernels' output (checked in full above) on every element
+    # a layer of 3 rounds of tiles: dq_linear takes the one-kernel form (its
+    # output was checked in full above); the two kernels on the same
+    # activation state give the same output (the core GEMM runs one round,
+    # every tile forwards: bit-identical)
+    assert dqm.dq_forward_form(L["weights"], L["qa"]) == "one kernel"
     y2 = torch.full((cfg.N, cfg.Co), float("nan"), device=DEV)
-    dqm.dq_linear_forward_fused(L["weights"], L["qa"], y2)
+    dqm.dq_core_term(L["weights"], L["qa"])
+    dqm.dq_delta_term(L["weights"], L["qa"], y2)
     torch.cuda.synchronize()
     a, b = y2.cpu().numpy(), L["y"]
-    assert np.isfinite(a).all(), "unwritten outputs (fused)"
+    assert np.isfinite(a).all(), "unwritten outputs (two kernels)"
     d = float(np.linalg.norm(a - b) / np.linalg.norm(b))
-    _say(f"wan1p3b_proj: fused forward against the two kernels {d:.2e} (bit-identical: {np.array_equal(a, b)})")
-    assert d <= 1e-6, d
+    _say(f"wan1p3b_proj: two kernels against the one-kernel form {d:.2e} (bit-identical: {np.array_equal(a, b)})")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), d
 
 
 def test_two_runs_bit_identical(dqm):
@@ -253,7 +257,8 @@ def test_two_runs_bit_identical(dqm):
 
 
 def test_forward_halves_match_forward(dqm):
-    """dq_core_term then dq_delta_term is dq_linear_forward (the same launches)."""
+    """dq_core_term then dq_delta_term is dq_linear_forward (the same launches;
+    with Ci = 256 the one-kernel form does not apply)."""
     _say("case forward halves")
     T, H, W, Ci, Co = 4, 10, 12, 256, 512
     x = synth.make_activation(T, H, W, Ci, seed=15, dtype="bf16", n_outliers=4).to(DEV)
@@ -304,6 +309,23 @@ def test_fused_forward_matches_halves(dqm, shape):
              g=cubes.Geometry(T, H, W, 1, 2, 2), core_group=core_group)
     err, row = _full_compare(dqm, L)
     _say(f"fused {shape}: rel err {err:.2e} worst row {row:.2e}")
+
+
+def test_forward_form_choice(dqm):
+    """dq_linear_forward takes the one-kernel form for 4-token FP8-core layers
+    of at most 16 rounds of 256 x 256 tiles per compute unit, the two kernels
+    beyond and wherever the one-kernel form does not apply."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wt = synth.make_weight(512, 8192, seed=46, dtype="bf16")
+    l1, l2 = _random_factors(512, 8192, 32, 49)
+    weights = dqm.dq_prepare_weights_lowrank(wt, l1, l2)
+    for (T, H, W), cube in (((4, 16, 16), (1, 2, 2)), ((4, 96, 96), (1, 2, 2)), ((4, 16, 16), (2, 2, 2))):
+        qa = dqm.dq_qact_create(weights, (T, H, W) + cube)
+        slots = -(-(T // cube[0]) * -(-H // cube[1]) * -(-W // cube[2]) * cube[0] * cube[1] * cube[2] // 256)
+        tiles = (8192 // 256) * slots
+        want = "one kernel" if (cube == (1, 2, 2) and tiles <= 16 * cus) else "two kernels"
+        _say(f"form {T}x{H}x{W} cube {cube}: {tiles} tiles -> {dqm.dq_forward_form(weights, qa)}")
+        assert dqm.dq_forward_form(weights, qa) == want
 
 
 def test_fused_forward_rejects_other_shapes(dqm):

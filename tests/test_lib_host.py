@@ -66,6 +66,7 @@ def test_argument_errors_before_any_device_work(lib):
     _expect(lib.dq_core_term(None, None, None), 1, lib)
     _expect(lib.dq_delta_term(None, None, None, None), 1, lib)
     _expect(lib.dq_linear_forward_fused(None, None, None, None), 1, lib)
+    _expect(lib.dq_forward_form(None, None, None), 1, lib)
     _expect(lib.dq_lowrank_factors(P(w), 0, 96, 64, -1, 0, P(l1), P(l2)), 1, lib)
     _expect(lib.dq_lowrank_factors(P(w), 0, 0, 64, 1, 0, P(l1), P(l2)), 2, lib)
 

@@ -143,6 +143,25 @@ bool fused_applies(const dq_weights* w, const dq_qact* q, const float* y) {
     return q->core_bits == 8 && q->g.S == 4 && q->nseg == 1 && w->Kp / 128 >= 4 && w->rp == 32 && w->Co % 256 == 0 &&
            (uintptr_t)y % 16 == 0 && q->g.N * w->Co < (1ll << 31) && q->Nslot_pad / 4 <= q->K_pad;
 }
+
+// The form the whole forward takes: the one-kernel form where it applies and
+// the layer has at most 16 rounds of 256 x 256 tiles per CU, else the two
+// kernels.  Measured with 4-token cubes on MI355X (one-kernel time over
+// two-kernel time): Wan 1.3B projection, 3 rounds, 0.77; 14B attention
+// projection, 9.5 rounds, 0.95; 720p FFN down, 23.6 rounds, 1.02; 720p FFN up,
+// 63.7 rounds, 1.03.  The two-kernel form's fixed costs (the core GEMM's
+// launch and partly filled last round, the per-cube term's round trip) weigh
+// most on small layers; on large ones the fused K loop's extra operand bytes
+// cost more than they save.
+bool fused_preferred(const dq_weights* w, const dq_qact* q, const float* y) {
+    if (!fused_applies(w, q, y)) return false;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    const long long tiles = (w->Cop / 256) * (q->Nslot_pad / 256);
+    return tiles <= 16ll * cus;
+}
 }  // namespace dq
 
 extern "C" {
@@ -585,6 +604,18 @@ static dq_status forward_parts(const dq_weights* w, dq_qact* q, float* y_dev, in
 
 dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {
     return forward_parts(w, q, y_dev, dq::FWD_CORE | dq::FWD_DELTA, stream);
+}
+
+dq_status dq_forward_form(const dq_weights* w, const dq_qact* q, int* one_kernel) {
+    g_last_error.clear();
+    dq_status st = check_pair(w, q);
+    if (st != DQ_OK) return st;
+    if (!one_kernel) return fail(DQ_ERR_INVALID_ARG, "one_kernel is NULL");
+    DeviceGuard dg(q->device);
+    if (!dg.ok) return fail(DQ_ERR_DEVICE, "hipSetDevice failed");
+    alignas(16) static const float aligned_y = 0.0f;           // stands for a 16-byte aligned y_dev
+    *one_kernel = dq::fused_preferred(w, q, &aligned_y) ? 1 : 0;
+    return DQ_OK;
 }
 
 dq_status dq_linear_forward_fused(const dq_weights* w, dq_qact* q, float* y_dev, void* stream) {

@@ -267,6 +267,8 @@ hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, 
 // shapes it takes (4-slot cubes, FP8 cores, one frame segment, rank 32,
 // Co % 256 == 0, Ci of 512 or more, y 16-byte aligned).
 bool fused_applies(const dq_weights* w, const dq_qact* q, const float* y);
+// ... and whether the whole forward takes it (small layers: at most 16 rounds of tiles)
+bool fused_preferred(const dq_weights* w, const dq_qact* q, const float* y);
 hipError_t launch_forward_fused(const dq_weights* w, dq_qact* q, float* y, hipStream_t st);
 // y = U L2 + Q6(X) Q6(R) for a 6-bit layer
 hipError_t launch_forward6(const dq_weights* w, dq_act6* a, float* y, hipStream_t st);

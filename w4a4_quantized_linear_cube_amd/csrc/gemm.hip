@@ -1419,10 +1419,10 @@ static hipError_t launch_store(const GemmArgs& a, const KSplit& ks, float* part,
 
 // The fused form (fused_applies: cubes of exactly 4 slots with FP8 cores in
 // one frame segment, so a 256-slot tile's cubes are the 64 rows 64 tn .. of
-// the core codes) is the dq_linear_forward_fused entry point;
-// dq_linear_forward keeps the two kernels, which measured faster on MI355X
-// (the fused K loop carries the cores' operand steps too, and it is bound by
-// operand delivery).
+// the core codes) is the dq_linear_forward_fused entry point, and the whole
+// forward of the layers fused_preferred picks (small ones: the two kernels
+// measured faster on large layers, whose fused K loop carries the cores'
+// operand steps too and is bound by operand delivery).
 hipError_t launch_forward_fused(const dq_weights* w, dq_qact* q, float* y, hipStream_t st) {
     if (!fused_applies(w, q, y)) return hipErrorInvalidValue;
     FusedArgs f{};
@@ -1446,6 +1446,7 @@ hipError_t launch_forward_fused(const dq_weights* w, dq_qact* q, float* y, hipSt
 }
 
 hipError_t launch_forward(const dq_weights* w, dq_qact* q, float* y, int parts, hipStream_t st) {
+    if ((parts & FWD_CORE) && (parts & FWD_DELTA) && fused_preferred(w, q, y)) return launch_forward_fused(w, q, y, st);
     GemmArgs d{};
     d.a = w->rq;
     d.as = w->rs;

@@ -25,7 +25,7 @@ STATUS = {0: "DQ_OK", 1: "DQ_ERR_INVALID_ARG", 2: "DQ_ERR_SHAPE", 3: "DQ_ERR_UNS
 EXPORTS = ("dq_last_error", "dq_status_str", "dq_lowrank_factors", "dq_prepare_weights_lowrank",
            "dq_prepare_weights", "dq_weights_destroy", "dq_weights_info", "dq_weights_export",
            "dq_qact_create", "dq_qact_create_ex", "dq_qact_destroy", "dq_qact_info", "dq_quantize_act", "dq_linear_forward",
-           "dq_core_term", "dq_delta_term", "dq_linear_forward_fused", "dq_linear", "dq_qact_export", "dq_linear_noalloc",
+           "dq_core_term", "dq_delta_term", "dq_linear_forward_fused", "dq_forward_form", "dq_linear", "dq_qact_export", "dq_linear_noalloc",
            "dq_prepare_weights_w6", "dq_act6_create", "dq_act6_destroy", "dq_quantize_act6", "dq_linear6_forward",
            "dq_linear6", "dq_act6_export", "dq_orbit_prepare", "dq_orbit_destroy", "dq_orbit_export",
            "dq_orbit_act_create", "dq_orbit_act_destroy", "dq_orbit_quantize_act", "dq_orbit_forward", "dq_orbit_linear",
@@ -77,6 +77,7 @@ def load():
         "dq_core_term": ([P, P, P], ctypes.c_int),
         "dq_delta_term": ([P, P, P, P], ctypes.c_int),
         "dq_linear_forward_fused": ([P, P, P, P], ctypes.c_int),
+        "dq_forward_form": ([P, P, P], ctypes.c_int),
         "dq_linear": ([P, P, ctypes.c_int, P, P, P], ctypes.c_int),
         "dq_qact_export": ([P, P, P, P, P, P, P], ctypes.c_int),
         "dq_linear_noalloc": ([P, P, ctypes.c_int, Geom, P, P], ctypes.c_int),
@@ -324,6 +325,14 @@ def dq_linear_forward_fused(w: Weights, q: QAct, y, stream=None):
     _check_pair("dq_linear_forward_fused", w, q)
     _check_y("dq_linear_forward_fused", w, q, y)
     _check(load().dq_linear_forward_fused(w.handle, q.handle, _ptr(y), _stream(stream)), "dq_linear_forward_fused")
+
+
+def dq_forward_form(w: Weights, q: QAct) -> str:
+    """'one kernel' or 'two kernels': the form dq_linear_forward takes for this pair."""
+    _check_pair("dq_forward_form", w, q)
+    flag = ctypes.c_int(0)
+    _check(load().dq_forward_form(w.handle, q.handle, ctypes.byref(flag)), "dq_forward_form")
+    return "one kernel" if flag.value else "two kernels"
 
 
 def dq_linear(w: Weights, x, q: QAct, y, stream=None):
