@@ -172,7 +172,10 @@ dq_status dq_quantize_act(const dq_weights* w, const void* x_dev, dq_dtype dt, d
  * written to y_dev [N][Co] fp32 (every element written; contiguous, 4-byte
  * aligned, else DQ_ERR_INVALID_ARG; a shorter buffer is written out of
  * bounds, which the library cannot detect).  Uses the state left in `q` by
- * the last dq_quantize_act.  Asynchronous on `stream`. */
+ * the last dq_quantize_act.  Asynchronous on `stream`.  It runs
+ * dq_core_term then dq_delta_term, or, for small layers of 4-token cubes, the
+ * one-kernel form dq_linear_forward_fused (dq_forward_form tells which); the
+ * per-cube term in `q` is then not written. */
 dq_status dq_linear_forward(const dq_weights* w, dq_qact* q, float* y_dev, void* stream);
 
 /* The two halves of dq_linear_forward, in its order, for callers that time
