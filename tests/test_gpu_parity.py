@@ -423,7 +423,7 @@ def _compare_every_cube(got, xf, g, chunk=2048):
 
 
 def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=512, versus_direct=False,
-                    every_cube=True, fused=False):
+                    every_cube=True, other_form=False):
     T, H, W = cfg.T, cfg.H, cfg.W
     g = cubes.Geometry(T, H, W, *cube)
     _say(f"case {cfg.name} cube {cube} seed {xseed}: generating")
@@ -466,20 +466,26 @@ def _full_size_case(dqm, cfg, cube, xseed, check_weights, n_cubes=48, max_rows=5
     err, row = _check_y(y.cpu().numpy()[q["tokens"]], yo, bound)
     _say(f"{cfg.name} cube {cube} seed {xseed}: codes bit-exact on {len(ids)} cubes; "
          f"Y rel err {err:.2e} worst row {row:.2e} on {len(q['tokens'])} tokens")
-    if fused:
-        # the one-kernel forward on the same activation state: the oracle's bar
-        # on the sampled tokens, and against the two kernels on every output
-        # (the core GEMM's odd tiles sum K backwards, so the two differ only in
-        # the order of the core term's fp32 additions)
+    if other_form:
+        # the form of the forward dq_linear did not take (one kernel, or the
+        # two kernels), on the same activation state: the oracle's bar on the
+        # sampled tokens, and against dq_linear's output on every element (the
+        # core GEMM's odd tiles sum K backwards, so the two may differ in the
+        # order of the core term's fp32 additions)
+        form = dqm.dq_forward_form(weights, qa)
         y2 = torch.full((cfg.N, cfg.Co), float("nan"), device=DEV)
-        dqm.dq_linear_forward_fused(weights, qa, y2)
+        if form == "one kernel":
+            dqm.dq_core_term(weights, qa)
+            dqm.dq_delta_term(weights, qa, y2)
+        else:
+            dqm.dq_linear_forward_fused(weights, qa, y2)
         torch.cuda.synchronize()
-        assert not torch.isnan(y2).any().item(), "unwritten outputs (fused)"
+        assert not torch.isnan(y2).any().item(), "unwritten outputs (other form)"
         err2, row2 = _check_y(y2.cpu().numpy()[q["tokens"]], yo, bound)
         d = (torch.linalg.vector_norm(y2 - y) / torch.linalg.vector_norm(y)).item()
         same = torch.equal(y2, y)
-        _say(f"{cfg.name} cube {cube}: fused forward Y rel err {err2:.2e} worst row {row2:.2e}; "
-             f"against the two kernels {d:.2e} over all outputs (bit-identical: {same})")
+        _say(f"{cfg.name} cube {cube}: dq_linear took {form}; the other form Y rel err {err2:.2e} worst row "
+             f"{row2:.2e}, against dq_linear {d:.2e} over all outputs (bit-identical: {same})")
         assert d <= 1e-6, d
     if versus_direct:
         # output error against the exact X W (fp64) on 128 of the sampled
@@ -503,9 +509,17 @@ def test_attn14b_projection_sampled(dqm):
         _full_size_case(dqm, cfg, cfg.cubes[0], seed, check_weights=(i == 0), n_cubes=24)
 
 
+def test_attn14b_projection_4token_cubes(dqm):
+    """The 14B attention projection with 4-token cubes: 9.5 rounds of tiles,
+    so dq_linear takes the one-kernel forward; checked against the oracle on
+    sampled cubes and against the two kernels on every output."""
+    cfg = synth.CONFIGS["attn14b_proj"]
+    _full_size_case(dqm, cfg, (1, 2, 2), cfg.x_seeds[0], check_weights=False, n_cubes=24, other_form=True)
+
+
 def test_ffn_up_720p_sampled(dqm):
     cfg = synth.CONFIGS["ffn_up_720p"]
-    _full_size_case(dqm, cfg, cfg.cubes[0], cfg.x_seeds[0], check_weights=True, fused=True)
+    _full_size_case(dqm, cfg, cfg.cubes[0], cfg.x_seeds[0], check_weights=True, other_form=True)
 
 
 @pytest.mark.parametrize("cube,step", [((4, 1, 4), 0), ((4, 2, 8), 1)], ids=["4x1x4", "4x2x8"])
