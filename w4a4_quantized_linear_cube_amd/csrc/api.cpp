@@ -155,12 +155,8 @@ bool fused_applies(const dq_weights* w, const dq_qact* q, const float* y) {
 // cost more than they save.
 bool fused_preferred(const dq_weights* w, const dq_qact* q, const float* y) {
     if (!fused_applies(w, q, y)) return false;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
     const long long tiles = (w->Cop / 256) * (q->Nslot_pad / 256);
-    return tiles <= 16ll * cus;
+    return tiles <= 16ll * q->cus;
 }
 }  // namespace dq
 
@@ -476,7 +472,8 @@ dq_status plan_qact(const dq_weights* w, const dq_geom& geom, int core_group, in
     if (!mul_ok(q->Nslot_pad, q->Kp, lim) || !mul_ok(q->K_pad, q->Cop, lim) || !mul_ok(max_partials, q->Kp, lim))
         return fail(DQ_ERR_SHAPE, "workspace too large");
     int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, w->device) != hipSuccess) cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, w->device) != hipSuccess || cus <= 0) cus = 256;
+    q->cus = cus;
     // the activation pass's channel split: the U partials of the largest
     // segment it may split (blocks of 64 slots, or of whole cubes up to 64
     // tokens)

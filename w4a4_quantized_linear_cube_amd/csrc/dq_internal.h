@@ -195,6 +195,7 @@ struct dq_qact {
     int64_t upart_rows = 0;    // largest slot count of a segment the activation pass may split by channels
     float* upart = nullptr;    // [QMAXPARTS][upart_rows][rp] fp32 U partials of such a segment (upart_rows > 0, rp > 0)
     dq::KSplit ks{};           // K split of the core GEMM's last round (set by plan_qact)
+    int cus = 256;             // compute units of the device (set by plan_qact)
     float* kpart = nullptr;    // [ks.rm * ks.p][256][256] fp32 K-chunk partials of that round (ks.rm > 0)
     size_t bytes = 0;
 };
