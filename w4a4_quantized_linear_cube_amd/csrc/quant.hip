@@ -417,7 +417,9 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
             const int ch = c0 + ((lane & 15) ^ (r & 15)) * EPC;   // first channel of the logical piece at this position
             const void* src = (tokr[j] >= 0 && ch < a.Ci) ? (const void*)(x + (long long)tokr[j] * a.Ci + ch)
                                                           : (const void*)(a.zero + 16 * (lane & 15));
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(base + j * 1024)), "v"(src)
+            // (nontemporal: each byte of X is read once; the L1 rows below are
+            // read by every block and keep the default policy)
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(__builtin_amdgcn_readfirstlane(base + j * 1024)), "v"(src)
                          : "memory", "m0");
         }
         // L1 rows of the chunk (in bounds: l1t rows are Kp wide, zero past Ci)
