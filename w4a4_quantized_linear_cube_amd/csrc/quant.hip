@@ -831,14 +831,15 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const bool lv = qq_l == 0 ? live[0] : qq_l == 1 ? live[1] : qq_l == 2 ? live[2] : live[3];
                     const int ex = qq_l == 0 ? exq[0] : qq_l == 1 ? exq[1] : qq_l == 2 ? exq[2] : exq[3];
                     const int r = (qtid >> 4) + 16 * qq_l;
+                    // (delta codes: nontemporal stores, read once by the delta GEMM)
                     if (lv) {
                         if (tile64) {
                             const int G = (c0 >> 5) + gc_l, rt = (int)(B.slot0 & 255) + r;
-                            *(uint4*)(dq_t + toff_fp4(rt, G)) = make_uint4(code[0], code[1], code[2], code[3]);
+                            __builtin_nontemporal_store(v4i{(int)code[0], (int)code[1], (int)code[2], (int)code[3]}, (v4i*)(dq_t + toff_fp4(rt, G)));
                             ds_t[toff_scale(rt, G)] = (uint8_t)(ex + 127);
                         } else {
                             const long long G = (c0 >> 5) + gc_l, sl = B.slot0 + r;
-                            *(uint4*)(a.dq + off_fp4(sl, G, nks)) = make_uint4(code[0], code[1], code[2], code[3]);
+                            __builtin_nontemporal_store(v4i{(int)code[0], (int)code[1], (int)code[2], (int)code[3]}, (v4i*)(a.dq + off_fp4(sl, G, nks)));
                             a.ds[off_scale(sl, G, nks)] = (uint8_t)(ex + 127);
                         }
                     }
@@ -851,11 +852,11 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
                     const int r = pr / NGC, gc = pr - r * NGC;
                     if (tile64) {
                         const int G = (c0 >> 5) + gc, rt = (int)(B.slot0 & 255) + r;
-                        *(uint32_t*)(dq_t + toff_fp4(rt, G) + 4 * qq) = code[n];
+                        __builtin_nontemporal_store(code[n], (uint32_t*)(dq_t + toff_fp4(rt, G) + 4 * qq));
                         if (qq == 0) ds_t[toff_scale(rt, G)] = (uint8_t)(exq[n] + 127);
                     } else {
                         const long long G = (c0 >> 5) + gc, sl = B.slot0 + r;
-                        *(uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq) = code[n];
+                        __builtin_nontemporal_store(code[n], (uint32_t*)(a.dq + off_fp4(sl, G, nks) + 4 * qq));
                         if (qq == 0) a.ds[off_scale(sl, G, nks)] = (uint8_t)(exq[n] + 127);
                     }
                 }
@@ -969,7 +970,13 @@ __global__ __launch_bounds__((QCfg<XT, NCT>::THREADS), 1) void k_quantize(QuantA
         };
         xchg(code, std::integral_constant<int, 1>{}, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
         xchg(code, std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
-        *(uint4*)(dq_t + (size_t)kc * 16384 + f4_drow) = make_uint4(code[0], code[1], code[2], code[3]);
+        // (nontemporal: the delta codes stream out and are read once, by the
+        // delta GEMM; the core codes keep the default policy, which measures
+        // faster for them)
+        {
+            const v4i cv = {(int)code[0], (int)code[1], (int)code[2], (int)code[3]};
+            __builtin_nontemporal_store(cv, (v4i*)(dq_t + (size_t)kc * 16384 + f4_drow));
+        }
         const int exq = f4_qq == 0 ? ex[0] : f4_qq == 1 ? ex[1] : f4_qq == 2 ? ex[2] : ex[3];
         ds_t[(size_t)kc * 1024 + f4_ds] = (uint8_t)(exq + 127);
       }
