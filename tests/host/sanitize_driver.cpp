@@ -206,6 +206,44 @@ int main() {
         EXPECT(dq::plan_qact(&fu, dq_geom{21, 45, 80, 4, 2, 8}, 32, 8, &q, &mp) == DQ_OK);
         EXPECT(q.nseg == 2 && q.upart_rows == q.seg[1].g.Nslot && q.seg[1].g.Nslot == 23 * 10 * 16);
     }
+    {   // the forward's form: one kernel for 4-token cubes with FP8 cores on
+        // layers of at most 16 rounds of 256 x 256 tiles per CU of the
+        // workspace's device (256 here: without a device the count falls back
+        // to it), two kernels otherwise
+        auto layer = [](int64_t Ci, int64_t Co) {
+            dq_weights f;
+            f.Ci = Ci;
+            f.Co = Co;
+            f.Kp = (Ci + 255) / 256 * 256;
+            f.Cop = (Co + 255) / 256 * 256;
+            f.rank = 32;
+            f.rp = 32;
+            return f;
+        };
+        alignas(16) static float yy[4];
+        auto form = [&](const dq_weights& f, dq_geom g, int bits, const float* y, int cus, bool* applies) {
+            dq_qact q{};
+            int64_t mp = 0;
+            if (dq::plan_qact(&f, g, 32, bits, &q, &mp) != DQ_OK) { ++failures; return false; }
+            EXPECT(q.cus == 256);
+            if (cus) q.cus = cus;
+            *applies = dq::fused_applies(&f, &q, y);
+            return dq::fused_preferred(&f, &q, y);
+        };
+        const dq_weights wan = layer(1536, 1536), attn = layer(5120, 5120), up = layer(5120, 13824), down = layer(13824, 5120);
+        bool ap = false;
+        EXPECT(form(wan, dq_geom{21, 30, 52, 1, 2, 2}, 8, yy, 0, &ap) && ap);            //   768 tiles
+        EXPECT(form(attn, dq_geom{20, 30, 52, 1, 2, 2}, 8, yy, 0, &ap) && ap);           //  2440 tiles
+        EXPECT(!form(up, dq_geom{21, 45, 80, 1, 2, 2}, 8, yy, 0, &ap) && ap);            // 16308 tiles
+        EXPECT(!form(down, dq_geom{21, 45, 80, 1, 2, 2}, 8, yy, 0, &ap) && ap);          //  6040 tiles
+        EXPECT(!form(attn, dq_geom{20, 30, 52, 1, 2, 2}, 8, yy, 64, &ap) && ap);         // a 64-CU device: 1024 at most
+        EXPECT(form(wan, dq_geom{21, 30, 52, 1, 2, 2}, 8, yy, 64, &ap) && ap);
+        EXPECT(!form(attn, dq_geom{20, 30, 52, 2, 2, 2}, 8, yy, 0, &ap) && !ap);         // 8-token cubes
+        EXPECT(!form(attn, dq_geom{20, 30, 52, 1, 2, 2}, 4, yy, 0, &ap) && !ap);         // FP4 cores
+        EXPECT(!form(attn, dq_geom{20, 30, 52, 1, 2, 2}, 8, yy + 1, 0, &ap) && !ap);     // y not 16-byte aligned
+        EXPECT(!form(layer(256, 5120), dq_geom{20, 30, 52, 1, 2, 2}, 8, yy, 0, &ap) && !ap);   // 2 K steps
+        EXPECT(form(layer(384, 5120), dq_geom{20, 30, 52, 1, 2, 2}, 8, yy, 0, &ap) && ap);     // 4 (Kp 512)
+    }
     std::printf("host sanitize driver: %lld geometries planned, %d failures\n", planned, failures);
     return failures ? 1 : 0;
 }
