@@ -57,7 +57,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20, help="untimed steps first (20: the GPU clock ramps up after the host-side weight preparation)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 20 and at least 0.25 s of them; the GPU clock ramps up "
+                         "after the host-side weight preparation, over longer than 20 steps of a small layer take)")
     ap.add_argument("--config", default="ffn_up_720p")
     ap.add_argument("--cube", default=None, help="t,h,w (default: the config's first cube)")
     ap.add_argument("--x-seed", type=int, default=None)
@@ -83,6 +85,22 @@ def parse():
     return ap.parse_args()
 
 
+def warm_up(step, warmup):
+    """Untimed steps before the timed ones: `warmup` of them when given, else
+    at least 20 and at least 0.25 s of them.  Returns the number run."""
+    import time
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while (n < warmup) if warmup is not None else (n < 20 or time.perf_counter() - t0 < 0.25):
+        step()
+        n += 1
+        if warmup is None and n % 10 == 0:
+            torch.cuda.synchronize()            # the wall clock then follows the GPU
+    torch.cuda.synchronize()
+    return n
+
+
 def time_steps(dq, weights, x, qa, y, stream, steps, warmup):
     """Mean ms per step over `steps` timed steps, each one dq_linear call
     (activation pass, core term, delta term), with HIP events on the launch
@@ -94,9 +112,7 @@ def time_steps(dq, weights, x, qa, y, stream, steps, warmup):
     import torch
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    for _ in range(warmup):
-        dq.dq_linear(weights, x, qa, y, stream)
-    torch.cuda.synchronize()
+    warmed = warm_up(lambda: dq.dq_linear(weights, x, qa, y, stream), warmup)
     start, end = ev(), ev()
     start.record(stream)
     for _ in range(steps):
@@ -119,7 +135,7 @@ def time_steps(dq, weights, x, qa, y, stream, steps, warmup):
     q_ms = float(np.mean([a.elapsed_time(b) for a, b, c, d in marks]))
     c_ms = float(np.mean([b.elapsed_time(c) for a, b, c, d in marks]))
     d_ms = float(np.mean([c.elapsed_time(d) for a, b, c, d in marks]))
-    return ms_step, q_ms, c_ms, d_ms
+    return ms_step, q_ms, c_ms, d_ms, warmed
 
 
 def time_fused(dq, weights, qa, y, stream, steps):
@@ -188,7 +204,7 @@ def sweep(args, cfg, dq, torch):
     for cube in cfg.cubes:
         qa = dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + tuple(cube), core_group=args.core_group, core_bits=args.core_bits)
         timing = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
-        print(json.dumps(shape_record(cfg, cube, *timing, core_bits=args.core_bits)), flush=True)
+        print(json.dumps(shape_record(cfg, cube, *timing[:4], core_bits=args.core_bits)), flush=True)
         torch.cuda.synchronize()
         del qa                      # frees the cube shape's buffers
 
@@ -245,7 +261,7 @@ def schedule(args, cfg, dq, torch):
     qas = [dq.dq_qact_create(weights, (cfg.T, cfg.H, cfg.W) + s, core_group=args.core_group, core_bits=args.core_bits) for s in SCHEDULE_SHAPES]
     recs = []
     for s, qa in zip(SCHEDULE_SHAPES, qas):
-        recs.append(shape_record(cfg, s, *time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup),
+        recs.append(shape_record(cfg, s, *time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)[:4],
                                  core_bits=args.core_bits))
         print(json.dumps(recs[-1]), flush=True)
     n = args.denoise_steps
@@ -293,9 +309,7 @@ def bench_text(args, cfg, dq, torch):
     y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    for _ in range(args.warmup):
-        dq.dq_linear6(weights, x, act, y, stream)
-    torch.cuda.synchronize()
+    warmed = warm_up(lambda: dq.dq_linear6(weights, x, act, y, stream), args.warmup)
     start, end = ev(), ev()
     marks = []
     start.record(stream)
@@ -319,7 +333,7 @@ def bench_text(args, cfg, dq, torch):
     out = {
         "metric": "effective TOPS of the 6-bit text-token layer (W6A6 + low rank)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": fmt,
+        "warmup": warmed, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": fmt,
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: X {N}x{Ci} ({cfg.prompts} contexts of {cfg.ctx} text tokens) {cfg.dtype} "
                                f"-> Y {N}x{Co} fp32, {fmt}, rank {r}", "tokens": N, "Ci": Ci, "Co": Co, "rank": r},
@@ -351,9 +365,7 @@ def bench_orbit(args, cfg, dq, torch):
     y = torch.empty(cfg.N, cfg.Co, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    for _ in range(args.warmup):
-        dq.dq_orbit_linear(o, x, act, y, stream)
-    torch.cuda.synchronize()
+    warmed = warm_up(lambda: dq.dq_orbit_linear(o, x, act, y, stream), args.warmup)
     start, end = ev(), ev()
     marks = []
     start.record(stream)
@@ -376,7 +388,7 @@ def bench_orbit(args, cfg, dq, torch):
     print(json.dumps({
         "metric": "effective TOPS of the rotated-basis W4A4 layer (RPBH + Lloyd-Max codebook)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16 (decoded levels)",
+        "warmup": warmed, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16 (decoded levels)",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: X {N}x{Ci} {cfg.dtype} -> Y {N}x{Co} fp32, W{args.orbit_bits}A{args.orbit_bits} "
                                f"Lloyd-Max, blocks of 256", "tokens": N, "Ci": Ci, "Co": Co},
@@ -457,7 +469,7 @@ def main():
 
     # timed steps (activation pass, core term, delta term: dq_linear's work);
     # per-phase events on the launch stream
-    ms_step, q_ms, c_ms, d_ms = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
+    ms_step, q_ms, c_ms, d_ms, warmed = time_steps(dq, weights, x, qa, y, stream, args.steps, args.warmup)
     fused_ms = time_fused(dq, weights, qa, y, stream, args.steps)
     form = dq.dq_forward_form(weights, qa)          # the form dq_linear's forward takes for this layer
     ctype = "bf16" if args.core_bits == 16 else f"fp{args.core_bits}"      # the core GEMM's input type
@@ -512,7 +524,7 @@ def main():
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmed,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
