@@ -147,7 +147,7 @@ bool fused_applies(const dq_weights* w, const dq_qact* q, const float* y) {
 // The form the whole forward takes: the one-kernel form where it applies and
 // the layer has at most 16 rounds of 256 x 256 tiles per CU, else the two
 // kernels.  Measured with 4-token cubes on MI355X (one-kernel time over
-// two-kernel time): Wan 1.3B projection, 3 rounds, 0.77; 14B attention
+// two-kernel time): Wan 1.3B projection, 3 rounds, 0.72-0.77; 14B attention
 // projection, 9.5 rounds, 0.95; 720p FFN down, 23.6 rounds, 1.02; 720p FFN up,
 // 63.7 rounds, 1.03.  The two-kernel form's fixed costs (the core GEMM's
 // launch and partly filled last round, the per-cube term's round trip) weigh
